@@ -1,0 +1,33 @@
+"""CPU oracle for the CompactAttention chunked-prefill hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import or call anything in this package.
+The product path (the HIP library and its Python binding) never does, and
+this package imports nothing from it: the two share no code, only the seeded
+inputs of the ``gen`` package.
+
+Contents (each function cites the passage it follows):
+
+* ``union_tables_ref``   -- Block-Union KV selection: Q-block union, then
+  intra-group union, giving the minimal coverage-preserving per-group block
+  table T[b,g] and its length.  Pinned by brute force, a hand-worked fixture,
+  set invariants and special cases.
+* ``chunk_attention_ref`` -- softmax attention of a chunk's queries over the
+  keys of the blocks in T[b,g], causal inside the current chunk.  Pinned by
+  torch's SDPA on the dense special case, brute-force loops, closed forms
+  (K=0, one-hot V, V=1, single admissible key), shift invariance and the
+  empty-set convention.
+* ``chunk_attention_dense_masked_ref`` -- the same result computed as dense
+  attention over all cached keys with a -inf mask (second formulation).
+* ``tables_to_csr_ref`` -- the (kv_indptr, kv_indices) view of the tables.
+
+Float work is float64 throughout; outputs are float32.
+"""
+from .union_ref import union_tables_ref, tables_to_csr_ref  # noqa: F401
+from .attention_ref import (  # noqa: F401
+    BLOCK,
+    admissible_keys,
+    chunk_attention_dense_masked_ref,
+    chunk_attention_ref,
+    chunk_attention_rows_ref,
+)
