@@ -1,0 +1,146 @@
+"""CompactAttention chunked-prefill hot path for MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libcompact_attn.so``
+(``include/compact_attn.h``): argument checks and marshalling only.  Every
+step of the path runs in the library's HIP kernels; torch supplies device
+memory and the current stream.
+
+    T, lens = build_union_tables(mask, H_kv, n_q_blocks, n_kv_blocks)
+    O       = chunk_attention(q, k_cache, v_cache, T, lens, prior_len, chunk_len)
+
+Selection (Block-Union KV tables) and execution (zero-copy paged attention over
+a KV-head-major cache) are separate calls, as in the method.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import CA_BLOCK, CA_MAX_BATCH, CompactAttnError  # noqa: F401
+
+__all__ = ["build_union_tables", "chunk_attention", "tables_to_csr", "CompactAttnError",
+           "library_path"]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _stream_ptr(stream: Optional[torch.cuda.Stream]) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _need_cuda(name: str, t: torch.Tensor, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (cuda) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _host_ints(name: str, vals: Sequence[int], B: int):
+    vals = [int(v) for v in (vals.tolist() if hasattr(vals, "tolist") else vals)]
+    if len(vals) != B:
+        raise ValueError(f"{name} must have {B} entries")
+    return _lib.int_array(vals)
+
+
+def build_union_tables(mask: torch.Tensor, H_kv: int, n_q_blocks: Sequence[int],
+                       n_kv_blocks: Sequence[int], T: Optional[torch.Tensor] = None,
+                       lens: Optional[torch.Tensor] = None,
+                       stream: Optional[torch.cuda.Stream] = None
+                       ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Block-Union KV selection: mask uint8 [B, H_q, NQ_max, NKB_max] (device) ->
+    (T int32 [B, H_kv, NKB_max] ascending, -1 padded; lens int32 [B, H_kv])."""
+    _need_cuda("mask", mask, torch.uint8)
+    if mask.dim() != 4:
+        raise ValueError("mask must be [B, H_q, NQ_max, NKB_max]")
+    B, H_q, NQ_max, NKB_max = mask.shape
+    if H_kv < 1 or H_q % H_kv:
+        raise ValueError("H_q must be a positive multiple of H_kv")
+    if T is None:
+        T = torch.empty((B, H_kv, NKB_max), dtype=torch.int32, device=mask.device)
+    if lens is None:
+        lens = torch.empty((B, H_kv), dtype=torch.int32, device=mask.device)
+    _need_cuda("T", T, torch.int32)
+    _need_cuda("lens", lens, torch.int32)
+    if tuple(T.shape) != (B, H_kv, NKB_max) or tuple(lens.shape) != (B, H_kv):
+        raise ValueError("T / lens have the wrong shape")
+    st = _lib.lib().ca_build_union_tables(
+        mask.data_ptr(), B, H_q, H_kv, NQ_max, NKB_max, _host_ints("n_q_blocks", n_q_blocks, B),
+        _host_ints("n_kv_blocks", n_kv_blocks, B), T.data_ptr(), lens.data_ptr(),
+        _stream_ptr(stream))
+    _lib.check(st, "ca_build_union_tables")
+    return T, lens
+
+
+def chunk_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    T: torch.Tensor, lens: torch.Tensor, prior_len: Sequence[int],
+                    chunk_len: Sequence[int], scale: Optional[float] = None,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    return_lse: bool = False, stream: Optional[torch.cuda.Stream] = None):
+    """Zero-copy paged chunk attention.
+
+    q [B, H_q, C_max, D] and k_cache/v_cache [B, H_kv, L, D] (bf16 or fp32, device);
+    T/lens from ``build_union_tables``; prior_len/chunk_len host ints per sequence.
+    Returns O [B, H_q, C_max, D] (and lse fp32 [B, H_q, C_max] if ``return_lse``).
+    """
+    _need_cuda("q", q)
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q must be bfloat16 or float32")
+    _need_cuda("k_cache", k_cache, q.dtype)
+    _need_cuda("v_cache", v_cache, q.dtype)
+    _need_cuda("T", T, torch.int32)
+    _need_cuda("lens", lens, torch.int32)
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B,H_q,C_max,D], caches [B,H_kv,L,D]")
+    B, H_q, C_max, D = q.shape
+    Bk, H_kv, L, Dk = k_cache.shape
+    if Bk != B or Dk != D:
+        raise ValueError("cache batch / head dim do not match q")
+    if T.dim() != 3 or tuple(T.shape[:2]) != (B, H_kv) or tuple(lens.shape) != (B, H_kv):
+        raise ValueError("T must be [B, H_kv, NKB_max] and lens [B, H_kv]")
+    NKB_max = T.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _need_cuda("out", out, q.dtype)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H_q, C_max), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need_cuda("lse", lse, torch.float32)
+        if tuple(lse.shape) != (B, H_q, C_max):
+            raise ValueError("lse must be [B, H_q, C_max]")
+    dt = _lib.CA_BF16 if q.dtype == torch.bfloat16 else _lib.CA_F32
+    st = _lib.lib().ca_chunk_attention(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), T.data_ptr(), lens.data_ptr(),
+        NKB_max, _host_ints("prior_len", prior_len, B), _host_ints("chunk_len", chunk_len, B),
+        B, H_q, H_kv, C_max, L, D, CA_BLOCK, float(scale), dt, out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, _stream_ptr(stream))
+    _lib.check(st, "ca_chunk_attention")
+    return (out, lse) if return_lse else out
+
+
+def tables_to_csr(T: torch.Tensor, lens: torch.Tensor, L: int,
+                  stream: Optional[torch.cuda.Stream] = None):
+    """Paged-metadata view: (kv_indptr int32 [B*H_kv+1], kv_indices int32
+    [B*H_kv*NKB_max], of which the first kv_indptr[-1] entries are valid)."""
+    _need_cuda("T", T, torch.int32)
+    _need_cuda("lens", lens, torch.int32)
+    B, H_kv, NKB_max = T.shape
+    indptr = torch.empty(B * H_kv + 1, dtype=torch.int32, device=T.device)
+    indices = torch.empty(B * H_kv * NKB_max, dtype=torch.int32, device=T.device)
+    st = _lib.lib().ca_tables_to_csr(T.data_ptr(), lens.data_ptr(), B, H_kv, NKB_max, int(L),
+                                     indptr.data_ptr(), indices.data_ptr(), _stream_ptr(stream))
+    _lib.check(st, "ca_tables_to_csr")
+    return indptr, indices

@@ -1,0 +1,86 @@
+"""ctypes loader for libcompact_attn.so (the HIP library built in-tree).
+
+There is no fallback: if the library is missing or fails to load, every call
+raises.  Build it with ``python -m chunked_prefill_sparse_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcompact_attn.so")
+
+CA_OK = 0
+CA_F32 = 0
+CA_BF16 = 1
+CA_BLOCK = 64
+CA_MAX_BATCH = 128
+
+EXPORTED = (
+    "ca_build_union_tables",
+    "ca_chunk_attention",
+    "ca_tables_to_csr",
+    "ca_status_string",
+    "ca_last_hip_error",
+)
+
+_lock = threading.Lock()
+_lib = None
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+def _declare(lib):
+    lib.ca_build_union_tables.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _i32p, _i32p,
+                                          _vp, _vp, _vp]
+    lib.ca_build_union_tables.restype = _i32
+    lib.ca_chunk_attention.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32p, _i32p, _i32, _i32,
+                                       _i32, _i32, _i64, _i32, _i32, ctypes.c_float, _i32, _vp,
+                                       _vp, _vp]
+    lib.ca_chunk_attention.restype = _i32
+    lib.ca_tables_to_csr.argtypes = [_vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _vp]
+    lib.ca_tables_to_csr.restype = _i32
+    lib.ca_status_string.argtypes = [_i32]
+    lib.ca_status_string.restype = ctypes.c_char_p
+    lib.ca_last_hip_error.argtypes = []
+    lib.ca_last_hip_error.restype = ctypes.c_char_p
+
+
+def lib():
+    """The loaded library (loaded once).  Raises RuntimeError if it is not built."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(
+                        f"{LIB_PATH} is missing: build it with "
+                        "`python -m chunked_prefill_sparse_amd.build` (hipcc, gfx950)")
+                handle = ctypes.CDLL(LIB_PATH)
+                _declare(handle)
+                _lib = handle
+    return _lib
+
+
+class CompactAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        l_ = lib()
+        msg = l_.ca_status_string(status).decode()
+        if status == 5:
+            msg += f" [{l_.ca_last_hip_error().decode()}]"
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+
+
+def check(status: int, where: str) -> None:
+    if status != CA_OK:
+        raise CompactAttnError(status, where)
+
+
+def int_array(values):
+    arr = (ctypes.c_int32 * len(values))(*[int(v) for v in values])
+    return arr

@@ -1,0 +1,144 @@
+// C ABI of the CompactAttention chunked-prefill path: host-side validation,
+// scheduling metadata and kernel launches.  The library allocates nothing and
+// keeps no state beyond a per-thread copy of the last HIP error text.
+
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <numeric>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+ca_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return CA_OK;
+  snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s (%d)", hipGetErrorString(e),
+           static_cast<int>(e));
+  return CA_ERR_HIP;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+constexpr int kMaxUnionBlocks = 1 << 19;  // NKB_max bound: bitmap fits 64 KiB of LDS
+
+}  // namespace
+
+extern "C" {
+
+CA_EXPORT const char* ca_status_string(ca_status s) {
+  switch (s) {
+    case CA_OK: return "CA_OK";
+    case CA_ERR_NULL: return "CA_ERR_NULL: a required pointer is NULL";
+    case CA_ERR_SHAPE: return "CA_ERR_SHAPE: sizes inconsistent or out of range";
+    case CA_ERR_DTYPE: return "CA_ERR_DTYPE: unknown element type";
+    case CA_ERR_UNSUPPORTED: return "CA_ERR_UNSUPPORTED: request not supported by this build";
+    case CA_ERR_HIP: return "CA_ERR_HIP: the HIP runtime reported an error";
+  }
+  return "unknown ca_status";
+}
+
+CA_EXPORT const char* ca_last_hip_error(void) { return g_last_hip_error; }
+
+CA_EXPORT ca_status ca_build_union_tables(const uint8_t* mask, int B, int H_q, int H_kv,
+                                          int NQ_max, int NKB_max, const int32_t* n_q_blocks,
+                                          const int32_t* n_kv_blocks, int32_t* T, int32_t* len,
+                                          hipStream_t stream) {
+  if (!mask || !n_q_blocks || !n_kv_blocks || !T || !len) return CA_ERR_NULL;
+  if (B < 1 || B > CA_MAX_BATCH || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || NQ_max < 1 ||
+      NKB_max < 1 || NKB_max > kMaxUnionBlocks)
+    return CA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H_kv > (1 << 30)) return CA_ERR_SHAPE;
+  ca::UnionExtents ext;
+  memset(&ext, 0, sizeof(ext));
+  for (int b = 0; b < B; ++b) {
+    if (n_q_blocks[b] < 0 || n_q_blocks[b] > NQ_max || n_kv_blocks[b] < 0 ||
+        n_kv_blocks[b] > NKB_max)
+      return CA_ERR_SHAPE;
+    ext.nq[b] = n_q_blocks[b];
+    ext.nkb[b] = n_kv_blocks[b];
+  }
+  return hip_status(
+      ca::launch_union_tables(mask, B, H_q, H_kv, NQ_max, NKB_max, ext, T, len, stream));
+}
+
+CA_EXPORT ca_status ca_tables_to_csr(const int32_t* T, const int32_t* len, int B, int H_kv,
+                                     int NKB_max, int64_t L, int32_t* kv_indptr,
+                                     int32_t* kv_indices, hipStream_t stream) {
+  if (!T || !len || !kv_indptr || !kv_indices) return CA_ERR_NULL;
+  if (B < 1 || B > CA_MAX_BATCH || H_kv < 1 || NKB_max < 1 || L < CA_BLOCK || L % CA_BLOCK != 0)
+    return CA_ERR_SHAPE;
+  const int64_t pages = L / CA_BLOCK;
+  const int64_t n_bg = static_cast<int64_t>(B) * H_kv;
+  // page ids and entry counts must fit int32
+  if (n_bg * pages > INT32_MAX || n_bg * NKB_max > INT32_MAX || NKB_max > pages)
+    return CA_ERR_SHAPE;
+  return hip_status(ca::launch_tables_to_csr(T, len, static_cast<int>(n_bg), NKB_max, pages,
+                                             kv_indptr, kv_indices, stream));
+}
+
+CA_EXPORT ca_status ca_chunk_attention(const void* Q, const void* K_cache, const void* V_cache,
+                                       const int32_t* T, const int32_t* len, int NKB_max,
+                                       const int32_t* prior_len, const int32_t* chunk_len,
+                                       int B, int H_q, int H_kv, int C_max, int64_t L, int D,
+                                       int block, float scale, ca_dtype dtype, void* O,
+                                       float* lse, hipStream_t stream) {
+  if (!Q || !K_cache || !V_cache || !T || !len || !prior_len || !chunk_len || !O)
+    return CA_ERR_NULL;
+  if (dtype != CA_F32 && dtype != CA_BF16) return CA_ERR_DTYPE;
+  if (B < 1 || B > CA_MAX_BATCH || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || C_max < 1 ||
+      L < 1 || NKB_max < 1 || !(scale > 0.f) || !isfinite(scale))
+    return CA_ERR_SHAPE;
+  if (block != CA_BLOCK || (D != 64 && D != 128)) return CA_ERR_UNSUPPORTED;
+  if (!aligned16(Q) || !aligned16(K_cache) || !aligned16(V_cache) || !aligned16(O) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+    return CA_ERR_UNSUPPORTED;
+  ca::SeqInfo seq;
+  memset(&seq, 0, sizeof(seq));
+  int64_t work[CA_MAX_BATCH];
+  for (int b = 0; b < B; ++b) {
+    const int64_t P = prior_len[b], C = chunk_len[b];
+    if (P < 0 || C < 0 || C > C_max || P + C > L || P + C > static_cast<int64_t>(NKB_max) * CA_BLOCK)
+      return CA_ERR_SHAPE;
+    if (P % CA_BLOCK != 0 || C % CA_BLOCK != 0) return CA_ERR_UNSUPPORTED;
+    seq.prior[b] = static_cast<int32_t>(P);
+    seq.chunk[b] = static_cast<int32_t>(C);
+    work[b] = (P + C) * C;  // dense upper bound of the sequence's attention work
+  }
+  int order[CA_MAX_BATCH];
+  std::iota(order, order + B, 0);
+  std::stable_sort(order, order + B, [&](int a, int c) { return work[a] > work[c]; });
+  for (int r = 0; r < B; ++r) seq.order[r] = order[r];
+
+  ca::AttnParams p;
+  p.H_q = H_q;
+  p.H_kv = H_kv;
+  p.G = H_q / H_kv;
+  p.C_max = C_max;
+  p.L = L;
+  p.NKB_max = NKB_max;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const int64_t n_bg = static_cast<int64_t>(B) * H_kv;
+  if (dtype == CA_BF16) {
+    const int64_t n_pb = (C_max + 31) / 32;
+    p.n_t = static_cast<int>((p.G * n_pb + 3) / 4);
+    p.xcd = (n_bg % 8 == 0) ? 1 : 0;
+    if (n_bg * p.n_t > INT32_MAX) return CA_ERR_SHAPE;
+    return hip_status(ca::launch_chunk_attn_bf16(Q, K_cache, V_cache, T, len, O, lse, B, D, p,
+                                                 seq, stream));
+  }
+  p.n_t = 0;
+  p.xcd = 0;
+  if (static_cast<int64_t>(B) * H_q * ((C_max + 63) / 64) > INT32_MAX) return CA_ERR_SHAPE;
+  return hip_status(ca::launch_chunk_attn_f32(
+      static_cast<const float*>(Q), static_cast<const float*>(K_cache),
+      static_cast<const float*>(V_cache), T, len, static_cast<float*>(O), lse, B, D, p, seq,
+      stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+// Zero-copy paged chunk attention, fp32 on the vector ALUs.
+//
+// Same contract as the bf16 path (CompactAttention, execution stage: the
+// block table drives a paged dense attention that reads the selected blocks
+// in place from the KV-head-major cache), for fp32 inputs, where fp32
+// arithmetic is kept end to end.  It serves small chunks where launch latency,
+// not arithmetic, sets the time, so it favours simplicity: a workgroup of 128
+// threads owns 64 consecutive query rows of one head, two threads per row,
+// each thread holding half of the row's q and output accumulator.  Each
+// selected block's K and V rows are staged in LDS (coalesced 16-byte loads)
+// and read back as broadcasts.
+
+#include "kernels.hpp"
+
+namespace ca {
+namespace {
+
+constexpr int kBlk = 64;
+constexpr int kThreadsF = 128;
+constexpr int kRowsF = 64;
+
+template <int D>
+__global__ __launch_bounds__(kThreadsF) void chunk_attn_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const int32_t* __restrict__ T, const int32_t* __restrict__ len, float* __restrict__ O,
+    float* __restrict__ lse, AttnParams p, SeqInfo seq, int n_tiles) {
+  constexpr int DH = D / 2;
+  __shared__ __attribute__((aligned(16))) float Ks[kBlk * D];
+  __shared__ __attribute__((aligned(16))) float Vs[kBlk * D];
+
+  const int tid = threadIdx.x;
+  const int wg = blockIdx.x;
+  const int bh = wg / n_tiles;
+  const int tile = wg - bh * n_tiles;
+  const int rank = bh / p.H_q;
+  const int h = bh - rank * p.H_q;
+  const int b = seq.order[rank];
+  const int g = h / p.G;
+  const int P = seq.prior[b];
+  const int C = seq.chunk[b];
+  const int bg = b * p.H_kv + g;
+
+  const int row = tile * kRowsF + (tid >> 1);
+  const int half = tid & 1;
+  const bool row_in = row < p.C_max;
+  const bool row_live = row < C;
+  const size_t qo = ((static_cast<size_t>(b) * p.H_q + h) * p.C_max + row) * D + half * DH;
+
+  if (tile * kRowsF >= C) {  // padding rows only
+    if (row_in) {
+      for (int i = 0; i < DH; ++i) O[qo + i] = 0.f;
+      if (lse && half == 0) lse[qo / D] = -INFINITY;
+    }
+    return;
+  }
+  const int last_row = min(C, (tile + 1) * kRowsF) - 1;
+  const int kb_limit = (P + last_row) / kBlk;
+  const int nkb = (P + C + kBlk - 1) / kBlk;
+  int nT = len[bg];
+  nT = nT < 0 ? 0 : (nT > p.NKB_max ? p.NKB_max : nT);
+  const int32_t* Trow = T + static_cast<size_t>(bg) * p.NKB_max;
+  const size_t kv_base = static_cast<size_t>(bg) * static_cast<size_t>(p.L) * D;
+
+  float q[DH], acc[DH];
+#pragma unroll
+  for (int i = 0; i < DH; ++i) {
+    q[i] = row_in ? Q[qo + i] : 0.f;
+    acc[i] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int qpos = P + row;
+
+  for (int j = 0; j < nT; ++j) {
+    const int kb = Trow[j];
+    if (kb < 0 || kb >= nkb || kb > kb_limit) continue;
+    __syncthreads();  // previous block fully consumed
+    const float4* ks = reinterpret_cast<const float4*>(K + kv_base + static_cast<size_t>(kb) * kBlk * D);
+    const float4* vs = reinterpret_cast<const float4*>(V + kv_base + static_cast<size_t>(kb) * kBlk * D);
+    for (int i = tid; i < kBlk * D / 4; i += kThreadsF) {
+      reinterpret_cast<float4*>(Ks)[i] = ks[i];
+      reinterpret_cast<float4*>(Vs)[i] = vs[i];
+    }
+    __syncthreads();
+
+    float s[kBlk];
+    float mx = -INFINITY;
+#pragma unroll 4
+    for (int k = 0; k < kBlk; ++k) {
+      const float* kr = Ks + k * D + half * DH;
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < DH; ++i) part = __builtin_fmaf(q[i], kr[i], part);
+      float sc = part + __shfl_xor(part, 1);
+      if (kb * kBlk + k > qpos) sc = -INFINITY;
+      s[k] = sc;
+      mx = fmaxf(mx, sc);
+    }
+    if (mx == -INFINITY) continue;  // no admissible key of this block for this row
+    const float m_new = fmaxf(m, mx);
+    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * p.scale_log2);
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < DH; ++i) acc[i] *= alpha;
+    m = m_new;
+#pragma unroll 4
+    for (int k = 0; k < kBlk; ++k) {
+      const float w = __builtin_amdgcn_exp2f((s[k] - m) * p.scale_log2);
+      l += w;
+      const float* vr = Vs + k * D + half * DH;
+#pragma unroll
+      for (int i = 0; i < DH; ++i) acc[i] = __builtin_fmaf(w, vr[i], acc[i]);
+    }
+  }
+
+  if (!row_in) return;
+  const float inv = (row_live && l > 0.f) ? 1.f / l : 0.f;
+  for (int i = 0; i < DH; ++i) O[qo + i] = row_live ? acc[i] * inv : 0.f;
+  if (lse && half == 0)
+    lse[qo / D] = (row_live && l > 0.f) ? m * p.scale + __logf(l) : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_chunk_attn_f32(const float* Q, const float* K, const float* V,
+                                 const int32_t* T, const int32_t* len, float* O, float* lse,
+                                 int B, int D, const AttnParams& p, const SeqInfo& seq,
+                                 hipStream_t stream) {
+  const int n_tiles = (p.C_max + kRowsF - 1) / kRowsF;
+  const dim3 grid(B * p.H_q * n_tiles), block(kThreadsF);
+  if (D == 128)
+    hipLaunchKernelGGL(chunk_attn_f32_kernel<128>, grid, block, 0, stream, Q, K, V, T, len, O,
+                       lse, p, seq, n_tiles);
+  else
+    hipLaunchKernelGGL(chunk_attn_f32_kernel<64>, grid, block, 0, stream, Q, K, V, T, len, O,
+                       lse, p, seq, n_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace ca

@@ -1,0 +1,58 @@
+// Internal interface between the C-ABI layer (capi.hip) and the kernel files.
+// Everything here is validated by the caller before a launcher is invoked.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "compact_attn.h"
+
+namespace ca {
+
+// Per-sequence extents of the block mask (union builder).
+struct UnionExtents {
+  int32_t nq[CA_MAX_BATCH];   // Q-block rows of the chunk
+  int32_t nkb[CA_MAX_BATCH];  // KV blocks of the sequence (prior + chunk)
+};
+
+// Per-sequence lengths of one chunk-attention call, plus the order in which
+// sequences are handed to workgroups (longest first, so the longest work
+// starts earliest).
+struct SeqInfo {
+  int32_t prior[CA_MAX_BATCH];
+  int32_t chunk[CA_MAX_BATCH];
+  int32_t order[CA_MAX_BATCH];
+};
+
+struct AttnParams {
+  int H_q, H_kv, G;     // heads; G = H_q / H_kv query heads per KV head
+  int C_max;            // rows of Q/O per head
+  int64_t L;            // cache capacity (tokens) per (b, KV head)
+  int NKB_max;          // row length of T
+  float scale;          // softmax scale on Q.K
+  float scale_log2;     // scale * log2(e)
+  int n_t;              // workgroups per (b, g) pseudo-request
+  int xcd;              // 1: keep each pseudo-request's workgroups on one XCD
+};
+
+hipError_t launch_union_tables(const uint8_t* mask, int B, int H_q, int H_kv, int NQ_max,
+                               int NKB_max, const UnionExtents& ext, int32_t* T,
+                               int32_t* len, hipStream_t stream);
+
+hipError_t launch_tables_to_csr(const int32_t* T, const int32_t* len, int n_bg, int NKB_max,
+                                int64_t pages, int32_t* kv_indptr, int32_t* kv_indices,
+                                hipStream_t stream);
+
+// bf16 path on the matrix cores; D in {64, 128}.
+hipError_t launch_chunk_attn_bf16(const void* Q, const void* K, const void* V,
+                                  const int32_t* T, const int32_t* len, void* O, float* lse,
+                                  int B, int D, const AttnParams& p, const SeqInfo& seq,
+                                  hipStream_t stream);
+
+// fp32 path on the vector ALUs; D in {64, 128}.
+hipError_t launch_chunk_attn_f32(const float* Q, const float* K, const float* V,
+                                 const int32_t* T, const int32_t* len, float* O, float* lse,
+                                 int B, int D, const AttnParams& p, const SeqInfo& seq,
+                                 hipStream_t stream);
+
+}  // namespace ca

@@ -179,9 +179,11 @@ def make_custom(B: int, H_q: int, H_kv: int, D: int, prior: Sequence[int],
                 chunk: Sequence[int], dtype: str, seed: int,
                 cell_fn: Callable, C_max: Optional[int] = None, L: Optional[int] = None,
                 NKB_max: Optional[int] = None, name: str = "custom",
-                with_tensors: bool = True, triangle: bool = True) -> Workload:
+                with_tensors: bool = True, triangle: bool = True,
+                tensor_seed: Optional[int] = None) -> Workload:
     """General workload.  ``cell_fn(rng, b, H_q, nq, p_blk) -> uint8 [H_q, nq, p_blk]``
-    gives the prior-block cells of sequence b."""
+    gives the prior-block cells of sequence b.  Q/K/V come from ``tensor_seed``
+    (default: ``seed``), the mask from ``seed``."""
     prior = [int(p) for p in prior]
     chunk = [int(c) for c in chunk]
     C_max = int(C_max if C_max is not None else max(chunk))
@@ -191,7 +193,8 @@ def make_custom(B: int, H_q: int, H_kv: int, D: int, prior: Sequence[int],
     nkb = [-(-t // BLOCK) for t in tot]
     NKB_max = int(NKB_max if NKB_max is not None else max(nkb))
     if with_tensors:
-        rng_t = np.random.Generator(np.random.PCG64([seed, 0]))
+        ts = seed if tensor_seed is None else tensor_seed
+        rng_t = np.random.Generator(np.random.PCG64([ts, 0]))
         q, k, v = _draw_qkv(rng_t, B, H_q, H_kv, D, prior, chunk, C_max, L, dtype)
     else:
         q = k = v = None
@@ -231,9 +234,10 @@ def make_workload(name: str, variant: Optional[str] = None, density: Optional[fl
     ragged_b4     bf16, B=4, prior {16384, 32768, 65536, 126976} + 1024-token
                   chunk each, cache capacity 128000; per-sequence density
                   p_b ~ U[0.05, 0.3]; sink + last 4 prior blocks forced.
-    vslash_128k   bf16, 128K shape; vertical-slash mask of nominal density
-                  ``density`` with the heads of a group ``identical`` or
-                  ``independent``.
+    vslash_128k   bf16, 128K shape (Q/K/V of llama8b_128k); vertical-slash mask
+                  of nominal density ``density`` with the heads of a group
+                  ``identical`` or ``independent`` (mask seed
+                  5000 + 10 * density index + head mode).
     """
     if name == "tiny_f32":
         s = 1001 if seed is None else seed
@@ -298,8 +302,9 @@ def make_workload(name: str, variant: Optional[str] = None, density: Optional[fl
                     out[h] = _vertical_slash_head(rng, nq, pb, density)
             return out
 
+        # Q/K/V are those of llama8b_128k (seed 1003); only the mask varies per sweep point
         w = make_custom(1, 32, 8, 128, [129024], [2048], "bf16", s, fn, name=name,
-                        with_tensors=with_tensors)
+                        with_tensors=with_tensors, tensor_seed=1003)
         if density >= 1.0:
             w.mask[:] = 1
         w.meta.update(mask="vertical_slash", density=density, heads=heads)

@@ -1,0 +1,168 @@
+/*
+ * compact_attn.h -- C ABI of the CompactAttention chunked-prefill hot path
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (CompactAttention: Accelerating Chunked Prefill with Block-Union
+ * KV Selection; "Methodology" of the technical summaries and the abstract) has
+ * two stages, exported here as two separate calls so that *which* KV blocks
+ * are selected stays decoupled from *how* they are executed:
+ *
+ *   1. Selection.  A per-head 2D block mask (Q-block x KV-block) becomes one KV
+ *      block table per (sequence, KV head): the union over the chunk's Q-blocks
+ *      and over the query heads that share the KV head.  The table is the
+ *      minimal one that keeps every selected block.       -> ca_build_union_tables
+ *   2. Execution.  Dense attention for the chunk's queries reads the blocks in
+ *      the table in place from a KV-head-major [B, H_kv, L, D] cache, where each
+ *      (batch, KV head, block) triple is one contiguous region; nothing is
+ *      gathered or compacted.                               -> ca_chunk_attention
+ *
+ * The tables can also be handed over as paged metadata (kv_indptr /
+ * kv_indices), the form the pages name for the paged dense kernel.
+ *                                                          -> ca_tables_to_csr
+ *
+ * Conventions shared by every call
+ *   - Ownership: the caller allocates and frees every buffer.  The library
+ *     never allocates or frees device memory and keeps no mutable state.
+ *   - Device pointers point to device memory of the current HIP device.  Host
+ *     arrays are read during the call only.
+ *   - Asynchrony: every call enqueues its kernels on `stream` (0 = the null
+ *     stream) and returns without synchronising.  Argument errors are found
+ *     on the host before anything is enqueued; the return value then says
+ *     which, and no device memory is touched.
+ *   - Block size: 64 tokens for both the KV block and the Q-block.
+ *   - Errors: a call returns CA_OK or the first error found; see
+ *     ca_status_string.  CA_ERR_HIP means a HIP launch reported an error (the
+ *     HIP error string is available from ca_last_hip_error).
+ */
+#ifndef COMPACT_ATTN_H
+#define COMPACT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef CA_EXPORT
+#define CA_EXPORT __attribute__((visibility("default")))
+#endif
+
+#define CA_BLOCK 64      /* tokens per KV block and per Q-block */
+#define CA_MAX_BATCH 128 /* sequences per call */
+
+typedef enum {
+  CA_OK = 0,
+  CA_ERR_NULL = 1,        /* a required pointer is NULL */
+  CA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
+  CA_ERR_DTYPE = 3,       /* unknown element type */
+  CA_ERR_UNSUPPORTED = 4, /* valid request this build does not run (see each call) */
+  CA_ERR_HIP = 5          /* the HIP runtime reported an error */
+} ca_status;
+
+typedef enum { CA_F32 = 0, CA_BF16 = 1 } ca_dtype;
+
+/*
+ * ca_build_union_tables -- Block-Union KV selection (selection stage: Q-block
+ * union, then intra-group union, giving the minimal coverage-preserving
+ * per-group table T[b,g]).
+ *
+ *   T[b,g] = ascending { kb < n_kv_blocks[b] : some head h of group g and some
+ *            Q-block qb < n_q_blocks[b] have mask[b,h,qb,kb] != 0 }
+ *
+ * mask        device uint8 [B, H_q, NQ_max, NKB_max], row-major.  Any nonzero
+ *             byte selects.  Cells with qb >= n_q_blocks[b] or
+ *             kb >= n_kv_blocks[b] are ignored.
+ * B           1..CA_MAX_BATCH sequences.
+ * H_q, H_kv   query heads and KV heads; H_q % H_kv == 0.  Query head h belongs
+ *             to group h / (H_q / H_kv).
+ * NQ_max      Q-block rows per head in `mask` (>= 1).
+ * NKB_max     KV-block columns in `mask`, and the row length of T (1..524288).
+ * n_q_blocks  host int32 [B], 0 <= n_q_blocks[b] <= NQ_max.
+ * n_kv_blocks host int32 [B], 0 <= n_kv_blocks[b] <= NKB_max.
+ * T           device int32 [B, H_kv, NKB_max] (out): strictly ascending block
+ *             ids, then -1 up to NKB_max.
+ * len         device int32 [B, H_kv] (out): number of valid entries of T[b,g].
+ * Errors: CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_HIP.
+ */
+CA_EXPORT ca_status ca_build_union_tables(const uint8_t* mask, int B, int H_q, int H_kv, int NQ_max,
+                                int NKB_max, const int32_t* n_q_blocks,
+                                const int32_t* n_kv_blocks, int32_t* T, int32_t* len,
+                                hipStream_t stream);
+
+/*
+ * ca_chunk_attention -- zero-copy paged chunk attention (execution stage).
+ *
+ * For sequence b, query head h (group g = h / (H_q/H_kv)) and chunk row
+ * i < chunk_len[b] at absolute position p = prior_len[b] + i:
+ *
+ *   A    = { t : T[b,g,j] == t/64 for some j < len[b,g],  t <= p }
+ *   O    = softmax_{t in A}( scale * Q[b,h,i,:] . K[b,g,t,:] ) @ V[b,g,A,:]
+ *   lse  = log sum_{t in A} exp(scale * Q[b,h,i,:] . K[b,g,t,:])   (natural log)
+ *
+ * The chunk's own keys/values must already be in the cache at rows
+ * [prior_len[b], prior_len[b] + chunk_len[b]).  Key/value rows outside the
+ * blocks of T[b,g] are never read.  An empty A gives O = 0, lse = -inf; rows
+ * chunk_len[b] <= i < C_max give O = 0, lse = -inf.
+ *
+ * Q, O        device [B, H_q, C_max, D], element type `dtype`, row-major, 16-byte
+ *             aligned.  O is fully written.
+ * K_cache,    device [B, H_kv, L, D], element type `dtype`, KV-head-major,
+ * V_cache     16-byte aligned.
+ * T, len      device, as produced by ca_build_union_tables: T int32
+ *             [B, H_kv, NKB_max] with strictly ascending entries, len int32
+ *             [B, H_kv].  Entries outside [0, n_kv_blocks[b]) and len values
+ *             outside [0, NKB_max] are clamped away, never dereferenced.
+ * prior_len,  host int32 [B]: cached tokens before the chunk, and chunk tokens.
+ * chunk_len   Both multiples of 64 in this build (else CA_ERR_UNSUPPORTED);
+ *             0 <= chunk_len[b] <= C_max; prior_len[b] + chunk_len[b] <= L and
+ *             <= 64 * NKB_max.
+ * B           1..CA_MAX_BATCH.  H_q % H_kv == 0.
+ * D           head dim: 64 or 128 (else CA_ERR_UNSUPPORTED).
+ * block       must be 64 (else CA_ERR_UNSUPPORTED).
+ * scale       softmax scale applied to Q.K (1/sqrt(D) in the usual case); > 0.
+ * dtype       CA_BF16: bf16 in/out, fp32 accumulation on the matrix cores,
+ *             probabilities rounded to bf16 for the P.V product.
+ *             CA_F32:  fp32 in/out and fp32 arithmetic throughout.
+ * lse         device float [B, H_q, C_max] (out) or NULL.
+ * Errors: CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_DTYPE, CA_ERR_UNSUPPORTED, CA_ERR_HIP.
+ */
+CA_EXPORT ca_status ca_chunk_attention(const void* Q, const void* K_cache, const void* V_cache,
+                             const int32_t* T, const int32_t* len, int NKB_max,
+                             const int32_t* prior_len, const int32_t* chunk_len, int B,
+                             int H_q, int H_kv, int C_max, int64_t L, int D, int block,
+                             float scale, ca_dtype dtype, void* O, float* lse,
+                             hipStream_t stream);
+
+/*
+ * ca_tables_to_csr -- the paged-metadata view of the tables (execution stage:
+ * the tables travel to a paged dense kernel as kv_indptr / kv_indices).
+ * Pseudo-request u = b*H_kv + g.
+ *
+ *   kv_indptr[0] = 0, kv_indptr[u+1] = kv_indptr[u] + len[u]
+ *   kv_indices[kv_indptr[u] + j] = u * (L/64) + T[b,g,j]      (j < len[u])
+ *
+ * i.e. global page ids of the cache viewed as [B*H_kv*L/64, 64, D].
+ * T, len      device, as produced by ca_build_union_tables (len in [0, NKB_max]).
+ * L           cache capacity in tokens; a multiple of 64 (else CA_ERR_SHAPE).
+ * kv_indptr   device int32 [B*H_kv + 1] (out).
+ * kv_indices  device int32 with room for B*H_kv*NKB_max entries (out; only the
+ *             first kv_indptr[B*H_kv] are written).
+ * Errors: CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_HIP.
+ */
+CA_EXPORT ca_status ca_tables_to_csr(const int32_t* T, const int32_t* len, int B, int H_kv, int NKB_max,
+                           int64_t L, int32_t* kv_indptr, int32_t* kv_indices,
+                           hipStream_t stream);
+
+/* Human-readable name of a status code (static string; never NULL). */
+CA_EXPORT const char* ca_status_string(ca_status s);
+
+/* Text of the last HIP error seen by a call on this thread ("" if none). */
+CA_EXPORT const char* ca_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COMPACT_ATTN_H */

@@ -1,0 +1,262 @@
+"""GPU parity of zero-copy paged chunk attention (through the C ABI) against
+the float64 oracle.
+
+* Small shapes (several tiles, ragged tails, C_max padding, D = 64 and 128,
+  group sizes 1..8): every output element is compared.
+* Full-size workloads (32K and 128K LLaMA-8B-shaped chunks, the ragged batch,
+  the vertical-slash sweep): sampled output rows are compared one by one, and
+  properties that hold at any size are checked on the whole output.
+* Poison invariance: NaN in every unselected block and in the unused cache
+  tail must leave O bit-identical (the kernel reads only the listed blocks).
+* Closed forms: K = 0 with one-hot V gives exact per-block key counts; V = 1
+  gives 1.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import chunked_prefill_sparse_amd as ca
+from tests.gpu_util import (BF16_MAX_ABS, F32_MAX_ABS, LSE_ABS, Dev, compare_bf16,
+                            f32_arrays, oracle_full, oracle_rows, sample_rows, say, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def _bern(p):
+    return lambda rng, b, H, nq, pb: (rng.random((H, nq, pb)) < p).astype(np.uint8)
+
+
+def _run(w, return_lse=True):
+    d = Dev(w)
+    T, lens = d.tables()
+    out = d.attention(T, lens, return_lse=return_lse)
+    torch.cuda.synchronize()
+    return d, T, lens, out
+
+
+# ----------------------------------------------------------------------------- fp32
+
+
+def test_tiny_f32_full_parity():
+    w = gen.make_workload("tiny_f32")
+    say("tiny_f32 full parity")
+    _, _, _, (O, lse) = _run(w)
+    Or, lr = oracle_full(w)
+    err = np.abs(to_np(O) - Or).max()
+    say(f"  max-abs {err:.3e}")
+    assert err <= F32_MAX_ABS
+    np.testing.assert_allclose(to_np(lse), lr, rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("B,H_q,H_kv,D,prior,chunk,C_max", [
+    (2, 4, 2, 128, (512, 1024), (192, 128), 200),
+    (3, 2, 1, 64, (0, 64, 4096), (128, 64, 256), 256),
+])
+def test_f32_small_full_parity(B, H_q, H_kv, D, prior, chunk, C_max):
+    w = gen.make_custom(B, H_q, H_kv, D, prior, chunk, "f32", 11, _bern(0.3), C_max=C_max)
+    say(f"f32 B={B} H={H_q}/{H_kv} D={D} prior={prior} chunk={chunk}")
+    _, _, _, (O, lse) = _run(w)
+    Or, lr = oracle_full(w)
+    assert np.abs(to_np(O) - Or).max() <= F32_MAX_ABS
+    np.testing.assert_allclose(to_np(lse), lr, rtol=0, atol=1e-5)
+
+
+# ----------------------------------------------------------------------------- bf16 small
+
+
+SMALL_BF16 = [
+    # B, H_q, H_kv, D, prior, chunk, C_max
+    (1, 4, 1, 128, (1024,), (256,), 256),
+    (2, 8, 2, 128, (1024, 2048), (256, 128), 300),   # ragged chunk, C_max not a tile multiple
+    (2, 8, 2, 64, (2048, 0), (192, 64), 192),        # D = 64, a sequence with no prior
+    (1, 4, 4, 128, (640,), (320,), 320),             # G = 1
+    (1, 16, 2, 128, (512,), (128,), 128),            # G = 8
+    (2, 6, 2, 128, (256, 1536), (192, 256), 256),    # G = 3
+    (8, 8, 1, 128, [64 * i for i in range(8)], [64] * 8, 64),  # B*H_kv = 8: XCD mapping
+]
+
+
+@pytest.mark.parametrize("B,H_q,H_kv,D,prior,chunk,C_max", SMALL_BF16)
+def test_bf16_small_full_parity(B, H_q, H_kv, D, prior, chunk, C_max):
+    w = gen.make_custom(B, H_q, H_kv, D, list(prior), list(chunk), "bf16", 21, _bern(0.2),
+                        C_max=C_max)
+    say(f"bf16 B={B} H={H_q}/{H_kv} D={D} prior={prior} chunk={chunk} C_max={C_max}")
+    _, _, _, (O, lse) = _run(w)
+    Or, lr = oracle_full(w)
+    compare_bf16(to_np(O), Or, "O")
+    live = np.isfinite(lr)
+    assert np.array_equal(np.isfinite(to_np(lse)), live)
+    np.testing.assert_allclose(to_np(lse)[live], lr[live], rtol=0, atol=LSE_ABS)
+    for b in range(B):  # padding rows are exact zeros
+        assert np.all(to_np(O)[b, :, chunk[b]:] == 0)
+
+
+def test_bf16_dense_and_sparse_agree_on_dense_mask():
+    # the all-ones mask run is the dense baseline: same as a table listing every block
+    w = gen.make_custom(1, 8, 2, 128, [2048], [256], "bf16", 5, _bern(1.0))
+    d = Dev(w)
+    T, lens = d.tables()
+    nkb = w.n_kv_blocks[0]
+    Td = torch.full_like(T, -1)
+    Td[..., :nkb] = torch.arange(nkb, dtype=torch.int32, device="cuda")
+    ld = torch.full_like(lens, nkb)
+    O1 = d.attention(T, lens)
+    O2 = d.attention(Td, ld)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2)
+
+
+def test_bf16_deterministic_repeat():
+    w = gen.make_custom(2, 8, 2, 128, [1024, 512], [256, 128], "bf16", 9, _bern(0.3))
+    d = Dev(w)
+    T, lens = d.tables()
+    O1 = d.attention(T, lens).clone()
+    O2 = d.attention(T, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2)
+
+
+# ----------------------------------------------------------------------------- closed forms
+
+
+def test_bf16_closed_form_one_hot_block_counts():
+    # K = 0 makes every admissible key weigh exactly 1 (exp2(0)), so with
+    # V_t = one_hot(t // 64) the output is the exact share of admissible keys per
+    # block: it shows which blocks were read, including causal cut-offs.
+    w = gen.make_custom(1, 8, 2, 64, [2048], [512], "bf16", 4, _bern(0.2))
+    w.k.zero_()
+    w.v.zero_()
+    n_tok = w.prior[0] + w.chunk[0]
+    assert n_tok // 64 <= w.D
+    t = torch.arange(n_tok)
+    w.v[0, :, t, t // 64] = 1.0
+    _, _, _, (O, _) = _run(w)
+    Or, _ = oracle_full(w)
+    err = np.abs(to_np(O) - Or)
+    # bf16 output rounding of a share in (0, 1]: relative 2^-9
+    assert np.all(err <= np.abs(Or) * 2.0 ** -8 + 1e-7)
+    assert np.array_equal(to_np(O) != 0, Or != 0)
+
+
+def test_bf16_closed_form_constant_values():
+    w = gen.make_custom(1, 8, 2, 128, [4096], [256], "bf16", 6, _bern(0.3))
+    w.v.fill_(1.0)
+    _, _, _, (O, _) = _run(w)
+    # P is rounded to bf16 before P.V while the denominator sums unrounded
+    # probabilities: 1 within the rounding of the probabilities
+    np.testing.assert_allclose(to_np(O), 1.0, rtol=0, atol=4e-3)
+
+
+# ----------------------------------------------------------------------------- full sizes
+
+
+_WL = {}
+
+
+def _workload(name, **kw):
+    """Full-size workloads; the 128K variants share Q/K/V (seed 1003) and differ in mask."""
+    key = (name, tuple(sorted(kw.items())))
+    if key in _WL:
+        return _WL[key]
+    if name in ("llama8b_128k", "vslash_128k"):
+        base = _WL.get("base128")
+        if base is None:
+            base = gen.make_workload("llama8b_128k", variant="pairwise")
+            _WL.clear()
+            _WL["base128"] = base
+            _WL["base128_f32"] = f32_arrays(base)
+        w = gen.make_workload(name, with_tensors=False, **kw)
+        w.q, w.k, w.v = base.q, base.k, base.v
+        w.meta["arrays"] = _WL["base128_f32"]
+    else:
+        _WL.clear()
+        w = gen.make_workload(name, **kw)
+        w.meta["arrays"] = f32_arrays(w)
+    _WL[key] = w
+    return w
+
+
+FULL = [
+    ("llama8b_32k", {}),
+    ("llama8b_128k", dict(variant="pairwise")),
+    ("llama8b_128k", dict(variant="colshared")),
+    ("llama8b_128k", dict(variant="dense")),
+    ("vslash_128k", dict(density=0.02, heads="identical")),
+    ("vslash_128k", dict(density=0.1, heads="independent")),
+    ("vslash_128k", dict(density=0.5, heads="identical")),
+    ("ragged_b4", {}),
+]
+
+
+@pytest.mark.parametrize("name,kw", FULL)
+def test_full_size_sampled_parity(name, kw):
+    say(f"full-size {name} {kw}: generating")
+    w = _workload(name, **kw)
+    d = Dev(w)
+    T, lens = d.tables()
+    O, lse = d.attention(T, lens, return_lse=True)
+    torch.cuda.synchronize()
+    say(f"  union sum len {int(lens.sum())}")
+    rows = sample_rows(w, seed=zlib.crc32(repr((name, kw)).encode()) % 1000)
+    Or, lr = oracle_rows(w, rows, arrays=w.meta["arrays"])
+    r = torch.from_numpy(rows).cuda()
+    got = to_np(O[r[:, 0], r[:, 1], r[:, 2]])
+    compare_bf16(got, Or, f"{len(rows)} sampled rows")
+    np.testing.assert_allclose(to_np(lse[r[:, 0], r[:, 1], r[:, 2]]), lr, rtol=0, atol=LSE_ABS)
+    # whole-output properties: finite everywhere, padding rows zero, bounded by max|V|
+    assert bool(torch.isfinite(O).all())
+    assert float(O.abs().max()) <= float(d.v.abs().max())
+    for b in range(w.B):
+        assert bool((O[b, :, w.chunk[b]:] == 0).all())
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("llama8b_128k", dict(variant="colshared")),
+    ("ragged_b4", {}),
+])
+def test_full_size_poison_invariance(name, kw):
+    say(f"poison {name} {kw}")
+    w = _workload(name, **kw)
+    d = Dev(w)
+    T, lens = d.tables()
+    O = d.attention(T, lens)
+    nblk = w.L // 64 + 1
+    sel = torch.zeros((w.B, w.H_kv, nblk), dtype=torch.bool, device="cuda")
+    Tc = torch.where(T >= 0, T, torch.full_like(T, nblk - 1)).long()
+    sel.scatter_(2, Tc, True)
+    sel[..., nblk - 1] = False
+    tok = torch.arange(w.L, device="cuda")
+    keep = sel[:, :, tok // 64]
+    for b in range(w.B):
+        keep[b, :, w.prior[b] + w.chunk[b]:] = False
+    kp = d.k.clone()
+    vp = d.v.clone()
+    kp[~keep] = float("nan")
+    vp[~keep] = float("nan")
+    say(f"  poisoned {float((~keep).float().mean()):.3f} of the cache rows")
+    O2 = d.attention(T, lens, k=kp, v=vp)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2)
+    del kp, vp
+
+
+# ----------------------------------------------------------------------------- errors
+
+
+def test_binding_rejects_bad_arguments():
+    w = gen.make_custom(1, 4, 1, 128, [1024], [128], "bf16", 1, _bern(0.2))
+    d = Dev(w)
+    T, lens = d.tables()
+    with pytest.raises(ValueError):
+        ca.chunk_attention(d.q.float(), d.k, d.v, T, lens, w.prior, w.chunk)
+    with pytest.raises(ValueError):
+        ca.chunk_attention(d.q, d.k, d.v, T.cpu(), lens, w.prior, w.chunk)
+    with pytest.raises(ca.CompactAttnError) as e:
+        ca.chunk_attention(d.q, d.k, d.v, T, lens, [1000], w.chunk)
+    assert e.value.status == 4
+    with pytest.raises(ca.CompactAttnError) as e:
+        ca.chunk_attention(d.q, d.k, d.v, T, lens, [1024], [192])  # chunk > C_max
+    assert e.value.status == 2
