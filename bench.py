@@ -1,0 +1,334 @@
+#!/usr/bin/env python3
+"""Benchmark of the CompactAttention chunked-prefill hot path on one MI355X.
+
+One step = the whole path on one synthetic batch: Block-Union table build
+(ca_build_union_tables) + zero-copy chunk attention (ca_chunk_attention), on
+the 128K-context LLaMA-3.1-8B-shaped chunk: B=1, 32 query / 8 KV heads, D=128,
+129024 cached tokens + a 2048-token chunk, bf16, per-head mask = sink + last 8
+prior blocks + Bernoulli(0.05) per (head, Q-block, KV-block) cell.  The dense
+baseline (all-ones mask, the same kernel fed every block) and a column-shared
+mask variant (one draw per (head, KV-block)) are timed beside it.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+prints ONE JSON line.  ``value`` is the effective TFLOP/s of a whole step
+(algorithmic FLOPs: 4*D per admissible query/key pair over the selected
+blocks, causal triangle included).  Inputs are resident in HBM before timing.
+
+Profiling helpers (for rocprofv3 runs): ``--profile attn|union|copy`` runs only
+that kernel a few times (``copy`` = a plain device copy of known size, used to
+scale the HBM byte counters).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published)
+WORKLOAD = "llama8b_128k"
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "chunk_attn_bf16_llama8b_128k_pmc.txt")
+KERNEL_SRC = os.path.join(ROOT, "chunked_prefill_sparse_amd", "csrc", "chunk_attn_bf16.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------- work accounting
+
+
+def admissible_pairs(T: np.ndarray, lens: np.ndarray, prior, chunk, G: int) -> int:
+    """Number of (query, key) pairs the path must compute: for every query head
+    and chunk row i, the keys t <= prior+i of the blocks in T[b,g]."""
+    total = 0
+    for b in range(T.shape[0]):
+        P, C = int(prior[b]), int(chunk[b])
+        i = np.arange(C, dtype=np.int64)
+        for g in range(T.shape[1]):
+            blocks = T[b, g, :lens[b, g]].astype(np.int64)
+            start = blocks * 64
+            full = blocks[start + 63 <= P]  # prior blocks below every row: 64 keys each
+            pairs = full.size * 64 * C
+            part = start[start + 63 > P]
+            if part.size:
+                # keys start..start+63 (and < P+C) with t <= P+i
+                cnt = np.clip(P + i[None, :] - part[:, None] + 1, 0, 64)
+                cnt = np.minimum(cnt, np.clip(P + C - part[:, None], 0, 64))
+                pairs += int(cnt.sum())
+            total += pairs * G
+    return int(total)
+
+
+def algorithmic(w, T, lens):
+    pairs = admissible_pairs(T, lens, w.prior, w.chunk, w.G)
+    flops = 4 * w.D * pairs
+    esz = 2 if w.dtype == "bf16" else 4
+    kv = 2 * 64 * int(lens.sum()) * w.D * esz
+    qo = 2 * w.B * w.H_q * w.C_max * w.D * esz
+    meta = T.size * 4 + lens.size * 4
+    return flops, kv + qo + meta, pairs
+
+
+# --------------------------------------------------------------------------- timing
+
+
+def time_calls(fn, reps, stream):
+    """Per-call durations (ms) from HIP events recorded on the launch stream."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def pct(xs, q):
+    return float(np.percentile(np.asarray(xs), q))
+
+
+# --------------------------------------------------------------------------- cpu baseline
+
+
+def cpu_baseline(w, seconds_budget=20.0):
+    """The oracle as it stands, on a bounded sample of the same workload: the
+    union of the whole mask, then attention for every chunk row of the query
+    heads of one KV group after another until the time budget is spent, timed
+    on this host's cores."""
+    import gen
+    from oracle import chunk_attention_rows_ref, union_tables_ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    t0 = time.perf_counter()
+    T, ln = union_tables_ref(w.mask, w.H_kv, w.n_q_blocks, w.n_kv_blocks)
+    t_union = time.perf_counter() - t0
+    q, k, v = (gen.tensor_to_f32(x) for x in (w.q, w.k, w.v))
+    C, P = w.chunk[0], w.prior[0]
+    elapsed, flops, groups, rows_done = 0.0, 0, 0, 0
+    for g in range(w.H_kv):
+        if elapsed >= seconds_budget:
+            break
+        rows = np.array([(0, h, i) for h in range(g * w.G, (g + 1) * w.G) for i in range(C)],
+                        np.int64)
+        t0 = time.perf_counter()
+        chunk_attention_rows_ref(q, k, v, T, ln, w.prior, w.chunk, w.scale, rows)
+        elapsed += time.perf_counter() - t0
+        flops += 4 * w.D * admissible_pairs(T[:, g:g + 1], ln[:, g:g + 1], w.prior, w.chunk, w.G)
+        groups += 1
+        rows_done += rows.shape[0]
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"float64 NumPy oracle on {WORKLOAD}: union tables of the whole mask "
+                   f"({t_union:.2f} s), then attention for all {C} chunk rows of the {w.G} "
+                   f"query heads of {groups} of {w.H_kv} KV groups ({rows_done} rows) in "
+                   f"{elapsed:.1f} s; value = algorithmic FLOPs of those rows / their time"),
+        "host_cpus": os.cpu_count(),
+        "cpu_model": platform.processor() or platform.machine(),
+    }
+
+
+# --------------------------------------------------------------------------- main
+
+
+def stored_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
+    or None if absent or taken on a different kernel source."""
+    import hashlib
+    if not os.path.exists(PMC_SUMMARY):
+        return None, None
+    vals = {}
+    for line in open(PMC_SUMMARY):
+        if ":" in line and not line.startswith("#"):
+            k_, _, v_ = line.partition(":")
+            vals[k_.strip()] = v_.strip()
+    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    if vals.get("kernel_source_sha256_16") != src_hash:
+        return None, vals
+    try:
+        return float(vals["hbm_bytes_per_launch"]), vals
+    except (KeyError, ValueError):
+        return None, vals
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=50, help="per-kernel timed calls")
+    ap.add_argument("--profile", choices=["attn", "union", "copy"], default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import gen
+    import chunked_prefill_sparse_amd as ca
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    if args.profile == "copy":
+        n = 1 << 30  # 1 GiB
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for i in range(3):
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            log(f"copy {i}: {n} bytes")
+        return
+
+    log(f"generating {WORKLOAD} (pairwise mask) ...")
+    w = gen.make_workload(WORKLOAD, variant="pairwise")
+    variants = {"pairwise": w}
+    for vname in ("dense", "colshared"):
+        wv = gen.make_workload(WORKLOAD, variant=vname, with_tensors=False)
+        wv.q, wv.k, wv.v = w.q, w.k, w.v
+        variants[vname] = wv
+    q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
+    out = torch.empty_like(q)
+    masks = {n_: torch.from_numpy(x.mask).to(dev) for n_, x in variants.items()}
+    torch.cuda.synchronize()
+
+    def tables(name):
+        x = variants[name]
+        return ca.build_union_tables(masks[name], x.H_kv, x.n_q_blocks, x.n_kv_blocks)
+
+    def attn(T, lens):
+        return ca.chunk_attention(q, k, v, T, lens, w.prior, w.chunk, w.scale, out=out)
+
+    if args.profile in ("attn", "union"):
+        T, lens = tables("pairwise")
+        for i in range(max(args.steps, 1)):
+            if args.profile == "attn":
+                attn(T, lens)
+            else:
+                tables("pairwise")
+            torch.cuda.synchronize()
+            log(f"{args.profile} launch {i}")
+        return
+
+    results = {}
+    for name in ("pairwise", "dense", "colshared"):
+        x = variants[name]
+        T, lens = tables(name)
+        torch.cuda.synchronize()
+        Th, lh = T.cpu().numpy(), lens.cpu().numpy()
+        flops, bytes_alg, pairs = algorithmic(x, Th, lh)
+
+        def step():
+            T_, l_ = tables(name)
+            attn(T_, l_)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        attn_ms = time_calls(lambda: attn(T, lens), args.reps, stream)
+        union_ms = time_calls(lambda: tables(name), args.reps, stream)
+        a_med = statistics.median(attn_ms)
+        a_mean = float(np.mean(attn_ms))
+        per_head_union = float(x.mask[:, :, :, :].any(axis=2).sum(axis=-1).mean())
+        results[name] = dict(
+            ms_per_step=ms_step,
+            attn_ms_median=a_med, attn_ms_mean=a_mean,
+            attn_ms_p10=pct(attn_ms, 10), attn_ms_p90=pct(attn_ms, 90),
+            union_us_median=statistics.median(union_ms) * 1e3,
+            flops=flops, bytes_alg=bytes_alg, pairs=pairs,
+            eff_tflops_step=flops / (ms_step * 1e-3) / 1e12,
+            eff_tflops_attn=flops / (a_med * 1e-3) / 1e12,
+            mfma_frac_attn=flops / (a_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            union_blocks_sum=int(lh.sum()), union_blocks_mean=float(lh.mean()),
+            per_head_qunion_blocks_mean=per_head_union,
+        )
+        log(f"{name}: step {ms_step:.3f} ms, attention {a_med:.3f} ms "
+            f"({results[name]['eff_tflops_attn']:.0f} TFLOP/s), union "
+            f"{results[name]['union_us_median']:.1f} us, mean len {lh.mean():.0f}")
+    for name in results:
+        results[name]["x_vs_dense_attn"] = results["dense"]["attn_ms_median"] / results[name]["attn_ms_median"]
+        results[name]["x_vs_dense_step"] = results["dense"]["ms_per_step"] / results[name]["ms_per_step"]
+
+    main_r = results["pairwise"]
+    traffic, pmc = stored_traffic()
+    achieved = main_r["flops"] / (main_r["attn_ms_mean"] * 1e-3) / 1e12
+    roofline = {
+        "bound": "mfma",
+        "kernel": "chunk_attn_bf16_kernel<128>",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic,
+        "alg_bytes": main_r["bytes_alg"],
+        "hbm_alg_GBps": round(main_r["bytes_alg"] / (main_r["attn_ms_mean"] * 1e-3) / 1e9, 1),
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    line = {
+        "metric": "chunk attention eff. TFLOP/s at 128K ctx, LLaMA-8B GQA (union build + attention per step); x vs dense",
+        "value": round(main_r["eff_tflops_step"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama8b_128k: B=1, H_q=32, H_kv=8, D=128, 129024 prior + 2048-token chunk, "
+                        "block 64, mask sink + last 8 prior blocks + Bernoulli(0.05) per "
+                        "(head, Q-block, KV-block)",
+            "global_batch": 1, "seq_len": 131072, "parallelism": "none (1 GPU)",
+        },
+        "attn_ms": round(main_r["attn_ms_median"], 4),
+        "union_us": round(main_r["union_us_median"], 2),
+        "x_vs_dense": round(main_r["x_vs_dense_step"], 4),
+        "variants": {n_: {k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in r.items()}
+                     for n_, r in results.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

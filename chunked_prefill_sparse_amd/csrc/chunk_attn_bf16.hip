@@ -16,32 +16,37 @@
 //     128 query rows.
 //   * Workgroup w runs on XCD w % 8.  When B*H_kv is a multiple of 8, all
 //     workgroups of a pseudo-request land on one XCD, so that XCD's L2 serves
-//     the block stream its ~64 workgroups read in near lockstep.  Sequences
-//     are taken longest first.
+//     the block stream its workgroups read in near lockstep.  Sequences are
+//     taken longest first.
 //   * Causality: keys t <= prior + i.  Blocks above the workgroup's last row
 //     are skipped; the token mask is applied only on blocks that straddle a
 //     wave's first row.
 //
-// Per block, per wave (D = 128):
-//   S^T[key][q] = K Q^T : 16 x v_mfma_f32_32x32x16_bf16 (K from LDS as the A
-//                 operand, Q held in VGPRs as the B operand).  The transposed
-//                 product leaves each lane with 32 scores of ONE query, so the
-//                 row max needs only one cross-lane exchange (lanes l, l^32).
-//   online softmax in fp32 with exp2 (scale * log2 e folded into one FMA);
-//                 the running max is only moved when some lane's block max
-//                 exceeds it by more than 8 (log2 units), otherwise the stale
-//                 max is kept (exact: numerator and denominator share it, and
-//                 every exponent stays <= 2^8).
-//   O^T[d][q]  += V^T P^T : 16 x v_mfma_f32_32x32x16_bf16.  The score
-//                 accumulator registers are reused directly as the B operand
-//                 after rounding to bf16: the MFMA contraction index is mapped
-//                 to keys in the order the accumulator already holds them, and
-//                 V is written to LDS transposed with the same key order.
+// Data movement
+//   * Each listed block's K and V (16 KiB each at D = 128) go from HBM/L2
+//     straight into LDS with global_load_lds_dwordx4 (no VGPR staging).  The
+//     copy of block j+1 is issued before block j is computed and is waited
+//     for only at the end of the iteration, into the other of two LDS buffers.
+//   * Both tiles are stored row-major with the 16-byte chunks of each row
+//     permuted (XOR swizzle by key); the permutation is applied by choosing
+//     each lane's source address, since the DMA writes lanes contiguously.
+//   * K is read with ds_read_b128 as the A operand of S^T = K Q^T; V is read
+//     with ds_read_b64_tr_b16, which transposes 16-bit elements across each
+//     group of 16 lanes, as the A operand of O^T = V^T P^T.  The swizzles make
+//     both reads bank-conflict free.
 //
-// LDS (per stage, double buffered): K tile [64][D] row-major with the 16-byte
-// chunks of each row XOR-swizzled, and the transposed V tile [D][64] with the
-// same kind of swizzle, so that every ds_read_b128 of an MFMA operand is
-// bank-conflict free.
+// Per block, per wave (D = 128): 16 + 16 v_mfma_f32_32x32x16_bf16.
+//   S^T[key][q]: each lane ends with 32 scores of ONE query, so the row max
+//   needs only one cross-lane exchange (lanes l, l^32).  Online softmax in
+//   fp32 with exp2 (scale * log2 e folded into one FMA); the running max moves
+//   only when some lane's block max exceeds it by more than 8 (log2 units),
+//   otherwise the stale max is kept (exact: numerator and denominator share
+//   it, and every exponent stays <= 2^8).  The probabilities are rounded to
+//   bf16 once; the same rounded values feed P.V and the denominator (summed
+//   with v_dot2c_f32_bf16).  The score accumulator registers serve directly as
+//   the B operand of O^T += V^T P^T: the MFMA contraction index is mapped to
+//   keys in the order the accumulator holds them, and the V operand is read
+//   in that same key order.
 
 #include "kernels.hpp"
 
@@ -49,91 +54,149 @@ namespace ca {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
-constexpr int kBlk = 64;      // keys per KV block
-constexpr int kThreads = 256; // 4 waves
+constexpr int kBlk = 64;       // keys per KV block
+constexpr int kThreads = 256;  // 4 waves
 constexpr int kRowsPerWave = 32;
 
 template <int D>
 struct Tile {
-  static constexpr int kKBytes = kBlk * D * 2;     // K tile
-  static constexpr int kVBytes = kBlk * D * 2;     // V^T tile
-  static constexpr int kStage = kKBytes + kVBytes;
-  static constexpr int kKLoads = kKBytes / 16 / kThreads;  // 16-byte loads per thread
-  static constexpr int kVKeys = D == 128 ? 4 : 2;          // keys per thread for V^T
-  static constexpr int kVGroups = kBlk / kVKeys;           // key groups
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;                 // 16-byte chunks per row
+  static constexpr int kBytes = kBlk * kRowBytes;       // one K or V tile
+  static constexpr int kDmaPerWave = kBytes / 1024 / 4; // 1 KiB wave copies per tile per wave
 };
 
-// Byte offset of 16-byte chunk c of K row r.
+// Chunk permutation of the K tile: chunk c of row r sits at c ^ k_swz(r).
 template <int D>
-__device__ __forceinline__ int k_off(int r, int c) {
-  if constexpr (D == 128) return r * 256 + ((c ^ (r & 15)) << 4);
-  else return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
-}
-// Byte offset of 16-byte chunk c (8 key slots) of V^T row d (64 keys = 128 bytes).
-__device__ __forceinline__ int vt_off(int d, int c) { return d * 128 + ((c ^ ((d >> 1) & 7)) << 4); }
-
-// Key slot of key k inside a V^T row: bits 2 and 3 swapped.  The score
-// accumulator holds, in lane half h, register r of key tile kt, the key
-// 32kt + 8(r/4) + 4h + r%4; slot order makes each lane's 8 contraction values
-// for one MFMA (registers 8u..8u+7) contiguous.
-__device__ __forceinline__ int key_slot(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
-
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
-
+__device__ __forceinline__ int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+// Chunk permutation of the V tile.
 template <int D>
-struct Stage {
-  uint4 k[Tile<D>::kKLoads];
-  uint4 v[Tile<D>::kVKeys];
-};
+__device__ __forceinline__ int v_swz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Issue the copies of K and V block kb into one LDS buffer (K tile, then V tile).
 template <int D>
-__device__ __forceinline__ void load_stage(Stage<D>& st, const __bf16* __restrict__ Kbg,
-                                           const __bf16* __restrict__ Vbg, int kb, int tid) {
-  const uint4* ksrc = reinterpret_cast<const uint4*>(Kbg + static_cast<size_t>(kb) * kBlk * D);
+__device__ __forceinline__ void dma_block(char* lds, const __bf16* __restrict__ Kbg,
+                                          const __bf16* __restrict__ Vbg, int kb,
+                                          const int* __restrict__ offk, const int* __restrict__ offv,
+                                          int wave) {
+  const char* ksrc = reinterpret_cast<const char*>(Kbg + static_cast<size_t>(kb) * kBlk * D);
+  const char* vsrc = reinterpret_cast<const char*>(Vbg + static_cast<size_t>(kb) * kBlk * D);
 #pragma unroll
-  for (int i = 0; i < Tile<D>::kKLoads; ++i) st.k[i] = ksrc[tid + i * kThreads];
-  constexpr int KV = Tile<D>::kVKeys;
-  const int kg = tid % Tile<D>::kVGroups;
-  const int dc = tid / Tile<D>::kVGroups;
-  const __bf16* vsrc = Vbg + (static_cast<size_t>(kb) * kBlk + kg * KV) * D + dc * 8;
-#pragma unroll
-  for (int i = 0; i < KV; ++i) st.v[i] = *reinterpret_cast<const uint4*>(vsrc + i * D);
-}
-
-template <int D>
-__device__ __forceinline__ void store_stage(const Stage<D>& st, char* __restrict__ lds, int tid) {
-  constexpr int CH = D / 8;  // 16-byte chunks per K row
-#pragma unroll
-  for (int i = 0; i < Tile<D>::kKLoads; ++i) {
-    const int ci = tid + i * kThreads;
-    *reinterpret_cast<uint4*>(lds + k_off<D>(ci / CH, ci % CH)) = st.k[i];
+  for (int i = 0; i < Tile<D>::kDmaPerWave; ++i) {
+    char* dst = lds + (i * 4 + wave) * 1024;
+    __builtin_amdgcn_global_load_lds(ksrc + offk[i], (lds_void_t*)dst, 16, 0, 0);
   }
-  char* vt = lds + Tile<D>::kKBytes;
-  constexpr int KV = Tile<D>::kVKeys;
-  const int kg = tid % Tile<D>::kVGroups;
-  const int dc = tid / Tile<D>::kVGroups;
-  const int slot = key_slot(kg * KV);      // KV consecutive keys -> KV consecutive slots
-  const int byte_in_chunk = (slot & 7) * 2;
-  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&st.v[0]);
-  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&st.v[1]);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int d = dc * 8 + e;
-    char* dst = vt + vt_off(d, slot >> 3) + byte_in_chunk;
-    const int wi = e >> 1;
-    if constexpr (KV == 4) {
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&st.v[2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&st.v[3]);
-      u32x2 val;
-      if (e & 1) { val.x = pack_hi(w0[wi], w1[wi]); val.y = pack_hi(w2[wi], w3[wi]); }
-      else       { val.x = pack_lo(w0[wi], w1[wi]); val.y = pack_lo(w2[wi], w3[wi]); }
-      *reinterpret_cast<u32x2*>(dst) = val;
-    } else {
-      *reinterpret_cast<uint32_t*>(dst) = (e & 1) ? pack_hi(w0[wi], w1[wi]) : pack_lo(w0[wi], w1[wi]);
+  for (int i = 0; i < Tile<D>::kDmaPerWave; ++i) {
+    char* dst = lds + Tile<D>::kBytes + (i * 4 + wave) * 1024;
+    __builtin_amdgcn_global_load_lds(vsrc + offv[i], (lds_void_t*)dst, 16, 0, 0);
+  }
+}
+
+template <int D>
+struct WaveState {
+  f32x16 acc[D / 32];
+  float m_used;
+  float l_part;
+};
+
+// One KV block for one wave: S^T, mask, online softmax, O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void compute_block(const char* __restrict__ lds, int kb,
+                                              WaveState<D>& ws, const bf16x8* qf,
+                                              const int* __restrict__ k_lane_off,
+                                              const int* __restrict__ v_lane_off,
+                                              int l32, int hh, int P, int row0, int qpos,
+                                              float c, float thr) {
+  constexpr int DS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int RB = Tile<D>::kRowBytes;
+  const char* Ks = lds;
+  const char* Vs = lds + Tile<D>::kBytes;
+
+  f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(Ks + k_lane_off[s]);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(Ks + k_lane_off[s] + 32 * RB);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], s1, 0, 0, 0);
+  }
+
+  if (kb * kBlk + kBlk - 1 > P + row0) {  // block reaches past the wave's first row
+    const int key0 = kb * kBlk + 4 * hh;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + 8 * (r >> 2) + (r & 3);
+      if (key > qpos) s0[r] = -INFINITY;
+      if (key + 32 > qpos) s1[r] = -INFINITY;
+    }
+  }
+
+  // row max: two chains of 3-input maxima (v_max3_f32), then the other lane half
+  float ma = __builtin_fmaxf(__builtin_fmaxf(s0[0], s0[1]), s0[2]);
+  float mb = __builtin_fmaxf(__builtin_fmaxf(s1[0], s1[1]), s1[2]);
+#pragma unroll
+  for (int r = 3; r < 15; r += 2) {
+    ma = __builtin_fmaxf(__builtin_fmaxf(ma, s0[r]), s0[r + 1]);
+    mb = __builtin_fmaxf(__builtin_fmaxf(mb, s1[r]), s1[r + 1]);
+  }
+  float mx = __builtin_fmaxf(__builtin_fmaxf(ma, mb), __builtin_fmaxf(s0[15], s1[15]));
+  mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+
+  if (__any(mx > ws.m_used + thr)) {
+    const float m_new = __builtin_fmaxf(ws.m_used, mx);
+    const float alpha = (ws.m_used == -INFINITY) ? 0.f
+                        : __builtin_amdgcn_exp2f((ws.m_used - m_new) * c);
+    ws.l_part *= alpha;
+#pragma unroll
+    for (int i = 0; i < DT; ++i) ws.acc[i] *= alpha;
+    ws.m_used = m_new;
+  }
+  const float msub = (ws.m_used == -INFINITY) ? 0.f : ws.m_used * c;
+
+  // probabilities -> bf16 B operands (kt, u) = (0,0) (0,1) (1,0) (1,1); the
+  // denominator sums the same rounded values
+  bf16x8 pf[4];
+  const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+  float lsum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    bf16x2 a, b;
+    a[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c, -msub)));
+    a[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r + 1], c, -msub)));
+    b[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c, -msub)));
+    b[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r + 1], c, -msub)));
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(a, ones, lsum, false);
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(b, ones, lsum, false);
+    pf[r >> 3][r & 7] = a[0];
+    pf[r >> 3][(r & 7) + 1] = a[1];
+    pf[2 + (r >> 3)][r & 7] = b[0];
+    pf[2 + (r >> 3)][(r & 7) + 1] = b[1];
+  }
+  ws.l_part += lsum;
+
+  // O^T += V^T P^T; V operand for (dt, kt, u) = two transposing reads (keys +0, +8)
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {  // q4 = 2*kt + u: keys 16*q4 + ...
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const char* p0 = Vs + v_lane_off[dt] + (16 * q4) * RB;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0 + 8 * RB));
+      const i16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      ws.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[q4],
+                                                           ws.acc[dt], 0, 0, 0);
     }
   }
 }
@@ -143,9 +206,14 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const int32_t* __restrict__ T, const int32_t* __restrict__ len, __bf16* __restrict__ O,
     float* __restrict__ lse, AttnParams p, SeqInfo seq) {
-  constexpr int DS = D / 16;  // MFMA steps along D for S
-  constexpr int DT = D / 32;  // 32-row output tiles of O^T
-  __shared__ __attribute__((aligned(16))) char smem[2 * Tile<D>::kStage];
+  constexpr int DS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int RB = Tile<D>::kRowBytes;
+  constexpr int CH = Tile<D>::kChunks;
+  constexpr int NDMA = Tile<D>::kDmaPerWave;
+  // two LDS buffers (K tile then V tile each), kept as distinct objects
+  __shared__ __attribute__((aligned(1024))) char buf0[2 * Tile<D>::kBytes];
+  __shared__ __attribute__((aligned(1024))) char buf1[2 * Tile<D>::kBytes];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -183,7 +251,6 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
   const bool row_live = row_in && row < C;
   const size_t qo_row = (static_cast<size_t>(b) * p.H_q + h) * p.C_max + row;
 
-  // rows of this workgroup that attend: [first_pb*32, min(C, (last_pb+1)*32))
   const int first_pb = (t * 4) / p.G;
   int last_pb = (t * 4 + 3) / p.G;
   last_pb = last_pb < n_pb - 1 ? last_pb : n_pb - 1;
@@ -197,14 +264,37 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
     return;
   }
   const int last_row = min(C, (last_pb + 1) * kRowsPerWave) - 1;
-  const int kb_limit = (P + last_row) / kBlk;            // last block any row may see
-  const int nkb = (P + C + kBlk - 1) / kBlk;             // blocks of this sequence
+  const int kb_limit = (P + last_row) / kBlk;  // last block any row may see
+  const int nkb = (P + C + kBlk - 1) / kBlk;   // blocks of this sequence
   int nT = len[bg];
   nT = nT < 0 ? 0 : (nT > p.NKB_max ? p.NKB_max : nT);
   const int32_t* __restrict__ Trow = T + static_cast<size_t>(bg) * p.NKB_max;
   const size_t kv_base = static_cast<size_t>(bg) * static_cast<size_t>(p.L) * D;
   const __bf16* Kbg = K + kv_base;
   const __bf16* Vbg = V + kv_base;
+
+  // ---- per-lane DMA source offsets (bytes within a block) realising the swizzles
+  int offk[NDMA], offv[NDMA];
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) {
+    const int pidx = (i * 4 + wave) * 64 + lane;  // LDS chunk this lane fills
+    const int r = pidx / CH, pc = pidx % CH;
+    offk[i] = r * RB + ((pc ^ k_swz<D>(r)) << 4);
+    offv[i] = r * RB + ((pc ^ v_swz<D>(r)) << 4);
+  }
+  // ---- per-lane LDS read offsets
+  int k_lane_off[DS];  // K rows l32 (+32), chunk 2s + hh
+#pragma unroll
+  for (int s = 0; s < DS; ++s) k_lane_off[s] = l32 * RB + (((2 * s + hh) ^ k_swz<D>(l32)) << 4);
+  int v_lane_off[DT];  // transposing reads: row 4hh + (lane&15)/4, d quad (lane&3) of half (lane>>4)&1
+  {
+    const int s16 = lane & 15;
+    const int key = 4 * hh + (s16 >> 2);
+    const int cl = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      v_lane_off[dt] = key * RB + (((4 * dt + cl) ^ v_swz<D>(key)) << 4) + 8 * (s16 & 1);
+  }
 
   // ---- Q fragments (B operand of S^T = K Q^T): row l32, d = 16s + 8hh + 0..7
   bf16x8 qf[DS];
@@ -217,12 +307,13 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
     for (int s = 0; s < DS; ++s) qf[s] = bf16x8{};
   }
 
-  f32x16 acc[DT];
+  WaveState<D> ws;
 #pragma unroll
-  for (int i = 0; i < DT; ++i) acc[i] = f32x16{};
-  float m_used = -INFINITY;  // max the exponentials are taken against (raw score units)
-  float l_part = 0.f;        // this lane half's share of the softmax denominator
-  const float thr = 8.f / p.scale_log2;
+  for (int i = 0; i < DT; ++i) ws.acc[i] = f32x16{};
+  ws.m_used = -INFINITY;  // max the exponentials are taken against (raw score units)
+  ws.l_part = 0.f;        // this lane half's share of the softmax denominator
+  const float c = p.scale_log2;
+  const float thr = 8.f / c;
   const int qpos = P + row;  // absolute position of this lane's query
 
   auto next_valid = [&](int j) {
@@ -234,112 +325,54 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
     return j;
   };
 
-  Stage<D> st;
   int j = next_valid(0);
-  if (j < nT) {
-    load_stage<D>(st, Kbg, Vbg, Trow[j], tid);
-    store_stage<D>(st, smem, tid);
-  }
+  if (j < nT) dma_block<D>(buf0, Kbg, Vbg, Trow[j], offk, offv, wave);
+  wait_vmem();
   __syncthreads();
-  int buf = 0;
-
   while (j < nT) {
-    const int kb = Trow[j];
-    const int jn = next_valid(j + 1);
-    if (jn < nT) load_stage<D>(st, Kbg, Vbg, Trow[jn], tid);
-
-    const char* Ks = smem + buf * Tile<D>::kStage;
-    const char* Vs = Ks + Tile<D>::kKBytes;
-
-    // S^T for keys [0,32) and [32,64) of the block
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(Ks + k_off<D>(l32, 2 * s + hh));
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(Ks + k_off<D>(32 + l32, 2 * s + hh));
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], s1, 0, 0, 0);
-    }
-
-    // causal mask on blocks that reach past the wave's first row
-    if (kb * kBlk + kBlk - 1 > P + row0) {
-      const int key0 = kb * kBlk + 4 * hh;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 8 * (r >> 2) + (r & 3);
-        if (key > qpos) s0[r] = -INFINITY;
-        if (key + 32 > qpos) s1[r] = -INFINITY;
-      }
-    }
-
-    float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-
-    if (__any(mx > m_used + thr)) {
-      const float m_new = fmaxf(m_used, mx);
-      const float alpha = (m_used == -INFINITY) ? 0.f
-                          : __builtin_amdgcn_exp2f((m_used - m_new) * p.scale_log2);
-      l_part *= alpha;
-#pragma unroll
-      for (int i = 0; i < DT; ++i) acc[i] *= alpha;
-      m_used = m_new;
-    }
-    const float msub = (m_used == -INFINITY) ? 0.f : m_used * p.scale_log2;
-
-    bf16x8 pf[4];  // B operands of O^T += V^T P^T: (kt, u) = (0,0) (0,1) (1,0) (1,1)
-    float lsum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], p.scale_log2, -msub));
-      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.scale_log2, -msub));
-      lsum += e0 + e1;
-      pf[r >> 3][r & 7] = static_cast<__bf16>(e0);
-      pf[2 + (r >> 3)][r & 7] = static_cast<__bf16>(e1);
-    }
-    l_part += lsum;
-
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {  // q4 = 2*kt + u -> V^T chunk 4kt + 2u + hh
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vs + vt_off(32 * dt + l32, 2 * q4 + hh));
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[q4], acc[dt], 0, 0, 0);
-      }
-    }
-
-    if (jn < nT) store_stage<D>(st, smem + (buf ^ 1) * Tile<D>::kStage, tid);
+    // block j in buf0; copy the next one into buf1
+    int jn = next_valid(j + 1);
+    if (jn < nT) dma_block<D>(buf1, Kbg, Vbg, Trow[jn], offk, offv, wave);
+    compute_block<D>(buf0, Trow[j], ws, qf, k_lane_off, v_lane_off, l32, hh, P, row0, qpos, c,
+                     thr);
+    wait_vmem();
     __syncthreads();
-    buf ^= 1;
+    j = jn;
+    if (j >= nT) break;
+    // block j in buf1; copy the next one into buf0
+    jn = next_valid(j + 1);
+    if (jn < nT) dma_block<D>(buf0, Kbg, Vbg, Trow[jn], offk, offv, wave);
+    compute_block<D>(buf1, Trow[j], ws, qf, k_lane_off, v_lane_off, l32, hh, P, row0, qpos, c,
+                     thr);
+    wait_vmem();
+    __syncthreads();
     j = jn;
   }
 
   // ---- epilogue: O = acc / l, rows >= C written as 0
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  const float l_tot = ws.l_part + __shfl_xor(ws.l_part, 32);
   if (!row_in) return;
   const float inv = (row_live && l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (!row_live) {  // padding rows: exact zeros whatever the (unused) Q row held
 #pragma unroll
-    for (int i = 0; i < DT; ++i) acc[i] = f32x16{};
+    for (int i = 0; i < DT; ++i) ws.acc[i] = f32x16{};
   }
   __bf16* orow = O + qo_row * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
+      const float* a = reinterpret_cast<const float*>(&ws.acc[dt]) + 4 * rr;
+      const bf16x2 lo = {static_cast<__bf16>(a[0] * inv), static_cast<__bf16>(a[1] * inv)};
+      const bf16x2 hi = {static_cast<__bf16>(a[2] * inv), static_cast<__bf16>(a[3] * inv)};
       u32x2 w;
-      const float* a = reinterpret_cast<const float*>(&acc[dt]) + 4 * rr;
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      bf16x2 lo = {static_cast<__bf16>(a[0] * inv), static_cast<__bf16>(a[1] * inv)};
-      bf16x2 hi = {static_cast<__bf16>(a[2] * inv), static_cast<__bf16>(a[3] * inv)};
       w.x = __builtin_bit_cast(uint32_t, lo);
       w.y = __builtin_bit_cast(uint32_t, hi);
       *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * rr + 4 * hh) = w;
     }
   }
   if (lse && hh == 0)
-    lse[qo_row] = (row_live && l_tot > 0.f) ? m_used * p.scale + __logf(l_tot) : -INFINITY;
+    lse[qo_row] = (row_live && l_tot > 0.f) ? ws.m_used * p.scale + __logf(l_tot) : -INFINITY;
 }
 
 }  // namespace

@@ -145,9 +145,9 @@ def test_bf16_closed_form_constant_values():
     w = gen.make_custom(1, 8, 2, 128, [4096], [256], "bf16", 6, _bern(0.3))
     w.v.fill_(1.0)
     _, _, _, (O, _) = _run(w)
-    # P is rounded to bf16 before P.V while the denominator sums unrounded
-    # probabilities: 1 within the rounding of the probabilities
-    np.testing.assert_allclose(to_np(O), 1.0, rtol=0, atol=4e-3)
+    # numerator and denominator sum the same bf16-rounded probabilities, so the
+    # result is 1 up to fp32 summation order, which bf16 output rounding absorbs
+    assert np.all(to_np(O) == 1.0)
 
 
 # ----------------------------------------------------------------------------- full sizes
