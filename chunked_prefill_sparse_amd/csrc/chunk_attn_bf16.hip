@@ -83,23 +83,17 @@ __device__ __forceinline__ int v_swz(int r) { return D == 128 ? 4 * (r & 3) : 4 
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Issue the copies of K and V block kb into one LDS buffer (K tile, then V tile).
+// Issue the copy of one 64-row tile (K or V block kb) into LDS.  The source is
+// a uniform base plus a 32-bit per-lane offset (SGPR-base addressing); the LDS
+// destination of each wave copy is uniform.
 template <int D>
-__device__ __forceinline__ void dma_block(char* lds, const __bf16* __restrict__ Kbg,
-                                          const __bf16* __restrict__ Vbg, int kb,
-                                          const int* __restrict__ offk, const int* __restrict__ offv,
-                                          int wave) {
-  const char* ksrc = reinterpret_cast<const char*>(Kbg + static_cast<size_t>(kb) * kBlk * D);
-  const char* vsrc = reinterpret_cast<const char*>(Vbg + static_cast<size_t>(kb) * kBlk * D);
+__device__ __forceinline__ void dma_tile(char* lds_tile, const __bf16* __restrict__ src_bg, int kb,
+                                         const uint32_t* __restrict__ off, int wave_u) {
+  const char* src = reinterpret_cast<const char*>(src_bg + static_cast<size_t>(kb) * kBlk * D);
 #pragma unroll
   for (int i = 0; i < Tile<D>::kDmaPerWave; ++i) {
-    char* dst = lds + (i * 4 + wave) * 1024;
-    __builtin_amdgcn_global_load_lds(ksrc + offk[i], (lds_void_t*)dst, 16, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < Tile<D>::kDmaPerWave; ++i) {
-    char* dst = lds + Tile<D>::kBytes + (i * 4 + wave) * 1024;
-    __builtin_amdgcn_global_load_lds(vsrc + offv[i], (lds_void_t*)dst, 16, 0, 0);
+    char* dst = lds_tile + (i * 4 + wave_u) * 1024;
+    __builtin_amdgcn_global_load_lds(src + off[i], (lds_void_t*)dst, 16, 0, 0);
   }
 }
 
@@ -110,21 +104,15 @@ struct WaveState {
   float l_part;
 };
 
-// One KV block for one wave: S^T, mask, online softmax, O^T += V^T P^T.
+// S^T = K Q^T for the 64 keys of one K tile: s0 = keys 0..31, s1 = keys 32..63.
 template <int D>
-__device__ __forceinline__ void compute_block(const char* __restrict__ lds, int kb,
-                                              WaveState<D>& ws, const bf16x8* qf,
-                                              const int* __restrict__ k_lane_off,
-                                              const int* __restrict__ v_lane_off,
-                                              int l32, int hh, int P, int row0, int qpos,
-                                              float c, float thr) {
+__device__ __forceinline__ void scores(const char* __restrict__ Ks, const bf16x8* qf,
+                                       const int* __restrict__ k_lane_off, f32x16& s0,
+                                       f32x16& s1) {
   constexpr int DS = D / 16;
-  constexpr int DT = D / 32;
   constexpr int RB = Tile<D>::kRowBytes;
-  const char* Ks = lds;
-  const char* Vs = lds + Tile<D>::kBytes;
-
-  f32x16 s0 = f32x16{}, s1 = f32x16{};
+  s0 = f32x16{};
+  s1 = f32x16{};
 #pragma unroll
   for (int s = 0; s < DS; ++s) {
     const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(Ks + k_lane_off[s]);
@@ -132,7 +120,17 @@ __device__ __forceinline__ void compute_block(const char* __restrict__ lds, int 
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], s1, 0, 0, 0);
   }
+}
 
+// First half of the online softmax for one block's scores, run as soon as
+// they exist: causal mask, row max, and the running-max update.  When the max
+// moves, the output accumulator and denominator are rescaled here, before
+// this block's probabilities are formed.
+template <int D>
+__device__ __forceinline__ void softmax_prepare(f32x16& s0, f32x16& s1, int kb, WaveState<D>& ws,
+                                                int hh, int P, int row0, int qpos, float c,
+                                                float thr, int xhalf) {
+  constexpr int DT = D / 32;
   if (kb * kBlk + kBlk - 1 > P + row0) {  // block reaches past the wave's first row
     const int key0 = kb * kBlk + 4 * hh;
 #pragma unroll
@@ -142,7 +140,6 @@ __device__ __forceinline__ void compute_block(const char* __restrict__ lds, int 
       if (key + 32 > qpos) s1[r] = -INFINITY;
     }
   }
-
   // row max: two chains of 3-input maxima (v_max3_f32), then the other lane half
   float ma = __builtin_fmaxf(__builtin_fmaxf(s0[0], s0[1]), s0[2]);
   float mb = __builtin_fmaxf(__builtin_fmaxf(s1[0], s1[1]), s1[2]);
@@ -152,7 +149,9 @@ __device__ __forceinline__ void compute_block(const char* __restrict__ lds, int 
     mb = __builtin_fmaxf(__builtin_fmaxf(mb, s1[r]), s1[r + 1]);
   }
   float mx = __builtin_fmaxf(__builtin_fmaxf(ma, mb), __builtin_fmaxf(s0[15], s1[15]));
-  mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+  // xhalf = byte address of lane ^ 32
+  mx = __builtin_fmaxf(mx, __builtin_bit_cast(
+                               float, __builtin_amdgcn_ds_bpermute(xhalf, __builtin_bit_cast(int, mx))));
 
   if (__any(mx > ws.m_used + thr)) {
     const float m_new = __builtin_fmaxf(ws.m_used, mx);
@@ -163,11 +162,15 @@ __device__ __forceinline__ void compute_block(const char* __restrict__ lds, int 
     for (int i = 0; i < DT; ++i) ws.acc[i] *= alpha;
     ws.m_used = m_new;
   }
-  const float msub = (ws.m_used == -INFINITY) ? 0.f : ws.m_used * c;
+}
 
-  // probabilities -> bf16 B operands (kt, u) = (0,0) (0,1) (1,0) (1,1); the
-  // denominator sums the same rounded values
-  bf16x8 pf[4];
+// Second half: bf16 probabilities against the running max (the B operands of
+// O^T += V^T P^T, in (kt, u) order (0,0) (0,1) (1,0) (1,1)) and the
+// denominator, which sums the same rounded values.  Branch-free.
+template <int D>
+__device__ __forceinline__ void softmax_probs(const f32x16& s0, const f32x16& s1,
+                                              WaveState<D>& ws, bf16x8* pf, float c) {
+  const float msub = (ws.m_used == -INFINITY) ? 0.f : ws.m_used * c;
   const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
   float lsum = 0.f;
 #pragma unroll
@@ -185,8 +188,16 @@ __device__ __forceinline__ void compute_block(const char* __restrict__ lds, int 
     pf[2 + (r >> 3)][(r & 7) + 1] = b[1];
   }
   ws.l_part += lsum;
+}
 
-  // O^T += V^T P^T; V operand for (dt, kt, u) = two transposing reads (keys +0, +8)
+// O^T += V^T P^T for one V tile; the V operand of (dt, kt, u) is two
+// transposing reads (keys +0..3 and +8..11 of the 16-key slice).
+template <int D>
+__device__ __forceinline__ void accumulate_pv(const char* __restrict__ Vs, const bf16x8* pf,
+                                              const int* __restrict__ v_lane_off,
+                                              WaveState<D>& ws) {
+  constexpr int DT = D / 32;
+  constexpr int RB = Tile<D>::kRowBytes;
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {  // q4 = 2*kt + u: keys 16*q4 + ...
 #pragma unroll
@@ -211,12 +222,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
   constexpr int RB = Tile<D>::kRowBytes;
   constexpr int CH = Tile<D>::kChunks;
   constexpr int NDMA = Tile<D>::kDmaPerWave;
-  // two LDS buffers (K tile then V tile each), kept as distinct objects
-  __shared__ __attribute__((aligned(1024))) char buf0[2 * Tile<D>::kBytes];
-  __shared__ __attribute__((aligned(1024))) char buf1[2 * Tile<D>::kBytes];
+  // LDS: two K tiles, then two V tiles
+  __shared__ __attribute__((aligned(1024))) char lds[4 * Tile<D>::kBytes];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // same value, known uniform
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -274,13 +285,13 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
   const __bf16* Vbg = V + kv_base;
 
   // ---- per-lane DMA source offsets (bytes within a block) realising the swizzles
-  int offk[NDMA], offv[NDMA];
+  uint32_t offk[NDMA], offv[NDMA];
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
     const int pidx = (i * 4 + wave) * 64 + lane;  // LDS chunk this lane fills
     const int r = pidx / CH, pc = pidx % CH;
-    offk[i] = r * RB + ((pc ^ k_swz<D>(r)) << 4);
-    offv[i] = r * RB + ((pc ^ v_swz<D>(r)) << 4);
+    offk[i] = static_cast<uint32_t>(r * RB + ((pc ^ k_swz<D>(r)) << 4));
+    offv[i] = static_cast<uint32_t>(r * RB + ((pc ^ v_swz<D>(r)) << 4));
   }
   // ---- per-lane LDS read offsets
   int k_lane_off[DS];  // K rows l32 (+32), chunk 2s + hh
@@ -314,6 +325,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
   ws.l_part = 0.f;        // this lane half's share of the softmax denominator
   const float c = p.scale_log2;
   const float thr = 8.f / c;
+  const int xhalf = (lane ^ 32) << 2;
   const int qpos = P + row;  // absolute position of this lane's query
 
   auto next_valid = [&](int j) {
@@ -325,28 +337,62 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
     return j;
   };
 
+  // Software pipeline over the table: K tiles run two blocks ahead of use, V
+  // tiles one.  Step for block j (its scores already masked and its running
+  // max settled): copy K(j2) and V(j1) into the free buffers; S(j1) on the
+  // matrix cores alongside the probabilities of block j on the vector ALUs;
+  // O += V(j) P(j); then mask / max / rescale for S(j1).  j1, j2 are the next
+  // two valid table entries; the entry after j2 is looked up during the step
+  // so its scalar load is off the critical path.  The loop is unrolled by two
+  // so buffer offsets and score registers keep fixed roles.
+  constexpr int TB = Tile<D>::kBytes;
+  char* const K0 = lds;
+  char* const K1 = lds + TB;
+  char* const V0 = lds + 2 * TB;
+  char* const V1 = lds + 3 * TB;
   int j = next_valid(0);
-  if (j < nT) dma_block<D>(buf0, Kbg, Vbg, Trow[j], offk, offv, wave);
+  int j1 = next_valid(j + 1);
+  int j2 = next_valid(j1 + 1);
+  const int kbj = j < nT ? Trow[j] : 0;
+  int kb1 = j1 < nT ? Trow[j1] : 0;
+  int kb2 = j2 < nT ? Trow[j2] : 0;
+  if (j < nT) {
+    dma_tile<D>(K0, Kbg, kbj, offk, wave_u);
+    dma_tile<D>(V0, Vbg, kbj, offv, wave_u);
+  }
+  if (j1 < nT) dma_tile<D>(K1, Kbg, kb1, offk, wave_u);
   wait_vmem();
   __syncthreads();
+  f32x16 sa0, sa1, sb0, sb1;
+  scores<D>(K0, qf, k_lane_off, sa0, sa1);
+  if (j < nT) softmax_prepare<D>(sa0, sa1, kbj, ws, hh, P, row0, qpos, c, thr, xhalf);
+  __syncthreads();  // every wave has read K(j) before its buffer is reused
+
+  // One pipeline step; Kin/Vin hold K(j1)/V(j), Kfree/Vfree receive K(j2)/V(j1).
+  auto step = [&](const f32x16& cur0, const f32x16& cur1, f32x16& nxt0, f32x16& nxt1,
+                  char* Kin, char* Vin, char* Kfree, char* Vfree) {
+    if (j2 < nT) dma_tile<D>(Kfree, Kbg, kb2, offk, wave_u);
+    if (j1 < nT) dma_tile<D>(Vfree, Vbg, kb1, offv, wave_u);
+    // when j1 is past the end the K tile holds stale data and S(j1) is unused
+    scores<D>(Kin, qf, k_lane_off, nxt0, nxt1);
+    bf16x8 pf[4];
+    softmax_probs<D>(cur0, cur1, ws, pf, c);
+    accumulate_pv<D>(Vin, pf, v_lane_off, ws);
+    if (j1 < nT) softmax_prepare<D>(nxt0, nxt1, kb1, ws, hh, P, row0, qpos, c, thr, xhalf);
+    const int j3 = next_valid(j2 + 1);
+    const int kb3 = j3 < nT ? Trow[j3] : 0;
+    wait_vmem();
+    __syncthreads();
+    j = j1;
+    j1 = j2;
+    kb1 = kb2;
+    j2 = j3;
+    kb2 = kb3;
+  };
   while (j < nT) {
-    // block j in buf0; copy the next one into buf1
-    int jn = next_valid(j + 1);
-    if (jn < nT) dma_block<D>(buf1, Kbg, Vbg, Trow[jn], offk, offv, wave);
-    compute_block<D>(buf0, Trow[j], ws, qf, k_lane_off, v_lane_off, l32, hh, P, row0, qpos, c,
-                     thr);
-    wait_vmem();
-    __syncthreads();
-    j = jn;
+    step(sa0, sa1, sb0, sb1, K1, V0, K0, V1);
     if (j >= nT) break;
-    // block j in buf1; copy the next one into buf0
-    jn = next_valid(j + 1);
-    if (jn < nT) dma_block<D>(buf0, Kbg, Vbg, Trow[jn], offk, offv, wave);
-    compute_block<D>(buf1, Trow[j], ws, qf, k_lane_off, v_lane_off, l32, hh, P, row0, qpos, c,
-                     thr);
-    wait_vmem();
-    __syncthreads();
-    j = jn;
+    step(sb0, sb1, sa0, sa1, K0, V1, K1, V0);
   }
 
   // ---- epilogue: O = acc / l, rows >= C written as 0
