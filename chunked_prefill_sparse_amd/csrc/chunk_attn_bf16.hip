@@ -59,6 +59,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
@@ -83,17 +84,19 @@ __device__ __forceinline__ int v_swz(int r) { return D == 128 ? 4 * (r & 3) : 4 
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Issue the copy of one 64-row tile (K or V block kb) into LDS.  The source is
-// a uniform base plus a 32-bit per-lane offset (SGPR-base addressing); the LDS
-// destination of each wave copy is uniform.
+// Issue the copy of one 64-row tile (K or V block kb) into LDS through a raw
+// buffer resource over the (b, g) cache slice: per-lane 32-bit offsets, the
+// block offset in an SGPR, and hardware bounds checking (a block offset at or
+// past the slice end reads zeros and touches no memory).  The LDS destination
+// of each wave copy is uniform (M0).
 template <int D>
-__device__ __forceinline__ void dma_tile(char* lds_tile, const __bf16* __restrict__ src_bg, int kb,
-                                         const uint32_t* __restrict__ off, int wave_u) {
-  const char* src = reinterpret_cast<const char*>(src_bg + static_cast<size_t>(kb) * kBlk * D);
+__device__ __forceinline__ void dma_tile(char* lds_tile, __amdgpu_buffer_rsrc_t rsrc,
+                                         uint32_t block_off, const uint32_t* __restrict__ off,
+                                         int wave_u) {
 #pragma unroll
   for (int i = 0; i < Tile<D>::kDmaPerWave; ++i) {
     char* dst = lds_tile + (i * 4 + wave_u) * 1024;
-    __builtin_amdgcn_global_load_lds(src + off[i], (lds_void_t*)dst, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, off[i], block_off, 0, 0);
   }
 }
 
@@ -122,25 +125,21 @@ __device__ __forceinline__ void scores(const char* __restrict__ Ks, const bf16x8
   }
 }
 
-// First half of the online softmax for one block's scores, run as soon as
-// they exist: causal mask, row max, and the running-max update.  When the max
-// moves, the output accumulator and denominator are rescaled here, before
-// this block's probabilities are formed.
-template <int D>
-__device__ __forceinline__ void softmax_prepare(f32x16& s0, f32x16& s1, int kb, WaveState<D>& ws,
-                                                int hh, int P, int row0, int qpos, float c,
-                                                float thr, int xhalf) {
-  constexpr int DT = D / 32;
-  if (kb * kBlk + kBlk - 1 > P + row0) {  // block reaches past the wave's first row
-    const int key0 = kb * kBlk + 4 * hh;
+// Causal mask of one block's scores: key t of this lane's query at absolute
+// position qpos is admissible iff t <= qpos.
+__device__ __forceinline__ void mask_scores(f32x16& s0, f32x16& s1, int kb, int hh, int qpos) {
+  const int key0 = kb * kBlk + 4 * hh;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = key0 + 8 * (r >> 2) + (r & 3);
-      if (key > qpos) s0[r] = -INFINITY;
-      if (key + 32 > qpos) s1[r] = -INFINITY;
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int key = key0 + 8 * (r >> 2) + (r & 3);
+    if (key > qpos) s0[r] = -INFINITY;
+    if (key + 32 > qpos) s1[r] = -INFINITY;
   }
-  // row max: two chains of 3-input maxima (v_max3_f32), then the other lane half
+}
+
+// Row max of one block's scores: two chains of 3-input maxima (v_max3_f32),
+// then the other lane half (xhalf = byte address of lane ^ 32).
+__device__ __forceinline__ float row_max(const f32x16& s0, const f32x16& s1, int xhalf) {
   float ma = __builtin_fmaxf(__builtin_fmaxf(s0[0], s0[1]), s0[2]);
   float mb = __builtin_fmaxf(__builtin_fmaxf(s1[0], s1[1]), s1[2]);
 #pragma unroll
@@ -148,11 +147,18 @@ __device__ __forceinline__ void softmax_prepare(f32x16& s0, f32x16& s1, int kb, 
     ma = __builtin_fmaxf(__builtin_fmaxf(ma, s0[r]), s0[r + 1]);
     mb = __builtin_fmaxf(__builtin_fmaxf(mb, s1[r]), s1[r + 1]);
   }
-  float mx = __builtin_fmaxf(__builtin_fmaxf(ma, mb), __builtin_fmaxf(s0[15], s1[15]));
-  // xhalf = byte address of lane ^ 32
-  mx = __builtin_fmaxf(mx, __builtin_bit_cast(
-                               float, __builtin_amdgcn_ds_bpermute(xhalf, __builtin_bit_cast(int, mx))));
+  const float mx = __builtin_fmaxf(__builtin_fmaxf(ma, mb), __builtin_fmaxf(s0[15], s1[15]));
+  return __builtin_fmaxf(
+      mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xhalf, __builtin_bit_cast(int, mx))));
+}
 
+// Running-max update for a block whose row max is mx: the max moves only when
+// some lane's block max exceeds it by more than thr; then the output
+// accumulator and the denominator are rescaled, before this block's
+// probabilities are formed.
+template <int D>
+__device__ __forceinline__ void update_max(float mx, WaveState<D>& ws, float c, float thr) {
+  constexpr int DT = D / 32;
   if (__any(mx > ws.m_used + thr)) {
     const float m_new = __builtin_fmaxf(ws.m_used, mx);
     const float alpha = (ws.m_used == -INFINITY) ? 0.f
@@ -164,9 +170,10 @@ __device__ __forceinline__ void softmax_prepare(f32x16& s0, f32x16& s1, int kb, 
   }
 }
 
-// Second half: bf16 probabilities against the running max (the B operands of
-// O^T += V^T P^T, in (kt, u) order (0,0) (0,1) (1,0) (1,1)) and the
-// denominator, which sums the same rounded values.  Branch-free.
+// Probabilities against the running max, rounded to bf16 as the B operands of
+// O^T += V^T P^T (in (kt, u) order (0,0) (0,1) (1,0) (1,1)), and the
+// denominator, which sums the same rounded values (v_dot2c_f32_bf16 against
+// ones).  Branch-free.
 template <int D>
 __device__ __forceinline__ void softmax_probs(const f32x16& s0, const f32x16& s1,
                                               WaveState<D>& ws, bf16x8* pf, float c) {
@@ -210,6 +217,73 @@ __device__ __forceinline__ void accumulate_pv(const char* __restrict__ Vs, const
                                                            ws.acc[dt], 0, 0, 0);
     }
   }
+}
+
+// Instruction interleaving for one pipeline body (scheduling hints only):
+// after the copies are issued, each matrix instruction is followed by LDS
+// reads for the next ones and a share of the softmax vector work, so the
+// matrix pipe is fed while the vector ALUs work.  Groups that cannot be
+// filled are skipped by the scheduler.
+#ifndef CA_SCHED_PATTERN
+#define CA_SCHED_PATTERN 5
+#endif
+template <int D>
+__device__ __forceinline__ void body_schedule() {
+  constexpr int DS = D / 16;  // S matrix instructions per key tile
+#if CA_SCHED_PATTERN == 1
+  __builtin_amdgcn_sched_group_barrier(0x020, 2 * Tile<D>::kDmaPerWave, 0);  // tile copies
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                         // first K reads
+#pragma unroll
+  for (int i = 0; i < 2 * DS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // S(j1) MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next LDS read
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // probabilities of block j
+  }
+#pragma unroll
+  for (int i = 0; i < 2 * DS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // P.V MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V reads
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // row max of S(j1)
+  }
+#elif CA_SCHED_PATTERN == 4 || CA_SCHED_PATTERN == 5
+  // S(j1) and P.V(j-1) matrix instructions alternate, each followed by LDS
+  // reads for the ones ahead and a share of the vector work
+  constexpr int VA = CA_SCHED_PATTERN == 4 ? 4 : 3;
+  __builtin_amdgcn_sched_group_barrier(0x020, 2 * Tile<D>::kDmaPerWave, 0);  // tile copies
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);                         // first reads
+#pragma unroll
+  for (int i = 0; i < 2 * DS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, VA, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, VA, 0);
+  }
+#elif CA_SCHED_PATTERN == 2 || CA_SCHED_PATTERN == 3
+  constexpr int VA = CA_SCHED_PATTERN == 2 ? 6 : 7;  // VALU per S MFMA
+  constexpr int VB = CA_SCHED_PATTERN == 2 ? 2 : 1;  // VALU per P.V MFMA
+  __builtin_amdgcn_sched_group_barrier(0x020, 2 * Tile<D>::kDmaPerWave, 0);  // tile copies
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                         // first K reads
+#pragma unroll
+  for (int i = 0; i < 2 * DS - 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // S(j1) MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // K read
+    __builtin_amdgcn_sched_group_barrier(0x002, VA, 0);  // probabilities of block j
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // S(j1) MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // first V reads
+    __builtin_amdgcn_sched_group_barrier(0x002, VA, 0);  // probabilities of block j
+  }
+#pragma unroll
+  for (int i = 0; i < 2 * DS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // P.V MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V reads ~5 MFMAs ahead
+    __builtin_amdgcn_sched_group_barrier(0x002, VB, 0); // row max of S(j1)
+  }
+#endif
 }
 
 template <int D>
@@ -328,71 +402,151 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
   const int xhalf = (lane ^ 32) << 2;
   const int qpos = P + row;  // absolute position of this lane's query
 
-  auto next_valid = [&](int j) {
-    while (j < nT) {
-      const int kb = Trow[j];
-      if (kb >= 0 && kb < nkb && kb <= kb_limit) break;
-      ++j;
-    }
-    return j;
-  };
-
   // Software pipeline over the table: K tiles run two blocks ahead of use, V
   // tiles one.  Step for block j (its scores already masked and its running
   // max settled): copy K(j2) and V(j1) into the free buffers; S(j1) on the
   // matrix cores alongside the probabilities of block j on the vector ALUs;
-  // O += V(j) P(j); then mask / max / rescale for S(j1).  j1, j2 are the next
-  // two valid table entries; the entry after j2 is looked up during the step
-  // so its scalar load is off the critical path.  The loop is unrolled by two
-  // so buffer offsets and score registers keep fixed roles.
+  // O += V(j) P(j); mask and row max of S(j1).  That body has no branches (a
+  // copy past the end of the table is turned into an out-of-range buffer read
+  // that fetches nothing), so the scheduler can interleave it; the tail then
+  // settles the running max for block j1 and looks up the entry after j2.
+  // The loop is unrolled by two so buffer offsets and score registers keep
+  // fixed roles, and each step has a masked and an unmasked form.
   constexpr int TB = Tile<D>::kBytes;
   char* const K0 = lds;
   char* const K1 = lds + TB;
   char* const V0 = lds + 2 * TB;
   char* const V1 = lds + 3 * TB;
-  int j = next_valid(0);
-  int j1 = next_valid(j + 1);
-  int j2 = next_valid(j1 + 1);
-  const int kbj = j < nT ? Trow[j] : 0;
-  int kb1 = j1 < nT ? Trow[j1] : 0;
-  int kb2 = j2 < nT ? Trow[j2] : 0;
-  if (j < nT) {
-    dma_tile<D>(K0, Kbg, kbj, offk, wave_u);
-    dma_tile<D>(V0, Vbg, kbj, offv, wave_u);
+  const uint32_t slice_bytes = static_cast<uint32_t>(p.L * D * 2);
+  const __amdgpu_buffer_rsrc_t krsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Kbg, (short)0, slice_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Vbg, (short)0, slice_bytes, 0x00020000);
+  const int row0_wg = first_pb * kRowsPerWave;
+  // blocks that reach past the workgroup's first row need the causal mask; with
+  // T ascending they are the last entries, [e, nT)
+  auto needs_mask = [&](int kb) { return kb * kBlk + kBlk - 1 > P + row0_wg; };
+  auto valid = [&](int kb) { return kb >= 0 && kb < nkb && kb <= kb_limit; };
+  int e = nT;
+  while (e > 0) {
+    const int kb = Trow[e - 1];
+    if (valid(kb) && !needs_mask(kb)) break;
+    --e;
   }
-  if (j1 < nT) dma_tile<D>(K1, Kbg, kb1, offk, wave_u);
-  wait_vmem();
-  __syncthreads();
-  f32x16 sa0, sa1, sb0, sb1;
-  scores<D>(K0, qf, k_lane_off, sa0, sa1);
-  if (j < nT) softmax_prepare<D>(sa0, sa1, kbj, ws, hh, P, row0, qpos, c, thr, xhalf);
-  __syncthreads();  // every wave has read K(j) before its buffer is reused
+  auto next_plain = [&](int jj) {
+    while (jj < e) {
+      const int kb = Trow[jj];
+      if (valid(kb) && !needs_mask(kb)) break;
+      ++jj;
+    }
+    return jj;
+  };
 
-  // One pipeline step; Kin/Vin hold K(j1)/V(j), Kfree/Vfree receive K(j2)/V(j1).
-  auto step = [&](const f32x16& cur0, const f32x16& cur1, f32x16& nxt0, f32x16& nxt1,
-                  char* Kin, char* Vin, char* Kfree, char* Vfree) {
-    if (j2 < nT) dma_tile<D>(Kfree, Kbg, kb2, offk, wave_u);
-    if (j1 < nT) dma_tile<D>(Vfree, Vbg, kb1, offv, wave_u);
-    // when j1 is past the end the K tile holds stale data and S(j1) is unused
-    scores<D>(Kin, qf, k_lane_off, nxt0, nxt1);
-    bf16x8 pf[4];
-    softmax_probs<D>(cur0, cur1, ws, pf, c);
-    accumulate_pv<D>(Vin, pf, v_lane_off, ws);
-    if (j1 < nT) softmax_prepare<D>(nxt0, nxt1, kb1, ws, hh, P, row0, qpos, c, thr, xhalf);
-    const int j3 = next_valid(j2 + 1);
-    const int kb3 = j3 < nT ? Trow[j3] : 0;
+  int j = next_plain(0);
+  int j1 = next_plain(j + 1);
+  int j2 = next_plain(j1 + 1);
+  const int kbj = j < e ? Trow[j] : 0;
+  int kb0 = kbj;
+  int kb1 = j1 < e ? Trow[j1] : 0;
+  int kb2 = j2 < e ? Trow[j2] : 0;
+  auto boff = [&](int jj, int kb) {  // block byte offset, or past the end when jj is not used
+    return jj < e ? static_cast<uint32_t>(kb) * (kBlk * D * 2) : slice_bytes;
+  };
+  f32x16 sa0, sa1, sb0, sb1;  // scores of the current / next block (roles alternate)
+  bf16x8 pxa[4], pxb[4];      // probabilities waiting for their P.V (roles alternate)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pxa[i] = pxb[i] = bf16x8{};
+  if (j < e) {
+    dma_tile<D>(K0, krsrc, boff(j, kbj), offk, wave_u);
+    dma_tile<D>(K1, krsrc, boff(j1, kb1), offk, wave_u);
+    // V1 is read by the first step with zero probabilities: make it finite
+    uint4* vz = reinterpret_cast<uint4*>(V1);
+    for (int i = tid; i < TB / 16; i += kThreads) vz[i] = make_uint4(0u, 0u, 0u, 0u);
     wait_vmem();
     __syncthreads();
+    scores<D>(K0, qf, k_lane_off, sa0, sa1);
+    update_max<D>(row_max(sa0, sa1, xhalf), ws, c, thr);
+    __syncthreads();  // every wave has read K(j) before its buffer is reused
+  }
+
+  // One pipeline step for block j (its scores settled against the running max;
+  // P(j-1) waiting in registers):
+  //   body  copy K(j2) and V(j) into the free buffers; S(j1) and
+  //         O += V(j-1) P(j-1) on the matrix cores; P(j) and the row max of
+  //         S(j1) on the vector ALUs.  No branches: a copy past the end of the
+  //         table becomes an out-of-range buffer read that fetches nothing.
+  //   tail  decide whether S(j1) moves the running max; then, after the
+  //         copies have landed, if it does (or at the last step) fold in
+  //         V(j) P(j) at once, rescale O and the denominator, and leave zero
+  //         probabilities pending.
+  // Kin/Vin hold K(j1)/V(j-1); Kfree/Vfree receive K(j2)/V(j).
+  auto step = [&](const f32x16& cur0, const f32x16& cur1, f32x16& nxt0, f32x16& nxt1,
+                  const bf16x8* pprev, bf16x8* pcur, char* Kin, char* Vin, char* Kfree,
+                  char* Vfree) {
+    dma_tile<D>(Kfree, krsrc, boff(j2, kb2), offk, wave_u);
+    dma_tile<D>(Vfree, vrsrc, boff(j, kb0), offv, wave_u);
+#if CA_SETPRIO
+    __builtin_amdgcn_s_setprio(1);  // matrix phase first: the other wave fills the VALU
+#endif
+    scores<D>(Kin, qf, k_lane_off, nxt0, nxt1);  // stale when j1 is past the end: unused
+    accumulate_pv<D>(Vin, pprev, v_lane_off, ws);
+    softmax_probs<D>(cur0, cur1, ws, pcur, c);
+    const float mx = row_max(nxt0, nxt1, xhalf);
+#if CA_SETPRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
+#if CA_ANCHOR_PROBS
+    // keep the probabilities inside the body so they overlap the matrix work
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x4 w = __builtin_bit_cast(u32x4, pcur[i]);
+      asm volatile("" : "+v"(w));
+      pcur[i] = __builtin_bit_cast(bf16x8, w);
+    }
+#endif
+    body_schedule<D>();
+    const bool last = j1 >= e;
+    const bool moves = !last && __any(mx > ws.m_used + thr);
+    const int j3 = next_plain(j2 + 1);
+    const int kb3 = j3 < e ? Trow[j3] : 0;
+    wait_vmem();
+    __syncthreads();
+    if (moves || last) {
+      accumulate_pv<D>(Vfree, pcur, v_lane_off, ws);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pcur[i] = bf16x8{};
+      if (moves) update_max<D>(mx, ws, c, thr);
+    }
     j = j1;
+    kb0 = kb1;
     j1 = j2;
     kb1 = kb2;
     j2 = j3;
     kb2 = kb3;
   };
-  while (j < nT) {
-    step(sa0, sa1, sb0, sb1, K1, V0, K0, V1);
-    if (j >= nT) break;
-    step(sb0, sb1, sa0, sa1, K0, V1, K1, V0);
+  while (j < e) {
+    step(sa0, sa1, sb0, sb1, pxb, pxa, K1, V1, K0, V0);
+    if (j >= e) break;
+    step(sb0, sb1, sa0, sa1, pxa, pxb, K0, V0, K1, V1);
+  }
+
+  // Blocks that straddle the workgroup's rows (usually one): one at a time,
+  // with the causal mask.
+  for (int jt = e; jt < nT; ++jt) {
+    const int kb = Trow[jt];
+    if (!valid(kb)) continue;
+    __syncthreads();  // every wave is done with the buffers
+    dma_tile<D>(K0, krsrc, static_cast<uint32_t>(kb) * (kBlk * D * 2), offk, wave_u);
+    dma_tile<D>(V0, vrsrc, static_cast<uint32_t>(kb) * (kBlk * D * 2), offv, wave_u);
+    wait_vmem();
+    __syncthreads();
+    scores<D>(K0, qf, k_lane_off, sa0, sa1);
+    mask_scores(sa0, sa1, kb, hh, qpos);
+    update_max<D>(row_max(sa0, sa1, xhalf), ws, c, thr);
+    bf16x8 pf[4];
+    softmax_probs<D>(sa0, sa1, ws, pf, c);
+    accumulate_pv<D>(V0, pf, v_lane_off, ws);
+    __syncthreads();
   }
 
   // ---- epilogue: O = acc / l, rows >= C written as 0
