@@ -14,10 +14,11 @@ from oracle import chunk_attention_ref, chunk_attention_rows_ref, union_tables_r
 F32_MAX_ABS = 1e-5
 BF16_MAX_ABS = 2e-2
 BF16_MEAN_ABS = 2e-3
-# The bf16 path sums the bf16-rounded probabilities in the softmax denominator;
-# each is within a relative 2^-9 of the exact value (round to nearest even), so
-# log(l) is within log(1 + 2^-9) ~= 1.95e-3 of the exact LSE, plus fp32 rounding.
-LSE_ABS = 2.5e-3
+# The bf16 path sums the bf16-rounded probabilities in the softmax denominator.
+# bf16 carries 8 significant bits, so round-to-nearest-even leaves each within a
+# relative 2^-8 of the exact value; log(l) is then within log(1 + 2^-8) ~= 3.9e-3
+# of the exact LSE, plus fp32 rounding of the scores and the exponentials.
+LSE_ABS = 4.5e-3
 
 
 def say(*a):

@@ -136,7 +136,7 @@ def test_bf16_closed_form_one_hot_block_counts():
     _, _, _, (O, _) = _run(w)
     Or, _ = oracle_full(w)
     err = np.abs(to_np(O) - Or)
-    # bf16 output rounding of a share in (0, 1]: relative 2^-9
+    # bf16 output rounding of a share in (0, 1]: relative 2^-8 (8 significant bits)
     assert np.all(err <= np.abs(Or) * 2.0 ** -8 + 1e-7)
     assert np.array_equal(to_np(O) != 0, Or != 0)
 
@@ -260,3 +260,48 @@ def test_binding_rejects_bad_arguments():
     with pytest.raises(ca.CompactAttnError) as e:
         ca.chunk_attention(d.q, d.k, d.v, T, lens, [1024], [192])  # chunk > C_max
     assert e.value.status == 2
+
+
+# ----------------------------------------------------------------------------- rare paths
+
+
+@pytest.mark.parametrize("D,growth", [(128, 0.35), (64, 0.5), (128, -0.03)])
+def test_bf16_running_max_moves(D, growth):
+    # Keys scaled by (1 + growth * block): with growth > 0 later blocks keep raising
+    # the row max past the kernel's rescale threshold, so the path that folds the
+    # pending P.V in early and rescales runs many times; growth < 0 never moves it.
+    w = gen.make_custom(2, 8, 2, D, [2048, 1024], [192, 128], "bf16", 31, _bern(0.5),
+                        C_max=192)
+    n_blk = w.L // 64
+    scale = (1.0 + growth * torch.arange(n_blk, dtype=torch.float32)).clamp_min(0.2)
+    w.k.copy_((w.k.float().view(w.B, w.H_kv, n_blk, 64, D) * scale.view(1, 1, n_blk, 1, 1))
+              .view_as(w.k).to(torch.bfloat16))
+    say(f"running max moves: D={D} growth={growth}")
+    _, _, _, (O, lse) = _run(w)
+    Or, lr = oracle_full(w)
+    compare_bf16(to_np(O), Or, "O")
+    live = np.isfinite(lr)
+    np.testing.assert_allclose(to_np(lse)[live], lr[live], rtol=0, atol=LSE_ABS)
+
+
+def test_bf16_junk_table_entries_are_skipped():
+    # Entries outside [0, n_kv_blocks) anywhere in T, and len past NKB_max, are never
+    # dereferenced: the output equals the run on the clean table bit for bit.
+    w = gen.make_custom(2, 8, 2, 128, [1024, 512], [128, 128], "bf16", 17, _bern(0.3),
+                        NKB_max=40)
+    d = Dev(w)
+    T, lens = d.tables()
+    O = d.attention(T, lens).clone()
+    Tj = T.clone()
+    lj = lens.clone()
+    for b in range(w.B):
+        for g in range(w.H_kv):
+            n = int(lens[b, g])
+            row = T[b, g, :n].tolist()
+            junk = [-5] + row[:n // 2] + [10 ** 6, -1] + row[n // 2:] + [w.n_kv_blocks[b]]
+            Tj[b, g, :] = -1
+            Tj[b, g, :len(junk)] = torch.tensor(junk, dtype=torch.int32)
+            lj[b, g] = 10 ** 6 if (b + g) % 2 else len(junk)
+    O2 = d.attention(Tj, lj)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2)
