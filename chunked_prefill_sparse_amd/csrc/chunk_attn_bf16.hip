@@ -219,71 +219,27 @@ __device__ __forceinline__ void accumulate_pv(const char* __restrict__ Vs, const
   }
 }
 
-// Instruction interleaving for one pipeline body (scheduling hints only):
-// after the copies are issued, each matrix instruction is followed by LDS
-// reads for the next ones and a share of the softmax vector work, so the
-// matrix pipe is fed while the vector ALUs work.  Groups that cannot be
-// filled are skipped by the scheduler.
-#ifndef CA_SCHED_PATTERN
-#define CA_SCHED_PATTERN 5
-#endif
+// Instruction interleaving for one pipeline body (scheduling hints only): after
+// the tile copies are issued, S(j1) and P.V(j-1) matrix instructions
+// alternate, each followed by LDS reads for the ones ahead and a share of the
+// vector work.  Groups that cannot be filled are skipped by the scheduler.
+// (Measured on MI355X: interleaving the softmax exponentials between the
+// matrix instructions of the same wave was slower than leaving them after the
+// matrix phase, where the other wave on the SIMD overlaps them.)
 template <int D>
 __device__ __forceinline__ void body_schedule() {
   constexpr int DS = D / 16;  // S matrix instructions per key tile
-#if CA_SCHED_PATTERN == 1
-  __builtin_amdgcn_sched_group_barrier(0x020, 2 * Tile<D>::kDmaPerWave, 0);  // tile copies
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                         // first K reads
-#pragma unroll
-  for (int i = 0; i < 2 * DS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // S(j1) MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next LDS read
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // probabilities of block j
-  }
-#pragma unroll
-  for (int i = 0; i < 2 * DS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // P.V MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V reads
-    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // row max of S(j1)
-  }
-#elif CA_SCHED_PATTERN == 4 || CA_SCHED_PATTERN == 5
-  // S(j1) and P.V(j-1) matrix instructions alternate, each followed by LDS
-  // reads for the ones ahead and a share of the vector work
-  constexpr int VA = CA_SCHED_PATTERN == 4 ? 4 : 3;
   __builtin_amdgcn_sched_group_barrier(0x020, 2 * Tile<D>::kDmaPerWave, 0);  // tile copies
   __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);                         // first reads
 #pragma unroll
   for (int i = 0; i < 2 * DS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, VA, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, VA, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
   }
-#elif CA_SCHED_PATTERN == 2 || CA_SCHED_PATTERN == 3
-  constexpr int VA = CA_SCHED_PATTERN == 2 ? 6 : 7;  // VALU per S MFMA
-  constexpr int VB = CA_SCHED_PATTERN == 2 ? 2 : 1;  // VALU per P.V MFMA
-  __builtin_amdgcn_sched_group_barrier(0x020, 2 * Tile<D>::kDmaPerWave, 0);  // tile copies
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                         // first K reads
-#pragma unroll
-  for (int i = 0; i < 2 * DS - 4; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // S(j1) MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // K read
-    __builtin_amdgcn_sched_group_barrier(0x002, VA, 0);  // probabilities of block j
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // S(j1) MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // first V reads
-    __builtin_amdgcn_sched_group_barrier(0x002, VA, 0);  // probabilities of block j
-  }
-#pragma unroll
-  for (int i = 0; i < 2 * DS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // P.V MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V reads ~5 MFMAs ahead
-    __builtin_amdgcn_sched_group_barrier(0x002, VB, 0); // row max of S(j1)
-  }
-#endif
 }
 
 template <int D>
@@ -485,25 +441,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
                   char* Vfree) {
     dma_tile<D>(Kfree, krsrc, boff(j2, kb2), offk, wave_u);
     dma_tile<D>(Vfree, vrsrc, boff(j, kb0), offv, wave_u);
-#if CA_SETPRIO
-    __builtin_amdgcn_s_setprio(1);  // matrix phase first: the other wave fills the VALU
-#endif
     scores<D>(Kin, qf, k_lane_off, nxt0, nxt1);  // stale when j1 is past the end: unused
     accumulate_pv<D>(Vin, pprev, v_lane_off, ws);
     softmax_probs<D>(cur0, cur1, ws, pcur, c);
     const float mx = row_max(nxt0, nxt1, xhalf);
-#if CA_SETPRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
-#if CA_ANCHOR_PROBS
-    // keep the probabilities inside the body so they overlap the matrix work
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x4 w = __builtin_bit_cast(u32x4, pcur[i]);
-      asm volatile("" : "+v"(w));
-      pcur[i] = __builtin_bit_cast(bf16x8, w);
-    }
-#endif
     body_schedule<D>();
     const bool last = j1 >= e;
     const bool moves = !last && __any(mx > ws.m_used + thr);
