@@ -7,7 +7,9 @@ the 128K-context LLaMA-3.1-8B-shaped chunk: B=1, 32 query / 8 KV heads, D=128,
 129024 cached tokens + a 2048-token chunk, bf16, per-head mask = sink + last 8
 prior blocks + Bernoulli(0.05) per (head, Q-block, KV-block) cell.  The dense
 baseline (all-ones mask, the same kernel fed every block) and a column-shared
-mask variant (one draw per (head, KV-block)) are timed beside it.
+mask variant (one draw per (head, KV-block)) are timed beside it, and so is
+the explicit-compaction baseline (ca_compact_kv gathers the selected blocks,
+then the same kernel runs on the compact buffer).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
@@ -15,7 +17,7 @@ prints ONE JSON line.  ``value`` is the effective TFLOP/s of a whole step
 (algorithmic FLOPs: 4*D per admissible query/key pair over the selected
 blocks, causal triangle included).  Inputs are resident in HBM before timing.
 
-Profiling helpers (for rocprofv3 runs): ``--profile attn|union|copy`` runs only
+Profiling helpers (for rocprofv3 runs): ``--profile attn|union|compact|copy`` runs only
 that kernel a few times (``copy`` = a plain device copy of known size, used to
 scale the HBM byte counters).
 """
@@ -176,7 +178,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--reps", type=int, default=50, help="per-kernel timed calls")
-    ap.add_argument("--profile", choices=["attn", "union", "copy"], default=None)
+    ap.add_argument("--profile", choices=["attn", "union", "copy", "compact"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     args = ap.parse_args()
@@ -226,11 +228,15 @@ def main():
     def attn(T, lens):
         return ca.chunk_attention(q, k, v, T, lens, w.prior, w.chunk, w.scale, out=out)
 
-    if args.profile in ("attn", "union"):
+    if args.profile in ("attn", "union", "compact"):
         T, lens = tables("pairwise")
+        if args.profile == "compact":
+            k_out, v_out, T_out = ca.compact_kv(k, v, T, lens, w.prior, w.chunk)
         for i in range(max(args.steps, 1)):
             if args.profile == "attn":
                 attn(T, lens)
+            elif args.profile == "compact":
+                ca.compact_kv(k, v, T, lens, w.prior, w.chunk, k_out, v_out, T_out)
             else:
                 tables("pairwise")
             torch.cuda.synchronize()
@@ -277,6 +283,31 @@ def main():
         log(f"{name}: step {ms_step:.3f} ms, attention {a_med:.3f} ms "
             f"({results[name]['eff_tflops_attn']:.0f} TFLOP/s), union "
             f"{results[name]['union_us_median']:.1f} us, mean len {lh.mean():.0f}")
+    # Explicit-compaction baseline: gather the selected blocks, then run the same
+    # kernel on the compact buffer; zero-copy execution skips the gather.
+    compaction = {}
+    k_out, v_out = torch.empty_like(k), torch.empty_like(v)
+    for name in ("pairwise", "colshared"):
+        T, lens = tables(name)
+        k_out, v_out, T_out = ca.compact_kv(k, v, T, lens, w.prior, w.chunk, k_out, v_out)
+        torch.cuda.synchronize()
+        blocks = int(lens.sum())
+        copy_ms = time_calls(lambda: ca.compact_kv(k, v, T, lens, w.prior, w.chunk, k_out,
+                                                   v_out, T_out), args.reps, stream)
+        attn_c_ms = time_calls(lambda: ca.chunk_attention(q, k_out, v_out, T_out, lens, w.prior,
+                                                          w.chunk, w.scale, out=out),
+                               args.reps, stream)
+        c_med, a_med = statistics.median(copy_ms), statistics.median(attn_c_ms)
+        moved = 2 * 2 * blocks * 64 * w.D * 2  # K and V, read once and written once
+        zc = results[name]["attn_ms_median"]
+        compaction[name] = dict(
+            copy_ms=round(c_med, 4), copy_GBps=round(moved / (c_med * 1e-3) / 1e9, 1),
+            attn_ms_compact=round(a_med, 4), attn_ms_zero_copy=round(zc, 4),
+            x_zero_copy_vs_compaction=round((c_med + a_med) / zc, 4))
+        log(f"{name}: compaction copy {c_med:.3f} ms ({compaction[name]['copy_GBps']:.0f} GB/s), "
+            f"attention on compact {a_med:.3f} ms, zero-copy {zc:.3f} ms")
+    del k_out, v_out
+
     for name in results:
         results[name]["x_vs_dense_attn"] = results["dense"]["attn_ms_median"] / results[name]["attn_ms_median"]
         results[name]["x_vs_dense_step"] = results["dense"]["ms_per_step"] / results[name]["ms_per_step"]
@@ -324,6 +355,7 @@ def main():
         "x_vs_dense": round(main_r["x_vs_dense_step"], 4),
         "variants": {n_: {k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in r.items()}
                      for n_, r in results.items()},
+        "compaction": compaction,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

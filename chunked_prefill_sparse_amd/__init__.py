@@ -21,8 +21,8 @@ import torch
 from . import _lib
 from ._lib import CA_BLOCK, CA_MAX_BATCH, CompactAttnError  # noqa: F401
 
-__all__ = ["build_union_tables", "chunk_attention", "tables_to_csr", "CompactAttnError",
-           "library_path"]
+__all__ = ["build_union_tables", "chunk_attention", "tables_to_csr", "compact_kv",
+           "CompactAttnError", "library_path"]
 
 
 def library_path() -> str:
@@ -144,3 +144,48 @@ def tables_to_csr(T: torch.Tensor, lens: torch.Tensor, L: int,
                                      indptr.data_ptr(), indices.data_ptr(), _stream_ptr(stream))
     _lib.check(st, "ca_tables_to_csr")
     return indptr, indices
+
+
+def compact_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, T: torch.Tensor,
+               lens: torch.Tensor, prior_len: Sequence[int], chunk_len: Sequence[int],
+               k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None,
+               T_out: Optional[torch.Tensor] = None,
+               stream: Optional[torch.cuda.Stream] = None):
+    """Explicit KV compaction (the copy that zero-copy execution avoids).
+
+    Copies the selected prior blocks of each (b, g) into contiguous blocks that
+    end where the chunk starts, keeps chunk blocks in place, and returns
+    (k_out, v_out, T_out) such that ``chunk_attention(q, k_out, v_out, T_out,
+    lens, ...)`` equals ``chunk_attention(q, k_cache, v_cache, T, lens, ...)``.
+    Blocks of k_out/v_out that no table entry lands on are left unwritten.
+    """
+    _need_cuda("k_cache", k_cache)
+    if k_cache.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("k_cache must be bfloat16 or float32")
+    _need_cuda("v_cache", v_cache, k_cache.dtype)
+    _need_cuda("T", T, torch.int32)
+    _need_cuda("lens", lens, torch.int32)
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, H_kv, L, D] and alike")
+    B, H_kv, L, D = k_cache.shape
+    if T.dim() != 3 or tuple(T.shape[:2]) != (B, H_kv) or tuple(lens.shape) != (B, H_kv):
+        raise ValueError("T must be [B, H_kv, NKB_max] and lens [B, H_kv]")
+    NKB_max = T.shape[2]
+    if k_out is None:
+        k_out = torch.empty_like(k_cache)
+    if v_out is None:
+        v_out = torch.empty_like(v_cache)
+    if T_out is None:
+        T_out = torch.empty_like(T)
+    _need_cuda("k_out", k_out, k_cache.dtype)
+    _need_cuda("v_out", v_out, k_cache.dtype)
+    _need_cuda("T_out", T_out, torch.int32)
+    if k_out.shape != k_cache.shape or v_out.shape != k_cache.shape or T_out.shape != T.shape:
+        raise ValueError("outputs must have the shapes of the caches and of T")
+    dt = _lib.CA_BF16 if k_cache.dtype == torch.bfloat16 else _lib.CA_F32
+    st = _lib.lib().ca_compact_kv(
+        k_cache.data_ptr(), v_cache.data_ptr(), T.data_ptr(), lens.data_ptr(), NKB_max,
+        _host_ints("prior_len", prior_len, B), _host_ints("chunk_len", chunk_len, B), B, H_kv,
+        L, D, dt, k_out.data_ptr(), v_out.data_ptr(), T_out.data_ptr(), _stream_ptr(stream))
+    _lib.check(st, "ca_compact_kv")
+    return k_out, v_out, T_out

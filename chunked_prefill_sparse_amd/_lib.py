@@ -21,6 +21,7 @@ EXPORTED = (
     "ca_build_union_tables",
     "ca_chunk_attention",
     "ca_tables_to_csr",
+    "ca_compact_kv",
     "ca_status_string",
     "ca_last_hip_error",
 )
@@ -44,6 +45,9 @@ def _declare(lib):
     lib.ca_chunk_attention.restype = _i32
     lib.ca_tables_to_csr.argtypes = [_vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _vp]
     lib.ca_tables_to_csr.restype = _i32
+    lib.ca_compact_kv.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32p, _i32p, _i32, _i32, _i64, _i32,
+                                  _i32, _vp, _vp, _vp, _vp]
+    lib.ca_compact_kv.restype = _i32
     lib.ca_status_string.argtypes = [_i32]
     lib.ca_status_string.restype = ctypes.c_char_p
     lib.ca_last_hip_error.argtypes = []

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcompact_attn.so")
-SOURCES = ("capi.hip", "union_tables.hip", "chunk_attn_bf16.hip", "chunk_attn_f32.hip")
+SOURCES = ("capi.hip", "union_tables.hip", "chunk_attn_bf16.hip", "chunk_attn_f32.hip",
+           "compact_kv.hip")
 ARCH = "gfx950"
 
 

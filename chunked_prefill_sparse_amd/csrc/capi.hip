@@ -141,4 +141,34 @@ CA_EXPORT ca_status ca_chunk_attention(const void* Q, const void* K_cache, const
       stream));
 }
 
+CA_EXPORT ca_status ca_compact_kv(const void* K_cache, const void* V_cache, const int32_t* T,
+                                  const int32_t* len, int NKB_max, const int32_t* prior_len,
+                                  const int32_t* chunk_len, int B, int H_kv, int64_t L, int D,
+                                  ca_dtype dtype, void* K_out, void* V_out, int32_t* T_out,
+                                  hipStream_t stream) {
+  if (!K_cache || !V_cache || !T || !len || !prior_len || !chunk_len || !K_out || !V_out ||
+      !T_out)
+    return CA_ERR_NULL;
+  if (dtype != CA_F32 && dtype != CA_BF16) return CA_ERR_DTYPE;
+  if (B < 1 || B > CA_MAX_BATCH || H_kv < 1 || L < 1 || NKB_max < 1 ||
+      static_cast<int64_t>(B) * H_kv > (1 << 24))
+    return CA_ERR_SHAPE;
+  if (D != 64 && D != 128) return CA_ERR_UNSUPPORTED;
+  if (!aligned16(K_cache) || !aligned16(V_cache) || !aligned16(K_out) || !aligned16(V_out))
+    return CA_ERR_UNSUPPORTED;
+  ca::SeqInfo seq;
+  memset(&seq, 0, sizeof(seq));
+  for (int b = 0; b < B; ++b) {
+    const int64_t P = prior_len[b], C = chunk_len[b];
+    if (P < 0 || C < 0 || P + C > L || P + C > static_cast<int64_t>(NKB_max) * CA_BLOCK)
+      return CA_ERR_SHAPE;
+    if (P % CA_BLOCK != 0 || C % CA_BLOCK != 0) return CA_ERR_UNSUPPORTED;
+    seq.prior[b] = static_cast<int32_t>(P);
+    seq.chunk[b] = static_cast<int32_t>(C);
+  }
+  const int esz = dtype == CA_BF16 ? 2 : 4;
+  return hip_status(ca::launch_compact_kv(K_cache, V_cache, T, len, NKB_max, B, H_kv, L, D, esz,
+                                          seq, K_out, V_out, T_out, stream));
+}
+
 }  // extern "C"

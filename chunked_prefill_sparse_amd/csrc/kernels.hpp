@@ -55,4 +55,10 @@ hipError_t launch_chunk_attn_f32(const float* Q, const float* K, const float* V,
                                  int B, int D, const AttnParams& p, const SeqInfo& seq,
                                  hipStream_t stream);
 
+// Explicit KV compaction (baseline); esz = element size in bytes.
+hipError_t launch_compact_kv(const void* K, const void* V, const int32_t* T, const int32_t* len,
+                             int NKB_max, int B, int H_kv, int64_t L, int D, int esz,
+                             const SeqInfo& seq, void* Ko, void* Vo, int32_t* To,
+                             hipStream_t stream);
+
 }  // namespace ca

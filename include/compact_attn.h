@@ -155,6 +155,43 @@ CA_EXPORT ca_status ca_tables_to_csr(const int32_t* T, const int32_t* len, int B
                            int64_t L, int32_t* kv_indptr, int32_t* kv_indices,
                            hipStream_t stream);
 
+/*
+ * ca_compact_kv -- explicit KV compaction: the selected blocks are gathered
+ * into a compact buffer before a dense kernel runs.  CompactAttention,
+ * abstract: its block tables let the attention read the selected blocks in
+ * place, so this copy (the KV-copy overhead it names for token-level
+ * selection) is avoided.  A baseline to measure that saving against, not part
+ * of the zero-copy path.
+ *
+ * For each (b, g) with n = len[b,g] entries, of which the first p are prior
+ * blocks (T[b,g,j] < prior_len[b]/64), block T[b,g,j] of K_cache/V_cache is
+ * copied to block
+ *     dst(j) = prior_len[b]/64 - p + j   (j < p: prior blocks, packed to end
+ *                                         where the chunk starts)
+ *     dst(j) = T[b,g,j]                 (j >= p: current-chunk blocks stay)
+ * of K_out/V_out, and T_out[b,g,j] = dst(j) (then -1 up to NKB_max).  So
+ * ca_chunk_attention(Q, K_out, V_out, T_out, len, prior_len, chunk_len, ...)
+ * computes exactly what it computes on the original cache and table (same
+ * blocks, same order, same causal positions).  Entries outside
+ * [0, (prior_len+chunk_len)/64), or whose destination would fall outside it,
+ * are not copied and get T_out = -1.
+ *
+ * K_cache, V_cache  device [B, H_kv, L, D] (dtype), 16-byte aligned.
+ * T, len            device, as produced by ca_build_union_tables (ascending).
+ * K_out, V_out      device [B, H_kv, L, D] (out); blocks not selected are not written.
+ * T_out             device int32 [B, H_kv, NKB_max] (out).
+ * prior_len, chunk_len  host int32 [B], as for ca_chunk_attention (multiples
+ *                   of 64, prior+chunk <= min(L, 64*NKB_max)).
+ * B in [1, CA_MAX_BATCH], B*H_kv <= 2^24, D in {64, 128}.
+ * The outputs must not overlap the inputs.  Asynchronous on `stream`.
+ * Errors: CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_DTYPE, CA_ERR_UNSUPPORTED, CA_ERR_HIP.
+ */
+CA_EXPORT ca_status ca_compact_kv(const void* K_cache, const void* V_cache, const int32_t* T,
+                                  const int32_t* len, int NKB_max, const int32_t* prior_len,
+                                  const int32_t* chunk_len, int B, int H_kv, int64_t L, int D,
+                                  ca_dtype dtype, void* K_out, void* V_out, int32_t* T_out,
+                                  hipStream_t stream);
+
 /* Human-readable name of a status code (static string; never NULL). */
 CA_EXPORT const char* ca_status_string(ca_status s);
 

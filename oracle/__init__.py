@@ -20,6 +20,10 @@ Contents (each function cites the passage it follows):
 * ``chunk_attention_dense_masked_ref`` -- the same result computed as dense
   attention over all cached keys with a -inf mask (second formulation).
 * ``tables_to_csr_ref`` -- the (kv_indptr, kv_indices) view of the tables.
+* ``compact_kv_ref`` -- explicit KV compaction (the copy zero-copy execution
+  avoids): selected prior blocks packed to end where the chunk starts.  Pinned
+  by a hand-worked case and by the invariant that attention over the
+  compacted cache equals attention over the original one.
 
 Float work is float64 throughout; outputs are float32.
 """
@@ -31,3 +35,4 @@ from .attention_ref import (  # noqa: F401
     chunk_attention_ref,
     chunk_attention_rows_ref,
 )
+from .compact_ref import compact_kv_ref  # noqa: F401

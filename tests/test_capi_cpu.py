@@ -102,3 +102,25 @@ def test_attention_validation(kw, status):
 ])
 def test_csr_validation(args, status):
     assert _lib.lib().ca_tables_to_csr(*args, None) == status
+
+
+def _compact(lib, **kw):
+    a = dict(K=FAKE, V=FAKE, T=FAKE, len=FAKE, NKB_max=20, prior=_ints(1024), chunk=_ints(256),
+             B=1, H_kv=1, L=1280, D=64, dtype=1, Ko=FAKE, Vo=FAKE, To=FAKE)
+    a.update(kw)
+    return lib.ca_compact_kv(a["K"], a["V"], a["T"], a["len"], a["NKB_max"], a["prior"],
+                             a["chunk"], a["B"], a["H_kv"], a["L"], a["D"], a["dtype"], a["Ko"],
+                             a["Vo"], a["To"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=None), 1), (dict(Vo=None), 1), (dict(To=None), 1), (dict(chunk=None), 1),
+    (dict(dtype=9), 3),
+    (dict(B=0), 2), (dict(B=129), 2), (dict(H_kv=0), 2),
+    (dict(L=1000), 2),                         # prior + chunk > L
+    (dict(NKB_max=19), 2),                     # table too short for the sequence
+    (dict(prior=_ints(-64)), 2),
+    (dict(D=80), 4), (dict(prior=_ints(1000)), 4), (dict(Ko=FAKE + 4), 4),
+])
+def test_compact_validation(kw, status):
+    assert _compact(_lib.lib(), **kw) == status
