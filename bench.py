@@ -7,9 +7,13 @@ the 128K-context LLaMA-3.1-8B-shaped chunk: B=1, 32 query / 8 KV heads, D=128,
 129024 cached tokens + a 2048-token chunk, bf16, per-head mask = sink + last 8
 prior blocks + Bernoulli(0.05) per (head, Q-block, KV-block) cell.  The dense
 baseline (all-ones mask, the same kernel fed every block) and a column-shared
-mask variant (one draw per (head, KV-block)) are timed beside it, and so is
+mask variant (one draw per (head, KV-block)) and a group-shared one (one draw
+per (KV group, KV-block): every mask row of a group is the group's union) are
+timed beside it, and so is
 the explicit-compaction baseline (ca_compact_kv gathers the selected blocks,
-then the same kernel runs on the compact buffer).
+then the same kernel runs on the compact buffer), and the block-sparse-kernel
+baseline (ca_chunk_attention_rows: each Q-block of each head attends its own
+mask row, no union).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
@@ -71,6 +75,22 @@ def admissible_pairs(T: np.ndarray, lens: np.ndarray, prior, chunk, G: int) -> i
                 pairs += int(cnt.sum())
             total += pairs * G
     return int(total)
+
+
+def admissible_pairs_rows(mask: np.ndarray, prior, chunk) -> int:
+    """(query, key) pairs of block-sparse execution: Q-block qb of each head
+    attends the blocks of its own mask row; 64*64 pairs per block wholly below
+    the Q-block, the causal triangle (2080 pairs) on its diagonal block."""
+    total = 0
+    for b in range(mask.shape[0]):
+        P, C = int(prior[b]), int(chunk[b])
+        nq, pblk = C // 64, P // 64
+        m = mask[b, :, :nq, :pblk + nq] != 0
+        below = np.tril(np.ones((nq, nq), bool), -1)  # chunk blocks wholly below each Q-block
+        full = m[:, :, :pblk].sum() + (m[:, :, pblk:] & below[None]).sum()
+        diag = m[:, np.arange(nq), pblk + np.arange(nq)].sum()
+        total += int(full) * 64 * 64 + int(diag) * 2080
+    return total
 
 
 def algorithmic(w, T, lens):
@@ -212,7 +232,7 @@ def main():
     log(f"generating {WORKLOAD} (pairwise mask) ...")
     w = gen.make_workload(WORKLOAD, variant="pairwise")
     variants = {"pairwise": w}
-    for vname in ("dense", "colshared"):
+    for vname in ("dense", "colshared", "groupshared"):
         wv = gen.make_workload(WORKLOAD, variant=vname, with_tensors=False)
         wv.q, wv.k, wv.v = w.q, w.k, w.v
         variants[vname] = wv
@@ -244,7 +264,7 @@ def main():
         return
 
     results = {}
-    for name in ("pairwise", "dense", "colshared"):
+    for name in ("pairwise", "dense", "colshared", "groupshared"):
         x = variants[name]
         T, lens = tables(name)
         torch.cuda.synchronize()
@@ -308,6 +328,45 @@ def main():
             f"attention on compact {a_med:.3f} ms, zero-copy {zc:.3f} ms")
     del k_out, v_out
 
+    # Block-sparse-kernel baseline: each Q-block of each head attends its own
+    # mask row (per-row lists, no union); also the same kernel fed the union as
+    # every row's list, which does the union's work in the per-Q-block layout.
+    sparse = {}
+    for name in ("pairwise", "colshared", "groupshared"):
+        x = variants[name]
+        Tr, lr = ca.build_row_tables(masks[name], x.n_kv_blocks)
+        torch.cuda.synchronize()
+        pairs_rows = admissible_pairs_rows(x.mask, x.prior, x.chunk)
+        flops_rows = 4 * w.D * pairs_rows
+        rows_ms = time_calls(lambda: ca.chunk_attention_rows(q, k, v, Tr, lr, w.prior, w.chunk,
+                                                             w.scale, out=out),
+                             args.reps, stream)
+        build_ms = time_calls(lambda: ca.build_row_tables(masks[name], x.n_kv_blocks, Tr, lr),
+                              args.reps, stream)
+        T, lens = tables(name)
+        G, NQ = x.G, x.mask.shape[2]
+        Tw = T.repeat_interleave(G, dim=1)[:, :, None, :].expand(-1, -1, NQ, -1).contiguous()
+        lw = lens.repeat_interleave(G, dim=1)[:, :, None].expand(-1, -1, NQ).contiguous()
+        wide_ms = time_calls(lambda: ca.chunk_attention_rows(q, k, v, Tw, lw, w.prior, w.chunk,
+                                                             w.scale, out=out),
+                             args.reps, stream)
+        r_med, b_med, w_med = (statistics.median(rows_ms), statistics.median(build_ms),
+                               statistics.median(wide_ms))
+        u = results[name]
+        sparse[name] = dict(
+            attn_ms=round(r_med, 4), lists_us=round(b_med * 1e3, 2),
+            eff_tflops=round(flops_rows / (r_med * 1e-3) / 1e12, 1),
+            flops_frac_of_union=round(flops_rows / u["flops"], 4),
+            mean_list_blocks=round(float(lr.float().mean()), 1),
+            union_lists_attn_ms=round(w_med, 4),
+            union_lists_eff_tflops=round(u["flops"] / (w_med * 1e-3) / 1e12, 1),
+            x_union_kernel_vs_rows_kernel_same_work=round(w_med / u["attn_ms_median"], 4),
+            x_union_vs_sparse=round((r_med + b_med) / (u["attn_ms_median"] + u["union_us_median"] * 1e-3), 4))
+        log(f"{name}: sparse rows {r_med:.3f} ms ({sparse[name]['eff_tflops']:.0f} TFLOP/s, "
+            f"{sparse[name]['flops_frac_of_union']:.3f} of the union's work); rows kernel on the "
+            f"union lists {w_med:.3f} ms ({sparse[name]['union_lists_eff_tflops']:.0f} TFLOP/s)")
+        del Tw, lw
+
     for name in results:
         results[name]["x_vs_dense_attn"] = results["dense"]["attn_ms_median"] / results[name]["attn_ms_median"]
         results[name]["x_vs_dense_step"] = results["dense"]["ms_per_step"] / results[name]["ms_per_step"]
@@ -356,6 +415,7 @@ def main():
         "variants": {n_: {k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in r.items()}
                      for n_, r in results.items()},
         "compaction": compaction,
+        "block_sparse": sparse,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

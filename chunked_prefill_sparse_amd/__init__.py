@@ -22,7 +22,7 @@ from . import _lib
 from ._lib import CA_BLOCK, CA_MAX_BATCH, CompactAttnError  # noqa: F401
 
 __all__ = ["build_union_tables", "chunk_attention", "tables_to_csr", "compact_kv",
-           "CompactAttnError", "library_path"]
+           "build_row_tables", "chunk_attention_rows", "CompactAttnError", "library_path"]
 
 
 def library_path() -> str:
@@ -79,6 +79,81 @@ def build_union_tables(mask: torch.Tensor, H_kv: int, n_q_blocks: Sequence[int],
         _stream_ptr(stream))
     _lib.check(st, "ca_build_union_tables")
     return T, lens
+
+
+def build_row_tables(mask: torch.Tensor, n_kv_blocks: Sequence[int],
+                     T: Optional[torch.Tensor] = None, lens: Optional[torch.Tensor] = None,
+                     stream: Optional[torch.cuda.Stream] = None
+                     ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-(head, Q-block) block lists of a block-sparse kernel (no union):
+    mask uint8 [B, H_q, NQ_max, NKB_max] -> (T_rows int32 [B, H_q, NQ_max, NKB_max]
+    ascending, -1 padded; lens int32 [B, H_q, NQ_max]).  The union builder on the
+    mask viewed as one-row groups."""
+    _need_cuda("mask", mask, torch.uint8)
+    if mask.dim() != 4:
+        raise ValueError("mask must be [B, H_q, NQ_max, NKB_max]")
+    B, H_q, NQ_max, NKB_max = mask.shape
+    rows = mask.view(B, H_q * NQ_max, 1, NKB_max)
+    if T is not None:
+        T = T.view(B, H_q * NQ_max, NKB_max)
+    if lens is not None:
+        lens = lens.view(B, H_q * NQ_max)
+    T, lens = build_union_tables(rows, H_q * NQ_max, [1] * B, n_kv_blocks, T, lens, stream)
+    return T.view(B, H_q, NQ_max, NKB_max), lens.view(B, H_q, NQ_max)
+
+
+def _attention_args(q, k_cache, v_cache, scale, out, lse, return_lse):
+    _need_cuda("q", q)
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q must be bfloat16 or float32")
+    _need_cuda("k_cache", k_cache, q.dtype)
+    _need_cuda("v_cache", v_cache, q.dtype)
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B,H_q,C_max,D], caches [B,H_kv,L,D]")
+    B, H_q, C_max, D = q.shape
+    Bk, H_kv, L, Dk = k_cache.shape
+    if Bk != B or Dk != D:
+        raise ValueError("cache batch / head dim do not match q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _need_cuda("out", out, q.dtype)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H_q, C_max), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need_cuda("lse", lse, torch.float32)
+        if tuple(lse.shape) != (B, H_q, C_max):
+            raise ValueError("lse must be [B, H_q, C_max]")
+    dt = _lib.CA_BF16 if q.dtype == torch.bfloat16 else _lib.CA_F32
+    return B, H_q, H_kv, C_max, L, D, float(scale), out, lse, dt
+
+
+def chunk_attention_rows(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         T_rows: torch.Tensor, lens_rows: torch.Tensor, prior_len: Sequence[int],
+                         chunk_len: Sequence[int], scale: Optional[float] = None,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         return_lse: bool = False, stream: Optional[torch.cuda.Stream] = None):
+    """Block-sparse-kernel execution (the baseline the union replaces): each
+    64-row Q-block of each head attends the blocks of its own list
+    T_rows[b, h, qb] (from ``build_row_tables``)."""
+    B, H_q, H_kv, C_max, L, D, scale, out, lse, dt = _attention_args(
+        q, k_cache, v_cache, scale, out, lse, return_lse)
+    _need_cuda("T_rows", T_rows, torch.int32)
+    _need_cuda("lens_rows", lens_rows, torch.int32)
+    if T_rows.dim() != 4 or tuple(T_rows.shape[:2]) != (B, H_q) or \
+            tuple(lens_rows.shape) != tuple(T_rows.shape[:3]):
+        raise ValueError("T_rows must be [B, H_q, NQ_max, NKB_max] and lens_rows [B, H_q, NQ_max]")
+    NQ_max, NKB_max = T_rows.shape[2], T_rows.shape[3]
+    st = _lib.lib().ca_chunk_attention_rows(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), T_rows.data_ptr(),
+        lens_rows.data_ptr(), NQ_max, NKB_max, _host_ints("prior_len", prior_len, B),
+        _host_ints("chunk_len", chunk_len, B), B, H_q, H_kv, C_max, L, D, CA_BLOCK, scale, dt,
+        out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream_ptr(stream))
+    _lib.check(st, "ca_chunk_attention_rows")
+    return (out, lse) if return_lse else out
 
 
 def chunk_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

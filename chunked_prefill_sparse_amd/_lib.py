@@ -20,6 +20,7 @@ CA_MAX_BATCH = 128
 EXPORTED = (
     "ca_build_union_tables",
     "ca_chunk_attention",
+    "ca_chunk_attention_rows",
     "ca_tables_to_csr",
     "ca_compact_kv",
     "ca_status_string",
@@ -43,6 +44,10 @@ def _declare(lib):
                                        _i32, _i32, _i64, _i32, _i32, ctypes.c_float, _i32, _vp,
                                        _vp, _vp]
     lib.ca_chunk_attention.restype = _i32
+    lib.ca_chunk_attention_rows.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32p, _i32p,
+                                            _i32, _i32, _i32, _i32, _i64, _i32, _i32,
+                                            ctypes.c_float, _i32, _vp, _vp, _vp]
+    lib.ca_chunk_attention_rows.restype = _i32
     lib.ca_tables_to_csr.argtypes = [_vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _vp]
     lib.ca_tables_to_csr.restype = _i32
     lib.ca_compact_kv.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32p, _i32p, _i32, _i32, _i64, _i32,

@@ -81,18 +81,23 @@ CA_EXPORT ca_status ca_tables_to_csr(const int32_t* T, const int32_t* len, int B
                                              kv_indptr, kv_indices, stream));
 }
 
-CA_EXPORT ca_status ca_chunk_attention(const void* Q, const void* K_cache, const void* V_cache,
-                                       const int32_t* T, const int32_t* len, int NKB_max,
-                                       const int32_t* prior_len, const int32_t* chunk_len,
-                                       int B, int H_q, int H_kv, int C_max, int64_t L, int D,
-                                       int block, float scale, ca_dtype dtype, void* O,
-                                       float* lse, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by both table layouts: validation, sequence order, launch parameters.
+ca_status attention(const void* Q, const void* K_cache, const void* V_cache, const int32_t* T,
+                    const int32_t* len, int NQ_max, int NKB_max, const int32_t* prior_len,
+                    const int32_t* chunk_len, int B, int H_q, int H_kv, int C_max, int64_t L,
+                    int D, int block, float scale, ca_dtype dtype, void* O, float* lse,
+                    bool row_tables, hipStream_t stream) {
   if (!Q || !K_cache || !V_cache || !T || !len || !prior_len || !chunk_len || !O)
     return CA_ERR_NULL;
   if (dtype != CA_F32 && dtype != CA_BF16) return CA_ERR_DTYPE;
   if (B < 1 || B > CA_MAX_BATCH || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || C_max < 1 ||
       L < 1 || NKB_max < 1 || !(scale > 0.f) || !isfinite(scale))
     return CA_ERR_SHAPE;
+  if (row_tables && NQ_max * CA_BLOCK < C_max) return CA_ERR_SHAPE;
   if (block != CA_BLOCK || (D != 64 && D != 128)) return CA_ERR_UNSUPPORTED;
   if (!aligned16(Q) || !aligned16(K_cache) || !aligned16(V_cache) || !aligned16(O) ||
       (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
@@ -123,10 +128,15 @@ CA_EXPORT ca_status ca_chunk_attention(const void* Q, const void* K_cache, const
   p.NKB_max = NKB_max;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.row_tables = row_tables ? 1 : 0;
+  p.NQ_max = row_tables ? NQ_max : 0;
   const int64_t n_bg = static_cast<int64_t>(B) * H_kv;
   if (dtype == CA_BF16) {
     const int64_t n_pb = (C_max + 31) / 32;
-    p.n_t = static_cast<int>((p.G * n_pb + 3) / 4);
+    // workgroups per (b, g): 4 waves of 32 rows over the group's heads, or one
+    // 64-row Q-block of one head per workgroup with per-Q-block tables
+    p.n_t = row_tables ? static_cast<int>(p.G * ((C_max + 63) / 64))
+                       : static_cast<int>((p.G * n_pb + 3) / 4);
     p.xcd = (n_bg % 8 == 0) ? 1 : 0;
     if (n_bg * p.n_t > INT32_MAX) return CA_ERR_SHAPE;
     return hip_status(ca::launch_chunk_attn_bf16(Q, K_cache, V_cache, T, len, O, lse, B, D, p,
@@ -139,6 +149,31 @@ CA_EXPORT ca_status ca_chunk_attention(const void* Q, const void* K_cache, const
       static_cast<const float*>(Q), static_cast<const float*>(K_cache),
       static_cast<const float*>(V_cache), T, len, static_cast<float*>(O), lse, B, D, p, seq,
       stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+CA_EXPORT ca_status ca_chunk_attention(const void* Q, const void* K_cache, const void* V_cache,
+                                       const int32_t* T, const int32_t* len, int NKB_max,
+                                       const int32_t* prior_len, const int32_t* chunk_len,
+                                       int B, int H_q, int H_kv, int C_max, int64_t L, int D,
+                                       int block, float scale, ca_dtype dtype, void* O,
+                                       float* lse, hipStream_t stream) {
+  return attention(Q, K_cache, V_cache, T, len, 0, NKB_max, prior_len, chunk_len, B, H_q, H_kv,
+                   C_max, L, D, block, scale, dtype, O, lse, false, stream);
+}
+
+CA_EXPORT ca_status ca_chunk_attention_rows(const void* Q, const void* K_cache,
+                                            const void* V_cache, const int32_t* T_rows,
+                                            const int32_t* len_rows, int NQ_max, int NKB_max,
+                                            const int32_t* prior_len, const int32_t* chunk_len,
+                                            int B, int H_q, int H_kv, int C_max, int64_t L,
+                                            int D, int block, float scale, ca_dtype dtype,
+                                            void* O, float* lse, hipStream_t stream) {
+  return attention(Q, K_cache, V_cache, T_rows, len_rows, NQ_max, NKB_max, prior_len, chunk_len,
+                   B, H_q, H_kv, C_max, L, D, block, scale, dtype, O, lse, true, stream);
 }
 
 CA_EXPORT ca_status ca_compact_kv(const void* K_cache, const void* V_cache, const int32_t* T,

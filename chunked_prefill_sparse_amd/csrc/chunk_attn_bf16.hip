@@ -64,7 +64,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 constexpr int kBlk = 64;       // keys per KV block
-constexpr int kThreads = 256;  // 4 waves
 constexpr int kRowsPerWave = 32;
 
 template <int D>
@@ -72,8 +71,11 @@ struct Tile {
   static constexpr int kRowBytes = D * 2;
   static constexpr int kChunks = D / 8;                 // 16-byte chunks per row
   static constexpr int kBytes = kBlk * kRowBytes;       // one K or V tile
-  static constexpr int kDmaPerWave = kBytes / 1024 / 4; // 1 KiB wave copies per tile per wave
 };
+
+// 1 KiB wave copies per tile per wave, for W waves per workgroup.
+template <int D, int W>
+constexpr int kDmaPerWave = Tile<D>::kBytes / 1024 / W;
 
 // Chunk permutation of the K tile: chunk c of row r sits at c ^ k_swz(r).
 template <int D>
@@ -89,13 +91,13 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // block offset in an SGPR, and hardware bounds checking (a block offset at or
 // past the slice end reads zeros and touches no memory).  The LDS destination
 // of each wave copy is uniform (M0).
-template <int D>
+template <int D, int W>
 __device__ __forceinline__ void dma_tile(char* lds_tile, __amdgpu_buffer_rsrc_t rsrc,
                                          uint32_t block_off, const uint32_t* __restrict__ off,
                                          int wave_u) {
 #pragma unroll
-  for (int i = 0; i < Tile<D>::kDmaPerWave; ++i) {
-    char* dst = lds_tile + (i * 4 + wave_u) * 1024;
+  for (int i = 0; i < kDmaPerWave<D, W>; ++i) {
+    char* dst = lds_tile + (i * W + wave_u) * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, off[i], block_off, 0, 0);
   }
 }
@@ -226,10 +228,10 @@ __device__ __forceinline__ void accumulate_pv(const char* __restrict__ Vs, const
 // (Measured on MI355X: interleaving the softmax exponentials between the
 // matrix instructions of the same wave was slower than leaving them after the
 // matrix phase, where the other wave on the SIMD overlaps them.)
-template <int D>
+template <int D, int W>
 __device__ __forceinline__ void body_schedule() {
   constexpr int DS = D / 16;  // S matrix instructions per key tile
-  __builtin_amdgcn_sched_group_barrier(0x020, 2 * Tile<D>::kDmaPerWave, 0);  // tile copies
+  __builtin_amdgcn_sched_group_barrier(0x020, 2 * kDmaPerWave<D, W>, 0);  // tile copies
   __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);                         // first reads
 #pragma unroll
   for (int i = 0; i < 2 * DS; ++i) {
@@ -242,8 +244,12 @@ __device__ __forceinline__ void body_schedule() {
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
+// W = waves per workgroup.  kRows = false: union tables, T[b,g] shared by the
+// 4 waves (W = 4).  kRows = true: one table per (b, h, Q-block), the
+// per-Q-block lists of a block-sparse kernel, so a workgroup is the 2 waves
+// (W = 2) of one 64-row Q-block of one head.
+template <int D, int W, bool kRows>
+__global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const int32_t* __restrict__ T, const int32_t* __restrict__ len, __bf16* __restrict__ O,
     float* __restrict__ lse, AttnParams p, SeqInfo seq) {
@@ -251,7 +257,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
   constexpr int DT = D / 32;
   constexpr int RB = Tile<D>::kRowBytes;
   constexpr int CH = Tile<D>::kChunks;
-  constexpr int NDMA = Tile<D>::kDmaPerWave;
+  constexpr int NDMA = kDmaPerWave<D, W>;
+  constexpr int kThreads = W * 64;
+  static_assert(kRows ? W == 2 : W == 4, "workgroup shape");
   // LDS: two K tiles, then two V tiles
   __shared__ __attribute__((aligned(1024))) char lds[4 * Tile<D>::kBytes];
 
@@ -282,9 +290,20 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
   const int bg = b * p.H_kv + g;
 
   const int n_pb = (p.C_max + kRowsPerWave - 1) / kRowsPerWave;
-  const int wt = t * 4 + wave;
-  const int pb = wt / p.G;
-  const int h = g * p.G + (wt - pb * p.G);
+  int pb, h, first_pb, last_pb;
+  if (kRows) {  // t -> (Q-block, head): position-major, then head
+    const int qb = t / p.G;
+    h = g * p.G + (t - qb * p.G);
+    pb = 2 * qb + wave;
+    first_pb = 2 * qb;
+    last_pb = 2 * qb + 1;
+  } else {
+    const int wt = t * 4 + wave;
+    pb = wt / p.G;
+    h = g * p.G + (wt - pb * p.G);
+    first_pb = (t * 4) / p.G;
+    last_pb = (t * 4 + 3) / p.G;
+  }
   const bool wave_on = pb < n_pb;
   const int row0 = pb * kRowsPerWave;
   const int row = row0 + l32;
@@ -292,8 +311,6 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
   const bool row_live = row_in && row < C;
   const size_t qo_row = (static_cast<size_t>(b) * p.H_q + h) * p.C_max + row;
 
-  const int first_pb = (t * 4) / p.G;
-  int last_pb = (t * 4 + 3) / p.G;
   last_pb = last_pb < n_pb - 1 ? last_pb : n_pb - 1;
   if (first_pb * kRowsPerWave >= C) {  // padding rows only: O = 0, lse = -inf
     if (row_in) {
@@ -307,9 +324,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
   const int last_row = min(C, (last_pb + 1) * kRowsPerWave) - 1;
   const int kb_limit = (P + last_row) / kBlk;  // last block any row may see
   const int nkb = (P + C + kBlk - 1) / kBlk;   // blocks of this sequence
-  int nT = len[bg];
+  // table of the workgroup: T[b,g], or T[b,h,Q-block] for per-Q-block lists
+  const size_t trow = kRows ? (static_cast<size_t>(b) * p.H_q + h) * p.NQ_max + first_pb / 2
+                            : static_cast<size_t>(bg);
+  int nT = len[trow];
   nT = nT < 0 ? 0 : (nT > p.NKB_max ? p.NKB_max : nT);
-  const int32_t* __restrict__ Trow = T + static_cast<size_t>(bg) * p.NKB_max;
+  const int32_t* __restrict__ Trow = T + trow * p.NKB_max;
   const size_t kv_base = static_cast<size_t>(bg) * static_cast<size_t>(p.L) * D;
   const __bf16* Kbg = K + kv_base;
   const __bf16* Vbg = V + kv_base;
@@ -318,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
   uint32_t offk[NDMA], offv[NDMA];
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
-    const int pidx = (i * 4 + wave) * 64 + lane;  // LDS chunk this lane fills
+    const int pidx = (i * W + wave) * 64 + lane;  // LDS chunk this lane fills
     const int r = pidx / CH, pc = pidx % CH;
     offk[i] = static_cast<uint32_t>(r * RB + ((pc ^ k_swz<D>(r)) << 4));
     offv[i] = static_cast<uint32_t>(r * RB + ((pc ^ v_swz<D>(r)) << 4));
@@ -413,8 +433,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) pxa[i] = pxb[i] = bf16x8{};
   if (j < e) {
-    dma_tile<D>(K0, krsrc, boff(j, kbj), offk, wave_u);
-    dma_tile<D>(K1, krsrc, boff(j1, kb1), offk, wave_u);
+    dma_tile<D, W>(K0, krsrc, boff(j, kbj), offk, wave_u);
+    dma_tile<D, W>(K1, krsrc, boff(j1, kb1), offk, wave_u);
     // V1 is read by the first step with zero probabilities: make it finite
     uint4* vz = reinterpret_cast<uint4*>(V1);
     for (int i = tid; i < TB / 16; i += kThreads) vz[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -439,13 +459,13 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
   auto step = [&](const f32x16& cur0, const f32x16& cur1, f32x16& nxt0, f32x16& nxt1,
                   const bf16x8* pprev, bf16x8* pcur, char* Kin, char* Vin, char* Kfree,
                   char* Vfree) {
-    dma_tile<D>(Kfree, krsrc, boff(j2, kb2), offk, wave_u);
-    dma_tile<D>(Vfree, vrsrc, boff(j, kb0), offv, wave_u);
+    dma_tile<D, W>(Kfree, krsrc, boff(j2, kb2), offk, wave_u);
+    dma_tile<D, W>(Vfree, vrsrc, boff(j, kb0), offv, wave_u);
     scores<D>(Kin, qf, k_lane_off, nxt0, nxt1);  // stale when j1 is past the end: unused
     accumulate_pv<D>(Vin, pprev, v_lane_off, ws);
     softmax_probs<D>(cur0, cur1, ws, pcur, c);
     const float mx = row_max(nxt0, nxt1, xhalf);
-    body_schedule<D>();
+    body_schedule<D, W>();
     const bool last = j1 >= e;
     const bool moves = !last && __any(mx > ws.m_used + thr);
     const int j3 = next_plain(j2 + 1);
@@ -477,8 +497,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_bf16_kernel(
     const int kb = Trow[jt];
     if (!valid(kb)) continue;
     __syncthreads();  // every wave is done with the buffers
-    dma_tile<D>(K0, krsrc, static_cast<uint32_t>(kb) * (kBlk * D * 2), offk, wave_u);
-    dma_tile<D>(V0, vrsrc, static_cast<uint32_t>(kb) * (kBlk * D * 2), offv, wave_u);
+    dma_tile<D, W>(K0, krsrc, static_cast<uint32_t>(kb) * (kBlk * D * 2), offk, wave_u);
+    dma_tile<D, W>(V0, vrsrc, static_cast<uint32_t>(kb) * (kBlk * D * 2), offv, wave_u);
     wait_vmem();
     __syncthreads();
     scores<D>(K0, qf, k_lane_off, sa0, sa1);
@@ -522,17 +542,26 @@ hipError_t launch_chunk_attn_bf16(const void* Q, const void* K, const void* V,
                                   const int32_t* T, const int32_t* len, void* O, float* lse,
                                   int B, int D, const AttnParams& p, const SeqInfo& seq,
                                   hipStream_t stream) {
-  const dim3 grid(B * p.H_kv * p.n_t), block(kThreads);
+  const dim3 grid(B * p.H_kv * p.n_t);
   const __bf16* q = static_cast<const __bf16*>(Q);
   const __bf16* k = static_cast<const __bf16*>(K);
   const __bf16* v = static_cast<const __bf16*>(V);
   __bf16* o = static_cast<__bf16*>(O);
-  if (D == 128)
-    hipLaunchKernelGGL(chunk_attn_bf16_kernel<128>, grid, block, 0, stream, q, k, v, T, len, o,
-                       lse, p, seq);
-  else
-    hipLaunchKernelGGL(chunk_attn_bf16_kernel<64>, grid, block, 0, stream, q, k, v, T, len, o,
-                       lse, p, seq);
+  if (p.row_tables) {
+    if (D == 128)
+      hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 2, true>), grid, dim3(128), 0, stream, q,
+                         k, v, T, len, o, lse, p, seq);
+    else
+      hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 2, true>), grid, dim3(128), 0, stream, q, k,
+                         v, T, len, o, lse, p, seq);
+  } else {
+    if (D == 128)
+      hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 4, false>), grid, dim3(256), 0, stream, q,
+                         k, v, T, len, o, lse, p, seq);
+    else
+      hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 4, false>), grid, dim3(256), 0, stream, q,
+                         k, v, T, len, o, lse, p, seq);
+  }
   return hipGetLastError();
 }
 

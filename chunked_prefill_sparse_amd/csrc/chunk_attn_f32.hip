@@ -8,7 +8,9 @@
 // threads owns 64 consecutive query rows of one head, two threads per row,
 // each thread holding half of the row's q and output accumulator.  Each
 // selected block's K and V rows are staged in LDS (coalesced 16-byte loads)
-// and read back as broadcasts.
+// and read back as broadcasts.  With per-(head, Q-block) tables (the lists of
+// a block-sparse kernel) the workgroup's 64 rows are exactly one Q-block, so
+// it simply reads its own table row.
 
 #include "kernels.hpp"
 
@@ -56,9 +58,12 @@ __global__ __launch_bounds__(kThreadsF) void chunk_attn_f32_kernel(
   const int last_row = min(C, (tile + 1) * kRowsF) - 1;
   const int kb_limit = (P + last_row) / kBlk;
   const int nkb = (P + C + kBlk - 1) / kBlk;
-  int nT = len[bg];
+  // table of the workgroup: T[b,g], or T[b,h,Q-block] for per-Q-block lists
+  const size_t trow = p.row_tables ? (static_cast<size_t>(b) * p.H_q + h) * p.NQ_max + tile
+                                   : static_cast<size_t>(bg);
+  int nT = len[trow];
   nT = nT < 0 ? 0 : (nT > p.NKB_max ? p.NKB_max : nT);
-  const int32_t* Trow = T + static_cast<size_t>(bg) * p.NKB_max;
+  const int32_t* Trow = T + trow * p.NKB_max;
   const size_t kv_base = static_cast<size_t>(bg) * static_cast<size_t>(p.L) * D;
 
   float q[DH], acc[DH];

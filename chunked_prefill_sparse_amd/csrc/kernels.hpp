@@ -33,6 +33,8 @@ struct AttnParams {
   float scale_log2;     // scale * log2(e)
   int n_t;              // workgroups per (b, g) pseudo-request
   int xcd;              // 1: keep each pseudo-request's workgroups on one XCD
+  int row_tables;       // 0: T[b,g] (union); 1: T[b,h,Q-block] (per-Q-block lists)
+  int NQ_max;           // Q-blocks per head in the per-Q-block table layout
 };
 
 hipError_t launch_union_tables(const uint8_t* mask, int B, int H_q, int H_kv, int NQ_max,

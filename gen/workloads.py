@@ -114,11 +114,16 @@ def _causal_triangle(mask_b: np.ndarray, prior: int, chunk: int) -> None:
         mask_b[:, qb, p_blk:last // BLOCK + 1] = 1
 
 
-def _bernoulli_sink_local(rng, H_q, nq, p_blk, p, local, colshared=False):
+def _bernoulli_sink_local(rng, H_q, nq, p_blk, p, local, colshared=False, group=0):
     """Prior-block cells: Bernoulli(p) per (head, Q-block, KV-block) cell
-    (``colshared``: one draw per (head, KV-block), same for every Q-block),
-    with block 0 (sink) and the last ``local`` prior blocks forced on."""
-    if colshared:
+    (``colshared``: one draw per (head, KV-block), same for every Q-block;
+    ``group`` = G > 0: one draw per (group of G heads, KV-block), same for the
+    group's heads and every Q-block), with block 0 (sink) and the last
+    ``local`` prior blocks forced on."""
+    if group:
+        cells = rng.random((H_q // group, 1, 1, p_blk)) < p
+        cells = np.broadcast_to(cells, (H_q // group, group, nq, p_blk)).reshape(H_q, nq, p_blk).copy()
+    elif colshared:
         cells = rng.random((H_q, 1, p_blk)) < p
         cells = np.broadcast_to(cells, (H_q, nq, p_blk)).copy()
     else:
@@ -230,7 +235,10 @@ def make_workload(name: str, variant: Optional[str] = None, density: Optional[fl
                   blocks + Bernoulli(0.05) drawn per head.  variant "pairwise"
                   (default: one draw per (head, Q-block, KV-block) cell),
                   "colshared" (one draw per (head, KV-block), shared by all
-                  Q-blocks), or "dense" (all-ones mask: the dense baseline).
+                  Q-blocks), "groupshared" (one draw per (KV group, KV-block),
+                  shared by the group's heads and all Q-blocks: every mask row
+                  of a group equals the group's union), or "dense" (all-ones
+                  mask: the dense baseline).
     ragged_b4     bf16, B=4, prior {16384, 32768, 65536, 126976} + 1024-token
                   chunk each, cache capacity 128000; per-sequence density
                   p_b ~ U[0.05, 0.3]; sink + last 4 prior blocks forced.
@@ -258,10 +266,11 @@ def make_workload(name: str, variant: Optional[str] = None, density: Optional[fl
         variant = variant or "pairwise"
         if variant == "dense":
             fn = lambda rng, b, H, nq, pb: np.ones((H, nq, pb), np.uint8)  # noqa: E731
-        elif variant in ("pairwise", "colshared"):
+        elif variant in ("pairwise", "colshared", "groupshared"):
             cs = variant == "colshared"
+            grp = 4 if variant == "groupshared" else 0
             fn = lambda rng, b, H, nq, pb: _bernoulli_sink_local(  # noqa: E731
-                rng, H, nq, pb, 0.05, 8, colshared=cs)
+                rng, H, nq, pb, 0.05, 8, colshared=cs, group=grp)
         else:
             raise ValueError(f"unknown variant {variant}")
         w = make_custom(1, 32, 8, 128, [129024], [2048], "bf16", s, fn, name=name,

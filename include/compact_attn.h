@@ -85,6 +85,11 @@ typedef enum { CA_F32 = 0, CA_BF16 = 1 } ca_dtype;
  *             ids, then -1 up to NKB_max.
  * len         device int32 [B, H_kv] (out): number of valid entries of T[b,g].
  * Errors: CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_HIP.
+ *
+ * Per-(head, Q-block) lists for ca_chunk_attention_rows come from the same
+ * call on the same mask bytes viewed as [B, H_q*NQ_max, 1, NKB_max] (H_q and
+ * H_kv both set to H_q*NQ_max, NQ_max = 1, n_q_blocks[b] = 1): each "group"
+ * is then a single mask row, and its union is that row's set of blocks.
  */
 CA_EXPORT ca_status ca_build_union_tables(const uint8_t* mask, int B, int H_q, int H_kv, int NQ_max,
                                 int NKB_max, const int32_t* n_q_blocks,
@@ -134,6 +139,35 @@ CA_EXPORT ca_status ca_chunk_attention(const void* Q, const void* K_cache, const
                              int H_q, int H_kv, int C_max, int64_t L, int D, int block,
                              float scale, ca_dtype dtype, void* O, float* lse,
                              hipStream_t stream);
+
+/*
+ * ca_chunk_attention_rows -- the block-sparse-kernel execution that the union
+ * replaces: each 64-row Q-block of each query head attends its own mask row,
+ * with no union over Q-blocks or heads.  CompactAttention, abstract and
+ * "Methodology": block-sparse kernels take the 2D mask as the execution plan,
+ * which loses efficiency when a chunk bounds the number of queries per KV
+ * list; the union turns the mask into selection signals instead.  A baseline
+ * for measurement beside ca_chunk_attention.
+ *
+ * Same as ca_chunk_attention, except that for chunk row i of head h
+ *
+ *   A = { t : T_rows[b,h,i/64,j] == t/64 for some j < len_rows[b,h,i/64],  t <= p }
+ *
+ * T_rows      device int32 [B, H_q, NQ_max, NKB_max], each row strictly
+ *             ascending then -1 (see ca_build_union_tables for how to build it).
+ * len_rows    device int32 [B, H_q, NQ_max].
+ * NQ_max      Q-blocks per head in T_rows; 64 * NQ_max >= C_max (else CA_ERR_SHAPE).
+ * Other arguments, layouts and errors as for ca_chunk_attention.  A workgroup
+ * of the bf16 path holds one Q-block of one head (64 query rows per KV tile
+ * staged, against 128 in ca_chunk_attention).
+ */
+CA_EXPORT ca_status ca_chunk_attention_rows(const void* Q, const void* K_cache,
+                                  const void* V_cache, const int32_t* T_rows,
+                                  const int32_t* len_rows, int NQ_max, int NKB_max,
+                                  const int32_t* prior_len, const int32_t* chunk_len, int B,
+                                  int H_q, int H_kv, int C_max, int64_t L, int D, int block,
+                                  float scale, ca_dtype dtype, void* O, float* lse,
+                                  hipStream_t stream);
 
 /*
  * ca_tables_to_csr -- the paged-metadata view of the tables (execution stage:

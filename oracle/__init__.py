@@ -24,6 +24,10 @@ Contents (each function cites the passage it follows):
   avoids): selected prior blocks packed to end where the chunk starts.  Pinned
   by a hand-worked case and by the invariant that attention over the
   compacted cache equals attention over the original one.
+* ``sparse_attention_ref`` -- block-sparse-kernel execution of the mask (each
+  Q-block of each head attends its own mask row, no union).  Pinned by
+  brute-force loops, by the reduction to the union attention when every row
+  of a group is the same, and by the dense special case.
 
 Float work is float64 throughout; outputs are float32.
 """
@@ -36,3 +40,4 @@ from .attention_ref import (  # noqa: F401
     chunk_attention_rows_ref,
 )
 from .compact_ref import compact_kv_ref  # noqa: F401
+from .sparse_ref import sparse_attention_ref, sparse_attention_rows_ref  # noqa: F401

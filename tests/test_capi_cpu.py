@@ -124,3 +124,15 @@ def _compact(lib, **kw):
 ])
 def test_compact_validation(kw, status):
     assert _compact(_lib.lib(), **kw) == status
+
+
+def test_rows_validation():
+    lib = _lib.lib()
+    base = (FAKE, FAKE, FAKE, FAKE, FAKE)
+    # NQ_max * 64 must cover C_max
+    assert lib.ca_chunk_attention_rows(*base, 3, 20, _ints(1024), _ints(256), 1, 4, 1, 256, 1280,
+                                       64, 64, 0.125, 1, FAKE, None, None) == 2
+    assert lib.ca_chunk_attention_rows(*base, 4, 20, _ints(1024), _ints(256), 1, 4, 1, 256, 1280,
+                                       96, 64, 0.125, 1, FAKE, None, None) == 4
+    assert lib.ca_chunk_attention_rows(None, *base[1:], 4, 20, _ints(1024), _ints(256), 1, 4, 1,
+                                       256, 1280, 64, 64, 0.125, 1, FAKE, None, None) == 1

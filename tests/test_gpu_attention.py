@@ -184,6 +184,7 @@ FULL = [
     ("llama8b_128k", dict(variant="pairwise")),
     ("llama8b_128k", dict(variant="colshared")),
     ("llama8b_128k", dict(variant="dense")),
+    ("llama8b_128k", dict(variant="groupshared")),
     ("vslash_128k", dict(density=0.02, heads="identical")),
     ("vslash_128k", dict(density=0.1, heads="independent")),
     ("vslash_128k", dict(density=0.5, heads="identical")),

@@ -54,6 +54,7 @@ def test_union_fuzz_tiny():
     ("llama8b_128k", dict(variant="pairwise")),
     ("llama8b_128k", dict(variant="colshared")),
     ("llama8b_128k", dict(variant="dense")),
+    ("llama8b_128k", dict(variant="groupshared")),
     ("ragged_b4", {}),
 ] + [("vslash_128k", dict(density=d, heads=m)) for d in gen.VSLASH_DENSITIES
      for m in ("identical", "independent")])

@@ -227,11 +227,12 @@ def _union_fraction(w, forced):
     return hits, trials
 
 
-@pytest.mark.parametrize("variant,expo", [("colshared", "G"), ("pairwise", "G*NQ")])
+@pytest.mark.parametrize("variant,expo", [("colshared", "G"), ("pairwise", "G*NQ"),
+                                          ("groupshared", "1")])
 def test_statistic_union_density_128k(variant, expo):
     w = gen.make_workload("llama8b_128k", variant=variant, with_tensors=False)
     hits, n = _union_fraction(w, lambda p_blk: {0} | set(range(p_blk - 8, p_blk)))
-    e = w.G if expo == "G" else w.G * 32
+    e = {"G": w.G, "G*NQ": w.G * 32, "1": 1}[expo]
     p = 1 - (1 - 0.05) ** e  # closed form: block missed by all e independent cells
     sigma = math.sqrt(n * p * (1 - p))
     assert abs(hits - n * p) <= 5 * sigma + 1e-9, (hits, n * p, sigma)
