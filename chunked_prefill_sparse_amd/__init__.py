@@ -22,7 +22,8 @@ from . import _lib
 from ._lib import CA_BLOCK, CA_MAX_BATCH, CompactAttnError  # noqa: F401
 
 __all__ = ["build_union_tables", "chunk_attention", "tables_to_csr", "compact_kv",
-           "build_row_tables", "chunk_attention_rows", "CompactAttnError", "library_path"]
+           "build_row_tables", "chunk_attention_rows", "pool_blocks", "block_mask_topk",
+           "CompactAttnError", "library_path"]
 
 
 def library_path() -> str:
@@ -264,3 +265,60 @@ def compact_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, T: torch.Tensor,
         L, D, dt, k_out.data_ptr(), v_out.data_ptr(), T_out.data_ptr(), _stream_ptr(stream))
     _lib.check(st, "ca_compact_kv")
     return k_out, v_out, T_out
+
+
+def pool_blocks(x: torch.Tensor, blk_begin: Sequence[int], blk_end: Sequence[int],
+                out: Optional[torch.Tensor] = None, n_out: Optional[int] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Mean of each 64-row block: x [B, H, R, D] (bf16/fp32) -> out float32
+    [B, H, n_out, D], entries blk_begin[b] <= kb < blk_end[b] written, the rest
+    left as they were (a new ``out`` starts as zeros)."""
+    _need_cuda("x", x)
+    if x.dtype not in (torch.bfloat16, torch.float32) or x.dim() != 4:
+        raise ValueError("x must be a bfloat16/float32 [B, H, R, D] tensor")
+    B, H, R, D = x.shape
+    if out is None:
+        out = torch.zeros((B, H, n_out if n_out is not None else R // CA_BLOCK, D),
+                          dtype=torch.float32, device=x.device)
+    _need_cuda("out", out, torch.float32)
+    if out.dim() != 4 or tuple(out.shape[:2]) != (B, H) or out.shape[3] != D:
+        raise ValueError("out must be [B, H, n_out, D]")
+    dt = _lib.CA_BF16 if x.dtype == torch.bfloat16 else _lib.CA_F32
+    st = _lib.lib().ca_pool_blocks(x.data_ptr(), dt, B, H, R, D,
+                                   _host_ints("blk_begin", blk_begin, B),
+                                   _host_ints("blk_end", blk_end, B), out.data_ptr(),
+                                   out.shape[2], _stream_ptr(stream))
+    _lib.check(st, "ca_pool_blocks")
+    return out
+
+
+def block_mask_topk(qbar: torch.Tensor, kbar: torch.Tensor, prior_len: Sequence[int],
+                    chunk_len: Sequence[int], budget: int, local: int,
+                    scores: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
+                    stream: Optional[torch.cuda.Stream] = None):
+    """Pooled block scores and the per-row top-k mask (sink, local window and
+    causal block triangle always on).  qbar [B, H_q, NQ_max, D], kbar
+    [B, H_kv, NKB_max, D] float32.  Returns (mask uint8 [B, H_q, NQ_max, NKB_max],
+    scores float32 of the same shape)."""
+    _need_cuda("qbar", qbar, torch.float32)
+    _need_cuda("kbar", kbar, torch.float32)
+    if qbar.dim() != 4 or kbar.dim() != 4 or qbar.shape[0] != kbar.shape[0] or \
+            qbar.shape[3] != kbar.shape[3]:
+        raise ValueError("qbar must be [B, H_q, NQ_max, D] and kbar [B, H_kv, NKB_max, D]")
+    B, H_q, NQ_max, D = qbar.shape
+    H_kv, NKB_max = kbar.shape[1], kbar.shape[2]
+    shape = (B, H_q, NQ_max, NKB_max)
+    if scores is None:
+        scores = torch.empty(shape, dtype=torch.float32, device=qbar.device)
+    if mask is None:
+        mask = torch.empty(shape, dtype=torch.uint8, device=qbar.device)
+    _need_cuda("scores", scores, torch.float32)
+    _need_cuda("mask", mask, torch.uint8)
+    if tuple(scores.shape) != shape or tuple(mask.shape) != shape:
+        raise ValueError(f"scores and mask must be {shape}")
+    st = _lib.lib().ca_block_mask_topk(
+        qbar.data_ptr(), kbar.data_ptr(), B, H_q, H_kv, NQ_max, NKB_max, D,
+        _host_ints("prior_len", prior_len, B), _host_ints("chunk_len", chunk_len, B),
+        int(budget), int(local), scores.data_ptr(), mask.data_ptr(), _stream_ptr(stream))
+    _lib.check(st, "ca_block_mask_topk")
+    return mask, scores

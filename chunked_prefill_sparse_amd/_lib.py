@@ -23,6 +23,8 @@ EXPORTED = (
     "ca_chunk_attention_rows",
     "ca_tables_to_csr",
     "ca_compact_kv",
+    "ca_pool_blocks",
+    "ca_block_mask_topk",
     "ca_status_string",
     "ca_last_hip_error",
 )
@@ -53,6 +55,12 @@ def _declare(lib):
     lib.ca_compact_kv.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32p, _i32p, _i32, _i32, _i64, _i32,
                                   _i32, _vp, _vp, _vp, _vp]
     lib.ca_compact_kv.restype = _i32
+    lib.ca_pool_blocks.argtypes = [_vp, _i32, _i32, _i32, _i64, _i32, _i32p, _i32p, _vp, _i32,
+                                   _vp]
+    lib.ca_pool_blocks.restype = _i32
+    lib.ca_block_mask_topk.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32p, _i32p,
+                                       _i32, _i32, _vp, _vp, _vp]
+    lib.ca_block_mask_topk.restype = _i32
     lib.ca_status_string.argtypes = [_i32]
     lib.ca_status_string.restype = ctypes.c_char_p
     lib.ca_last_hip_error.argtypes = []

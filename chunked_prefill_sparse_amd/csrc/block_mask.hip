@@ -1,0 +1,259 @@
+// A lightweight block-mask producer on gfx950 (the step upstream of the
+// union).  CompactAttention, "Methodology" (selection stage) and the problem
+// statement of the technical summaries: the union takes a per-head 2D block
+// mask from any lightweight pattern search, and that search runs again over
+// the growing KV cache at every chunk, so its cost matters.  The pages leave
+// the searcher open; this one is training-free:
+//
+//   qbar[b,h,qb]  = mean of the 64 rows of Q-block qb          (pool_blocks)
+//   kbar[b,g,kb]  = mean of the 64 rows of KV block kb         (pool_blocks,
+//                   kept across chunks: only the new blocks are pooled)
+//   s[b,h,qb,kb]  = qbar . kbar                                (block_scores)
+//   mask row      = sink + last `local` prior blocks + causal block triangle
+//                   + the `budget` best remaining prior blocks  (topk_mask)
+//
+// All three are HBM/L2-bound and tiny next to the attention: pooling reads
+// each new block once; the scores read kbar once per KV group; the selection
+// reads each score row a few times from L2 and writes one mask byte per cell.
+
+#include "kernels.hpp"
+
+namespace ca {
+namespace {
+
+constexpr int kMaskThreads = 256;
+
+// ---------------------------------------------------------------- pooling
+
+// Workgroup (b*H + h, y) pools block kb = begin[b] + y.  Each thread sums a
+// 16-byte column slice over every RPI-th row of the block; the RPI partial
+// sums of a column are then added in row-group order.
+template <typename TIn, int D>
+__global__ __launch_bounds__(kMaskThreads) void pool_blocks_kernel(const TIn* __restrict__ X,
+                                                                   int H, int64_t R,
+                                                                   BlockRange rng,
+                                                                   float* __restrict__ out,
+                                                                   int NB_out) {
+  constexpr int V = 16 / static_cast<int>(sizeof(TIn));  // elements per 16-byte load
+  constexpr int TPR = D / V;                              // threads per row
+  constexpr int RPI = kMaskThreads / TPR;                 // rows per iteration
+  __shared__ float part[RPI * D];
+  const int bh = blockIdx.x;
+  const int b = bh / H;
+  const int kb = rng.begin[b] + static_cast<int>(blockIdx.y);
+  if (kb >= rng.end[b]) return;
+  const int tid = threadIdx.x;
+  const int col = (tid % TPR) * V;
+  const int rsub = tid / TPR;
+  const TIn* src = X + (static_cast<size_t>(bh) * R + static_cast<size_t>(kb) * 64) * D + col;
+  float acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = 0.f;
+  for (int r = rsub; r < 64; r += RPI) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(r) * D);
+    const TIn* e = reinterpret_cast<const TIn*>(&raw);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] += static_cast<float>(e[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < V; ++i) part[rsub * D + col + i] = acc[i];
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+    for (int k = 0; k < RPI; ++k) s += part[k * D + tid];
+    out[(static_cast<size_t>(bh) * NB_out + kb) * D + tid] = s * (1.f / 64.f);
+  }
+}
+
+// ---------------------------------------------------------------- scores
+
+// Workgroup (b*H_kv + g, y) scores KV blocks 64y .. 64y+63 (one per lane, its
+// kbar row held in registers) against every pooled Q-block row of the group's
+// heads (one row per wave at a time, read as a wave-uniform broadcast).
+template <int D>
+__global__ __launch_bounds__(kMaskThreads) void block_scores_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar, int H_q, int H_kv,
+    int NQ_max, int NKB_max, SeqInfo seq, float* __restrict__ scores) {
+  const int bg = blockIdx.x;
+  const int b = bg / H_kv;
+  const int g = bg - b * H_kv;
+  const int G = H_q / H_kv;
+  const int pblk = seq.prior[b] / 64;
+  const int nq = seq.chunk[b] / 64;
+  const int kb0 = static_cast<int>(blockIdx.y) * 64;
+  if (kb0 >= pblk) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int kb = kb0 + lane;
+  const bool kin = kb < pblk;
+  float kr[D];
+  if (kin) {
+    const float4* src = reinterpret_cast<const float4*>(
+        kbar + (static_cast<size_t>(bg) * NKB_max + kb) * D);
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) {
+      const float4 x = src[i];
+      kr[4 * i] = x.x;
+      kr[4 * i + 1] = x.y;
+      kr[4 * i + 2] = x.z;
+      kr[4 * i + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < D; ++i) kr[i] = 0.f;
+  }
+  for (int r = wave; r < G * nq; r += kMaskThreads / 64) {
+    const int hl = r / nq;
+    const int qb = r - hl * nq;
+    const size_t row = (static_cast<size_t>(b) * H_q + g * G + hl) * NQ_max + qb;
+    const float* q = qbar + row * D;
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) s = __builtin_fmaf(q[d], kr[d], s);
+    if (kin) scores[row * NKB_max + kb] = s;
+  }
+}
+
+// ---------------------------------------------------------------- selection
+
+// Order-preserving map of a float to an unsigned key (-0 taken as +0).
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One workgroup per mask row (b, h, qb).  The budget-th largest candidate key
+// is found by a most-significant-digit-first radix select (four 8-bit passes
+// over the row, histograms in LDS); the row is then written in ascending kb,
+// taking keys above the threshold and, of the keys equal to it, the lowest
+// kb first.
+__global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
+    const float* __restrict__ scores, int H_q, int NQ_max, int NKB_max, SeqInfo seq,
+    int budget, int local, uint8_t* __restrict__ mask) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh_prefix, sh_need;
+  __shared__ int wave_eq[kMaskThreads / 64];
+  const size_t row = blockIdx.x;
+  const int b = static_cast<int>(row / (static_cast<size_t>(H_q) * NQ_max));
+  const int qb = static_cast<int>(row % NQ_max);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  uint8_t* mrow = mask + row * NKB_max;
+  const int pblk = seq.prior[b] / 64;
+  const int nq = seq.chunk[b] / 64;
+  if (qb >= nq) {
+    for (int kb = tid; kb < NKB_max; kb += kMaskThreads) mrow[kb] = 0;
+    return;
+  }
+  const int lo_local = pblk - local > 1 ? pblk - local : 1;  // candidates: [1, lo_local)
+  const int n_cand = lo_local - 1 > 0 ? lo_local - 1 : 0;
+  const uint32_t kk = static_cast<uint32_t>(budget < n_cand ? budget : n_cand);
+  const float* srow = scores + row * NKB_max;
+
+  uint32_t prefix = 0u, need = kk;
+  if (kk > 0u) {
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+      hist[tid] = 0u;
+      __syncthreads();
+      for (int kb = 1 + tid; kb < lo_local; kb += kMaskThreads) {
+        const uint32_t key = score_key(srow[kb]);
+        if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t cum = 0u;
+        for (int d = 255; d >= 0; --d) {
+          if (cum + hist[d] >= need) {
+            sh_prefix = prefix | (static_cast<uint32_t>(d) << shift);
+            sh_need = need - cum;
+            break;
+          }
+          cum += hist[d];
+        }
+      }
+      __syncthreads();
+      prefix = sh_prefix;
+      need = sh_need;
+    }
+  }
+  // prefix = key of the budget-th largest candidate; take `need` of its equals
+
+  uint32_t taken = 0u;  // equals already taken (uniform)
+  for (int base = 0; base < NKB_max; base += kMaskThreads) {
+    const int kb = base + tid;
+    bool sel = false, eq = false;
+    if (kb < NKB_max) {
+      sel = (pblk > 0 && kb == 0) || (kb >= lo_local && kb < pblk) ||
+            (kb >= pblk && kb <= pblk + qb);
+      if (kk > 0u && kb >= 1 && kb < lo_local) {
+        const uint32_t key = score_key(srow[kb]);
+        sel = sel || key > prefix;
+        eq = key == prefix;
+      }
+    }
+    const uint64_t bal = __ballot(eq);
+    const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
+    if (lane == 0) wave_eq[wave] = __popcll(bal);
+    __syncthreads();
+    uint32_t off = taken;
+    for (int w = 0; w < wave; ++w) off += wave_eq[w];
+    if (eq && off + below < need) sel = true;
+    if (kb < NKB_max) mrow[kb] = sel ? 1 : 0;
+    for (int w = 0; w < kMaskThreads / 64; ++w) taken += wave_eq[w];
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pool_blocks(const void* X, int esz, int B, int H, int64_t R, int D,
+                              const BlockRange& rng, int max_span, float* out, int NB_out,
+                              hipStream_t stream) {
+  if (max_span <= 0) return hipSuccess;
+  const dim3 grid(B * H, max_span);
+  if (esz == 2) {
+    const __bf16* x = static_cast<const __bf16*>(X);
+    if (D == 128)
+      hipLaunchKernelGGL((pool_blocks_kernel<__bf16, 128>), grid, dim3(kMaskThreads), 0, stream,
+                         x, H, R, rng, out, NB_out);
+    else
+      hipLaunchKernelGGL((pool_blocks_kernel<__bf16, 64>), grid, dim3(kMaskThreads), 0, stream,
+                         x, H, R, rng, out, NB_out);
+  } else {
+    const float* x = static_cast<const float*>(X);
+    if (D == 128)
+      hipLaunchKernelGGL((pool_blocks_kernel<float, 128>), grid, dim3(kMaskThreads), 0, stream,
+                         x, H, R, rng, out, NB_out);
+    else
+      hipLaunchKernelGGL((pool_blocks_kernel<float, 64>), grid, dim3(kMaskThreads), 0, stream, x,
+                         H, R, rng, out, NB_out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_block_mask(const float* qbar, const float* kbar, int B, int H_q, int H_kv,
+                             int NQ_max, int NKB_max, int D, const SeqInfo& seq, int max_pblk,
+                             int budget, int local, float* scores, uint8_t* mask,
+                             hipStream_t stream) {
+  if (max_pblk > 0) {
+    const dim3 grid(B * H_kv, (max_pblk + 63) / 64);
+    if (D == 128)
+      hipLaunchKernelGGL(block_scores_kernel<128>, grid, dim3(kMaskThreads), 0, stream, qbar,
+                         kbar, H_q, H_kv, NQ_max, NKB_max, seq, scores);
+    else
+      hipLaunchKernelGGL(block_scores_kernel<64>, grid, dim3(kMaskThreads), 0, stream, qbar, kbar,
+                         H_q, H_kv, NQ_max, NKB_max, seq, scores);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(topk_mask_kernel, dim3(B * H_q * NQ_max), dim3(kMaskThreads), 0, stream,
+                     scores, H_q, NQ_max, NKB_max, seq, budget, local, mask);
+  return hipGetLastError();
+}
+
+}  // namespace ca

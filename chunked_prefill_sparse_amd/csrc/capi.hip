@@ -206,4 +206,61 @@ CA_EXPORT ca_status ca_compact_kv(const void* K_cache, const void* V_cache, cons
                                           seq, K_out, V_out, T_out, stream));
 }
 
+CA_EXPORT ca_status ca_pool_blocks(const void* X, ca_dtype dtype, int B, int H, int64_t R, int D,
+                                   const int32_t* blk_begin, const int32_t* blk_end, float* out,
+                                   int NB_out, hipStream_t stream) {
+  if (!X || !blk_begin || !blk_end || !out) return CA_ERR_NULL;
+  if (dtype != CA_F32 && dtype != CA_BF16) return CA_ERR_DTYPE;
+  if (B < 1 || B > CA_MAX_BATCH || H < 1 || R < 1 || NB_out < 1 ||
+      static_cast<int64_t>(B) * H > (1 << 24))
+    return CA_ERR_SHAPE;
+  if (D != 64 && D != 128) return CA_ERR_UNSUPPORTED;
+  if (!aligned16(X) || !aligned16(out)) return CA_ERR_UNSUPPORTED;
+  ca::BlockRange rng;
+  memset(&rng, 0, sizeof(rng));
+  int max_span = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t lo = blk_begin[b], hi = blk_end[b];
+    if (lo < 0 || hi < lo || hi > NB_out || hi * CA_BLOCK > R) return CA_ERR_SHAPE;
+    rng.begin[b] = static_cast<int32_t>(lo);
+    rng.end[b] = static_cast<int32_t>(hi);
+    max_span = std::max(max_span, static_cast<int>(hi - lo));
+  }
+  if (max_span > 65535) return CA_ERR_SHAPE;
+  return hip_status(ca::launch_pool_blocks(X, dtype == CA_BF16 ? 2 : 4, B, H, R, D, rng, max_span,
+                                           out, NB_out, stream));
+}
+
+CA_EXPORT ca_status ca_block_mask_topk(const float* qbar, const float* kbar, int B, int H_q,
+                                       int H_kv, int NQ_max, int NKB_max, int D,
+                                       const int32_t* prior_len, const int32_t* chunk_len,
+                                       int budget, int local, float* scores, uint8_t* mask,
+                                       hipStream_t stream) {
+  if (!qbar || !kbar || !prior_len || !chunk_len || !scores || !mask) return CA_ERR_NULL;
+  if (B < 1 || B > CA_MAX_BATCH || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || NQ_max < 1 ||
+      NKB_max < 1 || budget < 0 || local < 0)
+    return CA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H_q * NQ_max > INT32_MAX ||
+      static_cast<int64_t>(B) * H_kv > 65535)
+    return CA_ERR_SHAPE;
+  if (D != 64 && D != 128) return CA_ERR_UNSUPPORTED;
+  if (!aligned16(qbar) || !aligned16(kbar)) return CA_ERR_UNSUPPORTED;
+  ca::SeqInfo seq;
+  memset(&seq, 0, sizeof(seq));
+  int max_pblk = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t P = prior_len[b], C = chunk_len[b];
+    if (P < 0 || C < 0 || C > static_cast<int64_t>(NQ_max) * CA_BLOCK ||
+        P + C > static_cast<int64_t>(NKB_max) * CA_BLOCK)
+      return CA_ERR_SHAPE;
+    if (P % CA_BLOCK != 0 || C % CA_BLOCK != 0) return CA_ERR_UNSUPPORTED;
+    seq.prior[b] = static_cast<int32_t>(P);
+    seq.chunk[b] = static_cast<int32_t>(C);
+    seq.order[b] = b;
+    max_pblk = std::max(max_pblk, static_cast<int>(P / CA_BLOCK));
+  }
+  return hip_status(ca::launch_block_mask(qbar, kbar, B, H_q, H_kv, NQ_max, NKB_max, D, seq,
+                                          max_pblk, budget, local, scores, mask, stream));
+}
+
 }  // extern "C"

@@ -24,6 +24,12 @@ struct SeqInfo {
   int32_t order[CA_MAX_BATCH];
 };
 
+// Per-sequence block ranges [begin, end) of a pooling call.
+struct BlockRange {
+  int32_t begin[CA_MAX_BATCH];
+  int32_t end[CA_MAX_BATCH];
+};
+
 struct AttnParams {
   int H_q, H_kv, G;     // heads; G = H_q / H_kv query heads per KV head
   int C_max;            // rows of Q/O per head
@@ -61,6 +67,17 @@ hipError_t launch_chunk_attn_f32(const float* Q, const float* K, const float* V,
 hipError_t launch_compact_kv(const void* K, const void* V, const int32_t* T, const int32_t* len,
                              int NKB_max, int B, int H_kv, int64_t L, int D, int esz,
                              const SeqInfo& seq, void* Ko, void* Vo, int32_t* To,
+                             hipStream_t stream);
+
+// Block-mask producer: mean pooling of 64-row blocks (esz = 2: bf16, 4: fp32).
+hipError_t launch_pool_blocks(const void* X, int esz, int B, int H, int64_t R, int D,
+                              const BlockRange& rng, int max_span, float* out, int NB_out,
+                              hipStream_t stream);
+
+// Block-mask producer: pooled scores, then per-row top-k selection.
+hipError_t launch_block_mask(const float* qbar, const float* kbar, int B, int H_q, int H_kv,
+                             int NQ_max, int NKB_max, int D, const SeqInfo& seq, int max_pblk,
+                             int budget, int local, float* scores, uint8_t* mask,
                              hipStream_t stream);
 
 }  // namespace ca

@@ -226,6 +226,61 @@ CA_EXPORT ca_status ca_compact_kv(const void* K_cache, const void* V_cache, cons
                                   ca_dtype dtype, void* K_out, void* V_out, int32_t* T_out,
                                   hipStream_t stream);
 
+/*
+ * Block-mask producer -- the step upstream of the union.  CompactAttention,
+ * "Methodology" (selection stage) and the problem statement of the technical
+ * summaries: the union consumes a per-head 2D block mask made by a
+ * lightweight pattern search, which runs again over the growing KV cache at
+ * every chunk.  The pages leave the searcher open; this one is training-free:
+ * mean-pooled Q-block . mean-pooled KV-block scores, then per-row top-k.
+ *
+ * ca_pool_blocks -- out[b,h,kb,:] = mean over r < 64 of X[b,h,64*kb + r,:]
+ * for blk_begin[b] <= kb < blk_end[b]; every other entry of `out` is left as
+ * it was (so pooled keys can be kept across chunks and only new blocks pooled).
+ *   X           device [B, H, R, D], element type `dtype` (bf16 or fp32),
+ *               16-byte aligned.
+ *   blk_begin,  host int32 [B]; 0 <= blk_begin[b] <= blk_end[b] <= NB_out,
+ *   blk_end     64 * blk_end[b] <= R, blk_end[b] - blk_begin[b] <= 65535.
+ *   out         device float [B, H, NB_out, D], 16-byte aligned.
+ *   B in [1, CA_MAX_BATCH], B*H <= 2^24, D in {64, 128}.
+ *   Sums are fp32, in a fixed order.
+ * Errors: CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_DTYPE, CA_ERR_UNSUPPORTED, CA_ERR_HIP.
+ */
+CA_EXPORT ca_status ca_pool_blocks(const void* X, ca_dtype dtype, int B, int H, int64_t R, int D,
+                         const int32_t* blk_begin, const int32_t* blk_end, float* out,
+                         int NB_out, hipStream_t stream);
+
+/*
+ * ca_block_mask_topk -- block scores and the mask built from them.  With
+ * P = prior_len[b]/64, nq = chunk_len[b]/64, g = h / (H_q/H_kv):
+ *
+ *   scores[b,h,qb,kb] = sum_d qbar[b,h,qb,d] * kbar[b,g,kb,d]  (qb < nq, kb < P;
+ *                       fp32 fused multiply-adds in ascending d)
+ *   mask[b,h,qb,kb]   = 1 for kb = 0 (when P > 0), for P - local <= kb < P,
+ *                       for P <= kb <= P + qb (causal block triangle), and for
+ *                       the `budget` candidates 1 <= kb < max(P - local, 1)
+ *                       with the highest scores (ties: lower kb first; all of
+ *                       them when there are fewer); 0 elsewhere and on every
+ *                       row qb >= nq.
+ *
+ *   qbar        device float [B, H_q, NQ_max, D] (pooled Q-blocks), 16-byte aligned.
+ *   kbar        device float [B, H_kv, NKB_max, D] (pooled KV blocks; rows
+ *               kb < P must be valid), 16-byte aligned.
+ *   prior_len,  host int32 [B], multiples of 64 (else CA_ERR_UNSUPPORTED);
+ *   chunk_len   chunk_len <= 64*NQ_max, prior_len + chunk_len <= 64*NKB_max.
+ *   budget, local  >= 0.
+ *   scores      device float [B, H_q, NQ_max, NKB_max] (out; entries with
+ *               qb >= nq or kb >= P are not written).  Scratch owned by the caller.
+ *   mask        device uint8 [B, H_q, NQ_max, NKB_max] (out, fully written): the
+ *               input of ca_build_union_tables.
+ *   B*H_kv <= 65535, D in {64, 128}.
+ * Errors: CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_UNSUPPORTED, CA_ERR_HIP.
+ */
+CA_EXPORT ca_status ca_block_mask_topk(const float* qbar, const float* kbar, int B, int H_q,
+                             int H_kv, int NQ_max, int NKB_max, int D,
+                             const int32_t* prior_len, const int32_t* chunk_len, int budget,
+                             int local, float* scores, uint8_t* mask, hipStream_t stream);
+
 /* Human-readable name of a status code (static string; never NULL). */
 CA_EXPORT const char* ca_status_string(ca_status s);
 

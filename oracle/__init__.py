@@ -28,6 +28,11 @@ Contents (each function cites the passage it follows):
   Q-block of each head attends its own mask row, no union).  Pinned by
   brute-force loops, by the reduction to the union attention when every row
   of a group is the same, and by the dense special case.
+* ``producer_mask_ref`` (with ``pool_blocks_ref``, ``block_scores_ref``,
+  ``topk_mask_ref``) -- a training-free block-mask producer: mean-pooled
+  Q-block . mean-pooled K-block scores, per-row top-k plus sink, local window
+  and the causal block triangle.  Pinned by closed forms of the pooling, brute
+  force on the scores and sort-based brute force on the selection.
 
 Float work is float64 throughout; outputs are float32.
 """
@@ -41,3 +46,5 @@ from .attention_ref import (  # noqa: F401
 )
 from .compact_ref import compact_kv_ref  # noqa: F401
 from .sparse_ref import sparse_attention_ref, sparse_attention_rows_ref  # noqa: F401
+from .producer_ref import (block_scores_ref, pool_blocks_ref, producer_mask_ref,  # noqa: F401
+                           topk_mask_ref)

@@ -1,0 +1,122 @@
+"""GPU parity of the block-mask producer (through the C ABI).
+
+Pooling and scores are floating point: compared with the float64 oracle
+within fp32 rounding bounds.  The selection turns scores into bits, so it is
+checked bit-exact against the oracle's selection fed the GPU's own fp32
+scores (both sides decide in the kernel's precision); the whole producer is
+then compared with the float64 oracle end to end, where rows may differ only
+if the oracle's scores at the budget boundary are within the score bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import chunked_prefill_sparse_amd as ca
+from oracle import block_scores_ref, pool_blocks_ref, producer_mask_ref, topk_mask_ref
+from tests.gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+POOL_ATOL = 2e-6    # |mean of 64 values| error in fp32: a few ulps of the partial sums
+SCORE_ATOL = 2e-5   # D products of pooled values in fp32, plus the pooling error
+
+
+def _f32(t):
+    return gen.tensor_to_f32(t.detach().cpu())
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
+def test_pool_blocks(dtype, D):
+    rng = np.random.default_rng(D)
+    B, H, R = 3, 4, 40 * 64
+    x32 = rng.standard_normal((B, H, R, D)).astype(np.float32)
+    x = torch.from_numpy(x32)
+    if dtype == "bf16":
+        x = x.to(torch.bfloat16)
+    xr = gen.tensor_to_f32(x)
+    lo, hi = [0, 5, 39], [40, 17, 39]
+    out = torch.full((B, H, 41, D), 7.0, device="cuda")
+    ca.pool_blocks(x.cuda(), lo, hi, out=out)
+    torch.cuda.synchronize()
+    ref = pool_blocks_ref(xr, lo, hi, 41)
+    got = out.cpu().numpy()
+    have = ~np.isnan(ref)
+    np.testing.assert_allclose(got[have], ref[have], rtol=0, atol=POOL_ATOL)
+    assert (got[~have] == 7.0).all()  # untouched outside the ranges
+
+
+def _producer(w, budget, local):
+    d_q = w.q.cuda()
+    d_k = w.k.cuda()
+    NQ_max = -(-w.C_max // 64)
+    qbar = ca.pool_blocks(d_q, [0] * w.B, [c // 64 for c in w.chunk], n_out=NQ_max)
+    kbar = ca.pool_blocks(d_k, [0] * w.B, [p // 64 for p in w.prior], n_out=w.NKB_max)
+    mask, scores = ca.block_mask_topk(qbar, kbar, w.prior, w.chunk, budget, local)
+    torch.cuda.synchronize()
+    return qbar, kbar, mask, scores
+
+
+def _check(w, budget, local):
+    qbar, kbar, mask, scores = _producer(w, budget, local)
+    q, k = gen.tensor_to_f32(w.q), gen.tensor_to_f32(w.k)
+    NQ_max = qbar.shape[2]
+    qr = np.nan_to_num(pool_blocks_ref(q, [0] * w.B, [c // 64 for c in w.chunk], NQ_max))
+    kr = np.nan_to_num(pool_blocks_ref(k, [0] * w.B, [p // 64 for p in w.prior], w.NKB_max))
+    sr = block_scores_ref(qr, kr)
+    sg = scores.cpu().numpy().astype(np.float64)
+    m = mask.cpu().numpy()
+    for b in range(w.B):
+        nq, P = w.chunk[b] // 64, w.prior[b] // 64
+        np.testing.assert_allclose(sg[b, :, :nq, :P], sr[b, :, :nq, :P], rtol=0, atol=SCORE_ATOL)
+    # selection: bit-exact on the GPU's own scores
+    sel_in = np.zeros_like(sg)
+    for b in range(w.B):
+        nq, P = w.chunk[b] // 64, w.prior[b] // 64
+        sel_in[b, :, :nq, :P] = sg[b, :, :nq, :P]
+    ref_bits = topk_mask_ref(sel_in, w.prior, w.chunk, budget, local, w.NKB_max)
+    np.testing.assert_array_equal(m, ref_bits)
+    # end to end against the float64 producer: differing rows must be ambiguous
+    full = producer_mask_ref(q, k, w.prior, w.chunk, budget, local, w.NKB_max)
+    bad = np.argwhere((full != m).any(axis=3))
+    for b, h, qb in bad:
+        P = w.prior[b] // 64
+        lo = max(P - local, 1)
+        s = np.sort(sr[b, h, qb, 1:lo])[::-1]
+        gap = s[budget - 1] - s[budget] if budget < s.size else np.inf
+        assert gap <= 2 * SCORE_ATOL, (b, h, qb, gap)
+    say(f"  rows {m.shape[0] * m.shape[1] * m.shape[2]}, ambiguous-row differences {len(bad)}")
+    return m
+
+
+@pytest.mark.parametrize("budget,local", [(0, 4), (3, 0), (8, 2), (500, 4)])
+def test_producer_small(budget, local):
+    w = gen.make_custom(3, 8, 2, 128, [64 * 60, 0, 64 * 7], [256, 128, 192], "bf16", 31,
+                        lambda rng, b, H, nq, pb: np.zeros((H, nq, pb), np.uint8), C_max=320,
+                        name="producer_small")
+    say(f"producer small budget={budget} local={local}")
+    _check(w, budget, local)
+
+
+def test_producer_ties_lower_block_first():
+    # K blocks repeated so that many block scores tie exactly
+    w = gen.make_custom(1, 4, 1, 64, [64 * 48], [128], "f32", 5,
+                        lambda rng, b, H, nq, pb: np.zeros((H, nq, pb), np.uint8),
+                        name="producer_ties")
+    k = w.k.clone()
+    base = k[:, :, 64:128].clone()
+    for kb in range(1, 48):
+        k[:, :, kb * 64:(kb + 1) * 64] = base if kb % 3 else base * 0.5
+    w.k = k
+    say("producer ties")
+    m = _check(w, budget=5, local=2)
+    row = np.flatnonzero(m[0, 0, 0, 1:46]) + 1
+    assert row.tolist() == [1, 2, 4, 5, 7]  # equal scores: lowest kb first
+
+
+def test_producer_full_size_128k():
+    w = gen.make_workload("llama8b_128k", variant="pairwise")
+    say("producer llama8b_128k budget=64 local=8")
+    m = _check(w, budget=64, local=8)
+    assert (m[0, :, :, 1:2016 - 8].sum(axis=2) >= 0).all()
+    assert (m[0, :, :, 1:2016 - 8].sum(axis=-1) == 64).all()
