@@ -169,6 +169,86 @@ def cpu_baseline(w, seconds_budget=20.0):
     }
 
 
+# --------------------------------------------------------------------------- whole prefill
+
+
+def prefill_leg(stream, budget=32, local=8):
+    """A 128K prompt in 64 chunks of 2048 (planted-structure synthetic stream):
+    per chunk, pool the new key blocks and the queries, make the top-k block
+    mask, build the union tables and run zero-copy attention; the dense
+    baseline runs the same attention over every block.  Cumulative times from
+    HIP events on the launch stream."""
+    import torch
+    import gen
+    from chunked_prefill_sparse_amd.prefill import ChunkedPrefill
+    log("generating prefill_128k stream ...")
+    s = gen.make_prefill_stream("prefill_128k")
+    k, v = s.k.cuda(), s.v.cuda()
+    qs = [s.q_chunk(c).cuda() for c in range(s.n_chunks)]
+    drv = ChunkedPrefill(k, v, s.H_q, s.C, budget=budget, local=local)
+    dense_lens = [drv.dense_lens(c * s.C) for c in range(s.n_chunks)]
+    torch.cuda.synchronize()
+    # untimed pass: work accounting per chunk
+    flops = flops_dense = 0
+    frac = []
+    for c in range(s.n_chunks):
+        P = c * s.C
+        drv.step(qs[c], P)
+        T, ln = drv.T.cpu().numpy(), drv.lens.cpu().numpy()
+        flops += 4 * s.D * admissible_pairs(T, ln, [P], [s.C], s.G)
+        nkb = (P + s.C) // 64
+        Td = np.broadcast_to(np.arange(nkb, dtype=np.int32), (1, s.H_kv, nkb))
+        flops_dense += 4 * s.D * admissible_pairs(Td, np.full((1, s.H_kv), nkb), [P], [s.C], s.G)
+        frac.append(float(ln.sum()) / (s.H_kv * nkb))
+
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    def run_sparse():
+        for c in range(s.n_chunks):
+            drv.step(qs[c], c * s.C)
+
+    def run_select():
+        for c in range(s.n_chunks):
+            drv.select(qs[c], c * s.C)
+
+    def run_dense():
+        for c in range(s.n_chunks):
+            drv.step_dense(qs[c], c * s.C, dense_lens[c])
+
+    reps = 3
+    run_sparse()
+    run_dense()
+    sparse_ms = statistics.median(timed(run_sparse) for _ in range(reps))
+    select_ms = statistics.median(timed(run_select) for _ in range(reps))
+    dense_ms = statistics.median(timed(run_dense) for _ in range(reps))
+    attn_ms = sparse_ms - select_ms
+    r = dict(
+        chunks=s.n_chunks, chunk=s.C, prompt=s.L, budget_blocks=budget, local_blocks=local,
+        total_ms=round(sparse_ms, 3), select_ms=round(select_ms, 3),
+        attention_ms=round(attn_ms, 3), dense_attention_ms=round(dense_ms, 3),
+        x_vs_dense=round(dense_ms / sparse_ms, 3),
+        attention_eff_tflops=round(flops / (attn_ms * 1e-3) / 1e12, 1),
+        dense_eff_tflops=round(flops_dense / (dense_ms * 1e-3) / 1e12, 1),
+        work_frac_of_dense=round(flops / flops_dense, 4),
+        union_block_frac_first_mid_last=[round(frac[0], 3), round(frac[len(frac) // 2], 3),
+                                         round(frac[-1], 3)],
+        data=("synthetic planted-structure stream: K, V, Q ~ N(0,1), 3% salient KV blocks per "
+              "KV head shifted along a per-head direction that the group's queries share"),
+    )
+    log(f"prefill_128k: total {sparse_ms:.2f} ms (select {select_ms:.2f}, attention "
+        f"{attn_ms:.2f}) vs dense attention {dense_ms:.2f} ms -> x{dense_ms / sparse_ms:.2f}; "
+        f"union fraction first/mid/last {r['union_block_frac_first_mid_last']}")
+    del qs, k, v, drv
+    torch.cuda.empty_cache()
+    return r
+
+
 # --------------------------------------------------------------------------- main
 
 
@@ -201,6 +281,7 @@ def main():
     ap.add_argument("--profile", choices=["attn", "union", "copy", "compact"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 64-chunk prefill leg")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -326,7 +407,6 @@ def main():
             x_zero_copy_vs_compaction=round((c_med + a_med) / zc, 4))
         log(f"{name}: compaction copy {c_med:.3f} ms ({compaction[name]['copy_GBps']:.0f} GB/s), "
             f"attention on compact {a_med:.3f} ms, zero-copy {zc:.3f} ms")
-    del k_out, v_out
 
     # Block-sparse-kernel baseline: each Q-block of each head attends its own
     # mask row (per-row lists, no union); also the same kernel fed the union as
@@ -376,7 +456,7 @@ def main():
     achieved = main_r["flops"] / (main_r["attn_ms_mean"] * 1e-3) / 1e12
     roofline = {
         "bound": "mfma",
-        "kernel": "chunk_attn_bf16_kernel<128>",
+        "kernel": "chunk_attn_bf16_kernel<128, 4, false>",
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
@@ -385,6 +465,9 @@ def main():
         "alg_bytes": main_r["bytes_alg"],
         "hbm_alg_GBps": round(main_r["bytes_alg"] / (main_r["attn_ms_mean"] * 1e-3) / 1e9, 1),
     }
+    del k_out, v_out
+    prefill = None if args.no_prefill else prefill_leg(stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
@@ -416,6 +499,7 @@ def main():
                      for n_, r in results.items()},
         "compaction": compaction,
         "block_sparse": sparse,
+        "prefill_128k": prefill,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

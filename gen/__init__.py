@@ -15,3 +15,4 @@ from .workloads import (  # noqa: F401
     make_workload,
     tensor_to_f32,
 )
+from .prefill import PREFILL_STREAMS, PrefillStream, make_prefill_stream  # noqa: F401
