@@ -21,7 +21,7 @@ prints ONE JSON line.  ``value`` is the effective TFLOP/s of a whole step
 (algorithmic FLOPs: 4*D per admissible query/key pair over the selected
 blocks, causal triangle included).  Inputs are resident in HBM before timing.
 
-Profiling helpers (for rocprofv3 runs): ``--profile attn|union|compact|copy`` runs only
+Profiling helpers (for rocprofv3 runs): ``--profile attn|union|compact|prefill|copy`` runs only
 that kernel a few times (``copy`` = a plain device copy of known size, used to
 scale the HBM byte counters).
 """
@@ -278,7 +278,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--reps", type=int, default=50, help="per-kernel timed calls")
-    ap.add_argument("--profile", choices=["attn", "union", "copy", "compact"], default=None)
+    ap.add_argument("--profile", choices=["attn", "union", "copy", "compact", "prefill"],
+                    default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-prefill", action="store_true", help="skip the 64-chunk prefill leg")
@@ -308,6 +309,10 @@ def main():
             dst.copy_(src)
             torch.cuda.synchronize()
             log(f"copy {i}: {n} bytes")
+        return
+
+    if args.profile == "prefill":
+        prefill_leg(stream)
         return
 
     log(f"generating {WORKLOAD} (pairwise mask) ...")

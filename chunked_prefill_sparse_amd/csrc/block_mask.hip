@@ -67,50 +67,99 @@ __global__ __launch_bounds__(kMaskThreads) void pool_blocks_kernel(const TIn* __
 
 // ---------------------------------------------------------------- scores
 
-// Workgroup (b*H_kv + g, y) scores KV blocks 64y .. 64y+63 (one per lane, its
-// kbar row held in registers) against every pooled Q-block row of the group's
-// heads (one row per wave at a time, read as a wave-uniform broadcast).
+// Workgroup (b*H_kv + g, y, z) computes the 64 x 64 tile of scores of the
+// group's pooled Q-block rows 64z .. 64z+63 (row r = head r / nq, Q-block
+// r % nq) against KV blocks 64y .. 64y+63.  Both operands are staged in LDS
+// 32 dimensions at a time, transposed (dimension-major), and each thread keeps
+// a 4 x 4 block of outputs, so every pair of 16-byte LDS reads feeds 16 fused
+// multiply-adds.  Each output is one chain of fused multiply-adds in
+// ascending d.
+constexpr int kScoreTile = 64;
+constexpr int kScoreDStep = 32;
+
 template <int D>
 __global__ __launch_bounds__(kMaskThreads) void block_scores_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int H_q, int H_kv,
     int NQ_max, int NKB_max, SeqInfo seq, float* __restrict__ scores) {
+  __shared__ __attribute__((aligned(16))) float Qs[kScoreDStep][kScoreTile];
+  __shared__ __attribute__((aligned(16))) float Ks[kScoreDStep][kScoreTile];
   const int bg = blockIdx.x;
   const int b = bg / H_kv;
   const int g = bg - b * H_kv;
   const int G = H_q / H_kv;
   const int pblk = seq.prior[b] / 64;
   const int nq = seq.chunk[b] / 64;
-  const int kb0 = static_cast<int>(blockIdx.y) * 64;
-  if (kb0 >= pblk) return;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int kb = kb0 + lane;
-  const bool kin = kb < pblk;
-  float kr[D];
-  if (kin) {
-    const float4* src = reinterpret_cast<const float4*>(
-        kbar + (static_cast<size_t>(bg) * NKB_max + kb) * D);
-#pragma unroll
-    for (int i = 0; i < D / 4; ++i) {
-      const float4 x = src[i];
-      kr[4 * i] = x.x;
-      kr[4 * i + 1] = x.y;
-      kr[4 * i + 2] = x.z;
-      kr[4 * i + 3] = x.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < D; ++i) kr[i] = 0.f;
-  }
-  for (int r = wave; r < G * nq; r += kMaskThreads / 64) {
+  const int kb0 = static_cast<int>(blockIdx.y) * kScoreTile;
+  const int r0 = static_cast<int>(blockIdx.z) * kScoreTile;
+  const int n_rows = G * nq;
+  if (kb0 >= pblk || r0 >= n_rows) return;
+  const int tid = threadIdx.x;
+  const size_t head_row0 = (static_cast<size_t>(b) * H_q + g * G) * NQ_max;
+  auto row_index = [&](int r) {
     const int hl = r / nq;
-    const int qb = r - hl * nq;
-    const size_t row = (static_cast<size_t>(b) * H_q + g * G + hl) * NQ_max + qb;
-    const float* q = qbar + row * D;
-    float s = 0.f;
+    return head_row0 + static_cast<size_t>(hl) * NQ_max + (r - hl * nq);
+  };
+  // loader: thread -> (tile row lr, 4-dim slice ld) twice per operand
+  const int ld = (tid & 7) * 4;
+  const int lr = tid >> 3;  // 0..31, and lr + 32
+  const float* qsrc[2];
+  const float* ksrc[2];
+  bool qin[2], kin[2];
 #pragma unroll
-    for (int d = 0; d < D; ++d) s = __builtin_fmaf(q[d], kr[d], s);
-    if (kin) scores[row * NKB_max + kb] = s;
+  for (int i = 0; i < 2; ++i) {
+    const int r = r0 + lr + 32 * i;
+    qin[i] = r < n_rows;
+    qsrc[i] = qbar + row_index(qin[i] ? r : r0) * D + ld;
+    const int kb = kb0 + lr + 32 * i;
+    kin[i] = kb < pblk;
+    ksrc[i] = kbar + (static_cast<size_t>(bg) * NKB_max + (kin[i] ? kb : kb0)) * D + ld;
+  }
+  const int tr = (tid >> 4) * 4;  // this thread's 4 rows of the tile
+  const int tc = (tid & 15) * 4;  // and its 4 KV blocks
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int d0 = 0; d0 < D; d0 += kScoreDStep) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float4 q = qin[i] ? *reinterpret_cast<const float4*>(qsrc[i] + d0)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 k = kin[i] ? *reinterpret_cast<const float4*>(ksrc[i] + d0)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int c = lr + 32 * i;
+      Qs[ld][c] = q.x;
+      Qs[ld + 1][c] = q.y;
+      Qs[ld + 2][c] = q.z;
+      Qs[ld + 3][c] = q.w;
+      Ks[ld][c] = k.x;
+      Ks[ld + 1][c] = k.y;
+      Ks[ld + 2][c] = k.z;
+      Ks[ld + 3][c] = k.w;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int d = 0; d < kScoreDStep; ++d) {
+      const float4 q = *reinterpret_cast<const float4*>(&Qs[d][tr]);
+      const float4 k = *reinterpret_cast<const float4*>(&Ks[d][tc]);
+      const float qv[4] = {q.x, q.y, q.z, q.w};
+      const float kv[4] = {k.x, k.y, k.z, k.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(qv[i], kv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + tr + i;
+    if (r >= n_rows) continue;
+    float* dst = scores + row_index(r) * NKB_max;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (kb0 + tc + j < pblk) dst[kb0 + tc + j] = acc[i][j];
   }
 }
 
@@ -164,15 +213,34 @@ __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
         if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (tid == 0) {
-        uint32_t cum = 0u;
-        for (int d = 255; d >= 0; --d) {
-          if (cum + hist[d] >= need) {
-            sh_prefix = prefix | (static_cast<uint32_t>(d) << shift);
-            sh_need = need - cum;
-            break;
+      if (tid < 64) {
+        // wave 0 finds the digit holding the need-th largest key: lane l owns
+        // digits 255-4l .. 252-4l; a scan over lanes gives the count above
+        // each lane's digits, and the lane whose range covers `need` walks them
+        uint32_t h[4], tot = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          h[j] = hist[255 - 4 * lane - j];
+          tot += h[j];
+        }
+        uint32_t inc = tot;
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_up(inc, o);
+          if (lane >= o) inc += y;
+        }
+        const uint32_t excl = inc - tot;
+        const uint64_t hit = __ballot(excl < need && need <= inc);
+        if (lane == __ffsll(static_cast<unsigned long long>(hit)) - 1) {
+          uint32_t cum = excl;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (cum + h[j] >= need) {
+              sh_prefix = prefix | (static_cast<uint32_t>(255 - 4 * lane - j) << shift);
+              sh_need = need - cum;
+              break;
+            }
+            cum += h[j];
           }
-          cum += hist[d];
         }
       }
       __syncthreads();
@@ -241,7 +309,9 @@ hipError_t launch_block_mask(const float* qbar, const float* kbar, int B, int H_
                              int budget, int local, float* scores, uint8_t* mask,
                              hipStream_t stream) {
   if (max_pblk > 0) {
-    const dim3 grid(B * H_kv, (max_pblk + 63) / 64);
+    const int ny = (max_pblk + kScoreTile - 1) / kScoreTile;
+    const int nz = ((H_q / H_kv) * NQ_max + kScoreTile - 1) / kScoreTile;
+    const dim3 grid(B * H_kv, ny, nz);
     if (D == 128)
       hipLaunchKernelGGL(block_scores_kernel<128>, grid, dim3(kMaskThreads), 0, stream, qbar,
                          kbar, H_q, H_kv, NQ_max, NKB_max, seq, scores);
