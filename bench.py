@@ -169,6 +169,53 @@ def cpu_baseline(w, seconds_budget=20.0):
     }
 
 
+# --------------------------------------------------------------------------- one GPU's TP share
+
+
+def tp_shard_leg(stream, reps):
+    """One GPU's share of the 128K chunk under tensor parallelism over KV heads:
+    4 query heads and their one KV head (only 64 workgroups of 128 rows), with
+    and without split-KV (each table cut into n ranges, then merged)."""
+    import torch
+    import gen
+    import chunked_prefill_sparse_amd as ca
+    from gen.workloads import _bernoulli_sink_local
+    out = {}
+    for variant in ("pairwise", "colshared"):
+        cs = variant == "colshared"
+        w = gen.make_custom(1, 4, 1, 128, [129024], [2048], "bf16", 1008,
+                            lambda rng, b, H, nq, pb: _bernoulli_sink_local(
+                                rng, H, nq, pb, 0.05, 8, colshared=cs),
+                            name=f"tp_shard_128k_{variant}")
+        q, k, v = w.q.cuda(), w.k.cuda(), w.v.cuda()
+        mask = torch.from_numpy(w.mask).cuda()
+        T, lens = ca.build_union_tables(mask, w.H_kv, w.n_q_blocks, w.n_kv_blocks)
+        o = torch.empty_like(q)
+        torch.cuda.synchronize()
+        flops = 4 * w.D * admissible_pairs(T.cpu().numpy(), lens.cpu().numpy(), w.prior, w.chunk,
+                                           w.G)
+        res = {}
+        for n in (1, 2, 4, 8):
+            ws = torch.empty(max(ca.workspace_size(1, 4, 2048, 128, n), 16), dtype=torch.uint8,
+                             device=q.device)
+            fn = lambda: ca.chunk_attention(q, k, v, T, lens, w.prior, w.chunk, w.scale, out=o,  # noqa: E731
+                                            n_splits=n, workspace=ws)
+            fn()
+            ms = statistics.median(time_calls(fn, reps, stream))
+            res[n] = ms
+        best = min(res, key=res.get)
+        out[variant] = dict(
+            ms_by_splits={str(n_): round(t_, 4) for n_, t_ in res.items()},
+            eff_tflops_no_split=round(flops / (res[1] * 1e-3) / 1e12, 1),
+            best_splits=best, eff_tflops_best=round(flops / (res[best] * 1e-3) / 1e12, 1))
+        log(f"tp_shard_128k {variant}: no split {res[1]:.3f} ms "
+            f"({out[variant]['eff_tflops_no_split']:.0f} TFLOP/s), best n={best} "
+            f"{res[best]:.3f} ms ({out[variant]['eff_tflops_best']:.0f} TFLOP/s)")
+        del q, k, v, mask, T, lens, o
+    torch.cuda.empty_cache()
+    return out
+
+
 # --------------------------------------------------------------------------- whole prefill
 
 
@@ -471,6 +518,7 @@ def main():
         "hbm_alg_GBps": round(main_r["bytes_alg"] / (main_r["attn_ms_mean"] * 1e-3) / 1e9, 1),
     }
     del k_out, v_out
+    tp_shard = tp_shard_leg(stream, args.reps)
     prefill = None if args.no_prefill else prefill_leg(stream)
 
     cpu = None
@@ -504,6 +552,7 @@ def main():
                      for n_, r in results.items()},
         "compaction": compaction,
         "block_sparse": sparse,
+        "tp_shard_128k": tp_shard,
         "prefill_128k": prefill,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -16,11 +16,14 @@ CA_F32 = 0
 CA_BF16 = 1
 CA_BLOCK = 64
 CA_MAX_BATCH = 128
+CA_MAX_SPLITS = 16
 
 EXPORTED = (
     "ca_build_union_tables",
     "ca_chunk_attention",
     "ca_chunk_attention_rows",
+    "ca_chunk_attention_split",
+    "ca_chunk_attention_workspace_size",
     "ca_tables_to_csr",
     "ca_compact_kv",
     "ca_pool_blocks",
@@ -50,6 +53,12 @@ def _declare(lib):
                                             _i32, _i32, _i32, _i32, _i64, _i32, _i32,
                                             ctypes.c_float, _i32, _vp, _vp, _vp]
     lib.ca_chunk_attention_rows.restype = _i32
+    lib.ca_chunk_attention_split.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32p, _i32p, _i32,
+                                             _i32, _i32, _i32, _i64, _i32, _i32, ctypes.c_float,
+                                             _i32, _i32, _vp, ctypes.c_size_t, _vp, _vp, _vp]
+    lib.ca_chunk_attention_split.restype = _i32
+    lib.ca_chunk_attention_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
+    lib.ca_chunk_attention_workspace_size.restype = ctypes.c_size_t
     lib.ca_tables_to_csr.argtypes = [_vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _vp]
     lib.ca_tables_to_csr.restype = _i32
     lib.ca_compact_kv.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32p, _i32p, _i32, _i32, _i64, _i32,

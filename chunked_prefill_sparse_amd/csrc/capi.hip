@@ -90,7 +90,8 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
                     const int32_t* len, int NQ_max, int NKB_max, const int32_t* prior_len,
                     const int32_t* chunk_len, int B, int H_q, int H_kv, int C_max, int64_t L,
                     int D, int block, float scale, ca_dtype dtype, void* O, float* lse,
-                    bool row_tables, hipStream_t stream) {
+                    bool row_tables, int n_split, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
   if (!Q || !K_cache || !V_cache || !T || !len || !prior_len || !chunk_len || !O)
     return CA_ERR_NULL;
   if (dtype != CA_F32 && dtype != CA_BF16) return CA_ERR_DTYPE;
@@ -130,6 +131,8 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
   p.scale_log2 = scale * 1.4426950408889634f;
   p.row_tables = row_tables ? 1 : 0;
   p.NQ_max = row_tables ? NQ_max : 0;
+  p.n_split = n_split;
+  p.rows_total = static_cast<int64_t>(B) * H_q * C_max;
   const int64_t n_bg = static_cast<int64_t>(B) * H_kv;
   if (dtype == CA_BF16) {
     const int64_t n_pb = (C_max + 31) / 32;
@@ -138,7 +141,13 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
     p.n_t = row_tables ? static_cast<int>(p.G * ((C_max + 63) / 64))
                        : static_cast<int>((p.G * n_pb + 3) / 4);
     p.xcd = (n_bg % 8 == 0) ? 1 : 0;
-    if (n_bg * p.n_t > INT32_MAX) return CA_ERR_SHAPE;
+    if (n_bg * p.n_t * n_split > INT32_MAX) return CA_ERR_SHAPE;
+    if (n_split > 1) {
+      float* part_o = static_cast<float*>(workspace);
+      float* part_ml = part_o + static_cast<size_t>(n_split) * p.rows_total * D;
+      return hip_status(ca::launch_chunk_attn_bf16_split(Q, K_cache, V_cache, T, len, O, lse, B,
+                                                         D, p, seq, part_o, part_ml, stream));
+    }
     return hip_status(ca::launch_chunk_attn_bf16(Q, K_cache, V_cache, T, len, O, lse, B, D, p,
                                                  seq, stream));
   }
@@ -162,7 +171,37 @@ CA_EXPORT ca_status ca_chunk_attention(const void* Q, const void* K_cache, const
                                        int block, float scale, ca_dtype dtype, void* O,
                                        float* lse, hipStream_t stream) {
   return attention(Q, K_cache, V_cache, T, len, 0, NKB_max, prior_len, chunk_len, B, H_q, H_kv,
-                   C_max, L, D, block, scale, dtype, O, lse, false, stream);
+                   C_max, L, D, block, scale, dtype, O, lse, false, 1, nullptr, 0, stream);
+}
+
+CA_EXPORT size_t ca_chunk_attention_workspace_size(int B, int H_q, int C_max, int D,
+                                                    int n_splits) {
+  if (B < 1 || H_q < 1 || C_max < 1 || D < 1 || n_splits < 2) return 0;
+  return static_cast<size_t>(n_splits) * B * H_q * C_max * (D + 2) * sizeof(float);
+}
+
+CA_EXPORT ca_status ca_chunk_attention_split(const void* Q, const void* K_cache,
+                                             const void* V_cache, const int32_t* T,
+                                             const int32_t* len, int NKB_max,
+                                             const int32_t* prior_len, const int32_t* chunk_len,
+                                             int B, int H_q, int H_kv, int C_max, int64_t L,
+                                             int D, int block, float scale, ca_dtype dtype,
+                                             int n_splits, void* workspace,
+                                             size_t workspace_bytes, void* O, float* lse,
+                                             hipStream_t stream) {
+  if (n_splits < 1 || n_splits > CA_MAX_SPLITS) return CA_ERR_SHAPE;
+  if (n_splits == 1)
+    return attention(Q, K_cache, V_cache, T, len, 0, NKB_max, prior_len, chunk_len, B, H_q,
+                     H_kv, C_max, L, D, block, scale, dtype, O, lse, false, 1, nullptr, 0, stream);
+  if (dtype == CA_F32) return CA_ERR_UNSUPPORTED;
+  if (!workspace) return CA_ERR_NULL;
+  if (!aligned16(workspace)) return CA_ERR_UNSUPPORTED;
+  if (B >= 1 && H_q >= 1 && C_max >= 1 && (D == 64 || D == 128) &&
+      workspace_bytes < ca_chunk_attention_workspace_size(B, H_q, C_max, D, n_splits))
+    return CA_ERR_SHAPE;
+  return attention(Q, K_cache, V_cache, T, len, 0, NKB_max, prior_len, chunk_len, B, H_q, H_kv,
+                   C_max, L, D, block, scale, dtype, O, lse, false, n_splits, workspace,
+                   workspace_bytes, stream);
 }
 
 CA_EXPORT ca_status ca_chunk_attention_rows(const void* Q, const void* K_cache,
@@ -173,7 +212,8 @@ CA_EXPORT ca_status ca_chunk_attention_rows(const void* Q, const void* K_cache,
                                             int D, int block, float scale, ca_dtype dtype,
                                             void* O, float* lse, hipStream_t stream) {
   return attention(Q, K_cache, V_cache, T_rows, len_rows, NQ_max, NKB_max, prior_len, chunk_len,
-                   B, H_q, H_kv, C_max, L, D, block, scale, dtype, O, lse, true, stream);
+                   B, H_q, H_kv, C_max, L, D, block, scale, dtype, O, lse, true, 1, nullptr, 0,
+                   stream);
 }
 
 CA_EXPORT ca_status ca_compact_kv(const void* K_cache, const void* V_cache, const int32_t* T,

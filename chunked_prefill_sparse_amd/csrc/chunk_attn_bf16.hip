@@ -80,11 +80,17 @@ __device__ __forceinline__ void body_schedule() {
 // 4 waves (W = 4).  kRows = true: one table per (b, h, Q-block), the
 // per-Q-block lists of a block-sparse kernel, so a workgroup is the 2 waves
 // (W = 2) of one 64-row Q-block of one head.
-template <int D, int W, bool kRows>
+// kSplit: the table of a (b, g) is cut into p.n_split contiguous ranges, one
+// per workgroup (the straddling blocks go to the last range), and each
+// workgroup writes its unnormalised partial output, running max and
+// denominator to part_o / part_ml for split_combine_kernel.  More workgroups
+// for shapes with few (b, g) pairs.
+template <int D, int W, bool kRows, bool kSplit>
 __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const int32_t* __restrict__ T, const int32_t* __restrict__ len, __bf16* __restrict__ O,
-    float* __restrict__ lse, AttnParams p, SeqInfo seq) {
+    float* __restrict__ lse, AttnParams p, SeqInfo seq, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
   constexpr int DS = D / 16;
   constexpr int DT = D / 32;
   constexpr int RB = Tile<D>::kRowBytes;
@@ -92,6 +98,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   constexpr int NDMA = kDmaPerWave<D, W>;
   constexpr int kThreads = W * 64;
   static_assert(kRows ? W == 2 : W == 4, "workgroup shape");
+  static_assert(!(kRows && kSplit), "split ranges are for union tables");
   // LDS: two K tiles, then two V tiles
   __shared__ __attribute__((aligned(1024))) char lds[4 * Tile<D>::kBytes];
 
@@ -102,17 +109,23 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // ---- workgroup -> (sequence, group, tile)
+  // ---- workgroup -> (sequence, group, tile[, split])
   const int wg = blockIdx.x;
+  const int n_tt = kSplit ? p.n_t * p.n_split : p.n_t;  // workgroups per (b, g)
   int u, t;
   if (p.xcd) {
     const int x = wg & 7, k = wg >> 3;
-    const int jj = k / p.n_t;
+    const int jj = k / n_tt;
     u = x + 8 * jj;
-    t = k - jj * p.n_t;
+    t = k - jj * n_tt;
   } else {
-    u = wg / p.n_t;
-    t = wg - u * p.n_t;
+    u = wg / n_tt;
+    t = wg - u * n_tt;
+  }
+  int split = 0;
+  if (kSplit) {
+    split = t / p.n_t;
+    t -= split * p.n_t;
   }
   const int rank = u / p.H_kv;
   const int g = u - rank * p.H_kv;
@@ -241,8 +254,11 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
     if (valid(kb) && !needs_mask(kb)) break;
     --e;
   }
+  // this workgroup's range of [0, e); all of it without splitting
+  const int e_lo = kSplit ? static_cast<int>((static_cast<int64_t>(e) * split) / p.n_split) : 0;
+  const int ee = kSplit ? static_cast<int>((static_cast<int64_t>(e) * (split + 1)) / p.n_split) : e;
   auto next_plain = [&](int jj) {
-    while (jj < e) {
+    while (jj < ee) {
       const int kb = Trow[jj];
       if (valid(kb) && !needs_mask(kb)) break;
       ++jj;
@@ -250,21 +266,21 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
     return jj;
   };
 
-  int j = next_plain(0);
+  int j = next_plain(e_lo);
   int j1 = next_plain(j + 1);
   int j2 = next_plain(j1 + 1);
-  const int kbj = j < e ? Trow[j] : 0;
+  const int kbj = j < ee ? Trow[j] : 0;
   int kb0 = kbj;
-  int kb1 = j1 < e ? Trow[j1] : 0;
-  int kb2 = j2 < e ? Trow[j2] : 0;
+  int kb1 = j1 < ee ? Trow[j1] : 0;
+  int kb2 = j2 < ee ? Trow[j2] : 0;
   auto boff = [&](int jj, int kb) {  // block byte offset, or past the end when jj is not used
-    return jj < e ? static_cast<uint32_t>(kb) * (kBlk * D * 2) : slice_bytes;
+    return jj < ee ? static_cast<uint32_t>(kb) * (kBlk * D * 2) : slice_bytes;
   };
   f32x16 sa0, sa1, sb0, sb1;  // scores of the current / next block (roles alternate)
   bf16x8 pxa[4], pxb[4];      // probabilities waiting for their P.V (roles alternate)
 #pragma unroll
   for (int i = 0; i < 4; ++i) pxa[i] = pxb[i] = bf16x8{};
-  if (j < e) {
+  if (j < ee) {
     dma_tile<D, W>(K0, krsrc, boff(j, kbj), offk, wave_u);
     dma_tile<D, W>(K1, krsrc, boff(j1, kb1), offk, wave_u);
     // V1 is read by the first step with zero probabilities: make it finite
@@ -298,10 +314,10 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
     softmax_probs<D>(cur0, cur1, ws, pcur, c);
     const float mx = row_max(nxt0, nxt1, xhalf);
     body_schedule<D, W>();
-    const bool last = j1 >= e;
+    const bool last = j1 >= ee;
     const bool moves = !last && __any(mx > ws.m_used + thr);
     const int j3 = next_plain(j2 + 1);
-    const int kb3 = j3 < e ? Trow[j3] : 0;
+    const int kb3 = j3 < ee ? Trow[j3] : 0;
     wait_vmem();
     __syncthreads();
     if (moves || last) {
@@ -317,15 +333,15 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
     j2 = j3;
     kb2 = kb3;
   };
-  while (j < e) {
+  while (j < ee) {
     step(sa0, sa1, sb0, sb1, pxb, pxa, K1, V1, K0, V0);
-    if (j >= e) break;
+    if (j >= ee) break;
     step(sb0, sb1, sa0, sa1, pxa, pxb, K0, V0, K1, V1);
   }
 
   // Blocks that straddle the workgroup's rows (usually one): one at a time,
   // with the causal mask.
-  for (int jt = e; jt < nT; ++jt) {
+  for (int jt = e; jt < ((!kSplit || split == p.n_split - 1) ? nT : e); ++jt) {
     const int kb = Trow[jt];
     if (!valid(kb)) continue;
     __syncthreads();  // every wave is done with the buffers
@@ -345,6 +361,22 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   // ---- epilogue: O = acc / l, rows >= C written as 0
   const float l_tot = ws.l_part + __shfl_xor(ws.l_part, 32);
   if (!row_in) return;
+  if (kSplit) {  // partial results: acc (unnormalised), running max, denominator
+    if (!row_live) return;
+    const size_t prow = static_cast<size_t>(split) * p.rows_total + qo_row;
+    float* po = part_o + prow * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float* a = reinterpret_cast<const float*>(&ws.acc[dt]) + 4 * rr;
+        *reinterpret_cast<float4*>(po + 32 * dt + 8 * rr + 4 * hh) =
+            make_float4(a[0], a[1], a[2], a[3]);
+      }
+    }
+    if (hh == 0) *reinterpret_cast<float2*>(part_ml + 2 * prow) = make_float2(ws.m_used, l_tot);
+    return;
+  }
   const float inv = (row_live && l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (!row_live) {  // padding rows: exact zeros whatever the (unused) Q row held
 #pragma unroll
@@ -379,21 +411,98 @@ hipError_t launch_chunk_attn_bf16(const void* Q, const void* K, const void* V,
   const __bf16* k = static_cast<const __bf16*>(K);
   const __bf16* v = static_cast<const __bf16*>(V);
   __bf16* o = static_cast<__bf16*>(O);
+  float* const no = nullptr;
   if (p.row_tables) {
     if (D == 128)
-      hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 2, true>), grid, dim3(128), 0, stream, q,
-                         k, v, T, len, o, lse, p, seq);
+      hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 2, true, false>), grid, dim3(128), 0, stream,
+                         q, k, v, T, len, o, lse, p, seq, no, no);
     else
-      hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 2, true>), grid, dim3(128), 0, stream, q, k,
-                         v, T, len, o, lse, p, seq);
+      hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 2, true, false>), grid, dim3(128), 0, stream,
+                         q, k, v, T, len, o, lse, p, seq, no, no);
   } else {
     if (D == 128)
-      hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 4, false>), grid, dim3(256), 0, stream, q,
-                         k, v, T, len, o, lse, p, seq);
+      hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 4, false, false>), grid, dim3(256), 0,
+                         stream, q, k, v, T, len, o, lse, p, seq, no, no);
     else
-      hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 4, false>), grid, dim3(256), 0, stream, q,
-                         k, v, T, len, o, lse, p, seq);
+      hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 4, false, false>), grid, dim3(256), 0, stream,
+                         q, k, v, T, len, o, lse, p, seq, no, no);
   }
+  return hipGetLastError();
+}
+
+namespace {
+
+// Merge of the split partials of one output row per wave: with m_s, l_s, a_s
+// the running max (raw score units), denominator and unnormalised output of
+// split s and M = max_s m_s, w_s = exp2((m_s - M) * scale * log2 e):
+//   O = sum_s w_s a_s / sum_s w_s l_s,   lse = M * scale + log(sum_s w_s l_s).
+// Rows past the chunk, and rows no split saw a key for, give O = 0, lse = -inf.
+template <int D>
+__global__ __launch_bounds__(256) void split_combine_kernel(const float* __restrict__ part_o,
+                                                            const float* __restrict__ part_ml,
+                                                            AttnParams p, SeqInfo seq,
+                                                            __bf16* __restrict__ O,
+                                                            float* __restrict__ lse) {
+  constexpr int E = D / 64;  // elements per lane
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= p.rows_total) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t per_b = static_cast<int64_t>(p.H_q) * p.C_max;
+  const int b = static_cast<int>(r / per_b);
+  const int i = static_cast<int>(r % p.C_max);
+  float M = -INFINITY;
+  if (i < seq.chunk[b])
+    for (int sp = 0; sp < p.n_split; ++sp)
+      M = fmaxf(M, part_ml[2 * (static_cast<size_t>(sp) * p.rows_total + r)]);
+  float acc[E], l = 0.f;
+#pragma unroll
+  for (int k = 0; k < E; ++k) acc[k] = 0.f;
+  if (M != -INFINITY) {
+    for (int sp = 0; sp < p.n_split; ++sp) {
+      const size_t pr = static_cast<size_t>(sp) * p.rows_total + r;
+      const float ms = part_ml[2 * pr];
+      if (ms == -INFINITY) continue;
+      const float wgt = __builtin_amdgcn_exp2f((ms - M) * p.scale_log2);
+      l += wgt * part_ml[2 * pr + 1];
+      const float* po = part_o + pr * D + E * lane;
+#pragma unroll
+      for (int k = 0; k < E; ++k) acc[k] += wgt * po[k];
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  __bf16* orow = O + r * D + E * lane;
+#pragma unroll
+  for (int k = 0; k < E; ++k) orow[k] = static_cast<__bf16>(acc[k] * inv);
+  if (lse && lane == 0) lse[r] = l > 0.f ? M * p.scale + __logf(l) : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_chunk_attn_bf16_split(const void* Q, const void* K, const void* V,
+                                        const int32_t* T, const int32_t* len, void* O,
+                                        float* lse, int B, int D, const AttnParams& p,
+                                        const SeqInfo& seq, float* part_o, float* part_ml,
+                                        hipStream_t stream) {
+  const dim3 grid(B * p.H_kv * p.n_t * p.n_split);
+  const __bf16* q = static_cast<const __bf16*>(Q);
+  const __bf16* k = static_cast<const __bf16*>(K);
+  const __bf16* v = static_cast<const __bf16*>(V);
+  __bf16* o = static_cast<__bf16*>(O);
+  if (D == 128)
+    hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 4, false, true>), grid, dim3(256), 0, stream,
+                       q, k, v, T, len, o, lse, p, seq, part_o, part_ml);
+  else
+    hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 4, false, true>), grid, dim3(256), 0, stream,
+                       q, k, v, T, len, o, lse, p, seq, part_o, part_ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 cgrid(static_cast<unsigned>((p.rows_total + 3) / 4));
+  if (D == 128)
+    hipLaunchKernelGGL(split_combine_kernel<128>, cgrid, dim3(256), 0, stream, part_o, part_ml, p,
+                       seq, o, lse);
+  else
+    hipLaunchKernelGGL(split_combine_kernel<64>, cgrid, dim3(256), 0, stream, part_o, part_ml, p,
+                       seq, o, lse);
   return hipGetLastError();
 }
 

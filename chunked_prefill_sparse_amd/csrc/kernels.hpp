@@ -41,6 +41,8 @@ struct AttnParams {
   int xcd;              // 1: keep each pseudo-request's workgroups on one XCD
   int row_tables;       // 0: T[b,g] (union); 1: T[b,h,Q-block] (per-Q-block lists)
   int NQ_max;           // Q-blocks per head in the per-Q-block table layout
+  int n_split;          // split-KV: table ranges per (b, g) (1: no split)
+  int64_t rows_total;   // B * H_q * C_max (split-KV partial layout)
 };
 
 hipError_t launch_union_tables(const uint8_t* mask, int B, int H_q, int H_kv, int NQ_max,
@@ -56,6 +58,16 @@ hipError_t launch_chunk_attn_bf16(const void* Q, const void* K, const void* V,
                                   const int32_t* T, const int32_t* len, void* O, float* lse,
                                   int B, int D, const AttnParams& p, const SeqInfo& seq,
                                   hipStream_t stream);
+
+// bf16 path with each (b, g) table cut into p.n_split ranges: partial
+// results in part_o (float [n_split, B*H_q*C_max, D]) and part_ml (float
+// [n_split, B*H_q*C_max, 2]: running max, denominator), then a combine kernel
+// writes O and lse.
+hipError_t launch_chunk_attn_bf16_split(const void* Q, const void* K, const void* V,
+                                        const int32_t* T, const int32_t* len, void* O,
+                                        float* lse, int B, int D, const AttnParams& p,
+                                        const SeqInfo& seq, float* part_o, float* part_ml,
+                                        hipStream_t stream);
 
 // fp32 path on the vector ALUs; D in {64, 128}.
 hipError_t launch_chunk_attn_f32(const float* Q, const float* K, const float* V,

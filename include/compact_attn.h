@@ -51,6 +51,7 @@ extern "C" {
 
 #define CA_BLOCK 64      /* tokens per KV block and per Q-block */
 #define CA_MAX_BATCH 128 /* sequences per call */
+#define CA_MAX_SPLITS 16 /* split-KV ranges per (sequence, KV head) */
 
 typedef enum {
   CA_OK = 0,
@@ -139,6 +140,42 @@ CA_EXPORT ca_status ca_chunk_attention(const void* Q, const void* K_cache, const
                              int H_q, int H_kv, int C_max, int64_t L, int D, int block,
                              float scale, ca_dtype dtype, void* O, float* lse,
                              hipStream_t stream);
+
+/*
+ * ca_chunk_attention_split -- ca_chunk_attention with each (b, g) table cut
+ * into n_splits contiguous ranges processed by separate workgroups, then
+ * merged.  For shapes with few (sequence, KV head) pairs, such as one GPU's
+ * share of the KV heads under tensor parallelism (H_kv = 1): the same result
+ * (the same admissible keys and the same softmax), up to the rounding of the
+ * merge.  Split s keeps an unnormalised partial output a_s, its running max
+ * m_s and denominator l_s; with M = max_s m_s and w_s = exp(scale*(m_s - M)),
+ *   O = sum_s w_s a_s / sum_s w_s l_s,   lse = scale*M + log(sum_s w_s l_s),
+ * The pages do not describe splitting one table over several workers; this
+ * is the usual merge of partial softmax results, exact up to rounding.
+ *
+ * n_splits   1..CA_MAX_SPLITS (else CA_ERR_SHAPE); 1 is ca_chunk_attention
+ *            itself (workspace unused).
+ * workspace  device memory owned by the caller, 16-byte aligned, at least
+ *            ca_chunk_attention_workspace_size(B, H_q, C_max, D, n_splits)
+ *            bytes (else CA_ERR_SHAPE); NULL only when n_splits == 1.
+ * dtype      CA_BF16 when n_splits > 1 (CA_F32: CA_ERR_UNSUPPORTED).
+ * Other arguments, layouts and errors as for ca_chunk_attention.  Calls that
+ * share one workspace must be ordered on one stream.
+ */
+CA_EXPORT ca_status ca_chunk_attention_split(const void* Q, const void* K_cache,
+                                   const void* V_cache, const int32_t* T, const int32_t* len,
+                                   int NKB_max, const int32_t* prior_len,
+                                   const int32_t* chunk_len, int B, int H_q, int H_kv,
+                                   int C_max, int64_t L, int D, int block, float scale,
+                                   ca_dtype dtype, int n_splits, void* workspace,
+                                   size_t workspace_bytes, void* O, float* lse,
+                                   hipStream_t stream);
+
+/* Bytes of workspace ca_chunk_attention_split needs: n_splits * B * H_q *
+ * C_max * (D + 2) * 4 (partial outputs, running maxima, denominators); 0 for
+ * n_splits < 2 or nonpositive sizes. */
+CA_EXPORT size_t ca_chunk_attention_workspace_size(int B, int H_q, int C_max, int D,
+                                         int n_splits);
 
 /*
  * ca_chunk_attention_rows -- the block-sparse-kernel execution that the union
