@@ -119,6 +119,22 @@ def time_calls(fn, reps, stream):
     return [a.elapsed_time(b) for a, b in evs]
 
 
+def time_calls_cold(fn, reps, stream, scratch):
+    """Like time_calls, but a write over ``scratch`` (>= 512 MiB, larger than the
+    caches) runs before each call, outside the timed events, so every call
+    starts with cold L2 and MALL."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        scratch.fill_(1)
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
 def pct(xs, q):
     return float(np.percentile(np.asarray(xs), q))
 
@@ -418,6 +434,9 @@ def main():
         ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
         attn_ms = time_calls(lambda: attn(T, lens), args.reps, stream)
         union_ms = time_calls(lambda: tables(name), args.reps, stream)
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold_ms = time_calls_cold(lambda: attn(T, lens), max(args.reps // 5, 5), stream, scratch)
+        del scratch
         a_med = statistics.median(attn_ms)
         a_mean = float(np.mean(attn_ms))
         per_head_union = float(x.mask[:, :, :, :].any(axis=2).sum(axis=-1).mean())
@@ -425,6 +444,7 @@ def main():
             ms_per_step=ms_step,
             attn_ms_median=a_med, attn_ms_mean=a_mean,
             attn_ms_p10=pct(attn_ms, 10), attn_ms_p90=pct(attn_ms, 90),
+            attn_ms_cold_median=statistics.median(cold_ms),
             union_us_median=statistics.median(union_ms) * 1e3,
             flops=flops, bytes_alg=bytes_alg, pairs=pairs,
             eff_tflops_step=flops / (ms_step * 1e-3) / 1e12,
