@@ -46,6 +46,7 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published)
 WORKLOAD = "llama8b_128k"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "chunk_attn_bf16_llama8b_128k_pmc.txt")
 KERNEL_SRC = os.path.join(ROOT, "chunked_prefill_sparse_amd", "csrc", "chunk_attn_bf16.hip")
+KERNEL_HDR = os.path.join(ROOT, "chunked_prefill_sparse_amd", "csrc", "attn_bf16_common.hpp")
 
 
 def log(msg):
@@ -327,7 +328,9 @@ def stored_traffic():
             k_, _, v_ = line.partition(":")
             vals[k_.strip()] = v_.strip()
     src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
-    if vals.get("kernel_source_sha256_16") != src_hash:
+    hdr_hash = hashlib.sha256(open(KERNEL_HDR, "rb").read()).hexdigest()[:16]
+    if vals.get("kernel_source_sha256_16") != src_hash or \
+            vals.get("helpers_source_sha256_16") != hdr_hash:
         return None, vals
     try:
         return float(vals["hbm_bytes_per_launch"]), vals
@@ -528,7 +531,7 @@ def main():
     achieved = main_r["flops"] / (main_r["attn_ms_mean"] * 1e-3) / 1e12
     roofline = {
         "bound": "mfma",
-        "kernel": "chunk_attn_bf16_kernel<128, 4, false>",
+        "kernel": "chunk_attn_bf16_kernel<128, 4, false, false>",
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
