@@ -152,9 +152,12 @@ def cpu_baseline(w, seconds_budget=20.0):
     from oracle import chunk_attention_rows_ref, union_tables_ref
     try:
         from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([int(i.get("num_threads", 1)) for i in info] or [1])
+        blas = ",".join(sorted({str(i.get("internal_api", "?")) for i in info
+                                if i.get("user_api") == "blas"})) or "unknown"
     except Exception:
-        threads = 1
+        threads, blas = 1, "unknown"
     t0 = time.perf_counter()
     T, ln = union_tables_ref(w.mask, w.H_kv, w.n_q_blocks, w.n_kv_blocks)
     t_union = time.perf_counter() - t0
@@ -182,6 +185,8 @@ def cpu_baseline(w, seconds_budget=20.0):
                    f"query heads of {groups} of {w.H_kv} KV groups ({rows_done} rows) in "
                    f"{elapsed:.1f} s; value = algorithmic FLOPs of those rows / their time"),
         "host_cpus": os.cpu_count(),
+        "blas": blas,
+        "note": "NumPy element-wise work (exp, max) runs on one thread; the products use BLAS threads",
         "cpu_model": platform.processor() or platform.machine(),
     }
 
@@ -343,7 +348,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--reps", type=int, default=50, help="per-kernel timed calls")
+    ap.add_argument("--reps", type=int, default=100, help="per-kernel timed calls")
     ap.add_argument("--profile", choices=["attn", "union", "copy", "compact", "prefill"],
                     default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -539,6 +544,9 @@ def main():
         "traffic": traffic,
         "alg_bytes": main_r["bytes_alg"],
         "hbm_alg_GBps": round(main_r["bytes_alg"] / (main_r["attn_ms_mean"] * 1e-3) / 1e9, 1),
+        "hbm_frac": (round(traffic / (main_r["attn_ms_mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+                     if traffic else None),
+        "reread_factor": round(traffic / main_r["bytes_alg"], 4) if traffic else None,
     }
     del k_out, v_out
     tp_shard = tp_shard_leg(stream, args.reps)

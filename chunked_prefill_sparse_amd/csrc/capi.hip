@@ -135,6 +135,9 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
   p.rows_total = static_cast<int64_t>(B) * H_q * C_max;
   const int64_t n_bg = static_cast<int64_t>(B) * H_kv;
   if (dtype == CA_BF16) {
+    // the bf16 kernels address one (b, g) cache slice through a buffer
+    // resource with 32-bit byte offsets
+    if (L * D * 2 > static_cast<int64_t>(UINT32_MAX)) return CA_ERR_UNSUPPORTED;
     const int64_t n_pb = (C_max + 31) / 32;
     // workgroups per (b, g): 4 waves of 32 rows over the group's heads, or one
     // 64-row Q-block of one head per workgroup with per-Q-block tables

@@ -129,7 +129,9 @@ CA_EXPORT ca_status ca_build_union_tables(const uint8_t* mask, int B, int H_q, i
  * block       must be 64 (else CA_ERR_UNSUPPORTED).
  * scale       softmax scale applied to Q.K (1/sqrt(D) in the usual case); > 0.
  * dtype       CA_BF16: bf16 in/out, fp32 accumulation on the matrix cores,
- *             probabilities rounded to bf16 for the P.V product.
+ *             probabilities rounded to bf16 for the P.V product.  Requires
+ *             L * D * 2 < 2^32 (a 4 GiB cache slice per (b, g); else
+ *             CA_ERR_UNSUPPORTED).
  *             CA_F32:  fp32 in/out and fp32 arithmetic throughout.
  * lse         device float [B, H_q, C_max] (out) or NULL.
  * Errors: CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_DTYPE, CA_ERR_UNSUPPORTED, CA_ERR_HIP.

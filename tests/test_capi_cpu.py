@@ -89,6 +89,7 @@ def _attn(lib, **kw):
     (dict(chunk=_ints(250)), 4),               # unaligned chunk
     (dict(Q=FAKE + 8), 4),                     # not 16-byte aligned
     (dict(lse=FAKE + 2), 4),
+    (dict(dtype=1, L=1 << 24, D=128), 4),      # bf16 cache slice of 4 GiB: beyond 32-bit offsets
 ])
 def test_attention_validation(kw, status):
     assert _attn(_lib.lib(), **kw) == status
