@@ -36,7 +36,7 @@ CA_EXPORT const char* ca_status_string(ca_status s) {
     case CA_ERR_NULL: return "CA_ERR_NULL: a required pointer is NULL";
     case CA_ERR_SHAPE: return "CA_ERR_SHAPE: sizes inconsistent or out of range";
     case CA_ERR_DTYPE: return "CA_ERR_DTYPE: unknown element type";
-    case CA_ERR_UNSUPPORTED: return "CA_ERR_UNSUPPORTED: request not supported by this build";
+    case CA_ERR_UNSUPPORTED: return "CA_ERR_UNSUPPORTED: request this library does not run";
     case CA_ERR_HIP: return "CA_ERR_HIP: the HIP runtime reported an error";
   }
   return "unknown ca_status";

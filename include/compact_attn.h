@@ -58,7 +58,7 @@ typedef enum {
   CA_ERR_NULL = 1,        /* a required pointer is NULL */
   CA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
   CA_ERR_DTYPE = 3,       /* unknown element type */
-  CA_ERR_UNSUPPORTED = 4, /* valid request this build does not run (see each call) */
+  CA_ERR_UNSUPPORTED = 4, /* valid request this library does not run (see each call) */
   CA_ERR_HIP = 5          /* the HIP runtime reported an error */
 } ca_status;
 
@@ -121,7 +121,7 @@ CA_EXPORT ca_status ca_build_union_tables(const uint8_t* mask, int B, int H_q, i
  *             [B, H_kv].  Entries outside [0, n_kv_blocks[b]) and len values
  *             outside [0, NKB_max] are clamped away, never dereferenced.
  * prior_len,  host int32 [B]: cached tokens before the chunk, and chunk tokens.
- * chunk_len   Both multiples of 64 in this build (else CA_ERR_UNSUPPORTED);
+ * chunk_len   Both multiples of 64 (else CA_ERR_UNSUPPORTED);
  *             0 <= chunk_len[b] <= C_max; prior_len[b] + chunk_len[b] <= L and
  *             <= 64 * NKB_max.
  * B           1..CA_MAX_BATCH.  H_q % H_kv == 0.
