@@ -1,0 +1,147 @@
+// Exercises the C ABI's host code (argument validation, sequence ordering,
+// launch parameters, workspace layout) with the kernel launchers replaced by
+// stand-ins, under AddressSanitizer and UndefinedBehaviorSanitizer.  Exits 0
+// and prints "host check OK" when every expectation holds.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "compact_attn.h"
+#include "stubs.hpp"
+
+static int failures = 0;
+#define EXPECT(cond)                                                   \
+  do {                                                                 \
+    if (!(cond)) {                                                     \
+      fprintf(stderr, "%s:%d: expectation failed: %s\n", __FILE__,     \
+              __LINE__, #cond);                                        \
+      ++failures;                                                      \
+    }                                                                  \
+  } while (0)
+
+static void* const FAKE = reinterpret_cast<void*>(0x10000);  // never dereferenced by the host code
+
+int main() {
+  // ---- union tables: a full batch, then errors
+  {
+    std::vector<int32_t> nq(CA_MAX_BATCH, 4), nkb(CA_MAX_BATCH, 20);
+    nq.back() = 3;
+    nkb.back() = 17;
+    EXPECT(ca_build_union_tables((const uint8_t*)FAKE, CA_MAX_BATCH, 32, 8, 4, 20, nq.data(),
+                                 nkb.data(), (int32_t*)FAKE, (int32_t*)FAKE, 0) == CA_OK);
+    EXPECT(strcmp(stub::last.what, "union") == 0);
+    EXPECT(stub::last.ints[4] == 3 && stub::last.ints[5] == 17);
+    EXPECT(ca_build_union_tables((const uint8_t*)FAKE, CA_MAX_BATCH + 1, 32, 8, 4, 20, nq.data(),
+                                 nkb.data(), (int32_t*)FAKE, (int32_t*)FAKE, 0) == CA_ERR_SHAPE);
+    nkb[5] = 21;
+    EXPECT(ca_build_union_tables((const uint8_t*)FAKE, 8, 32, 8, 4, 20, nq.data(), nkb.data(),
+                                 (int32_t*)FAKE, (int32_t*)FAKE, 0) == CA_ERR_SHAPE);
+  }
+  // ---- attention: ordering longest first, launch parameters, paths
+  {
+    const int32_t prior[3] = {1024, 8192, 0}, chunk[3] = {256, 128, 64};
+    EXPECT(ca_chunk_attention(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE, 200,
+                              prior, chunk, 3, 32, 8, 256, 8448, 128, 64, 0.125f, CA_BF16, FAKE,
+                              nullptr, 0) == CA_OK);
+    EXPECT(strcmp(stub::last.what, "attn_bf16") == 0);
+    // dense work (P+C)*C: 327680, 1064960, 4096 -> order 1, 0, 2
+    EXPECT(stub::last.seq.order[0] == 1 && stub::last.seq.order[1] == 0 &&
+           stub::last.seq.order[2] == 2);
+    EXPECT(stub::last.p.G == 4 && stub::last.p.n_t == (4 * 8 + 3) / 4);
+    EXPECT(stub::last.p.xcd == 1);  // B*H_kv = 24 is a multiple of 8
+    EXPECT(stub::last.p.n_split == 1 && stub::last.p.rows_total == 3LL * 32 * 256);
+    EXPECT(ca_chunk_attention(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE, 200,
+                              prior, chunk, 3, 32, 8, 256, 8448, 64, 64, 0.125f, CA_F32, FAKE,
+                              nullptr, 0) == CA_OK);
+    EXPECT(strcmp(stub::last.what, "attn_f32") == 0 && stub::last.D == 64);
+    // errors: chunk > C_max, unaligned prior, lse misaligned
+    const int32_t bad_chunk[3] = {256, 512, 64};
+    EXPECT(ca_chunk_attention(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE, 200,
+                              prior, bad_chunk, 3, 32, 8, 256, 8448, 128, 64, 0.125f, CA_BF16, FAKE,
+                              nullptr, 0) == CA_ERR_SHAPE);
+    const int32_t bad_prior[3] = {1000, 8192, 0};
+    EXPECT(ca_chunk_attention(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE, 200,
+                              bad_prior, chunk, 3, 32, 8, 256, 8448, 128, 64, 0.125f, CA_BF16,
+                              FAKE, nullptr, 0) == CA_ERR_UNSUPPORTED);
+    EXPECT(ca_chunk_attention(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE, 200,
+                              prior, chunk, 3, 32, 8, 256, 8448, 128, 64, 0.125f, CA_BF16, FAKE,
+                              (float*)((char*)FAKE + 2), 0) == CA_ERR_UNSUPPORTED);
+    // split: workspace layout and size check
+    const size_t need = ca_chunk_attention_workspace_size(3, 32, 256, 128, 4);
+    EXPECT(need == 4ull * 3 * 32 * 256 * 130 * 4);
+    EXPECT(ca_chunk_attention_split(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE,
+                                    200, prior, chunk, 3, 32, 8, 256, 8448, 128, 64, 0.125f,
+                                    CA_BF16, 4, FAKE, need, FAKE, nullptr, 0) == CA_OK);
+    EXPECT(strcmp(stub::last.what, "attn_bf16_split") == 0 && stub::last.p.n_split == 4);
+    EXPECT((char*)stub::last.ptrs[1] - (char*)stub::last.ptrs[0] ==
+           (ptrdiff_t)(4LL * 3 * 32 * 256 * 128 * 4));
+    EXPECT(ca_chunk_attention_split(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE,
+                                    200, prior, chunk, 3, 32, 8, 256, 8448, 128, 64, 0.125f,
+                                    CA_BF16, 4, FAKE, need - 1, FAKE, nullptr, 0) == CA_ERR_SHAPE);
+    // per-(head, Q-block) lists
+    EXPECT(ca_chunk_attention_rows(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE,
+                                   4, 200, prior, chunk, 3, 32, 8, 256, 8448, 128, 64, 0.125f,
+                                   CA_BF16, FAKE, nullptr, 0) == CA_OK);
+    EXPECT(strcmp(stub::last.what, "attn_bf16_rows") == 0 && stub::last.p.NQ_max == 4 &&
+           stub::last.p.n_t == 4 * 4);
+  }
+  // ---- a full batch of sequences through attention
+  {
+    std::vector<int32_t> prior(CA_MAX_BATCH), chunk(CA_MAX_BATCH);
+    for (int b = 0; b < CA_MAX_BATCH; ++b) {
+      prior[b] = 64 * (b % 7);
+      chunk[b] = 64 * (1 + b % 3);
+    }
+    EXPECT(ca_chunk_attention(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE, 16,
+                              prior.data(), chunk.data(), CA_MAX_BATCH, 8, 8, 192, 1024, 128, 64,
+                              0.125f, CA_BF16, FAKE, nullptr, 0) == CA_OK);
+    // the order is a permutation with non-increasing work
+    std::vector<int> seen(CA_MAX_BATCH, 0);
+    long long prev = -1;
+    for (int r = 0; r < CA_MAX_BATCH; ++r) {
+      const int b = stub::last.seq.order[r];
+      EXPECT(b >= 0 && b < CA_MAX_BATCH);
+      if (b < 0 || b >= CA_MAX_BATCH) break;
+      seen[b]++;
+      const long long w = (long long)(prior[b] + chunk[b]) * chunk[b];
+      EXPECT(prev < 0 || w <= prev);
+      prev = w;
+    }
+    for (int b = 0; b < CA_MAX_BATCH; ++b) EXPECT(seen[b] == 1);
+  }
+  // ---- compaction, pooling, mask producer, CSR
+  {
+    const int32_t prior[2] = {1024, 64}, chunk[2] = {128, 64};
+    EXPECT(ca_compact_kv(FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE, 20, prior, chunk,
+                         2, 8, 1280, 128, CA_BF16, FAKE, FAKE, (int32_t*)FAKE, 0) == CA_OK);
+    EXPECT(strcmp(stub::last.what, "compact") == 0 && stub::last.ints[3] == 2);
+    const int32_t lo[2] = {0, 3}, hi[2] = {16, 5};
+    EXPECT(ca_pool_blocks(FAKE, CA_F32, 2, 8, 1280, 64, lo, hi, (float*)FAKE, 20, 0) == CA_OK);
+    EXPECT(strcmp(stub::last.what, "pool") == 0 && stub::last.ints[3] == 16 &&
+           stub::last.ints[5] == 2);
+    const int32_t hi_bad[2] = {16, 21};
+    EXPECT(ca_pool_blocks(FAKE, CA_F32, 2, 8, 1280, 64, lo, hi_bad, (float*)FAKE, 20, 0) ==
+           CA_ERR_SHAPE);
+    EXPECT(ca_block_mask_topk((const float*)FAKE, (const float*)FAKE, 2, 32, 8, 2, 20, 128, prior,
+                              chunk, 8, 2, (float*)FAKE, (uint8_t*)FAKE, 0) == CA_OK);
+    EXPECT(strcmp(stub::last.what, "mask") == 0 && stub::last.ints[4] == 16);
+    EXPECT(ca_block_mask_topk((const float*)FAKE, (const float*)FAKE, 2, 32, 8, 2, 20, 128, prior,
+                              chunk, -1, 2, (float*)FAKE, (uint8_t*)FAKE, 0) == CA_ERR_SHAPE);
+    EXPECT(ca_tables_to_csr((const int32_t*)FAKE, (const int32_t*)FAKE, 2, 8, 16, 1024,
+                            (int32_t*)FAKE, (int32_t*)FAKE, 0) == CA_OK);
+    EXPECT(strcmp(stub::last.what, "csr") == 0 && stub::last.ints[0] == 16 &&
+           stub::last.ints[2] == 16);
+  }
+  // ---- status strings for every code and one past the end
+  for (int s = 0; s <= 6; ++s) EXPECT(ca_status_string((ca_status)s) != nullptr);
+  EXPECT(ca_last_hip_error() != nullptr);
+
+  if (failures) {
+    fprintf(stderr, "host check: %d expectation(s) failed\n", failures);
+    return 1;
+  }
+  printf("host check OK\n");
+  return 0;
+}

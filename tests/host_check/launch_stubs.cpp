@@ -1,0 +1,119 @@
+// Host-only stand-ins for the kernel launchers, so that the C ABI's host code
+// (validation, scheduling metadata, dispatch) can run under AddressSanitizer
+// and UndefinedBehaviorSanitizer without a GPU.  Each stub records what it
+// was asked to launch and returns hipSuccess.
+#include "stubs.hpp"
+
+namespace stub {
+Record last;
+}
+
+namespace ca {
+
+hipError_t launch_union_tables(const uint8_t*, int B, int H_q, int H_kv, int NQ_max, int NKB_max,
+                               const UnionExtents& ext, int32_t*, int32_t*, hipStream_t) {
+  stub::last = stub::Record{};
+  stub::last.what = "union";
+  stub::last.B = B;
+  stub::last.ints[0] = H_q;
+  stub::last.ints[1] = H_kv;
+  stub::last.ints[2] = NQ_max;
+  stub::last.ints[3] = NKB_max;
+  stub::last.ints[4] = ext.nq[B - 1];
+  stub::last.ints[5] = ext.nkb[B - 1];
+  return hipSuccess;
+}
+
+hipError_t launch_tables_to_csr(const int32_t*, const int32_t*, int n_bg, int NKB_max,
+                                int64_t pages, int32_t*, int32_t*, hipStream_t) {
+  stub::last = stub::Record{};
+  stub::last.what = "csr";
+  stub::last.ints[0] = n_bg;
+  stub::last.ints[1] = NKB_max;
+  stub::last.ints[2] = static_cast<int>(pages);
+  return hipSuccess;
+}
+
+static void record_attn(const char* what, int B, int D, const AttnParams& p, const SeqInfo& seq) {
+  stub::last = stub::Record{};
+  stub::last.what = what;
+  stub::last.B = B;
+  stub::last.D = D;
+  stub::last.p = p;
+  stub::last.seq = seq;
+}
+
+hipError_t launch_chunk_attn_bf16(const void*, const void*, const void*, const int32_t*,
+                                  const int32_t*, void*, float*, int B, int D,
+                                  const AttnParams& p, const SeqInfo& seq, hipStream_t) {
+  record_attn(p.row_tables ? "attn_bf16_rows" : "attn_bf16", B, D, p, seq);
+  return hipSuccess;
+}
+
+hipError_t launch_chunk_attn_bf16_split(const void*, const void*, const void*, const int32_t*,
+                                        const int32_t*, void*, float*, int B, int D,
+                                        const AttnParams& p, const SeqInfo& seq, float* part_o,
+                                        float* part_ml, hipStream_t) {
+  record_attn("attn_bf16_split", B, D, p, seq);
+  stub::last.ptrs[0] = part_o;
+  stub::last.ptrs[1] = part_ml;
+  return hipSuccess;
+}
+
+hipError_t launch_chunk_attn_f32(const float*, const float*, const float*, const int32_t*,
+                                 const int32_t*, float*, float*, int B, int D,
+                                 const AttnParams& p, const SeqInfo& seq, hipStream_t) {
+  record_attn(p.row_tables ? "attn_f32_rows" : "attn_f32", B, D, p, seq);
+  return hipSuccess;
+}
+
+hipError_t launch_compact_kv(const void*, const void*, const int32_t*, const int32_t*, int NKB_max,
+                             int B, int H_kv, int64_t L, int D, int esz, const SeqInfo& seq,
+                             void*, void*, int32_t*, hipStream_t) {
+  stub::last = stub::Record{};
+  stub::last.what = "compact";
+  stub::last.B = B;
+  stub::last.D = D;
+  stub::last.ints[0] = NKB_max;
+  stub::last.ints[1] = H_kv;
+  stub::last.ints[2] = static_cast<int>(L);
+  stub::last.ints[3] = esz;
+  stub::last.seq = seq;
+  return hipSuccess;
+}
+
+hipError_t launch_pool_blocks(const void*, int esz, int B, int H, int64_t R, int D,
+                              const BlockRange& rng, int max_span, float*, int NB_out,
+                              hipStream_t) {
+  stub::last = stub::Record{};
+  stub::last.what = "pool";
+  stub::last.B = B;
+  stub::last.D = D;
+  stub::last.ints[0] = esz;
+  stub::last.ints[1] = H;
+  stub::last.ints[2] = static_cast<int>(R);
+  stub::last.ints[3] = max_span;
+  stub::last.ints[4] = NB_out;
+  stub::last.ints[5] = rng.end[B - 1] - rng.begin[B - 1];
+  return hipSuccess;
+}
+
+hipError_t launch_block_mask(const float*, const float*, int B, int H_q, int H_kv, int NQ_max,
+                             int NKB_max, int D, const SeqInfo& seq, int max_pblk, int budget,
+                             int local, float*, uint8_t*, hipStream_t) {
+  stub::last = stub::Record{};
+  stub::last.what = "mask";
+  stub::last.B = B;
+  stub::last.D = D;
+  stub::last.ints[0] = H_q;
+  stub::last.ints[1] = H_kv;
+  stub::last.ints[2] = NQ_max;
+  stub::last.ints[3] = NKB_max;
+  stub::last.ints[4] = max_pblk;
+  stub::last.ints[5] = budget;
+  stub::last.ints[6] = local;
+  stub::last.seq = seq;
+  return hipSuccess;
+}
+
+}  // namespace ca
