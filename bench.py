@@ -536,7 +536,7 @@ def main():
     achieved = main_r["flops"] / (main_r["attn_ms_mean"] * 1e-3) / 1e12
     roofline = {
         "bound": "mfma",
-        "kernel": "chunk_attn_bf16_kernel<128, 4, false, false>",
+        "kernel": "chunk_attn_bf16_kernel<128, 8, false, false>",
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",

@@ -25,6 +25,7 @@ ca_status hip_status(hipError_t e) {
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 constexpr int kMaxUnionBlocks = 1 << 19;  // NKB_max bound: bitmap fits 64 KiB of LDS
+constexpr int64_t kCUs = 256;             // compute units of an MI355X
 
 }  // namespace
 
@@ -129,6 +130,7 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
   p.NKB_max = NKB_max;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.waves = 4;
   p.row_tables = row_tables ? 1 : 0;
   p.NQ_max = row_tables ? NQ_max : 0;
   p.n_split = n_split;
@@ -139,10 +141,13 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
     // resource with 32-bit byte offsets
     if (L * D * 2 > static_cast<int64_t>(UINT32_MAX)) return CA_ERR_UNSUPPORTED;
     const int64_t n_pb = (C_max + 31) / 32;
-    // workgroups per (b, g): 4 waves of 32 rows over the group's heads, or one
-    // 64-row Q-block of one head per workgroup with per-Q-block tables
+    // workgroups per (b, g): 8 waves of 32 rows over the group's heads while
+    // that still gives every CU a workgroup, else 4 (and 4 with split-KV); or
+    // one 64-row Q-block of one head with per-Q-block tables
+    const int64_t n_t8 = (p.G * n_pb + 7) / 8;
+    p.waves = (n_split == 1 && n_bg * n_t8 >= kCUs) ? 8 : 4;
     p.n_t = row_tables ? static_cast<int>(p.G * ((C_max + 63) / 64))
-                       : static_cast<int>((p.G * n_pb + 3) / 4);
+                       : static_cast<int>((p.G * n_pb + p.waves - 1) / p.waves);
     p.xcd = (n_bg % 8 == 0) ? 1 : 0;
     if (n_bg * p.n_t * n_split > INT32_MAX) return CA_ERR_SHAPE;
     if (n_split > 1) {

@@ -41,6 +41,7 @@ struct AttnParams {
   int xcd;              // 1: keep each pseudo-request's workgroups on one XCD
   int row_tables;       // 0: T[b,g] (union); 1: T[b,h,Q-block] (per-Q-block lists)
   int NQ_max;           // Q-blocks per head in the per-Q-block table layout
+  int waves;            // bf16 union tables: waves per workgroup (4 or 8)
   int n_split;          // split-KV: table ranges per (b, g) (1: no split)
   int64_t rows_total;   // B * H_q * C_max (split-KV partial layout)
 };

@@ -49,7 +49,8 @@ int main() {
     // dense work (P+C)*C: 327680, 1064960, 4096 -> order 1, 0, 2
     EXPECT(stub::last.seq.order[0] == 1 && stub::last.seq.order[1] == 0 &&
            stub::last.seq.order[2] == 2);
-    EXPECT(stub::last.p.G == 4 && stub::last.p.n_t == (4 * 8 + 3) / 4);
+    // 24 (b, g) pairs x 4 workgroups of 8 waves = 96 < 256 CUs: 4-wave workgroups
+    EXPECT(stub::last.p.G == 4 && stub::last.p.waves == 4 && stub::last.p.n_t == (4 * 8 + 3) / 4);
     EXPECT(stub::last.p.xcd == 1);  // B*H_kv = 24 is a multiple of 8
     EXPECT(stub::last.p.n_split == 1 && stub::last.p.rows_total == 3LL * 32 * 256);
     EXPECT(ca_chunk_attention(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE, 200,
@@ -68,6 +69,12 @@ int main() {
     EXPECT(ca_chunk_attention(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE, 200,
                               prior, chunk, 3, 32, 8, 256, 8448, 128, 64, 0.125f, CA_BF16, FAKE,
                               (float*)((char*)FAKE + 2), 0) == CA_ERR_UNSUPPORTED);
+    // the 128K shape: 8 (b, g) pairs x 32 workgroups of 8 waves cover the 256 CUs
+    const int32_t p1[1] = {129024}, c1[1] = {2048};
+    EXPECT(ca_chunk_attention(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE, 2048,
+                              p1, c1, 1, 32, 8, 2048, 131072, 128, 64, 0.088f, CA_BF16, FAKE,
+                              nullptr, 0) == CA_OK);
+    EXPECT(stub::last.p.waves == 8 && stub::last.p.n_t == 32 && stub::last.p.xcd == 1);
     // split: workspace layout and size check
     const size_t need = ca_chunk_attention_workspace_size(3, 32, 256, 128, 4);
     EXPECT(need == 4ull * 3 * 32 * 256 * 130 * 4);
@@ -75,6 +82,7 @@ int main() {
                                     200, prior, chunk, 3, 32, 8, 256, 8448, 128, 64, 0.125f,
                                     CA_BF16, 4, FAKE, need, FAKE, nullptr, 0) == CA_OK);
     EXPECT(strcmp(stub::last.what, "attn_bf16_split") == 0 && stub::last.p.n_split == 4);
+    EXPECT(stub::last.p.n_t == (4 * 8 + 3) / 4);  // split-KV keeps 4-wave workgroups
     EXPECT((char*)stub::last.ptrs[1] - (char*)stub::last.ptrs[0] ==
            (ptrdiff_t)(4LL * 3 * 32 * 256 * 128 * 4));
     EXPECT(ca_chunk_attention_split(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE,
