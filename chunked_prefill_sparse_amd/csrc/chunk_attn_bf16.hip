@@ -27,9 +27,11 @@
 //
 // Data movement
 //   * Each listed block's K and V (16 KiB each at D = 128) go from HBM/L2
-//     straight into LDS with global_load_lds_dwordx4 (no VGPR staging).  The
-//     copy of block j+1 is issued before block j is computed and is waited
-//     for only at the end of the iteration, into the other of two LDS buffers.
+//     straight into LDS with buffer_load_dwordx4 ... lds through a raw buffer
+//     resource over the (b, g) cache slice (no VGPR staging).  K tiles are
+//     copied two blocks ahead of use and V tiles one block ahead, each into
+//     the free one of two LDS buffers; a step waits for its copies only at
+//     its end.
 //   * Both tiles are stored row-major with the 16-byte chunks of each row
 //     permuted (XOR swizzle by key); the permutation is applied by choosing
 //     each lane's source address, since the DMA writes lanes contiguously.
