@@ -28,9 +28,11 @@ scale the HBM byte counters).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
+import re
 import statistics
 import sys
 import time
@@ -321,10 +323,26 @@ def prefill_leg(stream, budget=32, local=8):
 # --------------------------------------------------------------------------- main
 
 
+_C_TOKEN = re.compile(r'"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|//[^\n]*|/\*.*?\*/|\s+', re.S)
+
+
+def code_hash(path):
+    """First 16 hex digits of the SHA-256 of a C++/HIP source with its comments
+    dropped and every run of white space folded to one blank, so that an edit
+    to comments alone leaves it unchanged while any change to the code moves it."""
+    def tok(m):
+        t = m.group(0)
+        if t.startswith("//") or t.startswith("/*") or t.isspace():
+            return " "
+        return t
+    text = _C_TOKEN.sub(tok, open(path, encoding="utf-8").read())
+    text = re.sub(r" +", " ", text).strip()
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
+
+
 def stored_traffic():
     """HBM bytes per attention launch from the committed rocprofv3 counter summary,
-    or None if absent or taken on a different kernel source."""
-    import hashlib
+    or None if absent or taken on different kernel code."""
     if not os.path.exists(PMC_SUMMARY):
         return None, None
     vals = {}
@@ -332,10 +350,8 @@ def stored_traffic():
         if ":" in line and not line.startswith("#"):
             k_, _, v_ = line.partition(":")
             vals[k_.strip()] = v_.strip()
-    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
-    hdr_hash = hashlib.sha256(open(KERNEL_HDR, "rb").read()).hexdigest()[:16]
-    if vals.get("kernel_source_sha256_16") != src_hash or \
-            vals.get("helpers_source_sha256_16") != hdr_hash:
+    if vals.get("kernel_code_sha256_16") != code_hash(KERNEL_SRC) or \
+            vals.get("helpers_code_sha256_16") != code_hash(KERNEL_HDR):
         return None, vals
     try:
         return float(vals["hbm_bytes_per_launch"]), vals
