@@ -130,28 +130,26 @@ __device__ __forceinline__ void update_max(float mx, WaveState<D>& ws, float c, 
 }
 
 // Probabilities against the running max, rounded to bf16 as the B operands of
-// O^T += V^T P^T (in (kt, u) order (0,0) (0,1) (1,0) (1,1)), and the
-// denominator, which sums the same rounded values (v_dot2c_f32_bf16 against
-// ones).  Branch-free.
+// O^T += V^T P^T (in (kt, u) order (0,0) (0,1) (1,0) (1,1)), and this lane's
+// share of the denominator, summed in fp32 before the rounding (plain adds:
+// v_dot2c_f32_bf16 on the rounded pairs does not issue alongside the matrix
+// instructions, adds do).  Branch-free.
 template <int D>
 __device__ __forceinline__ void softmax_probs(const f32x16& s0, const f32x16& s1,
                                               WaveState<D>& ws, bf16x8* pf, float c) {
   const float msub = (ws.m_used == -INFINITY) ? 0.f : ws.m_used * c;
-  const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
   float lsum = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; r += 2) {
-    bf16x2 a, b;
-    a[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c, -msub)));
-    a[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r + 1], c, -msub)));
-    b[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c, -msub)));
-    b[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r + 1], c, -msub)));
-    lsum = __builtin_amdgcn_fdot2_f32_bf16(a, ones, lsum, false);
-    lsum = __builtin_amdgcn_fdot2_f32_bf16(b, ones, lsum, false);
-    pf[r >> 3][r & 7] = a[0];
-    pf[r >> 3][(r & 7) + 1] = a[1];
-    pf[2 + (r >> 3)][r & 7] = b[0];
-    pf[2 + (r >> 3)][(r & 7) + 1] = b[1];
+    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c, -msub));
+    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r + 1], c, -msub));
+    const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c, -msub));
+    const float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r + 1], c, -msub));
+    lsum += e0 + e1 + e2 + e3;
+    pf[r >> 3][r & 7] = static_cast<__bf16>(e0);
+    pf[r >> 3][(r & 7) + 1] = static_cast<__bf16>(e1);
+    pf[2 + (r >> 3)][r & 7] = static_cast<__bf16>(e2);
+    pf[2 + (r >> 3)][(r & 7) + 1] = static_cast<__bf16>(e3);
   }
   ws.l_part += lsum;
 }

@@ -47,8 +47,8 @@
 //   only when some lane's block max exceeds it by more than 8 (log2 units),
 //   otherwise the stale max is kept (exact: numerator and denominator share
 //   it, and every exponent stays <= 2^8).  The probabilities are rounded to
-//   bf16 once; the same rounded values feed P.V and the denominator (summed
-//   with v_dot2c_f32_bf16).  The score accumulator registers serve directly as
+//   bf16 once for P.V; the denominator sums them in fp32 before rounding.
+//   The score accumulator registers serve directly as
 //   the B operand of O^T += V^T P^T: the MFMA contraction index is mapped to
 //   keys in the order the accumulator holds them, and the V operand is read
 //   in that same key order.
@@ -59,12 +59,14 @@ namespace ca {
 namespace {
 
 // Instruction interleaving for one pipeline body (scheduling hints only): after
-// the tile copies are issued, S(j1) and P.V(j-1) matrix instructions
-// alternate, each followed by LDS reads for the ones ahead and a share of the
-// vector work.  Groups that cannot be filled are skipped by the scheduler.
-// (Measured on MI355X: interleaving the softmax exponentials between the
-// matrix instructions of the same wave was slower than leaving them after the
-// matrix phase, where the other wave on the SIMD overlaps them.)
+// the tile copies are issued, the matrix instructions of S(j1) and then of
+// P.V(j-1) each come with LDS reads for the ones ahead and three vector
+// instructions of the softmax of block j, which a wave issues while its own
+// matrix instruction runs.  Groups that cannot be filled are skipped by the
+// scheduler.  (Measured on MI355X: a vector instruction of one wave issued
+// while another wave's matrix instruction runs overlaps far less than one of
+// the same wave, so the softmax belongs inside each wave's matrix phase; three
+// per matrix instruction measured best of 2, 3 and 4.)
 template <int D, int W>
 __device__ __forceinline__ void body_schedule() {
   constexpr int DS = D / 16;  // S matrix instructions per key tile
@@ -320,6 +322,12 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
     softmax_probs<D>(cur0, cur1, ws, pcur, c);
     const float mx = row_max(nxt0, nxt1, xhalf);
     body_schedule<D, W>();
+    // Keep P(j) and its denominator in the body: without this the compiler
+    // sinks the softmax past the barrier below, out of reach of the matrix
+    // instructions it is meant to overlap (measured 4% slower at 128K).
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pcur[i]));
+    asm volatile("" : "+v"(ws.l_part));
     const bool last = j1 >= ee;
     const bool moves = !last && __any(mx > ws.m_used + thr);
     const int j3 = next_plain(j2 + 1);
