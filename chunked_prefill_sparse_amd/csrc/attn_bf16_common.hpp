@@ -47,13 +47,14 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // buffer resource over the (b, g) cache slice: per-lane 32-bit offsets, the
 // block offset in an SGPR, and hardware bounds checking (a block offset at or
 // past the slice end reads zeros and touches no memory).  The LDS destination
-// of each wave copy is uniform (M0).
+// of each wave copy is uniform (M0).  Wave copies i0 .. i1-1 of the tile (all
+// by default), so that callers can spread a tile's copies over a step.
 template <int D, int W>
 __device__ __forceinline__ void dma_tile(char* lds_tile, __amdgpu_buffer_rsrc_t rsrc,
                                          uint32_t block_off, const uint32_t* __restrict__ off,
-                                         int wave_u) {
+                                         int wave_u, int i0 = 0, int i1 = kDmaPerWave<D, W>) {
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave<D, W>; ++i) {
+  for (int i = i0; i < i1; ++i) {
     char* dst = lds_tile + (i * W + wave_u) * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, off[i], block_off, 0, 0);
   }
@@ -66,17 +67,20 @@ struct WaveState {
   float l_part;
 };
 
-// S^T = K Q^T for the 64 keys of one K tile: s0 = keys 0..31, s1 = keys 32..63.
+// S^T = K Q^T for the 64 keys of one K tile: s0 = keys 0..31, s1 = keys 32..63,
+// over the 16-wide d slices s_begin .. s_end-1 (all by default; the scores
+// start from zero at s_begin = 0 and accumulate otherwise).
 template <int D>
 __device__ __forceinline__ void scores(const char* __restrict__ Ks, const bf16x8* qf,
                                        const int* __restrict__ k_lane_off, f32x16& s0,
-                                       f32x16& s1) {
-  constexpr int DS = D / 16;
+                                       f32x16& s1, int s_begin = 0, int s_end = D / 16) {
   constexpr int RB = Tile<D>::kRowBytes;
-  s0 = f32x16{};
-  s1 = f32x16{};
+  if (s_begin == 0) {
+    s0 = f32x16{};
+    s1 = f32x16{};
+  }
 #pragma unroll
-  for (int s = 0; s < DS; ++s) {
+  for (int s = s_begin; s < s_end; ++s) {
     const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(Ks + k_lane_off[s]);
     const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(Ks + k_lane_off[s] + 32 * RB);
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], s0, 0, 0, 0);
@@ -154,16 +158,17 @@ __device__ __forceinline__ void softmax_probs(const f32x16& s0, const f32x16& s1
   ws.l_part += lsum;
 }
 
-// O^T += V^T P^T for one V tile; the V operand of (dt, kt, u) is two
-// transposing reads (keys +0..3 and +8..11 of the 16-key slice).
+// O^T += V^T P^T for one V tile, over the 16-key slices q_begin .. q_end-1
+// (all four by default); the V operand of (dt, kt, u) is two transposing
+// reads (keys +0..3 and +8..11 of the 16-key slice).
 template <int D>
 __device__ __forceinline__ void accumulate_pv(const char* __restrict__ Vs, const bf16x8* pf,
                                               const int* __restrict__ v_lane_off,
-                                              WaveState<D>& ws) {
+                                              WaveState<D>& ws, int q_begin = 0, int q_end = 4) {
   constexpr int DT = D / 32;
   constexpr int RB = Tile<D>::kRowBytes;
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {  // q4 = 2*kt + u: keys 16*q4 + ...
+  for (int q4 = q_begin; q4 < q_end; ++q4) {  // q4 = 2*kt + u: keys 16*q4 + ...
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const char* p0 = Vs + v_lane_off[dt] + (16 * q4) * RB;

@@ -53,34 +53,54 @@
 //   keys in the order the accumulator holds them, and the V operand is read
 //   in that same key order.
 
+#include <utility>
+
 #include "attn_bf16_common.hpp"
 
 namespace ca {
 namespace {
 
-// Instruction interleaving for one pipeline body (scheduling hints only): after
-// the tile copies are issued, the matrix instructions of S(j1) and then of
-// P.V(j-1) each come with LDS reads for the ones ahead and three vector
-// instructions of the softmax of block j, which a wave issues while its own
-// matrix instruction runs.  Groups that cannot be filled are skipped by the
-// scheduler.  (Measured on MI355X: a vector instruction of one wave issued
-// while another wave's matrix instruction runs overlaps far less than one of
-// the same wave, so the softmax belongs inside each wave's matrix phase; three
-// per matrix instruction measured best of 2, 3 and 4.)
+// Instruction interleaving for one pipeline body (scheduling hints only): the
+// matrix instructions of S(j1) and then of P.V(j-1) each come with LDS reads
+// for the ones ahead and three vector instructions of the softmax of block j,
+// which a wave issues while its own matrix instruction runs.  The tile copies
+// open the body when a workgroup has two waves; with four or eight, a quarter
+// of them opens each quarter of the body, as the step issues them.  Groups
+// that cannot be filled are skipped by the scheduler.  (Measured on MI355X: a
+// vector instruction of one wave issued while another wave's matrix
+// instruction runs overlaps far less than one of the same wave, so the
+// softmax belongs inside each wave's matrix phase; three per matrix
+// instruction measured best of 2, 3 and 4.)
+template <int D, int W, int I>
+__device__ __forceinline__ void body_pair() {
+  constexpr int DS = D / 16;  // S matrix instructions per key tile
+  constexpr int N = kDmaPerWave<D, W>;
+  // tile copies after matrix instruction pair I, a quarter of the body apart
+  constexpr int qc = W == 2 ? 0
+                     : (I == DS / 2 - 1 || I == 3 * DS / 2 - 1) ? N - N / 2
+                     : (I == DS - 1)                             ? N / 2
+                                                                 : 0;
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+  if constexpr (qc > 0) __builtin_amdgcn_sched_group_barrier(0x020, qc, 0);  // tile copies
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+  __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+  __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+}
+
+template <int D, int W, int... I>
+__device__ __forceinline__ void body_pairs(std::integer_sequence<int, I...>) {
+  (body_pair<D, W, I>(), ...);
+}
+
 template <int D, int W>
 __device__ __forceinline__ void body_schedule() {
-  constexpr int DS = D / 16;  // S matrix instructions per key tile
-  __builtin_amdgcn_sched_group_barrier(0x020, 2 * kDmaPerWave<D, W>, 0);  // tile copies
-  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);                         // first reads
-#pragma unroll
-  for (int i = 0; i < 2 * DS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
-    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-  }
+  constexpr int N = kDmaPerWave<D, W>;
+  constexpr int q0 = W == 2 ? 2 * N : N / 2;  // copies ahead of the first reads
+  if constexpr (q0 > 0) __builtin_amdgcn_sched_group_barrier(0x020, q0, 0);  // tile copies
+  __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);                          // first reads
+  body_pairs<D, W>(std::make_integer_sequence<int, D / 8>{});
 }
 
 // W = waves per workgroup.  kRows = false: union tables, T[b,g] shared by the
@@ -104,6 +124,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   constexpr int RB = Tile<D>::kRowBytes;
   constexpr int CH = Tile<D>::kChunks;
   constexpr int NDMA = kDmaPerWave<D, W>;
+  constexpr bool kSpread = W >= 4;  // tile copies spread over the step body
   constexpr int kThreads = W * 64;
   static_assert(kRows ? W == 2 : (W == 4 || W == 8), "workgroup shape");
   static_assert(!(kRows && kSplit), "split ranges are for union tables");
@@ -315,10 +336,27 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   auto step = [&](const f32x16& cur0, const f32x16& cur1, f32x16& nxt0, f32x16& nxt1,
                   const bf16x8* pprev, bf16x8* pcur, char* Kin, char* Vin, char* Kfree,
                   char* Vfree) {
-    dma_tile<D, W>(Kfree, krsrc, boff(j2, kb2), offk, wave_u);
-    dma_tile<D, W>(Vfree, vrsrc, boff(j, kb0), offv, wave_u);
-    scores<D>(Kin, qf, k_lane_off, nxt0, nxt1);  // stale when j1 is past the end: unused
-    accumulate_pv<D>(Vin, pprev, v_lane_off, ws);
+    // S(j1) is stale when j1 is past the end: then it is unused
+    if (kSpread) {
+      // a quarter of the tile copies before each quarter of the matrix work,
+      // rather than all of them at once: the copies of all waves entering
+      // the memory pipeline together held up the start of their matrix work
+      // (measured 2% faster at 128K, 12% on one GPU's tensor-parallel share)
+      const uint32_t bk = boff(j2, kb2), bv = boff(j, kb0);
+      dma_tile<D, W>(Kfree, krsrc, bk, offk, wave_u, 0, NDMA / 2);
+      scores<D>(Kin, qf, k_lane_off, nxt0, nxt1, 0, DS / 2);
+      dma_tile<D, W>(Kfree, krsrc, bk, offk, wave_u, NDMA / 2, NDMA);
+      scores<D>(Kin, qf, k_lane_off, nxt0, nxt1, DS / 2, DS);
+      dma_tile<D, W>(Vfree, vrsrc, bv, offv, wave_u, 0, NDMA / 2);
+      accumulate_pv<D>(Vin, pprev, v_lane_off, ws, 0, 2);
+      dma_tile<D, W>(Vfree, vrsrc, bv, offv, wave_u, NDMA / 2, NDMA);
+      accumulate_pv<D>(Vin, pprev, v_lane_off, ws, 2, 4);
+    } else {
+      dma_tile<D, W>(Kfree, krsrc, boff(j2, kb2), offk, wave_u);
+      dma_tile<D, W>(Vfree, vrsrc, boff(j, kb0), offv, wave_u);
+      scores<D>(Kin, qf, k_lane_off, nxt0, nxt1);
+      accumulate_pv<D>(Vin, pprev, v_lane_off, ws);
+    }
     softmax_probs<D>(cur0, cur1, ws, pcur, c);
     const float mx = row_max(nxt0, nxt1, xhalf);
     body_schedule<D, W>();
