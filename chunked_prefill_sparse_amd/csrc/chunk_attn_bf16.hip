@@ -128,8 +128,14 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   constexpr int kThreads = W * 64;
   static_assert(kRows ? W == 2 : (W == 4 || W == 8), "workgroup shape");
   static_assert(!(kRows && kSplit), "split ranges are for union tables");
-  // LDS: two K tiles, then two V tiles
-  __shared__ __attribute__((aligned(1024))) char lds[4 * Tile<D>::kBytes];
+  // LDS: two K tiles, two V tiles, then the compacted entry list (below) and
+  // per-wave counts for building it.  One array: with the list in a separate
+  // LDS object the compiler no longer proves that the tile reads stay clear of
+  // the in-flight tile copies and waits for those copies before every read.
+  constexpr int kListCap = 4096;
+  __shared__ __attribute__((aligned(1024))) char lds[4 * Tile<D>::kBytes + 2 * kListCap + 4 * W];
+  uint16_t* const plist = reinterpret_cast<uint16_t*>(lds + 4 * Tile<D>::kBytes);
+  int* const wcount = reinterpret_cast<int*>(lds + 4 * Tile<D>::kBytes + 2 * kListCap);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -283,10 +289,44 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
     if (valid(kb) && !needs_mask(kb)) break;
     --e;
   }
-  // this workgroup's range of [0, e); all of it without splitting
-  const int e_lo = kSplit ? static_cast<int>((static_cast<int64_t>(e) * split) / p.n_split) : 0;
-  const int ee = kSplit ? static_cast<int>((static_cast<int64_t>(e) * (split + 1)) / p.n_split) : e;
+  // The plain entries of [0, e) (valid, no mask needed), compacted into LDS
+  // in table order when they fit (block indices below 2^16, at most kListCap
+  // of them), so that a step reads the entry after next from LDS, in order
+  // with its other LDS reads, rather than by a scalar load it must wait for
+  // in its tail (measured 0.8% faster at 128K, 5% on one GPU's
+  // tensor-parallel share).  Longer tables walk T itself.
+  const bool use_list = e <= kListCap && nkb <= 65536;
+  int n_plain = 0;
+  if (use_list) {
+    for (int c0 = 0; c0 < e; c0 += kThreads) {
+      const int pos = c0 + tid;
+      const int kb = pos < e ? Trow[pos] : -1;
+      const bool pl = pos < e && valid(kb) && !needs_mask(kb);
+      const uint64_t m = __ballot(pl);
+      if (lane == 0) wcount[wave] = __popcll(m);
+      __syncthreads();
+      int before = n_plain, total = n_plain;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const int cw = wcount[w];
+        before += w < wave ? cw : 0;
+        total += cw;
+      }
+      if (pl) plist[before + __popcll(m & ((1ull << lane) - 1ull))] = static_cast<uint16_t>(kb);
+      n_plain = total;
+      __syncthreads();
+    }
+  }
+  const int n_all = use_list ? n_plain : e;
+  // this workgroup's range of [0, n_all); all of it without splitting
+  const int e_lo = kSplit ? static_cast<int>((static_cast<int64_t>(n_all) * split) / p.n_split) : 0;
+  const int ee =
+      kSplit ? static_cast<int>((static_cast<int64_t>(n_all) * (split + 1)) / p.n_split) : n_all;
+  auto entry = [&](int jj) -> int {
+    return use_list ? __builtin_amdgcn_readfirstlane(static_cast<int>(plist[jj])) : Trow[jj];
+  };
   auto next_plain = [&](int jj) {
+    if (use_list) return jj;
     while (jj < ee) {
       const int kb = Trow[jj];
       if (valid(kb) && !needs_mask(kb)) break;
@@ -298,10 +338,10 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   int j = next_plain(e_lo);
   int j1 = next_plain(j + 1);
   int j2 = next_plain(j1 + 1);
-  const int kbj = j < ee ? Trow[j] : 0;
+  const int kbj = j < ee ? entry(j) : 0;
   int kb0 = kbj;
-  int kb1 = j1 < ee ? Trow[j1] : 0;
-  int kb2 = j2 < ee ? Trow[j2] : 0;
+  int kb1 = j1 < ee ? entry(j1) : 0;
+  int kb2 = j2 < ee ? entry(j2) : 0;
   auto boff = [&](int jj, int kb) {  // block byte offset, or past the end when jj is not used
     return jj < ee ? static_cast<uint32_t>(kb) * (kBlk * D * 2) : slice_bytes;
   };
@@ -369,7 +409,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
     const bool last = j1 >= ee;
     const bool moves = !last && __any(mx > ws.m_used + thr);
     const int j3 = next_plain(j2 + 1);
-    const int kb3 = j3 < ee ? Trow[j3] : 0;
+    const int kb3 = j3 < ee ? entry(j3) : 0;
     wait_vmem();
     __syncthreads();
     if (moves || last) {

@@ -145,9 +145,13 @@ def test_bf16_closed_form_constant_values():
     w = gen.make_custom(1, 8, 2, 128, [4096], [256], "bf16", 6, _bern(0.3))
     w.v.fill_(1.0)
     _, _, _, (O, _) = _run(w)
-    # numerator and denominator sum the same bf16-rounded probabilities, so the
-    # result is 1 up to fp32 summation order, which bf16 output rounding absorbs
-    assert np.all(to_np(O) == 1.0)
+    # the numerator sums the bf16-rounded probabilities and the denominator the
+    # unrounded ones: each rounding is within 2^-8 relative, so O is within
+    # 2^-8 of 1 (one bf16 step below 1); the roundings largely cancel, so
+    # nearly every element is exactly 1
+    Oh = to_np(O)
+    assert np.all(np.abs(Oh - 1.0) <= 2.0 ** -8)
+    assert np.mean(Oh == 1.0) >= 0.99
 
 
 # ----------------------------------------------------------------------------- full sizes
@@ -242,6 +246,30 @@ def test_full_size_poison_invariance(name, kw):
     torch.cuda.synchronize()
     assert torch.equal(O, O2)
     del kp, vp
+
+
+def test_long_table_beyond_entry_list():
+    # More plain table entries (about 4350) than the kernel's LDS entry list
+    # holds (4096): those workgroups walk T itself.  Split-KV cuts the same
+    # long table into ranges.
+    w = gen.make_custom(1, 8, 2, 128, [4352 * 64], [192], "bf16", 41, _bern(0.6))
+    say(f"long table: prior {w.prior[0]}, L {w.L}")
+    d = Dev(w)
+    T, lens = d.tables()
+    say(f"  lens {lens.tolist()}")
+    assert int(lens.min()) > 4096
+    O, lse = d.attention(T, lens, return_lse=True)
+    Os, lses = ca.chunk_attention(d.q, d.k, d.v, T, lens, w.prior, w.chunk, w.scale,
+                                  return_lse=True, n_splits=4)
+    torch.cuda.synchronize()
+    rows = sample_rows(w, seed=41)
+    Or, lr = oracle_rows(w, rows)
+    r = torch.from_numpy(rows).cuda()
+    for name, (o, l) in (("no split", (O, lse)), ("4 splits", (Os, lses))):
+        compare_bf16(to_np(o[r[:, 0], r[:, 1], r[:, 2]]), Or, f"{name}, {len(rows)} rows")
+        np.testing.assert_allclose(to_np(l[r[:, 0], r[:, 1], r[:, 2]]), lr, rtol=0,
+                                   atol=LSE_ABS)
+    assert bool(torch.isfinite(O).all()) and bool(torch.isfinite(Os).all())
 
 
 # ----------------------------------------------------------------------------- errors
