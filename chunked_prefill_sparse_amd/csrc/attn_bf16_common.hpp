@@ -100,9 +100,23 @@ __device__ __forceinline__ void mask_scores(f32x16& s0, f32x16& s1, int kb, int 
   }
 }
 
+// The two lane halves of a wave exchanged with v_permlane32_swap (a VALU
+// swap, no LDS round trip): for x in every lane, lo holds x of lane l & 31
+// and hi x of lane (l & 31) + 32, so any symmetric combination of lo and hi
+// is lane l's value combined with lane l ^ 32's.
+struct LaneHalves {
+  float lo, hi;
+};
+__device__ __forceinline__ LaneHalves lane_halves(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return {__builtin_bit_cast(float, static_cast<uint32_t>(r[0])),
+          __builtin_bit_cast(float, static_cast<uint32_t>(r[1]))};
+}
+
 // Row max of one block's scores: two chains of 3-input maxima (v_max3_f32),
-// then the other lane half (xhalf = byte address of lane ^ 32).
-__device__ __forceinline__ float row_max(const f32x16& s0, const f32x16& s1, int xhalf) {
+// then the other lane half.
+__device__ __forceinline__ float row_max(const f32x16& s0, const f32x16& s1) {
   float ma = __builtin_fmaxf(__builtin_fmaxf(s0[0], s0[1]), s0[2]);
   float mb = __builtin_fmaxf(__builtin_fmaxf(s1[0], s1[1]), s1[2]);
 #pragma unroll
@@ -111,8 +125,8 @@ __device__ __forceinline__ float row_max(const f32x16& s0, const f32x16& s1, int
     mb = __builtin_fmaxf(__builtin_fmaxf(mb, s1[r]), s1[r + 1]);
   }
   const float mx = __builtin_fmaxf(__builtin_fmaxf(ma, mb), __builtin_fmaxf(s0[15], s1[15]));
-  return __builtin_fmaxf(
-      mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xhalf, __builtin_bit_cast(int, mx))));
+  const LaneHalves h = lane_halves(mx);
+  return __builtin_fmaxf(h.lo, h.hi);
 }
 
 // Running-max update for a block whose row max is mx: the max moves only when

@@ -255,7 +255,6 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   ws.l_part = 0.f;        // this lane half's share of the softmax denominator
   const float c = p.scale_log2;
   const float thr = 8.f / c;
-  const int xhalf = (lane ^ 32) << 2;
   const int qpos = P + row;  // absolute position of this lane's query
 
   // Software pipeline over the table: K tiles run two blocks ahead of use, V
@@ -358,7 +357,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
     wait_vmem();
     __syncthreads();
     scores<D>(K0, qf, k_lane_off, sa0, sa1);
-    update_max<D>(row_max(sa0, sa1, xhalf), ws, c, thr);
+    update_max<D>(row_max(sa0, sa1), ws, c, thr);
     __syncthreads();  // every wave has read K(j) before its buffer is reused
   }
 
@@ -398,7 +397,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
       accumulate_pv<D>(Vin, pprev, v_lane_off, ws);
     }
     softmax_probs<D>(cur0, cur1, ws, pcur, c);
-    const float mx = row_max(nxt0, nxt1, xhalf);
+    const float mx = row_max(nxt0, nxt1);
     body_schedule<D, W>();
     // Keep P(j) and its denominator in the body: without this the compiler
     // sinks the softmax past the barrier below, out of reach of the matrix
@@ -443,7 +442,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
     __syncthreads();
     scores<D>(K0, qf, k_lane_off, sa0, sa1);
     mask_scores(sa0, sa1, kb, hh, qpos);
-    update_max<D>(row_max(sa0, sa1, xhalf), ws, c, thr);
+    update_max<D>(row_max(sa0, sa1), ws, c, thr);
     bf16x8 pf[4];
     softmax_probs<D>(sa0, sa1, ws, pf, c);
     accumulate_pv<D>(V0, pf, v_lane_off, ws);
@@ -451,7 +450,8 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   }
 
   // ---- epilogue: O = acc / l, rows >= C written as 0
-  const float l_tot = ws.l_part + __shfl_xor(ws.l_part, 32);
+  const LaneHalves lh = lane_halves(ws.l_part);
+  const float l_tot = lh.lo + lh.hi;
   if (!row_in) return;
   if (kSplit) {  // partial results: acc (unnormalised), running max, denominator
     if (!row_live) return;
