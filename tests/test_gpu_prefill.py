@@ -1,10 +1,10 @@
-"""GPU parity of the chunk-by-chunk driver (producer -> union -> attention)
+"""GPU parity of ChunkedPrefill, the chunk-by-chunk loop (producer -> union -> attention)
 over a whole prompt, against the float64 oracle chained the same way.
 
 Each decision step is checked bit-exact in the kernel's precision (the mask
 from the GPU's own scores, the tables from the GPU's mask); each floating-point
 step within its bound (scores; attention over the GPU's tables).  The dense
-baseline of the driver is checked on every chunk too.
+baseline of ChunkedPrefill is checked on every chunk too.
 """
 import numpy as np
 import pytest
