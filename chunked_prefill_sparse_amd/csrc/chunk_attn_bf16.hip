@@ -30,8 +30,11 @@
 //     straight into LDS with buffer_load_dwordx4 ... lds through a raw buffer
 //     resource over the (b, g) cache slice (no VGPR staging).  K tiles are
 //     copied two blocks ahead of use and V tiles one block ahead, each into
-//     the free one of two LDS buffers; a step waits for its copies only at
-//     its end.
+//     the free one of two LDS buffers; with 4 or 8 waves a step issues them a
+//     quarter at a time between its matrix instructions, and waits for them
+//     only at its end.
+//   * The table's plain entries are compacted into an LDS list at kernel
+//     start, so a step finds its next block with an LDS read.
 //   * Both tiles are stored row-major with the 16-byte chunks of each row
 //     permuted (XOR swizzle by key); the permutation is applied by choosing
 //     each lane's source address, since the DMA writes lanes contiguously.
@@ -42,16 +45,18 @@
 //
 // Per block, per wave (D = 128): 16 + 16 v_mfma_f32_32x32x16_bf16.
 //   S^T[key][q]: each lane ends with 32 scores of ONE query, so the row max
-//   needs only one cross-lane exchange (lanes l, l^32).  Online softmax in
-//   fp32 with exp2 (scale * log2 e folded into one FMA); the running max moves
-//   only when some lane's block max exceeds it by more than 8 (log2 units),
-//   otherwise the stale max is kept (exact: numerator and denominator share
-//   it, and every exponent stays <= 2^8).  The probabilities are rounded to
-//   bf16 once for P.V; the denominator sums them in fp32 before rounding.
-//   The score accumulator registers serve directly as
-//   the B operand of O^T += V^T P^T: the MFMA contraction index is mapped to
-//   keys in the order the accumulator holds them, and the V operand is read
-//   in that same key order.
+//   needs only one cross-lane exchange (lanes l, l^32, v_permlane32_swap).
+//   Online softmax in fp32 with exp2 (scale * log2 e folded into one FMA);
+//   the running max moves only when some lane's block max exceeds it by more
+//   than 8 (log2 units), otherwise the stale max is kept (exact: numerator
+//   and denominator share it, and every exponent stays <= 2^8).  The
+//   probabilities are rounded to bf16 once for P.V; the denominator sums
+//   them in fp32 before rounding.  The softmax of one block runs on the
+//   vector ALUs between the matrix instructions of the next block's scores
+//   and the previous block's P.V, in the same wave.  The score accumulator
+//   registers serve directly as the B operand of O^T += V^T P^T: the MFMA
+//   contraction index is mapped to keys in the order the accumulator holds
+//   them, and the V operand is read in that same key order.
 
 #include <utility>
 
@@ -257,16 +262,17 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   const float thr = 8.f / c;
   const int qpos = P + row;  // absolute position of this lane's query
 
-  // Software pipeline over the table: K tiles run two blocks ahead of use, V
-  // tiles one.  Step for block j (its scores already masked and its running
-  // max settled): copy K(j2) and V(j1) into the free buffers; S(j1) on the
-  // matrix cores alongside the probabilities of block j on the vector ALUs;
-  // O += V(j) P(j); mask and row max of S(j1).  That body has no branches (a
-  // copy past the end of the table is turned into an out-of-range buffer read
-  // that fetches nothing), so the scheduler can interleave it; the tail then
-  // settles the running max for block j1 and looks up the entry after j2.
-  // The loop is unrolled by two so buffer offsets and score registers keep
-  // fixed roles, and each step has a masked and an unmasked form.
+  // Software pipeline over the plain entries (j, j1, j2 = this entry and the
+  // next two): K tiles run two blocks ahead of use, V tiles one.  Step for
+  // block j (its scores computed and its running max settled): copy K(j2)
+  // and V(j) into the free buffers; S(j1) and O += V(j-1) P(j-1) on the
+  // matrix cores alongside the probabilities P(j) and the row max of S(j1)
+  // on the vector ALUs.  That body has no branches (a copy past the end of
+  // the table is turned into an out-of-range buffer read that fetches
+  // nothing), so the scheduler can interleave it; the tail then settles the
+  // running max for block j1 and looks up the entry after j2.  The loop is
+  // unrolled by two so buffer offsets and score registers keep fixed roles.
+  // Blocks that need the causal mask come after the loop, one at a time.
   constexpr int TB = Tile<D>::kBytes;
   char* const K0 = lds;
   char* const K1 = lds + TB;
@@ -401,7 +407,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
     body_schedule<D, W>();
     // Keep P(j) and its denominator in the body: without this the compiler
     // sinks the softmax past the barrier below, out of reach of the matrix
-    // instructions it is meant to overlap (measured 4% slower at 128K).
+    // instructions it is meant to overlap (measured 2% slower at 128K).
 #pragma unroll
     for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pcur[i]));
     asm volatile("" : "+v"(ws.l_part));
