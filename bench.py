@@ -248,7 +248,8 @@ def prefill_leg(stream, budget=32, local=8):
     per chunk, pool the new key blocks and the queries, make the top-k block
     mask, build the union tables and run zero-copy attention; the dense
     baseline runs the same attention over every block.  Cumulative times from
-    HIP events on the launch stream."""
+    HIP events on the launch stream, for the Python loop of calls and for the
+    same calls recorded into HIP graphs and replayed."""
     import torch
     import gen
     from chunked_prefill_sparse_amd.prefill import ChunkedPrefill
@@ -299,6 +300,17 @@ def prefill_leg(stream, budget=32, local=8):
     select_ms = statistics.median(timed(run_select) for _ in range(reps))
     dense_ms = statistics.median(timed(run_dense) for _ in range(reps))
     attn_ms = sparse_ms - select_ms
+    # the same call sequences recorded once into HIP graphs and replayed: the
+    # GPU time without the per-call host work of the loop above
+    priors = [c * s.C for c in range(s.n_chunks)]
+    g_sparse = drv.capture(qs, priors)
+    g_select = drv.capture(qs, priors, select_only=True)
+    g_dense = drv.capture(qs, priors, dense=True)
+    g_sparse.replay()
+    g_dense.replay()
+    gs_ms = statistics.median(timed(g_sparse.replay) for _ in range(reps))
+    gsel_ms = statistics.median(timed(g_select.replay) for _ in range(reps))
+    gd_ms = statistics.median(timed(g_dense.replay) for _ in range(reps))
     r = dict(
         chunks=s.n_chunks, chunk=s.C, prompt=s.L, budget_blocks=budget, local_blocks=local,
         total_ms=round(sparse_ms, 3), select_ms=round(select_ms, 3),
@@ -309,13 +321,18 @@ def prefill_leg(stream, budget=32, local=8):
         work_frac_of_dense=round(flops / flops_dense, 4),
         union_block_frac_first_mid_last=[round(frac[0], 3), round(frac[len(frac) // 2], 3),
                                          round(frac[-1], 3)],
+        graph=dict(total_ms=round(gs_ms, 3), select_ms=round(gsel_ms, 3),
+                   attention_ms=round(gs_ms - gsel_ms, 3), dense_attention_ms=round(gd_ms, 3),
+                   x_vs_dense=round(gd_ms / gs_ms, 3)),
         data=("synthetic planted-structure stream: K, V, Q ~ N(0,1), 3% salient KV blocks per "
               "KV head shifted along a per-head direction that the group's queries share"),
     )
     log(f"prefill_128k: total {sparse_ms:.2f} ms (select {select_ms:.2f}, attention "
         f"{attn_ms:.2f}) vs dense attention {dense_ms:.2f} ms -> x{dense_ms / sparse_ms:.2f}; "
         f"union fraction first/mid/last {r['union_block_frac_first_mid_last']}")
-    del qs, k, v, drv
+    log(f"prefill_128k as HIP graphs: total {gs_ms:.2f} ms (select {gsel_ms:.2f}) vs dense "
+        f"{gd_ms:.2f} ms -> x{gd_ms / gs_ms:.2f}")
+    del qs, k, v, drv, g_sparse, g_select, g_dense
     torch.cuda.empty_cache()
     return r
 

@@ -72,6 +72,34 @@ class ChunkedPrefill:
         self.select(q_chunk, prior, stream)
         return self.attend(q_chunk, prior, out, stream)
 
+    def capture(self, q_chunks, priors, outs=None, dense: bool = False,
+                select_only: bool = False) -> torch.cuda.CUDAGraph:
+        """Record ``step`` (or ``step_dense``, or only ``select``) for a
+        sequence of chunks into one HIP graph; ``replay()`` then reissues every
+        kernel with the same arguments and buffers, without the per-call host
+        work.  ``outs[i]`` receives chunk i's output (default: the shared
+        ``self.out``, which the last chunk leaves).  The library records no
+        memset, copy, allocation or synchronisation, so the whole call
+        sequence can be captured; inputs must stay at the same addresses
+        between replays."""
+        if outs is not None and len(outs) != len(q_chunks):
+            raise ValueError("outs must give one output per chunk")
+        if len(priors) != len(q_chunks):
+            raise ValueError("priors must give one offset per chunk")
+        lens = [self.dense_lens(p) for p in priors] if dense else None
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i, (q, p) in enumerate(zip(q_chunks, priors)):
+                o = outs[i] if outs is not None else None
+                if select_only:
+                    self.select(q, p)
+                elif dense:
+                    self.step_dense(q, p, lens[i], out=o)
+                else:
+                    self.step(q, p, out=o)
+        g.ca_dense_lens = lens  # device buffers the graph reads: keep them alive
+        return g
+
     def dense_lens(self, prior: int) -> torch.Tensor:
         n = (prior + self.C) // CA_BLOCK
         return torch.full((self.B, self.H_kv), n, dtype=torch.int32, device=self.k.device)

@@ -66,3 +66,36 @@ def test_prefill_small_every_chunk():
                 want = set(np.flatnonzero(sal[g, :pblk]).tolist())
                 if len(want) <= 4:
                     assert want <= found, (c, g, want - found)
+
+
+def test_prefill_graph_replay_matches_eager():
+    # The whole prompt (select + attend per chunk, and the dense baseline)
+    # recorded into one HIP graph: every replay, with eager library work and
+    # synchronisations in between, reproduces the eager outputs bit for bit.
+    s = gen.make_prefill_stream("prefill_small")
+    k_dev, v_dev = s.k.cuda(), s.v.cuda()
+    drv = ChunkedPrefill(k_dev, v_dev, s.H_q, s.C, budget=4, local=2)
+    qs = [s.q_chunk(c).cuda() for c in range(s.n_chunks)]
+    priors = [c * s.C for c in range(s.n_chunks)]
+    eager = [drv.step(q, p).clone() for q, p in zip(qs, priors)]
+    eager_T, eager_lens = drv.T.clone(), drv.lens.clone()
+    eager_d = [drv.step_dense(q, p, drv.dense_lens(p)).clone() for q, p in zip(qs, priors)]
+    torch.cuda.synchronize()
+    outs = [torch.full_like(qs[0], float("nan")) for _ in qs]
+    outs_d = [torch.full_like(qs[0], float("nan")) for _ in qs]
+    g = drv.capture(qs, priors, outs=outs)
+    gd = drv.capture(qs, priors, outs=outs_d, dense=True)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say(f"graph replay {rep}")
+        for o in outs + outs_d:
+            o.fill_(float("nan"))
+        drv.step(qs[0], 0)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        gd.replay()
+        torch.cuda.synchronize()
+        for c in range(s.n_chunks):
+            assert torch.equal(outs[c], eager[c]), (rep, c)
+            assert torch.equal(outs_d[c], eager_d[c]), (rep, c)
+        assert torch.equal(drv.T, eager_T) and torch.equal(drv.lens, eager_lens)
