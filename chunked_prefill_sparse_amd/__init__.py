@@ -21,7 +21,8 @@ import torch
 from . import _lib
 from ._lib import CA_BLOCK, CA_MAX_BATCH, CompactAttnError  # noqa: F401
 
-__all__ = ["build_union_tables", "chunk_attention", "tables_to_csr", "compact_kv",
+__all__ = ["build_union_tables", "chunk_attention", "tables_to_csr", "check_tables",
+           "compact_kv",
            "build_row_tables", "chunk_attention_rows", "pool_blocks", "block_mask_topk",
            "workspace_size",
            "CompactAttnError", "library_path"]
@@ -81,6 +82,29 @@ def build_union_tables(mask: torch.Tensor, H_kv: int, n_q_blocks: Sequence[int],
         _stream_ptr(stream))
     _lib.check(st, "ca_build_union_tables")
     return T, lens
+
+
+def check_tables(T: torch.Tensor, lens: torch.Tensor, n_kv_blocks: Sequence[int],
+                 row_bad: Optional[torch.Tensor] = None,
+                 stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Contract check of tables (``ca_check_tables``): int32 [B, H_kv] (device),
+    0 for a well-formed row, else a bitmask (1 length out of range, 2 entry
+    out of range, 4 not strictly ascending, 8 padding other than -1)."""
+    _need_cuda("T", T, torch.int32)
+    _need_cuda("lens", lens, torch.int32)
+    if T.dim() != 3 or lens.dim() != 2 or tuple(lens.shape) != tuple(T.shape[:2]):
+        raise ValueError("T must be [B, H_kv, NKB_max] and lens [B, H_kv]")
+    B, H_kv, NKB_max = T.shape
+    if row_bad is None:
+        row_bad = torch.empty((B, H_kv), dtype=torch.int32, device=T.device)
+    _need_cuda("row_bad", row_bad, torch.int32)
+    if tuple(row_bad.shape) != (B, H_kv):
+        raise ValueError("row_bad must be [B, H_kv]")
+    st = _lib.lib().ca_check_tables(T.data_ptr(), lens.data_ptr(), B, H_kv, NKB_max,
+                                    _host_ints("n_kv_blocks", n_kv_blocks, B),
+                                    row_bad.data_ptr(), _stream_ptr(stream))
+    _lib.check(st, "ca_check_tables")
+    return row_bad
 
 
 def build_row_tables(mask: torch.Tensor, n_kv_blocks: Sequence[int],

@@ -25,6 +25,7 @@ EXPORTED = (
     "ca_chunk_attention_split",
     "ca_chunk_attention_workspace_size",
     "ca_tables_to_csr",
+    "ca_check_tables",
     "ca_compact_kv",
     "ca_pool_blocks",
     "ca_block_mask_topk",
@@ -61,6 +62,8 @@ def _declare(lib):
     lib.ca_chunk_attention_workspace_size.restype = ctypes.c_size_t
     lib.ca_tables_to_csr.argtypes = [_vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _vp]
     lib.ca_tables_to_csr.restype = _i32
+    lib.ca_check_tables.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]
+    lib.ca_check_tables.restype = _i32
     lib.ca_compact_kv.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32p, _i32p, _i32, _i32, _i64, _i32,
                                   _i32, _vp, _vp, _vp, _vp]
     lib.ca_compact_kv.restype = _i32

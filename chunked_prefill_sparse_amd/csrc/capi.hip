@@ -67,6 +67,22 @@ CA_EXPORT ca_status ca_build_union_tables(const uint8_t* mask, int B, int H_q, i
       ca::launch_union_tables(mask, B, H_q, H_kv, NQ_max, NKB_max, ext, T, len, stream));
 }
 
+CA_EXPORT ca_status ca_check_tables(const int32_t* T, const int32_t* len, int B, int H_kv,
+                                    int NKB_max, const int32_t* n_kv_blocks, int32_t* row_bad,
+                                    hipStream_t stream) {
+  if (!T || !len || !n_kv_blocks || !row_bad) return CA_ERR_NULL;
+  if (B < 1 || B > CA_MAX_BATCH || H_kv < 1 || NKB_max < 1) return CA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H_kv > (1 << 30)) return CA_ERR_SHAPE;
+  ca::UnionExtents ext;
+  memset(&ext, 0, sizeof(ext));
+  for (int b = 0; b < B; ++b) {
+    if (n_kv_blocks[b] < 0 || n_kv_blocks[b] > NKB_max) return CA_ERR_SHAPE;
+    ext.nkb[b] = n_kv_blocks[b];
+  }
+  return hip_status(ca::launch_check_tables(T, len, B * H_kv, H_kv, NKB_max, ext, row_bad,
+                                            stream));
+}
+
 CA_EXPORT ca_status ca_tables_to_csr(const int32_t* T, const int32_t* len, int B, int H_kv,
                                      int NKB_max, int64_t L, int32_t* kv_indptr,
                                      int32_t* kv_indices, hipStream_t stream) {

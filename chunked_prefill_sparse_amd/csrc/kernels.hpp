@@ -50,6 +50,9 @@ hipError_t launch_union_tables(const uint8_t* mask, int B, int H_q, int H_kv, in
                                int NKB_max, const UnionExtents& ext, int32_t* T,
                                int32_t* len, hipStream_t stream);
 
+hipError_t launch_check_tables(const int32_t* T, const int32_t* len, int n_bg, int H_kv,
+                               int NKB_max, const UnionExtents& ext, int32_t* row_bad,
+                               hipStream_t stream);
 hipError_t launch_tables_to_csr(const int32_t* T, const int32_t* len, int n_bg, int NKB_max,
                                 int64_t pages, int32_t* kv_indptr, int32_t* kv_indices,
                                 hipStream_t stream);

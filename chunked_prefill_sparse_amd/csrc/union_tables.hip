@@ -162,6 +162,43 @@ __global__ __launch_bounds__(kCsrThreads) void tables_to_csr_kernel(
     kv_indices[off + j] = static_cast<int32_t>(page0 + trow[j]);
 }
 
+// Contract check of one table row (the properties chunk attention relies on
+// without checking them on the device): one workgroup per pseudo-request, a
+// bitmask of the violations found (see ca_check_tables).
+constexpr int kCheckThreads = 256;
+
+__global__ __launch_bounds__(kCheckThreads) void check_tables_kernel(
+    const int32_t* __restrict__ T, const int32_t* __restrict__ len, int H_kv, int NKB_max,
+    UnionExtents ext, int32_t* __restrict__ row_bad) {
+  __shared__ int flags[kCheckThreads / 64];
+  const int bg = blockIdx.x;
+  const int b = bg / H_kv;
+  const int tid = threadIdx.x;
+  const int nkb = ext.nkb[b];
+  const int n = len[bg];
+  int f = (n < 0 || n > NKB_max) ? 1 : 0;
+  const int nc = n < 0 ? 0 : (n > NKB_max ? NKB_max : n);
+  const int32_t* trow = T + static_cast<size_t>(bg) * NKB_max;
+  for (int j = tid; j < NKB_max; j += kCheckThreads) {
+    const int v = trow[j];
+    if (j < nc) {
+      if (v < 0 || v >= nkb) f |= 2;
+      if (j > 0 && v <= trow[j - 1]) f |= 4;
+    } else if (v != -1) {
+      f |= 8;
+    }
+  }
+  // OR over the workgroup: per wave through its lanes, then across waves
+  for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o);
+  if ((tid & 63) == 0) flags[tid >> 6] = f;
+  __syncthreads();
+  if (tid == 0) {
+    int all = 0;
+    for (int w = 0; w < kCheckThreads / 64; ++w) all |= flags[w];
+    row_bad[bg] = all;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_union_tables(const uint8_t* mask, int B, int H_q, int H_kv, int NQ_max,
@@ -176,6 +213,14 @@ hipError_t launch_union_tables(const uint8_t* mask, int B, int H_q, int H_kv, in
   else
     hipLaunchKernelGGL(union_tables_kernel<1>, grid, block, lds, stream, mask, H_q, H_kv,
                        NQ_max, NKB_max, ext, T, len);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_tables(const int32_t* T, const int32_t* len, int n_bg, int H_kv,
+                               int NKB_max, const UnionExtents& ext, int32_t* row_bad,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(check_tables_kernel, dim3(n_bg), dim3(kCheckThreads), 0, stream, T, len,
+                     H_kv, NKB_max, ext, row_bad);
   return hipGetLastError();
 }
 

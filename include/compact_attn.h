@@ -209,6 +209,28 @@ CA_EXPORT ca_status ca_chunk_attention_rows(const void* Q, const void* K_cache,
                                   hipStream_t stream);
 
 /*
+ * ca_check_tables -- checks tables against the contract that
+ * ca_chunk_attention relies on without checking it on the device (selection
+ * stage output: minimal tables, strictly ascending, padded).  For each
+ * pseudo-request u = b*H_kv + g, row_bad[u] is a bitmask, 0 when the row is
+ * well formed:
+ *   1  len[u] outside [0, NKB_max]
+ *   2  an entry T[b,g,j], j < len[u], outside [0, n_kv_blocks[b])
+ *   4  T[b,g,0 .. len[u]) not strictly ascending (a repeat counts)
+ *   8  an entry past len[u] (padding) other than -1
+ * (with len[u] out of range, entries are judged against len clamped to
+ * [0, NKB_max]).  Tables from ca_build_union_tables give all zeros.
+ * T, len       device int32 [B, H_kv, NKB_max] and [B, H_kv].
+ * n_kv_blocks  host int32 [B], each in [0, NKB_max] (else CA_ERR_SHAPE).
+ * row_bad      device int32 [B * H_kv] (out), owned by the caller.
+ * Asynchronous on `stream`; a caller who wants the answer on the host copies
+ * row_bad back.  Errors: CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_HIP.
+ */
+CA_EXPORT ca_status ca_check_tables(const int32_t* T, const int32_t* len, int B, int H_kv,
+                                    int NKB_max, const int32_t* n_kv_blocks, int32_t* row_bad,
+                                    hipStream_t stream);
+
+/*
  * ca_tables_to_csr -- the paged-metadata view of the tables (execution stage:
  * the tables travel to a paged dense kernel as kv_indptr / kv_indices).
  * Pseudo-request u = b*H_kv + g.

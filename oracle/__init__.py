@@ -20,6 +20,10 @@ Contents (each function cites the passage it follows):
 * ``chunk_attention_dense_masked_ref`` -- the same result computed as dense
   attention over all cached keys with a -inf mask (second formulation).
 * ``tables_to_csr_ref`` -- the (kv_indptr, kv_indices) view of the tables.
+* ``check_tables_ref`` -- the table contract attention relies on (range,
+  strict ascent, -1 padding), checked row by row.  Pinned by the tables of
+  ``union_tables_ref`` (all rows pass) and by planted single violations,
+  each giving exactly its own flag.
 * ``compact_kv_ref`` -- explicit KV compaction (the copy zero-copy execution
   avoids): selected prior blocks packed to end where the chunk starts.  Pinned
   by a hand-worked case and by the invariant that attention over the
@@ -36,7 +40,7 @@ Contents (each function cites the passage it follows):
 
 Float work is float64 throughout; outputs are float32.
 """
-from .union_ref import union_tables_ref, tables_to_csr_ref  # noqa: F401
+from .union_ref import check_tables_ref, tables_to_csr_ref, union_tables_ref  # noqa: F401
 from .attention_ref import (  # noqa: F401
     BLOCK,
     admissible_keys,

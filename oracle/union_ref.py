@@ -63,3 +63,31 @@ def tables_to_csr_ref(T: np.ndarray, ln: np.ndarray, L: int, block: int = 64):
         parts.append(u * pages + T[b, g, :ln[b, g]].astype(np.int64))
     indices = np.concatenate(parts).astype(np.int32) if parts else np.zeros(0, np.int32)
     return indptr, indices
+
+
+def check_tables_ref(T: np.ndarray, ln: np.ndarray, n_kv_blocks, NKB_max: int) -> np.ndarray:
+    """The table contract that attention relies on (selection-stage output,
+    "Methodology": one minimal table per group, here read as strictly ascending
+    block ids padded with -1), checked row by row in plain Python.  Returns
+    int32 [B, H_kv]: 0 for a well-formed row, else the OR of 1 (len outside
+    [0, NKB_max]), 2 (an entry j < len outside [0, n_kv_blocks[b])), 4 (the
+    first len entries not strictly ascending), 8 (an entry past len other than
+    -1); entries are judged against len clamped to [0, NKB_max]."""
+    B, H_kv, _ = T.shape
+    out = np.zeros((B, H_kv), np.int32)
+    for b in range(B):
+        for g in range(H_kv):
+            n = int(ln[b, g])
+            f = 0 if 0 <= n <= NKB_max else 1
+            n = min(max(n, 0), NKB_max)
+            row = [int(x) for x in T[b, g]]
+            for j in range(NKB_max):
+                if j < n:
+                    if not 0 <= row[j] < int(n_kv_blocks[b]):
+                        f |= 2
+                    if j > 0 and row[j] <= row[j - 1]:
+                        f |= 4
+                elif row[j] != -1:
+                    f |= 8
+            out[b, g] = f
+    return out

@@ -141,6 +141,14 @@ int main() {
                             (int32_t*)FAKE, (int32_t*)FAKE, 0) == CA_OK);
     EXPECT(strcmp(stub::last.what, "csr") == 0 && stub::last.ints[0] == 16 &&
            stub::last.ints[2] == 16);
+    const int32_t nkb2[2] = {12, 16};
+    EXPECT(ca_check_tables((const int32_t*)FAKE, (const int32_t*)FAKE, 2, 8, 16, nkb2,
+                           (int32_t*)FAKE, 0) == CA_OK);
+    EXPECT(strcmp(stub::last.what, "check") == 0 && stub::last.ints[0] == 16 &&
+           stub::last.ints[3] == 16);
+    const int32_t nkb_bad[2] = {12, 17};
+    EXPECT(ca_check_tables((const int32_t*)FAKE, (const int32_t*)FAKE, 2, 8, 16, nkb_bad,
+                           (int32_t*)FAKE, 0) == CA_ERR_SHAPE);
   }
   // ---- status strings for every code and one past the end
   for (int s = 0; s <= 6; ++s) EXPECT(ca_status_string((ca_status)s) != nullptr);

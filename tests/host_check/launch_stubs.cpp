@@ -24,6 +24,17 @@ hipError_t launch_union_tables(const uint8_t*, int B, int H_q, int H_kv, int NQ_
   return hipSuccess;
 }
 
+hipError_t launch_check_tables(const int32_t*, const int32_t*, int n_bg, int H_kv, int NKB_max,
+                               const UnionExtents& ext, int32_t*, hipStream_t) {
+  stub::last = stub::Record{};
+  stub::last.what = "check";
+  stub::last.ints[0] = n_bg;
+  stub::last.ints[1] = H_kv;
+  stub::last.ints[2] = NKB_max;
+  stub::last.ints[3] = ext.nkb[n_bg / H_kv - 1];
+  return hipSuccess;
+}
+
 hipError_t launch_tables_to_csr(const int32_t*, const int32_t*, int n_bg, int NKB_max,
                                 int64_t pages, int32_t*, int32_t*, hipStream_t) {
   stub::last = stub::Record{};

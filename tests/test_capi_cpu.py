@@ -105,6 +105,19 @@ def test_csr_validation(args, status):
     assert _lib.lib().ca_tables_to_csr(*args, None) == status
 
 
+@pytest.mark.parametrize("args,status", [
+    ((None, FAKE, 1, 8, 16, _ints(16), FAKE), 1),
+    ((FAKE, FAKE, 1, 8, 16, None, FAKE), 1),
+    ((FAKE, FAKE, 1, 8, 16, _ints(16), None), 1),
+    ((FAKE, FAKE, 0, 8, 16, _ints(16), FAKE), 2),
+    ((FAKE, FAKE, 1, 0, 16, _ints(16), FAKE), 2),
+    ((FAKE, FAKE, 1, 8, 16, _ints(17), FAKE), 2),    # n_kv_blocks > NKB_max
+    ((FAKE, FAKE, 1, 8, 16, _ints(-1), FAKE), 2),
+])
+def test_check_tables_validation(args, status):
+    assert _lib.lib().ca_check_tables(*args, None) == status
+
+
 def _compact(lib, **kw):
     a = dict(K=FAKE, V=FAKE, T=FAKE, len=FAKE, NKB_max=20, prior=_ints(1024), chunk=_ints(256),
              B=1, H_kv=1, L=1280, D=64, dtype=1, Ko=FAKE, Vo=FAKE, To=FAKE)

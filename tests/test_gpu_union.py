@@ -7,7 +7,7 @@ import torch
 
 import gen
 import chunked_prefill_sparse_amd as ca
-from oracle import tables_to_csr_ref, union_tables_ref
+from oracle import check_tables_ref, tables_to_csr_ref, union_tables_ref
 from tests.gpu_util import say
 
 pytestmark = pytest.mark.gpu
@@ -106,3 +106,38 @@ def test_csr_view_matches_oracle():
     ip = indptr.cpu().numpy()
     np.testing.assert_array_equal(ip, ip_r)
     np.testing.assert_array_equal(indices.cpu().numpy()[:ip[-1]], ix_r)
+
+
+def test_check_tables_parity():
+    # The contract check: every union table passes; fuzzed tables (entries
+    # and lengths drawn around the valid ranges, some rows sorted, some padded
+    # correctly) give the oracle's flags bit for bit.
+    rng = np.random.default_rng(77)
+    mask = (rng.random((3, 8, 4, 200)) < 0.05).astype(np.uint8)
+    nq, nkb = [4, 2, 3], [200, 130, 77]
+    T, ln = _gpu_tables(mask, 2, nq, nkb)
+    Td, ld = torch.from_numpy(T).cuda(), torch.from_numpy(ln).cuda()
+    bad = ca.check_tables(Td, ld, nkb)
+    torch.cuda.synchronize()
+    assert not bad.any(), bad
+    for trial in range(20):
+        B, H_kv, NKB = 3, 4, int(rng.integers(1, 300))
+        nk = [int(rng.integers(0, NKB + 1)) for _ in range(B)]
+        Tf = rng.integers(-2, NKB + 3, size=(B, H_kv, NKB)).astype(np.int32)
+        lf = rng.integers(-1, NKB + 2, size=(B, H_kv)).astype(np.int32)
+        for b in range(B):
+            for g in range(H_kv):
+                r = rng.random()
+                if r < 0.5:  # a well-formed row, maybe one entry disturbed
+                    n = int(rng.integers(0, nk[b] + 1))
+                    row = np.sort(rng.choice(nk[b], size=n, replace=False)) if n else []
+                    Tf[b, g] = -1
+                    Tf[b, g, :n] = row
+                    lf[b, g] = n
+                    if r < 0.25 and NKB > 1:
+                        Tf[b, g, int(rng.integers(0, NKB))] = int(rng.integers(-2, NKB + 3))
+        want = check_tables_ref(Tf, lf, nk, NKB)
+        got = ca.check_tables(torch.from_numpy(Tf).cuda(), torch.from_numpy(lf).cuda(), nk)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(got.cpu().numpy(), want, err_msg=f"trial {trial}")
+

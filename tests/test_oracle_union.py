@@ -14,7 +14,7 @@ import pytest
 from hypothesis import given, settings, strategies as st
 
 import gen
-from oracle import tables_to_csr_ref, union_tables_ref
+from oracle import check_tables_ref, tables_to_csr_ref, union_tables_ref
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "union_hand_worked.txt")
 
@@ -260,3 +260,48 @@ def test_generators_current_chunk_blocks_always_selected():
                 s = set(T[b, g, :ln[b, g]].tolist())
                 assert set(range(p_blk, w.n_kv_blocks[b])) <= s
                 assert 0 in s  # sink
+
+
+def test_table_contract_check():
+    # Tables from the union pass; each planted violation raises exactly its own
+    # flag (1 len out of range, 2 entry out of range, 4 not strictly
+    # ascending, 8 padding other than -1).
+    rng = np.random.default_rng(5)
+    mask = (rng.random((2, 4, 3, 12)) < 0.3).astype(np.uint8)
+    nkb = [12, 9]
+    T, ln = union_tables_ref(mask, 2, [3, 2], nkb)
+    assert not check_tables_ref(T, ln, nkb, 12).any()
+    # a row with at least two entries and room for padding
+    b, g = next((b, g) for b in range(2) for g in range(2) if 2 <= ln[b, g] < 12)
+    n = int(ln[b, g])
+
+    def planted(fn):
+        T2, l2 = T.copy(), ln.copy()
+        fn(T2, l2)
+        return check_tables_ref(T2, l2, nkb, 12)
+
+    cases = [
+        (lambda T2, l2: l2.__setitem__((b, g), 13), 1 | 8 * 0),
+        (lambda T2, l2: l2.__setitem__((b, g), -1), None),
+        (lambda T2, l2: T2.__setitem__((b, g, 0), nkb[b]), None),
+        (lambda T2, l2: T2.__setitem__((b, g, 1), T2[b, g, 0]), 4),
+        (lambda T2, l2: T2.__setitem__((b, g, n), 0), 8),
+    ]
+    # len 13 > NKB_max: flag 1; the row is then judged over all 12 entries,
+    # whose -1 padding breaks range and ascent too
+    got = planted(cases[0][0])
+    assert got[b, g] & 1 and got[b, g] & 2
+    # negative len: flag 1, and the real entries now count as bad padding
+    got = planted(cases[1][0])
+    assert got[b, g] == 1 | 8
+    # entry past the sequence's blocks: flag 2 (and ascent, if it exceeds the next)
+    got = planted(cases[2][0])
+    assert got[b, g] & 2
+    assert planted(cases[3][0])[b, g] == 4
+    assert planted(cases[4][0])[b, g] == 8
+    for c in cases:  # the other rows are untouched
+        got = planted(c[0])
+        others = np.ones((2, 2), bool)
+        others[b, g] = False
+        assert not got[others].any()
+
