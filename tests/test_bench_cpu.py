@@ -1,0 +1,80 @@
+"""CPU checks of the benchmark's own arithmetic and contract.
+
+* The work accounting behind the metric (admissible (query, key) pairs, hence
+  the algorithmic FLOPs) against brute-force loops on tiny tables, for union
+  execution and for block-sparse per-Q-block execution.
+* The code hash that ties the stored counter summary to the kernel: blind to
+  comments and white space, sensitive to code.
+* One GPU only: ``--gpus 2`` exits with a message before touching a GPU.
+"""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+from oracle import union_tables_ref
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _brute_pairs(T, lens, prior, chunk, G):
+    n = 0
+    for b in range(T.shape[0]):
+        P, C = prior[b], chunk[b]
+        for g in range(T.shape[1]):
+            keys = [t for kb in T[b, g, :lens[b, g]] for t in range(64 * kb, 64 * kb + 64)]
+            for i in range(C):
+                n += G * sum(1 for t in keys if t <= P + i and t < P + C)
+    return n
+
+
+def _brute_pairs_rows(mask, prior, chunk):
+    n = 0
+    for b in range(mask.shape[0]):
+        P, C = prior[b], chunk[b]
+        for h in range(mask.shape[1]):
+            for qb in range(C // 64):
+                for kb in np.flatnonzero(mask[b, h, qb, :(P + C) // 64]):
+                    for i in range(64 * qb, 64 * qb + 64):
+                        n += sum(1 for t in range(64 * kb, 64 * kb + 64) if t <= P + i)
+    return n
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_admissible_pairs_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    B, H_kv, G = 2, 2, 2
+    prior = [64 * int(rng.integers(0, 5)) for _ in range(B)]
+    chunk = [64 * int(rng.integers(1, 4)) for _ in range(B)]
+    nq = [c // 64 for c in chunk]
+    nkb = [(p + c) // 64 for p, c in zip(prior, chunk)]
+    NKB = max(nkb)
+    mask = (rng.random((B, H_kv * G, max(nq), NKB)) < 0.4).astype(np.uint8)
+    T, ln = union_tables_ref(mask, H_kv, nq, nkb)
+    assert bench.admissible_pairs(T, ln, prior, chunk, G) == _brute_pairs(T, ln, prior, chunk, G)
+    assert bench.admissible_pairs_rows(mask, prior, chunk) == _brute_pairs_rows(mask, prior, chunk)
+
+
+def test_code_hash_ignores_comments_only(tmp_path):
+    a = tmp_path / "a.hip"
+    a.write_text('// one\nint f(int x) {  /* two */ return x + 1; }\nconst char* s = "// kept";\n')
+    b = tmp_path / "b.hip"
+    b.write_text('// changed\n\nint f(int x) {\n  return x + 1;  // three\n}\nconst char* s = "// kept";\n')
+    c = tmp_path / "c.hip"
+    c.write_text('int f(int x) { return x + 2; }\nconst char* s = "// kept";\n')
+    d = tmp_path / "d.hip"
+    d.write_text('int f(int x) { return x + 1; }\nconst char* s = "// other";\n')
+    assert bench.code_hash(a) == bench.code_hash(b)
+    assert bench.code_hash(a) != bench.code_hash(c)
+    assert bench.code_hash(a) != bench.code_hash(d)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
+    assert not r.stdout.strip().startswith("{")
