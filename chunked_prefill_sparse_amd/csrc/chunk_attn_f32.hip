@@ -5,13 +5,14 @@
 // in place from the KV-head-major cache), for fp32 inputs, where fp32
 // arithmetic is kept end to end.  It serves small chunks, where latency
 // rather than arithmetic sets the time.  A workgroup of 512 threads owns 64
-// consecutive query rows of one head, eight threads per row, each holding an
-// eighth of the row's q and output accumulator; a score is the sum of the
-// eight partial dot products (three lane exchanges).  Each selected block's K
+// consecutive query rows of one head, eight threads per row (32 rows, sixteen
+// threads per row, when 64-row tiles would leave most CUs idle), each thread
+// holding its share of the row's q and output accumulator; a score is the sum
+// of the partial dot products (DPP lane moves, fused into the adds).  Each selected block's K
 // and V rows are staged in LDS (coalesced 16-byte loads) and read back as
 // broadcasts.  With per-(head, Q-block) tables (the lists of a block-sparse
-// kernel) the workgroup's 64 rows are exactly one Q-block, so it simply reads
-// its own table row.
+// kernel) the workgroup's rows lie inside one Q-block, so it simply reads that
+// Q-block's table row.
 
 #include "kernels.hpp"
 
@@ -19,15 +20,35 @@ namespace ca {
 namespace {
 
 constexpr int kBlk = 64;
-constexpr int kTpr = 8;  // threads per query row
-constexpr int kRowsF = 64;
-constexpr int kThreadsF = kRowsF * kTpr;
+constexpr int kThreadsF = 512;  // threads per workgroup
 
-template <int D>
+// Sum over the R lanes of a row (R = 8 or 16 consecutive lanes, aligned), in
+// every one of them, by DPP moves on the vector ALU (no LDS round trip): swap
+// neighbours, swap pairs, add the mirror image within 8 lanes, then within 16.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, true));
+}
+template <int R>
+__device__ __forceinline__ float row_sum(float x) {
+  static_assert(R == 8 || R == 16, "row width");
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  x += dpp<0x141>(x);  // row_half_mirror: lane 7 - i within each 8 lanes
+  if (R == 16) x += dpp<0x140>(x);  // row_mirror: lane 15 - i within each 16 lanes
+  return x;
+}
+
+// kTpr threads per query row (8, or 16 when 64-row tiles would leave most CUs
+// idle: twice the workgroups, each thread with half the products); a
+// workgroup owns kThreadsF / kTpr consecutive rows.
+template <int D, int kTpr>
 __global__ __launch_bounds__(kThreadsF) void chunk_attn_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const int32_t* __restrict__ T, const int32_t* __restrict__ len, float* __restrict__ O,
     float* __restrict__ lse, AttnParams p, SeqInfo seq, int n_tiles) {
+  constexpr int kRowsF = kThreadsF / kTpr;
   constexpr int SL = D / kTpr;  // this thread's slice of the row
   __shared__ __attribute__((aligned(16))) float Ks[kBlk * D];
   __shared__ __attribute__((aligned(16))) float Vs[kBlk * D];
@@ -62,7 +83,8 @@ __global__ __launch_bounds__(kThreadsF) void chunk_attn_f32_kernel(
   const int kb_limit = (P + last_row) / kBlk;
   const int nkb = (P + C + kBlk - 1) / kBlk;
   // table of the workgroup: T[b,g], or T[b,h,Q-block] for per-Q-block lists
-  const size_t trow = p.row_tables ? (static_cast<size_t>(b) * p.H_q + h) * p.NQ_max + tile
+  const size_t trow = p.row_tables ? (static_cast<size_t>(b) * p.H_q + h) * p.NQ_max +
+                                         (tile * kRowsF) / kBlk
                                    : static_cast<size_t>(bg);
   int nT = len[trow];
   nT = nT < 0 ? 0 : (nT > p.NKB_max ? p.NKB_max : nT);
@@ -125,9 +147,7 @@ __global__ __launch_bounds__(kThreadsF) void chunk_attn_f32_kernel(
       float dot = 0.f;
 #pragma unroll
       for (int i = 0; i < SL; ++i) dot = __builtin_fmaf(q[i], kr[i], dot);
-      dot += __shfl_xor(dot, 1);
-      dot += __shfl_xor(dot, 2);
-      float sc = dot + __shfl_xor(dot, 4);
+      float sc = row_sum<kTpr>(dot);
       if (kb * kBlk + k > qpos) sc = -INFINITY;
       s[k] = sc;
       mx = fmaxf(mx, sc);
@@ -162,14 +182,24 @@ hipError_t launch_chunk_attn_f32(const float* Q, const float* K, const float* V,
                                  const int32_t* T, const int32_t* len, float* O, float* lse,
                                  int B, int D, const AttnParams& p, const SeqInfo& seq,
                                  hipStream_t stream) {
-  const int n_tiles = (p.C_max + kRowsF - 1) / kRowsF;
+  // 16 threads per row (32-row tiles) when 64-row tiles would occupy fewer
+  // workgroups than the chip has CUs
+  const bool narrow = static_cast<int64_t>(B) * p.H_q * ((p.C_max + 63) / 64) < 256;
+  const int rows = narrow ? kThreadsF / 16 : kThreadsF / 8;
+  const int n_tiles = (p.C_max + rows - 1) / rows;
   const dim3 grid(B * p.H_q * n_tiles), block(kThreadsF);
-  if (D == 128)
-    hipLaunchKernelGGL(chunk_attn_f32_kernel<128>, grid, block, 0, stream, Q, K, V, T, len, O,
-                       lse, p, seq, n_tiles);
+  if (D == 128 && narrow)
+    hipLaunchKernelGGL((chunk_attn_f32_kernel<128, 16>), grid, block, 0, stream, Q, K, V, T, len,
+                       O, lse, p, seq, n_tiles);
+  else if (D == 128)
+    hipLaunchKernelGGL((chunk_attn_f32_kernel<128, 8>), grid, block, 0, stream, Q, K, V, T, len,
+                       O, lse, p, seq, n_tiles);
+  else if (narrow)
+    hipLaunchKernelGGL((chunk_attn_f32_kernel<64, 16>), grid, block, 0, stream, Q, K, V, T, len,
+                       O, lse, p, seq, n_tiles);
   else
-    hipLaunchKernelGGL(chunk_attn_f32_kernel<64>, grid, block, 0, stream, Q, K, V, T, len, O,
-                       lse, p, seq, n_tiles);
+    hipLaunchKernelGGL((chunk_attn_f32_kernel<64, 8>), grid, block, 0, stream, Q, K, V, T, len,
+                       O, lse, p, seq, n_tiles);
   return hipGetLastError();
 }
 
