@@ -198,7 +198,7 @@ def chunk_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     q [B, H_q, C_max, D] and k_cache/v_cache [B, H_kv, L, D] (bf16 or fp32, device);
     T/lens from ``build_union_tables``; prior_len/chunk_len host ints per sequence.
     Returns O [B, H_q, C_max, D] (and lse fp32 [B, H_q, C_max] if ``return_lse``).
-    ``n_splits`` > 1 (bf16) cuts each table into that many ranges run by separate
+    ``n_splits`` > 1 (bf16 or fp32) cuts each table into that many ranges run by separate
     workgroups and merged (``ca_chunk_attention_split``); ``workspace`` is then a
     device tensor of at least ``workspace_size(...)`` bytes (allocated if None).
     """

@@ -177,11 +177,21 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
   }
   p.n_t = 0;
   p.xcd = 0;
-  if (static_cast<int64_t>(B) * H_q * ((C_max + 63) / 64) > INT32_MAX) return CA_ERR_SHAPE;
-  return hip_status(ca::launch_chunk_attn_f32(
-      static_cast<const float*>(Q), static_cast<const float*>(K_cache),
-      static_cast<const float*>(V_cache), T, len, static_cast<float*>(O), lse, B, D, p, seq,
-      stream));
+  if (static_cast<int64_t>(B) * H_q * n_split * ((C_max + 31) / 32) > INT32_MAX)
+    return CA_ERR_SHAPE;
+  const float* q = static_cast<const float*>(Q);
+  const float* k = static_cast<const float*>(K_cache);
+  const float* v = static_cast<const float*>(V_cache);
+  if (n_split > 1) {
+    float* part_o = static_cast<float*>(workspace);
+    float* part_ml = part_o + static_cast<size_t>(n_split) * p.rows_total * D;
+    return hip_status(ca::launch_chunk_attn_f32_split(q, k, v, T, len, static_cast<float*>(O),
+                                                      lse, B, D, p, seq, part_o, part_ml,
+                                                      stream));
+  }
+  return hip_status(
+      ca::launch_chunk_attn_f32(q, k, v, T, len, static_cast<float*>(O), lse, B, D, p, seq,
+                                stream));
 }
 
 }  // namespace
@@ -217,7 +227,6 @@ CA_EXPORT ca_status ca_chunk_attention_split(const void* Q, const void* K_cache,
   if (n_splits == 1)
     return attention(Q, K_cache, V_cache, T, len, 0, NKB_max, prior_len, chunk_len, B, H_q,
                      H_kv, C_max, L, D, block, scale, dtype, O, lse, false, 1, nullptr, 0, stream);
-  if (dtype == CA_F32) return CA_ERR_UNSUPPORTED;
   if (!workspace) return CA_ERR_NULL;
   if (!aligned16(workspace)) return CA_ERR_UNSUPPORTED;
   if (B >= 1 && H_q >= 1 && C_max >= 1 && (D == 64 || D == 128) &&

@@ -544,11 +544,11 @@ namespace {
 // split s and M = max_s m_s, w_s = exp2((m_s - M) * scale * log2 e):
 //   O = sum_s w_s a_s / sum_s w_s l_s,   lse = M * scale + log(sum_s w_s l_s).
 // Rows past the chunk, and rows no split saw a key for, give O = 0, lse = -inf.
-template <int D>
+template <int D, typename TOut>
 __global__ __launch_bounds__(256) void split_combine_kernel(const float* __restrict__ part_o,
                                                             const float* __restrict__ part_ml,
                                                             AttnParams p, SeqInfo seq,
-                                                            __bf16* __restrict__ O,
+                                                            TOut* __restrict__ O,
                                                             float* __restrict__ lse) {
   constexpr int E = D / 64;  // elements per lane
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -577,9 +577,9 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const float* __restr
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  __bf16* orow = O + r * D + E * lane;
+  TOut* orow = O + r * D + E * lane;
 #pragma unroll
-  for (int k = 0; k < E; ++k) orow[k] = static_cast<__bf16>(acc[k] * inv);
+  for (int k = 0; k < E; ++k) orow[k] = static_cast<TOut>(acc[k] * inv);
   if (lse && lane == 0) lse[r] = l > 0.f ? M * p.scale + __logf(l) : -INFINITY;
 }
 
@@ -603,13 +603,30 @@ hipError_t launch_chunk_attn_bf16_split(const void* Q, const void* K, const void
                        q, k, v, T, len, o, lse, p, seq, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_split_combine(part_o, part_ml, D, false, o, lse, p, seq, stream);
+}
+
+hipError_t launch_split_combine(const float* part_o, const float* part_ml, int D, bool f32_out,
+                                void* O, float* lse, const AttnParams& p, const SeqInfo& seq,
+                                hipStream_t stream) {
   const dim3 cgrid(static_cast<unsigned>((p.rows_total + 3) / 4));
-  if (D == 128)
-    hipLaunchKernelGGL(split_combine_kernel<128>, cgrid, dim3(256), 0, stream, part_o, part_ml, p,
-                       seq, o, lse);
-  else
-    hipLaunchKernelGGL(split_combine_kernel<64>, cgrid, dim3(256), 0, stream, part_o, part_ml, p,
-                       seq, o, lse);
+  if (f32_out) {
+    float* o = static_cast<float*>(O);
+    if (D == 128)
+      hipLaunchKernelGGL((split_combine_kernel<128, float>), cgrid, dim3(256), 0, stream, part_o,
+                         part_ml, p, seq, o, lse);
+    else
+      hipLaunchKernelGGL((split_combine_kernel<64, float>), cgrid, dim3(256), 0, stream, part_o,
+                         part_ml, p, seq, o, lse);
+  } else {
+    __bf16* o = static_cast<__bf16*>(O);
+    if (D == 128)
+      hipLaunchKernelGGL((split_combine_kernel<128, __bf16>), cgrid, dim3(256), 0, stream, part_o,
+                         part_ml, p, seq, o, lse);
+    else
+      hipLaunchKernelGGL((split_combine_kernel<64, __bf16>), cgrid, dim3(256), 0, stream, part_o,
+                         part_ml, p, seq, o, lse);
+  }
   return hipGetLastError();
 }
 

@@ -42,12 +42,16 @@ __device__ __forceinline__ float row_sum(float x) {
 
 // kTpr threads per query row (8, or 16 when 64-row tiles would leave most CUs
 // idle: twice the workgroups, each thread with half the products); a
-// workgroup owns kThreadsF / kTpr consecutive rows.
-template <int D, int kTpr>
+// workgroup owns kThreadsF / kTpr consecutive rows.  kSplit: the table is cut
+// into p.n_split contiguous position ranges, one per workgroup, and each
+// writes its unnormalised output, running max and denominator to part_o /
+// part_ml for the split-KV merge (more workgroups for small chunks).
+template <int D, int kTpr, bool kSplit>
 __global__ __launch_bounds__(kThreadsF) void chunk_attn_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const int32_t* __restrict__ T, const int32_t* __restrict__ len, float* __restrict__ O,
-    float* __restrict__ lse, AttnParams p, SeqInfo seq, int n_tiles) {
+    float* __restrict__ lse, AttnParams p, SeqInfo seq, int n_tiles, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
   constexpr int kRowsF = kThreadsF / kTpr;
   constexpr int SL = D / kTpr;  // this thread's slice of the row
   __shared__ __attribute__((aligned(16))) float Ks[kBlk * D];
@@ -55,8 +59,11 @@ __global__ __launch_bounds__(kThreadsF) void chunk_attn_f32_kernel(
 
   const int tid = threadIdx.x;
   const int wg = blockIdx.x;
-  const int bh = wg / n_tiles;
-  const int tile = wg - bh * n_tiles;
+  const int nsp = kSplit ? p.n_split : 1;
+  const int bhs = wg / n_tiles;  // (head, split)
+  const int tile = wg - bhs * n_tiles;
+  const int bh = bhs / nsp;
+  const int split = bhs - bh * nsp;
   const int rank = bh / p.H_q;
   const int h = bh - rank * p.H_q;
   const int b = seq.order[rank];
@@ -72,8 +79,8 @@ __global__ __launch_bounds__(kThreadsF) void chunk_attn_f32_kernel(
   const size_t qrow = (static_cast<size_t>(b) * p.H_q + h) * p.C_max + row;
   const size_t qo = qrow * D + part * SL;
 
-  if (tile * kRowsF >= C) {  // padding rows only
-    if (row_in) {
+  if (tile * kRowsF >= C) {  // padding rows only (the merge writes them when split)
+    if (row_in && !kSplit) {
       for (int i = 0; i < SL; ++i) O[qo + i] = 0.f;
       if (lse && part == 0) lse[qrow] = -INFINITY;
     }
@@ -105,23 +112,26 @@ __global__ __launch_bounds__(kThreadsF) void chunk_attn_f32_kernel(
   constexpr int NV = kBlk * D / 4 / kThreadsF;  // 16-byte pieces per thread
   float4 pk[NV], pv[NV];
   auto valid = [&](int kb) { return kb >= 0 && kb < nkb && kb <= kb_limit; };
+  // this workgroup's range of table positions: all of them without splitting
+  const int lo = kSplit ? static_cast<int>((static_cast<int64_t>(nT) * split) / nsp) : 0;
+  const int hi = kSplit ? static_cast<int>((static_cast<int64_t>(nT) * (split + 1)) / nsp) : nT;
   auto next_valid = [&](int jj) {
-    while (jj < nT && !valid(Trow[jj])) ++jj;
+    while (jj < hi && !valid(Trow[jj])) ++jj;
     return jj;
   };
   auto kv_piece = [&](const float* base, int jj, int i) {
     const size_t off = kv_base + static_cast<size_t>(Trow[jj]) * kBlk * D;
     return reinterpret_cast<const float4*>(base + off)[tid + i * kThreadsF];
   };
-  int jn = next_valid(0);
-  if (jn < nT) {
+  int jn = next_valid(lo);
+  if (jn < hi) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       pk[i] = kv_piece(K, jn, i);
       pv[i] = kv_piece(V, jn, i);
     }
   }
-  while (jn < nT) {
+  while (jn < hi) {
     const int kb = Trow[jn];
     __syncthreads();  // previous block fully consumed
 #pragma unroll
@@ -130,7 +140,7 @@ __global__ __launch_bounds__(kThreadsF) void chunk_attn_f32_kernel(
       reinterpret_cast<float4*>(Vs)[tid + i * kThreadsF] = pv[i];
     }
     jn = next_valid(jn + 1);
-    if (jn < nT) {
+    if (jn < hi) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         pk[i] = kv_piece(K, jn, i);
@@ -170,10 +180,47 @@ __global__ __launch_bounds__(kThreadsF) void chunk_attn_f32_kernel(
   }
 
   if (!row_in) return;
+  if (kSplit) {  // partial results: acc (unnormalised), running max, denominator
+    if (!row_live) return;
+    const size_t prow = static_cast<size_t>(split) * p.rows_total + qrow;
+    for (int i = 0; i < SL; ++i) part_o[prow * D + part * SL + i] = acc[i];
+    if (part == 0) {
+      part_ml[2 * prow] = m;
+      part_ml[2 * prow + 1] = l;
+    }
+    return;
+  }
   const float inv = (row_live && l > 0.f) ? 1.f / l : 0.f;
   for (int i = 0; i < SL; ++i) O[qo + i] = row_live ? acc[i] * inv : 0.f;
   if (lse && part == 0)
     lse[qrow] = (row_live && l > 0.f) ? m * p.scale + __logf(l) : -INFINITY;
+}
+
+template <bool kSplit>
+hipError_t launch_f32(const float* Q, const float* K, const float* V, const int32_t* T,
+                      const int32_t* len, float* O, float* lse, int B, int D,
+                      const AttnParams& p, const SeqInfo& seq, float* part_o, float* part_ml,
+                      hipStream_t stream) {
+  // 16 threads per row (32-row tiles) when 64-row tiles would occupy fewer
+  // workgroups than the chip has CUs
+  const int nsp = kSplit ? p.n_split : 1;
+  const bool narrow = static_cast<int64_t>(B) * p.H_q * nsp * ((p.C_max + 63) / 64) < 256;
+  const int rows = narrow ? kThreadsF / 16 : kThreadsF / 8;
+  const int n_tiles = (p.C_max + rows - 1) / rows;
+  const dim3 grid(B * p.H_q * nsp * n_tiles), block(kThreadsF);
+  if (D == 128 && narrow)
+    hipLaunchKernelGGL((chunk_attn_f32_kernel<128, 16, kSplit>), grid, block, 0, stream, Q, K, V,
+                       T, len, O, lse, p, seq, n_tiles, part_o, part_ml);
+  else if (D == 128)
+    hipLaunchKernelGGL((chunk_attn_f32_kernel<128, 8, kSplit>), grid, block, 0, stream, Q, K, V,
+                       T, len, O, lse, p, seq, n_tiles, part_o, part_ml);
+  else if (narrow)
+    hipLaunchKernelGGL((chunk_attn_f32_kernel<64, 16, kSplit>), grid, block, 0, stream, Q, K, V,
+                       T, len, O, lse, p, seq, n_tiles, part_o, part_ml);
+  else
+    hipLaunchKernelGGL((chunk_attn_f32_kernel<64, 8, kSplit>), grid, block, 0, stream, Q, K, V,
+                       T, len, O, lse, p, seq, n_tiles, part_o, part_ml);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -182,25 +229,18 @@ hipError_t launch_chunk_attn_f32(const float* Q, const float* K, const float* V,
                                  const int32_t* T, const int32_t* len, float* O, float* lse,
                                  int B, int D, const AttnParams& p, const SeqInfo& seq,
                                  hipStream_t stream) {
-  // 16 threads per row (32-row tiles) when 64-row tiles would occupy fewer
-  // workgroups than the chip has CUs
-  const bool narrow = static_cast<int64_t>(B) * p.H_q * ((p.C_max + 63) / 64) < 256;
-  const int rows = narrow ? kThreadsF / 16 : kThreadsF / 8;
-  const int n_tiles = (p.C_max + rows - 1) / rows;
-  const dim3 grid(B * p.H_q * n_tiles), block(kThreadsF);
-  if (D == 128 && narrow)
-    hipLaunchKernelGGL((chunk_attn_f32_kernel<128, 16>), grid, block, 0, stream, Q, K, V, T, len,
-                       O, lse, p, seq, n_tiles);
-  else if (D == 128)
-    hipLaunchKernelGGL((chunk_attn_f32_kernel<128, 8>), grid, block, 0, stream, Q, K, V, T, len,
-                       O, lse, p, seq, n_tiles);
-  else if (narrow)
-    hipLaunchKernelGGL((chunk_attn_f32_kernel<64, 16>), grid, block, 0, stream, Q, K, V, T, len,
-                       O, lse, p, seq, n_tiles);
-  else
-    hipLaunchKernelGGL((chunk_attn_f32_kernel<64, 8>), grid, block, 0, stream, Q, K, V, T, len,
-                       O, lse, p, seq, n_tiles);
-  return hipGetLastError();
+  return launch_f32<false>(Q, K, V, T, len, O, lse, B, D, p, seq, nullptr, nullptr, stream);
+}
+
+hipError_t launch_chunk_attn_f32_split(const float* Q, const float* K, const float* V,
+                                       const int32_t* T, const int32_t* len, float* O,
+                                       float* lse, int B, int D, const AttnParams& p,
+                                       const SeqInfo& seq, float* part_o, float* part_ml,
+                                       hipStream_t stream) {
+  const hipError_t e =
+      launch_f32<true>(Q, K, V, T, len, O, lse, B, D, p, seq, part_o, part_ml, stream);
+  if (e != hipSuccess) return e;
+  return launch_split_combine(part_o, part_ml, D, true, O, lse, p, seq, stream);
 }
 
 }  // namespace ca

@@ -78,6 +78,18 @@ hipError_t launch_chunk_attn_f32(const float* Q, const float* K, const float* V,
                                  const int32_t* T, const int32_t* len, float* O, float* lse,
                                  int B, int D, const AttnParams& p, const SeqInfo& seq,
                                  hipStream_t stream);
+// fp32 split-KV: partials of p.n_split table ranges, then the merge.
+hipError_t launch_chunk_attn_f32_split(const float* Q, const float* K, const float* V,
+                                       const int32_t* T, const int32_t* len, float* O,
+                                       float* lse, int B, int D, const AttnParams& p,
+                                       const SeqInfo& seq, float* part_o, float* part_ml,
+                                       hipStream_t stream);
+// Merge of split-KV partials (part_o unnormalised fp32 [n_split, rows, D],
+// part_ml (running max, denominator) per row) into O (bf16, or fp32 when
+// f32_out) and lse.
+hipError_t launch_split_combine(const float* part_o, const float* part_ml, int D, bool f32_out,
+                                void* O, float* lse, const AttnParams& p, const SeqInfo& seq,
+                                hipStream_t stream);
 
 // Explicit KV compaction (baseline); esz = element size in bytes.
 hipError_t launch_compact_kv(const void* K, const void* V, const int32_t* T, const int32_t* len,

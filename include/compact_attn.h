@@ -160,7 +160,7 @@ CA_EXPORT ca_status ca_chunk_attention(const void* Q, const void* K_cache, const
  * workspace  device memory owned by the caller, 16-byte aligned, at least
  *            ca_chunk_attention_workspace_size(B, H_q, C_max, D, n_splits)
  *            bytes (else CA_ERR_SHAPE); NULL only when n_splits == 1.
- * dtype      CA_BF16 when n_splits > 1 (CA_F32: CA_ERR_UNSUPPORTED).
+ * dtype      CA_BF16 or CA_F32; the partials and the merge are fp32 for both.
  * Other arguments, layouts and errors as for ca_chunk_attention.  Calls that
  * share one workspace must be ordered on one stream.
  */

@@ -88,6 +88,12 @@ int main() {
     EXPECT(ca_chunk_attention_split(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE,
                                     200, prior, chunk, 3, 32, 8, 256, 8448, 128, 64, 0.125f,
                                     CA_BF16, 4, FAKE, need - 1, FAKE, nullptr, 0) == CA_ERR_SHAPE);
+    EXPECT(ca_chunk_attention_split(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE,
+                                    200, prior, chunk, 3, 32, 8, 256, 8448, 128, 64, 0.125f,
+                                    CA_F32, 4, FAKE, need, FAKE, nullptr, 0) == CA_OK);
+    EXPECT(strcmp(stub::last.what, "attn_f32_split") == 0 && stub::last.p.n_split == 4);
+    EXPECT((char*)stub::last.ptrs[1] - (char*)stub::last.ptrs[0] ==
+           (ptrdiff_t)(4LL * 3 * 32 * 256 * 128 * 4));
     // per-(head, Q-block) lists
     EXPECT(ca_chunk_attention_rows(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE,
                                    4, 200, prior, chunk, 3, 32, 8, 256, 8448, 128, 64, 0.125f,

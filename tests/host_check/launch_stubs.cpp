@@ -78,6 +78,16 @@ hipError_t launch_chunk_attn_f32(const float*, const float*, const float*, const
   return hipSuccess;
 }
 
+hipError_t launch_chunk_attn_f32_split(const float*, const float*, const float*, const int32_t*,
+                                       const int32_t*, float*, float*, int B, int D,
+                                       const AttnParams& p, const SeqInfo& seq, float* part_o,
+                                       float* part_ml, hipStream_t) {
+  record_attn("attn_f32_split", B, D, p, seq);
+  stub::last.ptrs[0] = part_o;
+  stub::last.ptrs[1] = part_ml;
+  return hipSuccess;
+}
+
 hipError_t launch_compact_kv(const void*, const void*, const int32_t*, const int32_t*, int NKB_max,
                              int B, int H_kv, int64_t L, int D, int esz, const SeqInfo& seq,
                              void*, void*, int32_t*, hipStream_t) {

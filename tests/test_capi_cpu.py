@@ -159,9 +159,10 @@ def test_split_validation_and_workspace_size():
     base = (FAKE, FAKE, FAKE, FAKE, FAKE, 20, _ints(1024), _ints(256), 1, 4, 1, 256, 1280, 64, 64,
             0.125)
     need = lib.ca_chunk_attention_workspace_size(1, 4, 256, 64, 4)
-    # too many splits, fp32 split, no workspace, short workspace, unaligned workspace
+    # too many splits, fp32 split with a short workspace, no workspace, short workspace,
+    # unaligned workspace
     assert lib.ca_chunk_attention_split(*base, 1, 17, FAKE, need, FAKE, None, None) == 2
-    assert lib.ca_chunk_attention_split(*base, 0, 4, FAKE, need, FAKE, None, None) == 4
+    assert lib.ca_chunk_attention_split(*base, 0, 4, FAKE, need - 1, FAKE, None, None) == 2
     assert lib.ca_chunk_attention_split(*base, 1, 4, None, need, FAKE, None, None) == 1
     assert lib.ca_chunk_attention_split(*base, 1, 4, FAKE, need - 1, FAKE, None, None) == 2
     assert lib.ca_chunk_attention_split(*base, 1, 4, FAKE + 4, need, FAKE, None, None) == 4

@@ -12,8 +12,8 @@ import torch
 
 import gen
 import chunked_prefill_sparse_amd as ca
-from tests.gpu_util import (LSE_ABS, Dev, compare_bf16, f32_arrays, oracle_full, oracle_rows,
-                            sample_rows, say, to_np)
+from tests.gpu_util import (F32_MAX_ABS, LSE_ABS, Dev, compare_bf16, f32_arrays, oracle_full,
+                            oracle_rows, sample_rows, say, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +56,36 @@ def test_split_small_full_parity(B, H_q, H_kv, D, prior, chunk, C_max, n):
     np.testing.assert_allclose(gl[fin], lr[fin], rtol=0, atol=LSE_ABS)
     # the same admissible keys as the unsplit kernel: only merge rounding differs
     assert float((O.float() - O1.float()).abs().max()) <= 2e-2
+    for b in range(B):
+        assert bool((O[b, :, chunk[b]:] == 0).all())
+
+
+SMALL_F32 = [
+    # B, H_q, H_kv, D, prior, chunk, C_max, n_splits
+    (1, 4, 1, 64, [1024], [256], 256, 8),           # the tiny fp32 shape
+    (1, 4, 1, 64, [1024], [256], 256, 16),          # ranges with no block
+    (2, 4, 2, 128, [512, 1024], [192, 128], 200, 3),
+    (3, 2, 1, 64, [0, 64, 4096], [128, 64, 256], 256, 2),
+]
+
+
+@pytest.mark.parametrize("B,H_q,H_kv,D,prior,chunk,C_max,n", SMALL_F32)
+def test_split_f32_small_full_parity(B, H_q, H_kv, D, prior, chunk, C_max, n):
+    w = gen.make_custom(B, H_q, H_kv, D, prior, chunk, "f32", 950 + n + D, _bern(0.3),
+                        C_max=C_max, name="split_f32")
+    say(f"split f32 B={B} H={H_q}/{H_kv} D={D} prior={prior} chunk={chunk} n={n}")
+    d = Dev(w)
+    T, lens = d.tables()
+    O, lse = _split(d, T, lens, n)
+    O1 = d.attention(T, lens)
+    torch.cuda.synchronize()
+    Or, lr = oracle_full(w)
+    assert np.abs(to_np(O) - Or).max() <= F32_MAX_ABS
+    fin = np.isfinite(lr)
+    gl = lse.cpu().numpy()
+    assert (np.isfinite(gl) == fin).all()
+    np.testing.assert_allclose(gl[fin], lr[fin], rtol=0, atol=1e-5)
+    assert float((O - O1).abs().max()) <= F32_MAX_ABS
     for b in range(B):
         assert bool((O[b, :, chunk[b]:] == 0).all())
 
