@@ -1,12 +1,14 @@
 // C ABI of the CompactAttention chunked-prefill path: host-side validation,
 // scheduling metadata and kernel launches.  The library allocates nothing and
-// keeps no state beyond a per-thread copy of the last HIP error text.
+// keeps no state beyond a per-thread copy of the last HIP error text and a
+// per-device cache of the compute-unit count.
 
 #include <math.h>
 #include <stdio.h>
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <numeric>
 
 #include "kernels.hpp"
@@ -25,7 +27,23 @@ ca_status hip_status(hipError_t e) {
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 constexpr int kMaxUnionBlocks = 1 << 19;  // NKB_max bound: bitmap fits 64 KiB of LDS
-constexpr int64_t kCUs = 256;             // compute units of an MI355X
+constexpr int kCUs = 256;                 // compute units of a whole MI355X
+
+// Compute units of the current device, queried once per device (a
+// partitioned MI355X exposes fewer); the full chip's count if the query fails.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kCUs;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = kCUs;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 }  // namespace
 
@@ -151,6 +169,7 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
   p.NQ_max = row_tables ? NQ_max : 0;
   p.n_split = n_split;
   p.rows_total = static_cast<int64_t>(B) * H_q * C_max;
+  p.cus = device_cus();
   const int64_t n_bg = static_cast<int64_t>(B) * H_kv;
   if (dtype == CA_BF16) {
     // the bf16 kernels address one (b, g) cache slice through a buffer
@@ -161,7 +180,7 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
     // that still gives every CU a workgroup, else 4 (and 4 with split-KV); or
     // one 64-row Q-block of one head with per-Q-block tables
     const int64_t n_t8 = (p.G * n_pb + 7) / 8;
-    p.waves = (n_split == 1 && n_bg * n_t8 >= kCUs) ? 8 : 4;
+    p.waves = (n_split == 1 && n_bg * n_t8 >= p.cus) ? 8 : 4;
     p.n_t = row_tables ? static_cast<int>(p.G * ((C_max + 63) / 64))
                        : static_cast<int>((p.G * n_pb + p.waves - 1) / p.waves);
     p.xcd = (n_bg % 8 == 0) ? 1 : 0;

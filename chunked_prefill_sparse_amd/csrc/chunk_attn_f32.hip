@@ -202,9 +202,9 @@ hipError_t launch_f32(const float* Q, const float* K, const float* V, const int3
                       const AttnParams& p, const SeqInfo& seq, float* part_o, float* part_ml,
                       hipStream_t stream) {
   // 16 threads per row (32-row tiles) when 64-row tiles would occupy fewer
-  // workgroups than the chip has CUs
+  // workgroups than the device has CUs
   const int nsp = kSplit ? p.n_split : 1;
-  const bool narrow = static_cast<int64_t>(B) * p.H_q * nsp * ((p.C_max + 63) / 64) < 256;
+  const bool narrow = static_cast<int64_t>(B) * p.H_q * nsp * ((p.C_max + 63) / 64) < p.cus;
   const int rows = narrow ? kThreadsF / 16 : kThreadsF / 8;
   const int n_tiles = (p.C_max + rows - 1) / rows;
   const dim3 grid(B * p.H_q * nsp * n_tiles), block(kThreadsF);

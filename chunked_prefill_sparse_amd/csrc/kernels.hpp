@@ -44,6 +44,7 @@ struct AttnParams {
   int waves;            // bf16 union tables: waves per workgroup (4 or 8)
   int n_split;          // split-KV: table ranges per (b, g) (1: no split)
   int64_t rows_total;   // B * H_q * C_max (split-KV partial layout)
+  int cus;              // compute units of the device (launch shape choices only)
 };
 
 hipError_t launch_union_tables(const uint8_t* mask, int B, int H_q, int H_kv, int NQ_max,
