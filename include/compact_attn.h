@@ -198,7 +198,7 @@ CA_EXPORT size_t ca_chunk_attention_workspace_size(int B, int H_q, int C_max, in
  * NQ_max      Q-blocks per head in T_rows; 64 * NQ_max >= C_max (else CA_ERR_SHAPE).
  * Other arguments, layouts and errors as for ca_chunk_attention.  A workgroup
  * of the bf16 path holds one Q-block of one head (64 query rows per KV tile
- * staged, against 128 in ca_chunk_attention).
+ * staged, against up to 256 in ca_chunk_attention).
  */
 CA_EXPORT ca_status ca_chunk_attention_rows(const void* Q, const void* K_cache,
                                   const void* V_cache, const int32_t* T_rows,
