@@ -70,3 +70,26 @@ def test_compact_full_size_32k():
     w = gen.make_workload("llama8b_32k")
     say("compact llama8b_32k")
     _check(w)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_compact_fuzz(seed):
+    # seeded random batch, heads, head dim, element type, ragged prior / chunk
+    # lengths (zero included), padding and mask density
+    rng = np.random.default_rng(50_000 + seed)
+    H_kv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4]))
+    B = int(rng.integers(1, 5))
+    D = int(rng.choice([64, 128]))
+    dtype = "bf16" if rng.random() < 0.6 else "f32"
+    prior = [64 * int(rng.integers(0, 40)) for _ in range(B)]
+    chunk = [64 * int(rng.integers(0, 5)) for _ in range(B)]
+    if max(chunk) == 0:
+        chunk[0] = 64
+    C_max = max(chunk) + 64 * int(rng.integers(0, 2))
+    p = float(rng.choice([0.0, 0.1, 0.5, 1.0]))
+    w = gen.make_custom(B, G * H_kv, H_kv, D, prior, chunk, dtype, 60_000 + seed, _bern(p),
+                        C_max=C_max, name=f"compact_fuzz{seed}")
+    say(f"compact fuzz {seed}: B={B} H={G * H_kv}/{H_kv} D={D} {dtype} prior={prior} "
+        f"chunk={chunk} p={p}")
+    _check(w)

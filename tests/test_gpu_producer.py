@@ -120,3 +120,28 @@ def test_producer_full_size_128k():
     m = _check(w, budget=64, local=8)
     assert (m[0, :, :, 1:2016 - 8].sum(axis=2) >= 0).all()
     assert (m[0, :, :, 1:2016 - 8].sum(axis=-1) == 64).all()
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_producer_fuzz(seed):
+    # seeded random batch, heads, group size, head dim, element type, ragged
+    # prior / chunk lengths (zero included), padding, budget and local window
+    rng = np.random.default_rng(30_000 + seed)
+    H_kv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.integers(1, 5))
+    D = int(rng.choice([64, 128]))
+    dtype = "bf16" if rng.random() < 0.6 else "f32"
+    prior = [64 * int(rng.integers(0, 80)) for _ in range(B)]
+    chunk = [64 * int(rng.integers(0, 6)) for _ in range(B)]
+    if max(chunk) == 0:
+        chunk[0] = 64
+    C_max = max(chunk) + 64 * int(rng.integers(0, 2))
+    budget = int(rng.choice([0, 1, 5, 16, 100]))
+    local = int(rng.choice([0, 1, 3, 8]))
+    w = gen.make_custom(B, G * H_kv, H_kv, D, prior, chunk, dtype, 40_000 + seed,
+                        lambda r, b, H, nq, pb: np.zeros((H, nq, pb), np.uint8), C_max=C_max,
+                        name=f"producer_fuzz{seed}")
+    say(f"producer fuzz {seed}: B={B} H={G * H_kv}/{H_kv} D={D} {dtype} prior={prior} "
+        f"chunk={chunk} C_max={C_max} budget={budget} local={local}")
+    _check(w, budget, local)
