@@ -313,6 +313,28 @@ def test_bf16_running_max_moves(D, growth):
     np.testing.assert_allclose(to_np(lse)[live], lr[live], rtol=0, atol=LSE_ABS)
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_bf16_logit_spikes(D):
+    # A few blocks with keys scaled by 300 (logits far past the fp32 range of an
+    # exponential taken against the earlier running max) and some by 20, in the
+    # middle of the tables: the running max jumps by hundreds of log2 units at
+    # once, and by a few units elsewhere.
+    w = gen.make_custom(2, 8, 2, D, [2048, 1024], [192, 128], "bf16", 47, _bern(0.6),
+                        C_max=192)
+    n_blk = w.L // 64
+    scale = torch.ones(n_blk)
+    scale[[5, 17, 26]] = 300.0
+    scale[[3, 9, 12, 21]] = 20.0
+    w.k.copy_((w.k.float().view(w.B, w.H_kv, n_blk, 64, D) * scale.view(1, 1, n_blk, 1, 1))
+              .view_as(w.k).to(torch.bfloat16))
+    say(f"logit spikes: D={D}")
+    _, _, _, (O, lse) = _run(w)
+    Or, lr = oracle_full(w)
+    compare_bf16(to_np(O), Or, "O")
+    live = np.isfinite(lr)
+    np.testing.assert_allclose(to_np(lse)[live], lr[live], rtol=0, atol=LSE_ABS)
+
+
 def test_bf16_junk_table_entries_are_skipped():
     # Entries outside [0, n_kv_blocks) anywhere in T, and len past NKB_max, are never
     # dereferenced: the output equals the run on the clean table bit for bit.
