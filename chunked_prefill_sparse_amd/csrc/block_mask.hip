@@ -37,6 +37,7 @@ __global__ __launch_bounds__(kMaskThreads) void pool_blocks_kernel(const TIn* __
   constexpr int V = 16 / static_cast<int>(sizeof(TIn));  // elements per 16-byte load
   constexpr int TPR = D / V;                              // threads per row
   constexpr int RPI = kMaskThreads / TPR;                 // rows per iteration
+  static_assert(64 % RPI == 0, "rows of a block split evenly over the row groups");
   __shared__ float part[RPI * D];
   const int bh = blockIdx.x;
   const int b = bh / H;
@@ -46,12 +47,18 @@ __global__ __launch_bounds__(kMaskThreads) void pool_blocks_kernel(const TIn* __
   const int col = (tid % TPR) * V;
   const int rsub = tid / TPR;
   const TIn* src = X + (static_cast<size_t>(bh) * R + static_cast<size_t>(kb) * 64) * D + col;
+  // all of this thread's row loads in flight before the sums (in row order)
+  constexpr int NR = 64 / RPI;
+  uint4 raw[NR];
+#pragma unroll
+  for (int k = 0; k < NR; ++k)
+    raw[k] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(rsub + k * RPI) * D);
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
-  for (int r = rsub; r < 64; r += RPI) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(r) * D);
-    const TIn* e = reinterpret_cast<const TIn*>(&raw);
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    const TIn* e = reinterpret_cast<const TIn*>(&raw[k]);
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] += static_cast<float>(e[i]);
   }

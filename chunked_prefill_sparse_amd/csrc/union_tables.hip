@@ -76,12 +76,28 @@ __global__ __launch_bounds__(kUnionThreads) void union_tables_kernel(
       const int rg = item / nchunks;
       uint32_t bits = 0;
       if constexpr (VW == 16) {
-        uint4 acc = make_uint4(0u, 0u, 0u, 0u);
-        for (int r = rg; r < rows; r += rgroups) {
+        auto slice = [&](int r) {  // 16 bytes of mask row r (head hg of the group, Q-block qb)
           const int hg = r / nq;
           const int qb = r - hg * nq;
           const uint8_t* row = mask + ((head0 + hg) * NQ_max + qb) * static_cast<size_t>(NKB_max);
-          const uint4 x = *reinterpret_cast<const uint4*>(row + static_cast<size_t>(ch) * 16);
+          return *reinterpret_cast<const uint4*>(row + static_cast<size_t>(ch) * 16);
+        };
+        uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+        // eight rows' loads in flight before any is combined: the reduction is
+        // bound by memory latency, not bandwidth, at these sizes
+        constexpr int kBatch = 8;
+        int r = rg;
+        for (; r + (kBatch - 1) * rgroups < rows; r += kBatch * rgroups) {
+          uint4 x[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) x[u] = slice(r + u * rgroups);
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            acc.x |= x[u].x; acc.y |= x[u].y; acc.z |= x[u].z; acc.w |= x[u].w;
+          }
+        }
+        for (; r < rows; r += rgroups) {
+          const uint4 x = slice(r);
           acc.x |= x.x; acc.y |= x.y; acc.z |= x.z; acc.w |= x.w;
         }
         bits = nonzero_bytes4(acc.x) | (nonzero_bytes4(acc.y) << 4) |
