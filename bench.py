@@ -228,13 +228,21 @@ def tp_shard_leg(stream, reps):
             ms = statistics.median(time_calls(fn, reps, stream))
             res[n] = ms
         best = min(res, key=res.get)
+        bws = torch.empty(ca.balanced_workspace_size(1, 4, 1, 2048, 128), dtype=torch.uint8,
+                          device=q.device)
+        fb = lambda: ca.chunk_attention(q, k, v, T, lens, w.prior, w.chunk, w.scale, out=o,  # noqa: E731
+                                        balanced=True, workspace=bws)
+        fb()
+        bal = statistics.median(time_calls(fb, reps, stream))
         out[variant] = dict(
             ms_by_splits={str(n_): round(t_, 4) for n_, t_ in res.items()},
             eff_tflops_no_split=round(flops / (res[1] * 1e-3) / 1e12, 1),
-            best_splits=best, eff_tflops_best=round(flops / (res[best] * 1e-3) / 1e12, 1))
+            best_splits=best, eff_tflops_best=round(flops / (res[best] * 1e-3) / 1e12, 1),
+            balanced_ms=round(bal, 4), eff_tflops_balanced=round(flops / (bal * 1e-3) / 1e12, 1))
         log(f"tp_shard_128k {variant}: no split {res[1]:.3f} ms "
             f"({out[variant]['eff_tflops_no_split']:.0f} TFLOP/s), best n={best} "
-            f"{res[best]:.3f} ms ({out[variant]['eff_tflops_best']:.0f} TFLOP/s)")
+            f"{res[best]:.3f} ms ({out[variant]['eff_tflops_best']:.0f} TFLOP/s), balanced "
+            f"{bal:.3f} ms ({out[variant]['eff_tflops_balanced']:.0f} TFLOP/s)")
         del q, k, v, mask, T, lens, o
     torch.cuda.empty_cache()
     return out
@@ -246,8 +254,9 @@ def tp_shard_leg(stream, reps):
 def prefill_leg(stream, budget=32, local=8):
     """A 128K prompt in 64 chunks of 2048 (planted-structure synthetic stream):
     per chunk, pool the new key blocks and the queries, make the top-k block
-    mask, build the union tables and run zero-copy attention; the dense
-    baseline runs the same attention over every block.  Cumulative times from
+    mask, build the union tables and run zero-copy attention (also timed with
+    balanced attention, for reference); the dense baseline runs the same
+    attention over every block.  Cumulative times from
     HIP events on the launch stream, for the Python loop of calls and for the
     same calls recorded into HIP graphs and replayed."""
     import torch
@@ -257,7 +266,8 @@ def prefill_leg(stream, budget=32, local=8):
     s = gen.make_prefill_stream("prefill_128k")
     k, v = s.k.cuda(), s.v.cuda()
     qs = [s.q_chunk(c).cuda() for c in range(s.n_chunks)]
-    drv = ChunkedPrefill(k, v, s.H_q, s.C, budget=budget, local=local)
+    drv = ChunkedPrefill(k, v, s.H_q, s.C, budget=budget, local=local, balanced=False)
+    drv_bal = ChunkedPrefill(k, v, s.H_q, s.C, budget=budget, local=local, balanced=True)
     dense_lens = [drv.dense_lens(c * s.C) for c in range(s.n_chunks)]
     torch.cuda.synchronize()
     # untimed pass: work accounting per chunk
@@ -300,6 +310,12 @@ def prefill_leg(stream, budget=32, local=8):
     select_ms = statistics.median(timed(run_select) for _ in range(reps))
     dense_ms = statistics.median(timed(run_dense) for _ in range(reps))
     attn_ms = sparse_ms - select_ms
+    def run_balanced():  # the same loop with balanced attention, for reference
+        for c in range(s.n_chunks):
+            drv_bal.step(qs[c], c * s.C)
+
+    run_balanced()
+    bal_ms = statistics.median(timed(run_balanced) for _ in range(reps))
     # the same call sequences recorded once into HIP graphs and replayed: the
     # GPU time without the per-call host work of the loop above
     priors = [c * s.C for c in range(s.n_chunks)]
@@ -321,6 +337,9 @@ def prefill_leg(stream, budget=32, local=8):
         work_frac_of_dense=round(flops / flops_dense, 4),
         union_block_frac_first_mid_last=[round(frac[0], 3), round(frac[len(frac) // 2], 3),
                                          round(frac[-1], 3)],
+        balanced=dict(total_ms=round(bal_ms, 3), attention_ms=round(bal_ms - select_ms, 3),
+                      x_vs_dense=round(dense_ms / bal_ms, 3),
+                      attention_eff_tflops=round(flops / ((bal_ms - select_ms) * 1e-3) / 1e12, 1)),
         graph=dict(total_ms=round(gs_ms, 3), select_ms=round(gsel_ms, 3),
                    attention_ms=round(gs_ms - gsel_ms, 3), dense_attention_ms=round(gd_ms, 3),
                    x_vs_dense=round(gd_ms / gs_ms, 3)),
@@ -330,9 +349,11 @@ def prefill_leg(stream, budget=32, local=8):
     log(f"prefill_128k: total {sparse_ms:.2f} ms (select {select_ms:.2f}, attention "
         f"{attn_ms:.2f}) vs dense attention {dense_ms:.2f} ms -> x{dense_ms / sparse_ms:.2f}; "
         f"union fraction first/mid/last {r['union_block_frac_first_mid_last']}")
+    log(f"prefill_128k with balanced attention: total {bal_ms:.2f} ms (attention "
+        f"{bal_ms - select_ms:.2f}) -> x{dense_ms / bal_ms:.2f}")
     log(f"prefill_128k as HIP graphs: total {gs_ms:.2f} ms (select {gsel_ms:.2f}) vs dense "
         f"{gd_ms:.2f} ms -> x{gd_ms / gs_ms:.2f}")
-    del qs, k, v, drv, g_sparse, g_select, g_dense
+    del qs, k, v, drv, drv_bal, g_sparse, g_select, g_dense
     torch.cuda.empty_cache()
     return r
 
@@ -438,6 +459,13 @@ def main():
     def attn(T, lens):
         return ca.chunk_attention(q, k, v, T, lens, w.prior, w.chunk, w.scale, out=out)
 
+    bal_ws = torch.empty(ca.balanced_workspace_size(w.B, w.H_q, w.H_kv, w.C_max, w.D),
+                         dtype=torch.uint8, device=dev)
+
+    def attn_balanced(T, lens):
+        return ca.chunk_attention(q, k, v, T, lens, w.prior, w.chunk, w.scale, out=out,
+                                  balanced=True, workspace=bal_ws)
+
     if args.profile in ("attn", "union", "compact"):
         T, lens = tables("pairwise")
         if args.profile == "compact":
@@ -474,6 +502,7 @@ def main():
         torch.cuda.synchronize()
         ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
         attn_ms = time_calls(lambda: attn(T, lens), args.reps, stream)
+        attn_bal_ms = time_calls(lambda: attn_balanced(T, lens), args.reps, stream)
         union_ms = time_calls(lambda: tables(name), args.reps, stream)
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         cold_ms = time_calls_cold(lambda: attn(T, lens), max(args.reps // 5, 5), stream, scratch)
@@ -490,12 +519,15 @@ def main():
             flops=flops, bytes_alg=bytes_alg, pairs=pairs,
             eff_tflops_step=flops / (ms_step * 1e-3) / 1e12,
             eff_tflops_attn=flops / (a_med * 1e-3) / 1e12,
+            attn_balanced_ms_median=statistics.median(attn_bal_ms),
+            eff_tflops_attn_balanced=flops / (statistics.median(attn_bal_ms) * 1e-3) / 1e12,
             mfma_frac_attn=flops / (a_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             union_blocks_sum=int(lh.sum()), union_blocks_mean=float(lh.mean()),
             per_head_qunion_blocks_mean=per_head_union,
         )
         log(f"{name}: step {ms_step:.3f} ms, attention {a_med:.3f} ms "
-            f"({results[name]['eff_tflops_attn']:.0f} TFLOP/s), union "
+            f"({results[name]['eff_tflops_attn']:.0f} TFLOP/s), balanced "
+            f"{results[name]['attn_balanced_ms_median']:.3f} ms, union "
             f"{results[name]['union_us_median']:.1f} us, mean len {lh.mean():.0f}")
     # Explicit-compaction baseline: gather the selected blocks, then run the same
     # kernel on the compact buffer; zero-copy execution skips the gather.
@@ -569,7 +601,7 @@ def main():
     achieved = main_r["flops"] / (main_r["attn_ms_mean"] * 1e-3) / 1e12
     roofline = {
         "bound": "mfma",
-        "kernel": "chunk_attn_bf16_kernel<128, 8, false, false>",
+        "kernel": "chunk_attn_bf16_kernel<128, 8, false, 0>",
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",

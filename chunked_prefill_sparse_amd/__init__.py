@@ -24,7 +24,7 @@ from ._lib import CA_BLOCK, CA_MAX_BATCH, CompactAttnError  # noqa: F401
 __all__ = ["build_union_tables", "chunk_attention", "tables_to_csr", "check_tables",
            "compact_kv",
            "build_row_tables", "chunk_attention_rows", "pool_blocks", "block_mask_topk",
-           "workspace_size",
+           "workspace_size", "balanced_workspace_size",
            "CompactAttnError", "library_path"]
 
 
@@ -187,12 +187,18 @@ def workspace_size(B: int, H_q: int, C_max: int, D: int, n_splits: int) -> int:
     return int(_lib.lib().ca_chunk_attention_workspace_size(B, H_q, C_max, D, n_splits))
 
 
+def balanced_workspace_size(B: int, H_q: int, H_kv: int, C_max: int, D: int) -> int:
+    """Bytes of workspace ``chunk_attention(..., balanced=True)`` needs."""
+    return int(_lib.lib().ca_chunk_attention_balanced_workspace_size(B, H_q, H_kv, C_max, D))
+
+
 def chunk_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                     T: torch.Tensor, lens: torch.Tensor, prior_len: Sequence[int],
                     chunk_len: Sequence[int], scale: Optional[float] = None,
                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                     return_lse: bool = False, stream: Optional[torch.cuda.Stream] = None,
-                    n_splits: int = 1, workspace: Optional[torch.Tensor] = None):
+                    n_splits: int = 1, workspace: Optional[torch.Tensor] = None,
+                    balanced: bool = False):
     """Zero-copy paged chunk attention.
 
     q [B, H_q, C_max, D] and k_cache/v_cache [B, H_kv, L, D] (bf16 or fp32, device);
@@ -201,6 +207,9 @@ def chunk_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     ``n_splits`` > 1 (bf16 or fp32) cuts each table into that many ranges run by separate
     workgroups and merged (``ca_chunk_attention_split``); ``workspace`` is then a
     device tensor of at least ``workspace_size(...)`` bytes (allocated if None).
+    ``balanced`` plans the work on the device so that uneven tables spread evenly over
+    the compute units (``ca_chunk_attention_balanced``); ``workspace`` is then at least
+    ``balanced_workspace_size(...)`` bytes (allocated if None).
     """
     _need_cuda("q", q)
     if q.dtype not in (torch.bfloat16, torch.float32):
@@ -232,6 +241,21 @@ def chunk_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
         if tuple(lse.shape) != (B, H_q, C_max):
             raise ValueError("lse must be [B, H_q, C_max]")
     dt = _lib.CA_BF16 if q.dtype == torch.bfloat16 else _lib.CA_F32
+    if balanced and n_splits > 1:
+        raise ValueError("balanced and n_splits > 1 are exclusive")
+    if balanced:
+        need = balanced_workspace_size(B, H_q, H_kv, C_max, D)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _need_cuda("workspace", workspace)
+        wbytes = workspace.numel() * workspace.element_size()
+        st = _lib.lib().ca_chunk_attention_balanced(
+            q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), T.data_ptr(), lens.data_ptr(),
+            NKB_max, _host_ints("prior_len", prior_len, B), _host_ints("chunk_len", chunk_len, B),
+            B, H_q, H_kv, C_max, L, D, CA_BLOCK, float(scale), dt, workspace.data_ptr(), wbytes,
+            out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream_ptr(stream))
+        _lib.check(st, "ca_chunk_attention_balanced")
+        return (out, lse) if return_lse else out
     if n_splits > 1:
         need = workspace_size(B, H_q, C_max, D, n_splits)
         if workspace is None:

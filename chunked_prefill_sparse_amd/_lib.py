@@ -24,6 +24,8 @@ EXPORTED = (
     "ca_chunk_attention_rows",
     "ca_chunk_attention_split",
     "ca_chunk_attention_workspace_size",
+    "ca_chunk_attention_balanced",
+    "ca_chunk_attention_balanced_workspace_size",
     "ca_tables_to_csr",
     "ca_check_tables",
     "ca_compact_kv",
@@ -60,6 +62,13 @@ def _declare(lib):
     lib.ca_chunk_attention_split.restype = _i32
     lib.ca_chunk_attention_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
     lib.ca_chunk_attention_workspace_size.restype = ctypes.c_size_t
+    lib.ca_chunk_attention_balanced.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32p, _i32p, _i32,
+                                                _i32, _i32, _i32, _i64, _i32, _i32,
+                                                ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp,
+                                                _vp, _vp]
+    lib.ca_chunk_attention_balanced.restype = _i32
+    lib.ca_chunk_attention_balanced_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
+    lib.ca_chunk_attention_balanced_workspace_size.restype = ctypes.c_size_t
     lib.ca_tables_to_csr.argtypes = [_vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _vp]
     lib.ca_tables_to_csr.restype = _i32
     lib.ca_check_tables.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]

@@ -120,13 +120,34 @@ CA_EXPORT ca_status ca_tables_to_csr(const int32_t* T, const int32_t* len, int B
 
 namespace {
 
+// Byte offsets of the balanced path's workspace parts (each 16-byte aligned)
+// and its total size: partial outputs and (max, denominator) pairs for up to
+// kMaxPieces pieces of every row, the plan (count, then one int4 per piece),
+// and the pieces per (b, g, tile).
+struct BalancedLayout {
+  size_t part_o, part_ml, plan, pieces, total;
+};
+BalancedLayout balanced_layout(int B, int H_q, int H_kv, int C_max, int D) {
+  auto up16 = [](size_t x) { return (x + 15) & ~static_cast<size_t>(15); };
+  const size_t rows = static_cast<size_t>(B) * H_q * C_max;
+  const size_t n_pb = (static_cast<size_t>(C_max) + 31) / 32;
+  const size_t n_units = static_cast<size_t>(B) * H_kv * (((H_q / H_kv) * n_pb + 7) / 8);
+  BalancedLayout l;
+  l.part_o = 0;
+  l.part_ml = up16(l.part_o + ca::kMaxPieces * rows * D * sizeof(float));
+  l.plan = up16(l.part_ml + ca::kMaxPieces * rows * 2 * sizeof(float));
+  l.pieces = up16(l.plan + (4 + 4 * (n_units + 2 * ca::kPlanMaxSlots)) * sizeof(int32_t));
+  l.total = up16(l.pieces + n_units * sizeof(int32_t));
+  return l;
+}
+
 // Shared by both table layouts: validation, sequence order, launch parameters.
 ca_status attention(const void* Q, const void* K_cache, const void* V_cache, const int32_t* T,
                     const int32_t* len, int NQ_max, int NKB_max, const int32_t* prior_len,
                     const int32_t* chunk_len, int B, int H_q, int H_kv, int C_max, int64_t L,
                     int D, int block, float scale, ca_dtype dtype, void* O, float* lse,
                     bool row_tables, int n_split, void* workspace, size_t workspace_bytes,
-                    hipStream_t stream) {
+                    hipStream_t stream, bool balanced = false) {
   if (!Q || !K_cache || !V_cache || !T || !len || !prior_len || !chunk_len || !O)
     return CA_ERR_NULL;
   if (dtype != CA_F32 && dtype != CA_BF16) return CA_ERR_DTYPE;
@@ -170,6 +191,8 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
   p.n_split = n_split;
   p.rows_total = static_cast<int64_t>(B) * H_q * C_max;
   p.cus = device_cus();
+  p.plan_items = nullptr;
+  p.plan_pieces = nullptr;
   const int64_t n_bg = static_cast<int64_t>(B) * H_kv;
   if (dtype == CA_BF16) {
     // the bf16 kernels address one (b, g) cache slice through a buffer
@@ -180,6 +203,25 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
     // that still gives every CU a workgroup, else 4 (and 4 with split-KV); or
     // one 64-row Q-block of one head with per-Q-block tables
     const int64_t n_t8 = (p.G * n_pb + 7) / 8;
+    if (balanced) {
+      p.waves = 8;
+      p.n_t = static_cast<int>(n_t8);
+      p.xcd = 0;
+      p.n_split = ca::kMaxPieces;
+      const BalancedLayout ws = balanced_layout(B, H_q, H_kv, C_max, D);
+      // planned-piece grid (tiles + 2 x slots), merge grid (8 x tiles), and
+      // the plan's 32-bit piece arithmetic
+      if (n_bg * n_t8 * 8 + 2 * ca::kPlanMaxSlots > INT32_MAX || NKB_max > ca::kPlanMaxBlocks)
+        return CA_ERR_SHAPE;
+      char* base = static_cast<char*>(workspace);
+      float* part_o = reinterpret_cast<float*>(base + ws.part_o);
+      float* part_ml = reinterpret_cast<float*>(base + ws.part_ml);
+      p.plan_items = reinterpret_cast<const int32_t*>(base + ws.plan);
+      p.plan_pieces = reinterpret_cast<const int32_t*>(base + ws.pieces);
+      return hip_status(ca::launch_chunk_attn_bf16_balanced(Q, K_cache, V_cache, T, len, O, lse,
+                                                            B, D, p, seq, part_o, part_ml,
+                                                            stream));
+    }
     p.waves = (n_split == 1 && n_bg * n_t8 >= p.cus) ? 8 : 4;
     p.n_t = row_tables ? static_cast<int>(p.G * ((C_max + 63) / 64))
                        : static_cast<int>((p.G * n_pb + p.waves - 1) / p.waves);
@@ -254,6 +296,34 @@ CA_EXPORT ca_status ca_chunk_attention_split(const void* Q, const void* K_cache,
   return attention(Q, K_cache, V_cache, T, len, 0, NKB_max, prior_len, chunk_len, B, H_q, H_kv,
                    C_max, L, D, block, scale, dtype, O, lse, false, n_splits, workspace,
                    workspace_bytes, stream);
+}
+
+CA_EXPORT size_t ca_chunk_attention_balanced_workspace_size(int B, int H_q, int H_kv, int C_max,
+                                                             int D) {
+  if (B < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || C_max < 1 || (D != 64 && D != 128))
+    return 0;
+  return balanced_layout(B, H_q, H_kv, C_max, D).total;
+}
+
+CA_EXPORT ca_status ca_chunk_attention_balanced(const void* Q, const void* K_cache,
+                                                const void* V_cache, const int32_t* T,
+                                                const int32_t* len, int NKB_max,
+                                                const int32_t* prior_len,
+                                                const int32_t* chunk_len, int B, int H_q,
+                                                int H_kv, int C_max, int64_t L, int D, int block,
+                                                float scale, ca_dtype dtype, void* workspace,
+                                                size_t workspace_bytes, void* O, float* lse,
+                                                hipStream_t stream) {
+  if (dtype == CA_F32)  // the fp32 path runs unplanned: the workspace is not used
+    return attention(Q, K_cache, V_cache, T, len, 0, NKB_max, prior_len, chunk_len, B, H_q,
+                     H_kv, C_max, L, D, block, scale, dtype, O, lse, false, 1, nullptr, 0, stream);
+  if (!workspace) return CA_ERR_NULL;
+  if (!aligned16(workspace)) return CA_ERR_UNSUPPORTED;
+  const size_t need = ca_chunk_attention_balanced_workspace_size(B, H_q, H_kv, C_max, D);
+  if (need > 0 && workspace_bytes < need) return CA_ERR_SHAPE;
+  return attention(Q, K_cache, V_cache, T, len, 0, NKB_max, prior_len, chunk_len, B, H_q, H_kv,
+                   C_max, L, D, block, scale, dtype, O, lse, false, 1, workspace, workspace_bytes,
+                   stream, true);
 }
 
 CA_EXPORT ca_status ca_chunk_attention_rows(const void* Q, const void* K_cache,

@@ -113,12 +113,15 @@ __device__ __forceinline__ void body_schedule() {
 // per CU, when 8 would leave CUs idle, and with kSplit).  kRows = true: one table per (b, h, Q-block), the
 // per-Q-block lists of a block-sparse kernel, so a workgroup is the 2 waves
 // (W = 2) of one 64-row Q-block of one head.
-// kSplit: the table of a (b, g) is cut into p.n_split contiguous ranges, one
-// per workgroup (the straddling blocks go to the last range), and each
+// kSplit = 1: the table of a (b, g) is cut into p.n_split contiguous ranges,
+// one per workgroup (the straddling blocks go to the last range), and each
 // workgroup writes its unnormalised partial output, running max and
 // denominator to part_o / part_ml for split_combine_kernel.  More workgroups
-// for shapes with few (b, g) pairs.
-template <int D, int W, bool kRows, bool kSplit>
+// for shapes with few (b, g) pairs.  kSplit = 2: workgroup w runs the piece
+// that a balance plan lists at p.plan_items[w] (sequence and group, tile,
+// piece k of n), cut the same way; pieces of an uncut tile (n = 1) write O
+// and lse themselves.
+template <int D, int W, bool kRows, int kSplit>
 __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const int32_t* __restrict__ T, const int32_t* __restrict__ len, __bf16* __restrict__ O,
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   constexpr bool kSpread = W >= 4;  // tile copies spread over the step body
   constexpr int kThreads = W * 64;
   static_assert(kRows ? W == 2 : (W == 4 || W == 8), "workgroup shape");
-  static_assert(!(kRows && kSplit), "split ranges are for union tables");
+  static_assert(!(kRows && kSplit != 0), "split ranges are for union tables");
   // LDS: two K tiles, two V tiles, then the compacted entry list (below) and
   // per-wave counts for building it.  One array: with the list in a separate
   // LDS object the compiler no longer proves that the tile reads stay clear of
@@ -151,25 +154,38 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
 
   // ---- workgroup -> (sequence, group, tile[, split])
   const int wg = blockIdx.x;
-  const int n_tt = kSplit ? p.n_t * p.n_split : p.n_t;  // workgroups per (b, g)
-  int u, t;
-  if (p.xcd) {
-    const int x = wg & 7, k = wg >> 3;
-    const int jj = k / n_tt;
-    u = x + 8 * jj;
-    t = k - jj * n_tt;
+  int b, g, t;
+  int split = 0, n_split = 1;  // this workgroup's range k of n of the tile's plain entries
+  if (kSplit == 2) {
+    if (wg >= p.plan_items[0]) return;  // past the plan's pieces (uniform)
+    const int4 it = reinterpret_cast<const int4*>(p.plan_items)[1 + wg];
+    b = it.x / p.H_kv;
+    g = it.x - b * p.H_kv;
+    t = it.y;
+    split = it.z;
+    n_split = it.w;
   } else {
-    u = wg / n_tt;
-    t = wg - u * n_tt;
+    const int n_tt = kSplit ? p.n_t * p.n_split : p.n_t;  // workgroups per (b, g)
+    int u;
+    if (p.xcd) {
+      const int x = wg & 7, k = wg >> 3;
+      const int jj = k / n_tt;
+      u = x + 8 * jj;
+      t = k - jj * n_tt;
+    } else {
+      u = wg / n_tt;
+      t = wg - u * n_tt;
+    }
+    if (kSplit) {
+      n_split = p.n_split;
+      split = t / p.n_t;
+      t -= split * p.n_t;
+    }
+    const int rank = u / p.H_kv;
+    g = u - rank * p.H_kv;
+    b = seq.order[rank];
   }
-  int split = 0;
-  if (kSplit) {
-    split = t / p.n_t;
-    t -= split * p.n_t;
-  }
-  const int rank = u / p.H_kv;
-  const int g = u - rank * p.H_kv;
-  const int b = seq.order[rank];
+  const bool partials = kSplit != 0 && n_split > 1;  // else O and lse written here
   const int P = seq.prior[b];
   const int C = seq.chunk[b];
   const int bg = b * p.H_kv + g;
@@ -324,9 +340,9 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   }
   const int n_all = use_list ? n_plain : e;
   // this workgroup's range of [0, n_all); all of it without splitting
-  const int e_lo = kSplit ? static_cast<int>((static_cast<int64_t>(n_all) * split) / p.n_split) : 0;
+  const int e_lo = static_cast<int>((static_cast<int64_t>(n_all) * split) / n_split);
   const int ee =
-      kSplit ? static_cast<int>((static_cast<int64_t>(n_all) * (split + 1)) / p.n_split) : n_all;
+      static_cast<int>((static_cast<int64_t>(n_all) * (split + 1)) / n_split);
   auto entry = [&](int jj) -> int {
     return use_list ? __builtin_amdgcn_readfirstlane(static_cast<int>(plist[jj])) : Trow[jj];
   };
@@ -438,7 +454,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
 
   // Blocks that straddle the workgroup's rows (usually one): one at a time,
   // with the causal mask.
-  for (int jt = e; jt < ((!kSplit || split == p.n_split - 1) ? nT : e); ++jt) {
+  for (int jt = e; jt < (split == n_split - 1 ? nT : e); ++jt) {
     const int kb = Trow[jt];
     if (!valid(kb)) continue;
     __syncthreads();  // every wave is done with the buffers
@@ -459,7 +475,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   const LaneHalves lh = lane_halves(ws.l_part);
   const float l_tot = lh.lo + lh.hi;
   if (!row_in) return;
-  if (kSplit) {  // partial results: acc (unnormalised), running max, denominator
+  if (partials) {  // partial results: acc (unnormalised), running max, denominator
     if (!row_live) return;
     const size_t prow = static_cast<size_t>(split) * p.rows_total + qo_row;
     float* po = part_o + prow * D;
@@ -512,25 +528,25 @@ hipError_t launch_chunk_attn_bf16(const void* Q, const void* K, const void* V,
   float* const no = nullptr;
   if (p.row_tables) {
     if (D == 128)
-      hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 2, true, false>), grid, dim3(128), 0, stream,
+      hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 2, true, 0>), grid, dim3(128), 0, stream,
                          q, k, v, T, len, o, lse, p, seq, no, no);
     else
-      hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 2, true, false>), grid, dim3(128), 0, stream,
+      hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 2, true, 0>), grid, dim3(128), 0, stream,
                          q, k, v, T, len, o, lse, p, seq, no, no);
   } else {
     if (p.waves == 8) {
       if (D == 128)
-        hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 8, false, false>), grid, dim3(512), 0,
+        hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 8, false, 0>), grid, dim3(512), 0,
                            stream, q, k, v, T, len, o, lse, p, seq, no, no);
       else
-        hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 8, false, false>), grid, dim3(512), 0,
+        hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 8, false, 0>), grid, dim3(512), 0,
                            stream, q, k, v, T, len, o, lse, p, seq, no, no);
     } else {
       if (D == 128)
-        hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 4, false, false>), grid, dim3(256), 0,
+        hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 4, false, 0>), grid, dim3(256), 0,
                            stream, q, k, v, T, len, o, lse, p, seq, no, no);
       else
-        hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 4, false, false>), grid, dim3(256), 0,
+        hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 4, false, 0>), grid, dim3(256), 0,
                            stream, q, k, v, T, len, o, lse, p, seq, no, no);
     }
   }
@@ -583,6 +599,198 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const float* __restr
   if (lse && lane == 0) lse[r] = l > 0.f ? M * p.scale + __logf(l) : -INFINITY;
 }
 
+// Balance plan for planned pieces of W-wave workgroups, in one workgroup.
+//   work(u, t): the table entries that tile t of pseudo-request u = b*H_kv + g
+//     walks, from len alone: the entries up to the last block any of its rows
+//     may see are all but the chunk's blocks above that block (a table that
+//     lacks some of those only makes the estimate high), 0 for a tile of
+//     padding rows only.
+//   When the longest walk is within 1/8 of the total work per compute unit,
+//     nothing is cut (those shapes already balance).  Otherwise walks longer
+//     than tau = max(3/4 of the work per compute unit, 16) are cut into
+//     min(kMaxPieces, ceil(work / tau)) pieces of even length (measured: tau
+//     at the full work per compute unit cut about as many tiles and balanced
+//     worse).
+//   Pieces are listed longest first (by size class), so the dispatcher, which
+//     hands workgroups to compute units in order as they free up, runs a
+//     greedy longest-first schedule.
+// The piece count is below n_units + 4/3 slots (tau >= 3/4 work / slots).
+// The order within a size class depends on atomics and changes no result: a
+// piece's work and its partial slot follow from (u, t, k) alone.  Each
+// tile's work is kept between the passes in LDS (up to kPlanCached tiles), or
+// else in pieces[] (each thread rereads what it wrote), which ends with the
+// piece counts.
+constexpr int kPlanThreads = 256;
+constexpr int kPlanCached = 8192;
+constexpr int kPlanClasses = 64;
+
+template <int W>
+__global__ __launch_bounds__(kPlanThreads) void balance_plan_kernel(
+    const int32_t* __restrict__ len, AttnParams p, SeqInfo seq,
+    int n_units, int slots, int32_t* __restrict__ plan, int32_t* __restrict__ pieces) {
+  __shared__ unsigned long long s_total;
+  __shared__ int s_max;
+  __shared__ int s_count[kPlanClasses];
+  __shared__ int s_cursor[kPlanClasses];
+  __shared__ int s_work[kPlanCached];
+  int* const wbuf = n_units <= kPlanCached ? s_work : pieces;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    s_total = 0ull;
+    s_max = 0;
+  }
+  if (tid < kPlanClasses) s_count[tid] = 0;
+  __syncthreads();
+  const int n_pb = (p.C_max + kRowsPerWave - 1) / kRowsPerWave;
+  auto work = [&](int unit) -> int {
+    const int u = unit / p.n_t;
+    const int t = unit - u * p.n_t;
+    const int b = u / p.H_kv;
+    const int P = seq.prior[b], C = seq.chunk[b];
+    if ((t * W) / p.G * kRowsPerWave >= C) return 0;
+    const int last_pb = min((t * W + W - 1) / p.G, n_pb - 1);
+    const int kb_limit = (P + min(C, (last_pb + 1) * kRowsPerWave) - 1) / kBlk;
+    const int nkb = (P + C + kBlk - 1) / kBlk;
+    // the chunk's own blocks are in the table (its causal block triangle is
+    // selected), so the entries past the tile's last visible block are the
+    // nkb - 1 - kb_limit chunk blocks above it
+    const int n = min(max(len[u], 0), p.NKB_max);
+    return max(n - (nkb - 1 - kb_limit), 0);
+  };
+  unsigned long long part = 0ull;
+  int wmax = 0;
+  for (int unit = tid; unit < n_units; unit += kPlanThreads) {
+    const int w = work(unit);
+    wbuf[unit] = w;
+    part += static_cast<unsigned long long>(w);
+    wmax = max(wmax, w);
+  }
+  for (int o = 32; o > 0; o >>= 1) {  // wave sums first: one LDS atomic per wave
+    part += __shfl_xor(part, o);
+    wmax = max(wmax, __shfl_xor(wmax, o));
+  }
+  if ((tid & 63) == 0) {
+    atomicAdd(&s_total, part);
+    atomicMax(&s_max, wmax);
+  }
+  __syncthreads();
+  const long long total = static_cast<long long>(s_total);
+  wmax = s_max;
+  const long long per_slot = (total + slots - 1) / slots;
+  // walks are at most NKB_max <= kPlanMaxBlocks entries, so the per-piece
+  // arithmetic below stays in 32 bits
+  const int tau = 8ll * wmax <= 9ll * per_slot
+                      ? INT_MAX
+                      : static_cast<int>(max((3ll * total + 4ll * slots - 1) / (4ll * slots), 16ll));
+  const int class_step = wmax / kPlanClasses + 1;
+  auto n_of = [&](int w) { return w > tau ? min(kMaxPieces, (w - 1) / tau + 1) : 1; };
+  auto size_class = [&](int w, int n, int k) {
+    const int sz = (w * (k + 1)) / n - (w * k) / n;
+    return min(kPlanClasses - 1, sz / class_step);
+  };
+  for (int unit = tid; unit < n_units; unit += kPlanThreads) {
+    const int w = wbuf[unit];
+    const int n = n_of(w);
+    for (int k = 0; k < n; ++k) atomicAdd(&s_count[size_class(w, n, k)], 1);
+  }
+  __syncthreads();
+  if (tid < 64) {  // longest class first: lane l takes class 63 - l; a scan over lanes
+    static_assert(kPlanClasses == 64, "one class per lane");
+    const int cnt = s_count[kPlanClasses - 1 - tid];
+    int inc = cnt;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (tid >= o) inc += y;
+    }
+    s_cursor[kPlanClasses - 1 - tid] = inc - cnt;
+    if (tid == 63) plan[0] = inc;
+  }
+  __syncthreads();
+  int4* items = reinterpret_cast<int4*>(plan) + 1;
+  for (int unit = tid; unit < n_units; unit += kPlanThreads) {
+    const int w = wbuf[unit];
+    const int n = n_of(w);
+    const int u = unit / p.n_t;
+    for (int k = 0; k < n; ++k) {
+      const int pos = atomicAdd(&s_cursor[size_class(w, n, k)], 1);
+      items[pos] = make_int4(u, unit - u * p.n_t, k, n);
+    }
+    pieces[unit] = n;
+  }
+}
+
+// Merge of the pieces of cut tiles: workgroup (tile (b, g, t), wave tile w)
+// holds the 32 rows that wave w of the tile's attention workgroup owns, one
+// row per wave at a time; a tile left whole returns at once (its workgroup
+// wrote O and lse).  With m_s, l_s, a_s the running max (raw score units),
+// denominator and unnormalised output of piece s, M = max_s m_s and
+// w_s = exp2((m_s - M) * scale * log2 e):
+//   O = sum_s w_s a_s / sum_s w_s l_s,   lse = M * scale + log(sum_s w_s l_s).
+// Every piece's loads of a row are issued before any is used.
+constexpr int kCombineThreads = 256;
+
+template <int D, int W>
+__global__ __launch_bounds__(kCombineThreads) void plan_combine_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, AttnParams p,
+    SeqInfo seq, __bf16* __restrict__ O, float* __restrict__ lse) {
+  constexpr int E = D / 64;  // elements per lane
+  const int unit = blockIdx.x / W;
+  const int n = p.plan_pieces[unit];
+  if (n <= 1) return;
+  const int u = unit / p.n_t;
+  const int t = unit - u * p.n_t;
+  const int b = u / p.H_kv;
+  const int g = u - b * p.H_kv;
+  const int wt = t * W + static_cast<int>(blockIdx.x - unit * W);
+  const int pb = wt / p.G;
+  const int h = g * p.G + (wt - pb * p.G);
+  const int C = seq.chunk[b];
+  const int lane = threadIdx.x & 63;
+  for (int rr = threadIdx.x >> 6; rr < kRowsPerWave; rr += kCombineThreads / 64) {
+    const int i = pb * kRowsPerWave + rr;
+    if (i >= p.C_max) break;
+    const int64_t r = (static_cast<int64_t>(b) * p.H_q + h) * p.C_max + i;
+    float ms[kMaxPieces], ls[kMaxPieces], a[kMaxPieces][E];
+#pragma unroll
+    for (int sp = 0; sp < kMaxPieces; ++sp) {
+      ms[sp] = -INFINITY;
+      ls[sp] = 0.f;
+#pragma unroll
+      for (int k = 0; k < E; ++k) a[sp][k] = 0.f;
+      if (sp < n && i < C) {
+        const size_t pr = static_cast<size_t>(sp) * p.rows_total + r;
+        const float2 ml = *reinterpret_cast<const float2*>(part_ml + 2 * pr);
+        ms[sp] = ml.x;
+        ls[sp] = ml.y;
+        const float* po = part_o + pr * D + E * lane;
+#pragma unroll
+        for (int k = 0; k < E; ++k) a[sp][k] = po[k];
+      }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int sp = 0; sp < kMaxPieces; ++sp) M = fmaxf(M, ms[sp]);
+    float acc[E], l = 0.f;
+#pragma unroll
+    for (int k = 0; k < E; ++k) acc[k] = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int sp = 0; sp < kMaxPieces; ++sp) {
+        if (ms[sp] == -INFINITY) continue;
+        const float wgt = __builtin_amdgcn_exp2f((ms[sp] - M) * p.scale_log2);
+        l += wgt * ls[sp];
+#pragma unroll
+        for (int k = 0; k < E; ++k) acc[k] += wgt * a[sp][k];
+      }
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    __bf16* orow = O + r * D + E * lane;
+#pragma unroll
+    for (int k = 0; k < E; ++k) orow[k] = static_cast<__bf16>(acc[k] * inv);
+    if (lse && lane == 0) lse[r] = l > 0.f ? M * p.scale + __logf(l) : -INFINITY;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_chunk_attn_bf16_split(const void* Q, const void* K, const void* V,
@@ -596,14 +804,50 @@ hipError_t launch_chunk_attn_bf16_split(const void* Q, const void* K, const void
   const __bf16* v = static_cast<const __bf16*>(V);
   __bf16* o = static_cast<__bf16*>(O);
   if (D == 128)
-    hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 4, false, true>), grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 4, false, 1>), grid, dim3(256), 0, stream,
                        q, k, v, T, len, o, lse, p, seq, part_o, part_ml);
   else
-    hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 4, false, true>), grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 4, false, 1>), grid, dim3(256), 0, stream,
                        q, k, v, T, len, o, lse, p, seq, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_split_combine(part_o, part_ml, D, false, o, lse, p, seq, stream);
+}
+
+hipError_t launch_chunk_attn_bf16_balanced(const void* Q, const void* K, const void* V,
+                                           const int32_t* T, const int32_t* len, void* O,
+                                           float* lse, int B, int D, const AttnParams& p,
+                                           const SeqInfo& seq, float* part_o, float* part_ml,
+                                           hipStream_t stream) {
+  const int n_units = B * p.H_kv * p.n_t;
+  const int slots = min(p.cus, kPlanMaxSlots);
+  int32_t* plan = const_cast<int32_t*>(p.plan_items);
+  int32_t* pieces = const_cast<int32_t*>(p.plan_pieces);
+  hipLaunchKernelGGL(balance_plan_kernel<8>, dim3(1), dim3(kPlanThreads), 0, stream, len, p,
+                     seq, n_units, slots, plan, pieces);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid(n_units + 2 * slots);  // at least the plan's pieces
+  const __bf16* q = static_cast<const __bf16*>(Q);
+  const __bf16* k = static_cast<const __bf16*>(K);
+  const __bf16* v = static_cast<const __bf16*>(V);
+  __bf16* o = static_cast<__bf16*>(O);
+  if (D == 128)
+    hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 8, false, 2>), grid, dim3(512), 0, stream, q,
+                       k, v, T, len, o, lse, p, seq, part_o, part_ml);
+  else
+    hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 8, false, 2>), grid, dim3(512), 0, stream, q,
+                       k, v, T, len, o, lse, p, seq, part_o, part_ml);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 cgrid(n_units * 8);  // one workgroup per wave tile of every tile
+  if (D == 128)
+    hipLaunchKernelGGL((plan_combine_kernel<128, 8>), cgrid, dim3(kCombineThreads), 0, stream,
+                       part_o, part_ml, p, seq, o, lse);
+  else
+    hipLaunchKernelGGL((plan_combine_kernel<64, 8>), cgrid, dim3(kCombineThreads), 0, stream,
+                       part_o, part_ml, p, seq, o, lse);
+  return hipGetLastError();
 }
 
 hipError_t launch_split_combine(const float* part_o, const float* part_ml, int D, bool f32_out,

@@ -30,6 +30,12 @@ struct BlockRange {
   int32_t end[CA_MAX_BATCH];
 };
 
+// Balance plan limits: pieces per (b, g, tile), and compute units the plan
+// spreads pieces over (the device's count, up to this many).
+constexpr int kMaxPieces = 8;
+constexpr int kPlanMaxSlots = 1024;
+constexpr int kPlanMaxBlocks = 1 << 24;  // NKB_max the plan's 32-bit piece arithmetic allows
+
 struct AttnParams {
   int H_q, H_kv, G;     // heads; G = H_q / H_kv query heads per KV head
   int C_max;            // rows of Q/O per head
@@ -45,6 +51,11 @@ struct AttnParams {
   int n_split;          // split-KV: table ranges per (b, g) (1: no split)
   int64_t rows_total;   // B * H_q * C_max (split-KV partial layout)
   int cus;              // compute units of the device (launch shape choices only)
+  // balance plan (bf16 planned pieces): plan_items[0] = number of pieces, then
+  // one int4 (b * H_kv + g, tile, piece k, pieces n) per piece from int 4 on;
+  // plan_pieces[(b * H_kv + g) * n_t + tile] = n
+  const int32_t* plan_items;
+  const int32_t* plan_pieces;
 };
 
 hipError_t launch_union_tables(const uint8_t* mask, int B, int H_q, int H_kv, int NQ_max,
@@ -73,6 +84,17 @@ hipError_t launch_chunk_attn_bf16_split(const void* Q, const void* K, const void
                                         float* lse, int B, int D, const AttnParams& p,
                                         const SeqInfo& seq, float* part_o, float* part_ml,
                                         hipStream_t stream);
+
+// bf16 path with a balance plan: a planning kernel cuts the (b, g, tile)
+// workgroups whose table walks are longest into pieces so that the pieces
+// spread evenly over p.cus compute units (longest first), writes the plan to
+// plan (p.plan_items / p.plan_pieces point into it), then the pieces run
+// (8-wave workgroups) and a merge combines the cut tiles' partials.
+hipError_t launch_chunk_attn_bf16_balanced(const void* Q, const void* K, const void* V,
+                                           const int32_t* T, const int32_t* len, void* O,
+                                           float* lse, int B, int D, const AttnParams& p,
+                                           const SeqInfo& seq, float* part_o, float* part_ml,
+                                           hipStream_t stream);
 
 // fp32 path on the vector ALUs; D in {64, 128}.
 hipError_t launch_chunk_attn_f32(const float* Q, const float* K, const float* V,

@@ -16,7 +16,8 @@ from typing import Optional
 
 import torch
 
-from . import (block_mask_topk, build_union_tables, chunk_attention, pool_blocks)
+from . import (balanced_workspace_size, block_mask_topk, build_union_tables, chunk_attention,
+               pool_blocks)
 from ._lib import CA_BLOCK
 
 
@@ -27,10 +28,14 @@ class ChunkedPrefill:
 
     ``step(q_chunk, prior)`` runs one chunk of C tokens at absolute offset
     ``prior``; ``step_dense`` runs the same attention over every block (the
-    dense baseline)."""
+    dense baseline).  ``balanced`` runs the sparse attention through
+    ``chunk_attention(..., balanced=True)``: the union's per-group tables differ
+    in length from group to group, and the plan spreads that work evenly over
+    the compute units (the workspace is allocated here, once)."""
 
     def __init__(self, k_cache: torch.Tensor, v_cache: torch.Tensor, H_q: int, C: int,
-                 budget: int, local: int, scale: Optional[float] = None):
+                 budget: int, local: int, scale: Optional[float] = None,
+                 balanced: bool = False):
         B, H_kv, L, D = k_cache.shape
         if C % CA_BLOCK or L % CA_BLOCK:
             raise ValueError("chunk length and cache capacity must be multiples of 64")
@@ -50,6 +55,11 @@ class ChunkedPrefill:
         self.T_dense = torch.arange(self.NKB, dtype=torch.int32, device=dev).repeat(B * H_kv, 1) \
             .view(B, H_kv, self.NKB)
         self.out = torch.empty((B, H_q, C, D), dtype=k_cache.dtype, device=dev)
+        self.balanced = bool(balanced)
+        self.ws = None
+        if self.balanced:
+            self.ws = torch.empty(balanced_workspace_size(B, H_q, H_kv, C, D), dtype=torch.uint8,
+                                  device=dev)
 
     def select(self, q_chunk: torch.Tensor, prior: int, stream=None) -> None:
         """Pool the chunk's new key blocks and its queries, make the mask and
@@ -66,7 +76,8 @@ class ChunkedPrefill:
     def attend(self, q_chunk: torch.Tensor, prior: int, out=None, stream=None) -> torch.Tensor:
         out = self.out if out is None else out
         return chunk_attention(q_chunk, self.k, self.v, self.T, self.lens, [prior] * self.B,
-                               [self.C] * self.B, self.scale, out=out, stream=stream)
+                               [self.C] * self.B, self.scale, out=out, stream=stream,
+                               balanced=self.balanced, workspace=self.ws)
 
     def step(self, q_chunk: torch.Tensor, prior: int, out=None, stream=None) -> torch.Tensor:
         self.select(q_chunk, prior, stream)

@@ -180,6 +180,48 @@ CA_EXPORT size_t ca_chunk_attention_workspace_size(int B, int H_q, int C_max, in
                                          int n_splits);
 
 /*
+ * ca_chunk_attention_balanced -- ca_chunk_attention with the work spread
+ * evenly over the compute units when the tables are uneven: tables of
+ * different lengths across (sequence, KV head) pairs, as a mask producer's
+ * union gives from chunk to chunk (CompactAttention, selection stage: T[b,g]
+ * holds what each group's union selected, so lengths differ by group), and
+ * the causal part, which grows along the chunk.  The pages do not describe
+ * how work is scheduled; this is the merge of partial softmax results given
+ * for ca_chunk_attention_split, applied only where it pays:
+ *   - a planning kernel measures each tile's walk (the entries its 32-row
+ *     query blocks can see) and, unless the walks already balance, cuts the
+ *     longest into up to 8 pieces of even length, then lists all pieces
+ *     longest first;
+ *   - the pieces run; a tile left whole writes O and lse itself, and the
+ *     pieces of a cut tile are merged as in ca_chunk_attention_split.
+ * Same result as ca_chunk_attention (the same admissible keys and softmax),
+ * bit for bit where nothing is cut, else up to the rounding of the merge.
+ *
+ * workspace  device memory owned by the caller, 16-byte aligned, at least
+ *            ca_chunk_attention_balanced_workspace_size(B, H_q, H_kv, C_max, D)
+ *            bytes (else CA_ERR_SHAPE; NULL gives CA_ERR_NULL).  The plan
+ *            lives there: calls that share one workspace must be ordered on
+ *            one stream.
+ * dtype      CA_BF16; CA_F32 runs ca_chunk_attention (workspace unused).
+ * NKB_max    at most 2^24 for CA_BF16 (else CA_ERR_SHAPE).
+ * Other arguments, layouts and errors as for ca_chunk_attention.
+ */
+CA_EXPORT ca_status ca_chunk_attention_balanced(const void* Q, const void* K_cache,
+                                      const void* V_cache, const int32_t* T, const int32_t* len,
+                                      int NKB_max, const int32_t* prior_len,
+                                      const int32_t* chunk_len, int B, int H_q, int H_kv,
+                                      int C_max, int64_t L, int D, int block, float scale,
+                                      ca_dtype dtype, void* workspace, size_t workspace_bytes,
+                                      void* O, float* lse, hipStream_t stream);
+
+/* Bytes of workspace ca_chunk_attention_balanced needs: partial outputs for
+ * up to 8 pieces of every output row (8 * B * H_q * C_max * (D + 2) * 4) plus
+ * the plan (a few KiB); 0 for invalid sizes (H_q % H_kv != 0, D not 64 or
+ * 128, nonpositive sizes). */
+CA_EXPORT size_t ca_chunk_attention_balanced_workspace_size(int B, int H_q, int H_kv,
+                                                            int C_max, int D);
+
+/*
  * ca_chunk_attention_rows -- the block-sparse-kernel execution that the union
  * replaces: each 64-row Q-block of each query head attends its own mask row,
  * with no union over Q-blocks or heads.  CompactAttention, abstract and

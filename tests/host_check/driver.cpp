@@ -94,6 +94,39 @@ int main() {
     EXPECT(strcmp(stub::last.what, "attn_f32_split") == 0 && stub::last.p.n_split == 4);
     EXPECT((char*)stub::last.ptrs[1] - (char*)stub::last.ptrs[0] ==
            (ptrdiff_t)(4LL * 3 * 32 * 256 * 128 * 4));
+    // balanced: workspace layout (partials for 8 pieces, then the plan and the
+    // pieces per tile), size check, 8-wave tiles, fp32 runs unplanned
+    const size_t bneed = ca_chunk_attention_balanced_workspace_size(3, 32, 8, 256, 128);
+    const long long units = 3LL * 8 * ((4 * 8 + 7) / 8);
+    const long long po = 8LL * 3 * 32 * 256 * 128 * 4, pml = 8LL * 3 * 32 * 256 * 2 * 4;
+    const long long plan_bytes = (4 + 4 * (units + 2 * 1024)) * 4;
+    EXPECT(bneed == (size_t)(po + pml + ((plan_bytes + 15) / 16) * 16 + ((units * 4 + 15) / 16) * 16));
+    EXPECT(ca_chunk_attention_balanced_workspace_size(3, 32, 7, 256, 128) == 0);
+    EXPECT(ca_chunk_attention_balanced_workspace_size(3, 32, 8, 256, 96) == 0);
+    EXPECT(ca_chunk_attention_balanced(FAKE, FAKE, FAKE, (const int32_t*)FAKE,
+                                       (const int32_t*)FAKE, 200, prior, chunk, 3, 32, 8, 256,
+                                       8448, 128, 64, 0.125f, CA_BF16, FAKE, bneed, FAKE, nullptr,
+                                       0) == CA_OK);
+    EXPECT(strcmp(stub::last.what, "attn_bf16_balanced") == 0 && stub::last.p.waves == 8 &&
+           stub::last.p.n_t == (4 * 8 + 7) / 8 && stub::last.p.xcd == 0);
+    EXPECT((char*)stub::last.ptrs[1] - (char*)stub::last.ptrs[0] == (ptrdiff_t)po);
+    EXPECT((const char*)stub::last.p.plan_items - (char*)stub::last.ptrs[0] ==
+           (ptrdiff_t)(po + pml));
+    EXPECT((const char*)stub::last.p.plan_pieces - (const char*)stub::last.p.plan_items ==
+           (ptrdiff_t)(((plan_bytes + 15) / 16) * 16));
+    EXPECT(ca_chunk_attention_balanced(FAKE, FAKE, FAKE, (const int32_t*)FAKE,
+                                       (const int32_t*)FAKE, 200, prior, chunk, 3, 32, 8, 256,
+                                       8448, 128, 64, 0.125f, CA_BF16, FAKE, bneed - 1, FAKE,
+                                       nullptr, 0) == CA_ERR_SHAPE);
+    EXPECT(ca_chunk_attention_balanced(FAKE, FAKE, FAKE, (const int32_t*)FAKE,
+                                       (const int32_t*)FAKE, 200, prior, chunk, 3, 32, 8, 256,
+                                       8448, 128, 64, 0.125f, CA_BF16, nullptr, bneed, FAKE,
+                                       nullptr, 0) == CA_ERR_NULL);
+    EXPECT(ca_chunk_attention_balanced(FAKE, FAKE, FAKE, (const int32_t*)FAKE,
+                                       (const int32_t*)FAKE, 200, prior, chunk, 3, 32, 8, 256,
+                                       8448, 128, 64, 0.125f, CA_F32, nullptr, 0, FAKE, nullptr,
+                                       0) == CA_OK);
+    EXPECT(strcmp(stub::last.what, "attn_f32") == 0);
     // per-(head, Q-block) lists
     EXPECT(ca_chunk_attention_rows(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE,
                                    4, 200, prior, chunk, 3, 32, 8, 256, 8448, 128, 64, 0.125f,

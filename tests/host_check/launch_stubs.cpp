@@ -71,6 +71,16 @@ hipError_t launch_chunk_attn_bf16_split(const void*, const void*, const void*, c
   return hipSuccess;
 }
 
+hipError_t launch_chunk_attn_bf16_balanced(const void*, const void*, const void*,
+                                           const int32_t*, const int32_t*, void*, float*, int B,
+                                           int D, const AttnParams& p, const SeqInfo& seq,
+                                           float* part_o, float* part_ml, hipStream_t) {
+  record_attn("attn_bf16_balanced", B, D, p, seq);
+  stub::last.ptrs[0] = part_o;
+  stub::last.ptrs[1] = part_ml;
+  return hipSuccess;
+}
+
 hipError_t launch_chunk_attn_f32(const float*, const float*, const float*, const int32_t*,
                                  const int32_t*, float*, float*, int B, int D,
                                  const AttnParams& p, const SeqInfo& seq, hipStream_t) {

@@ -166,3 +166,27 @@ def test_split_validation_and_workspace_size():
     assert lib.ca_chunk_attention_split(*base, 1, 4, None, need, FAKE, None, None) == 1
     assert lib.ca_chunk_attention_split(*base, 1, 4, FAKE, need - 1, FAKE, None, None) == 2
     assert lib.ca_chunk_attention_split(*base, 1, 4, FAKE + 4, need, FAKE, None, None) == 4
+
+
+def test_balanced_validation_and_workspace_size():
+    lib = _lib.lib()
+    # 8 pieces of partials per output row, then the plan (4 + 4 * (tiles + 2048) ints) and
+    # the pieces per tile (tiles = B * H_kv * ceil(G * ceil(C_max / 32) / 8)), 16-byte aligned
+    tiles = 1 * 8 * ((4 * 64 + 7) // 8)
+    up16 = lambda x: (x + 15) // 16 * 16
+    want = (8 * 32 * 2048 * 128 * 4 + 8 * 32 * 2048 * 2 * 4 + up16((4 + 4 * (tiles + 2048)) * 4)
+            + up16(tiles * 4))
+    assert lib.ca_chunk_attention_balanced_workspace_size(1, 32, 8, 2048, 128) == want
+    assert lib.ca_chunk_attention_balanced_workspace_size(1, 32, 7, 2048, 128) == 0
+    assert lib.ca_chunk_attention_balanced_workspace_size(1, 32, 8, 2048, 80) == 0
+    assert lib.ca_chunk_attention_balanced_workspace_size(0, 32, 8, 2048, 128) == 0
+    base = (FAKE, FAKE, FAKE, FAKE, FAKE, 20, _ints(1024), _ints(256), 1, 4, 1, 256, 1280, 64, 64,
+            0.125)
+    need = lib.ca_chunk_attention_balanced_workspace_size(1, 4, 1, 256, 64)
+    # no workspace, short workspace, unaligned workspace, bad dtype, bad shape
+    assert lib.ca_chunk_attention_balanced(*base, 1, None, need, FAKE, None, None) == 1
+    assert lib.ca_chunk_attention_balanced(*base, 1, FAKE, need - 1, FAKE, None, None) == 2
+    assert lib.ca_chunk_attention_balanced(*base, 1, FAKE + 4, need, FAKE, None, None) == 4
+    assert lib.ca_chunk_attention_balanced(*base, 7, FAKE, need, FAKE, None, None) == 3
+    bad = base[:10] + (3,) + base[11:]  # H_q = 4 over H_kv = 3
+    assert lib.ca_chunk_attention_balanced(*bad, 1, FAKE, need, FAKE, None, None) == 2

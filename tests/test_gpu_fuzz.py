@@ -1,7 +1,7 @@
-"""Seeded random shapes through every attention entry point, against the
-float64 oracle: batch, head counts and group size, head dim, ragged prior and
-chunk lengths (zero included), C_max padding, element type and mask density
-all drawn at random.  Tables are compared bit-exact, outputs at the stated
+"""Seeded random shapes through every attention entry point (whole tables,
+split, balanced, per-Q-block lists), against the float64 oracle: batch, head
+counts and group size, head dim, ragged prior and chunk lengths (zero
+included), C_max padding, element type and mask density all drawn at random.  Tables are compared bit-exact, outputs at the stated
 bounds (bf16: max-abs 2e-2, mean-abs 2e-3; fp32: max-abs 1e-5).
 """
 import numpy as np
@@ -70,8 +70,12 @@ def test_fuzz_shapes_all_entry_points(seed):
     Os, lses = ca.chunk_attention(d.q, d.k, d.v, T, lens, w.prior, w.chunk, w.scale,
                                   return_lse=True, n_splits=n_split)
     torch.cuda.synchronize()
+    Ob, lseb = ca.chunk_attention(d.q, d.k, d.v, T, lens, w.prior, w.chunk, w.scale,
+                                  return_lse=True, balanced=True)
+    torch.cuda.synchronize()
     _compare(w, O, lse, Or, lr, "union")
     _compare(w, Os, lses, Or, lr, f"union, {n_split} splits")
+    _compare(w, Ob, lseb, Or, lr, "union, balanced")
     # block-sparse execution of the same mask (per-(head, Q-block) lists)
     Trw, lrw = ca.build_row_tables(d.mask, w.n_kv_blocks)
     Orw, lserw = ca.chunk_attention_rows(d.q, d.k, d.v, Trw, lrw, w.prior, w.chunk, w.scale,

@@ -21,15 +21,16 @@ pytestmark = pytest.mark.gpu
 SCORE_ATOL = 2e-5
 
 
-def test_prefill_small_every_chunk():
+@pytest.mark.parametrize("balanced", [False, True])
+def test_prefill_small_every_chunk(balanced):
     s = gen.make_prefill_stream("prefill_small")
     k_dev, v_dev = s.k.cuda(), s.v.cuda()
-    drv = ChunkedPrefill(k_dev, v_dev, s.H_q, s.C, budget=4, local=2)
+    drv = ChunkedPrefill(k_dev, v_dev, s.H_q, s.C, budget=4, local=2, balanced=balanced)
     k, v = gen.tensor_to_f32(s.k), gen.tensor_to_f32(s.v)
     kr = np.nan_to_num(pool_blocks_ref(k, [0], [s.L // 64], s.L // 64))
     for c in range(s.n_chunks):
         P = c * s.C
-        say(f"prefill_small chunk {c} prior {P}")
+        say(f"prefill_small chunk {c} prior {P} balanced={balanced}")
         q_cpu = s.q_chunk(c)
         q_dev = q_cpu.cuda()
         O = drv.step(q_dev, P).clone()
@@ -68,13 +69,14 @@ def test_prefill_small_every_chunk():
                     assert want <= found, (c, g, want - found)
 
 
-def test_prefill_graph_replay_matches_eager():
+@pytest.mark.parametrize("balanced", [False, True])
+def test_prefill_graph_replay_matches_eager(balanced):
     # The whole prompt (select + attend per chunk, and the dense baseline)
     # recorded into one HIP graph: every replay, with eager library work and
     # synchronisations in between, reproduces the eager outputs bit for bit.
     s = gen.make_prefill_stream("prefill_small")
     k_dev, v_dev = s.k.cuda(), s.v.cuda()
-    drv = ChunkedPrefill(k_dev, v_dev, s.H_q, s.C, budget=4, local=2)
+    drv = ChunkedPrefill(k_dev, v_dev, s.H_q, s.C, budget=4, local=2, balanced=balanced)
     qs = [s.q_chunk(c).cuda() for c in range(s.n_chunks)]
     priors = [c * s.C for c in range(s.n_chunks)]
     eager = [drv.step(q, p).clone() for q, p in zip(qs, priors)]
