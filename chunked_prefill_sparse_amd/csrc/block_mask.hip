@@ -8,7 +8,8 @@
 //   qbar[b,h,qb]  = mean of the 64 rows of Q-block qb          (pool_blocks)
 //   kbar[b,g,kb]  = mean of the 64 rows of KV block kb         (pool_blocks,
 //                   kept across chunks: only the new blocks are pooled)
-//   s[b,h,qb,kb]  = qbar . kbar                                (block_scores)
+//   s[b,h,qb,kb]  = qbar . kbar                                (block_scores,
+//                   fp32 on the matrix cores)
 //   mask row      = sink + last `local` prior blocks + causal block triangle
 //                   + the `budget` best remaining prior blocks  (topk_mask)
 //
@@ -76,20 +77,27 @@ __global__ __launch_bounds__(kMaskThreads) void pool_blocks_kernel(const TIn* __
 
 // Workgroup (b*H_kv + g, y, z) computes the 64 x 64 tile of scores of the
 // group's pooled Q-block rows 64z .. 64z+63 (row r = head r / nq, Q-block
-// r % nq) against KV blocks 64y .. 64y+63.  Both operands are staged in LDS
-// 32 dimensions at a time, transposed (dimension-major), and each thread keeps
-// a 4 x 4 block of outputs, so every pair of 16-byte LDS reads feeds 16 fused
-// multiply-adds.  Each output is one chain of fused multiply-adds in
-// ascending d.
+// r % nq) against KV blocks 64y .. 64y+63, on the fp32 matrix cores
+// (v_mfma_f32_32x32x2_f32, twice the fp32 rate of the vector ALUs with packed
+// fp32 off).  Both 64 x D operand tiles are staged in LDS whole (rows padded
+// by 16 bytes, so the 32 rows a read touches fall in distinct banks); wave w
+// computes the 32 x 32 block (KV blocks 32 (w / 2) .., Q rows 32 (w % 2) ..)
+// as S^T = Kbar Qbar^T over D/2 steps of 2 dimensions.  Lane l takes the
+// dimensions (l / 32) * D/2 + s of step s, so its operands for four steps are
+// one 16-byte read.  Its 16 results are KV blocks 8(r/4) + 4(l/32) + r%4 of
+// Q row l % 32: four 16-byte stores (when rows of the score matrix are
+// 16-byte aligned; else single floats).
 constexpr int kScoreTile = 64;
-constexpr int kScoreDStep = 32;
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 template <int D>
 __global__ __launch_bounds__(kMaskThreads) void block_scores_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int H_q, int H_kv,
     int NQ_max, int NKB_max, SeqInfo seq, float* __restrict__ scores) {
-  __shared__ __attribute__((aligned(16))) float Qs[kScoreDStep][kScoreTile];
-  __shared__ __attribute__((aligned(16))) float Ks[kScoreDStep][kScoreTile];
+  constexpr int RS = D + 4;  // padded row stride (floats)
+  __shared__ __attribute__((aligned(16))) float Qs[kScoreTile * RS];
+  __shared__ __attribute__((aligned(16))) float Ks[kScoreTile * RS];
   const int bg = blockIdx.x;
   const int b = bg / H_kv;
   const int g = bg - b * H_kv;
@@ -106,67 +114,59 @@ __global__ __launch_bounds__(kMaskThreads) void block_scores_kernel(
     const int hl = r / nq;
     return head_row0 + static_cast<size_t>(hl) * NQ_max + (r - hl * nq);
   };
-  // loader: thread -> (tile row lr, 4-dim slice ld) twice per operand
-  const int ld = (tid & 7) * 4;
-  const int lr = tid >> 3;  // 0..31, and lr + 32
-  const float* qsrc[2];
-  const float* ksrc[2];
-  bool qin[2], kin[2];
+  // stage both tiles: D / 4 float4 per row, rows past the range as zeros; all
+  // loads in flight before the LDS writes
+  constexpr int F4 = kScoreTile * D / 4 / kMaskThreads;  // float4 per thread per tile
+  float4 qv[F4], kv[F4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = r0 + lr + 32 * i;
-    qin[i] = r < n_rows;
-    qsrc[i] = qbar + row_index(qin[i] ? r : r0) * D + ld;
-    const int kb = kb0 + lr + 32 * i;
-    kin[i] = kb < pblk;
-    ksrc[i] = kbar + (static_cast<size_t>(bg) * NKB_max + (kin[i] ? kb : kb0)) * D + ld;
-  }
-  const int tr = (tid >> 4) * 4;  // this thread's 4 rows of the tile
-  const int tc = (tid & 15) * 4;  // and its 4 KV blocks
-  float acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-  for (int d0 = 0; d0 < D; d0 += kScoreDStep) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float4 q = qin[i] ? *reinterpret_cast<const float4*>(qsrc[i] + d0)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 k = kin[i] ? *reinterpret_cast<const float4*>(ksrc[i] + d0)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-      const int c = lr + 32 * i;
-      Qs[ld][c] = q.x;
-      Qs[ld + 1][c] = q.y;
-      Qs[ld + 2][c] = q.z;
-      Qs[ld + 3][c] = q.w;
-      Ks[ld][c] = k.x;
-      Ks[ld + 1][c] = k.y;
-      Ks[ld + 2][c] = k.z;
-      Ks[ld + 3][c] = k.w;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int d = 0; d < kScoreDStep; ++d) {
-      const float4 q = *reinterpret_cast<const float4*>(&Qs[d][tr]);
-      const float4 k = *reinterpret_cast<const float4*>(&Ks[d][tc]);
-      const float qv[4] = {q.x, q.y, q.z, q.w};
-      const float kv[4] = {k.x, k.y, k.z, k.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(qv[i], kv[j], acc[i][j]);
-    }
-    __syncthreads();
+  for (int i = 0; i < F4; ++i) {
+    const int e = tid + i * kMaskThreads;  // float4 index in the tile
+    const int row = e / (D / 4), c4 = e - row * (D / 4);
+    const int r = r0 + row, kb = kb0 + row;
+    qv[i] = r < n_rows ? reinterpret_cast<const float4*>(qbar + row_index(r) * D)[c4]
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    kv[i] = kb < pblk
+                ? reinterpret_cast<const float4*>(kbar + (static_cast<size_t>(bg) * NKB_max + kb) * D)[c4]
+                : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = r0 + tr + i;
-    if (r >= n_rows) continue;
-    float* dst = scores + row_index(r) * NKB_max;
+  for (int i = 0; i < F4; ++i) {
+    const int e = tid + i * kMaskThreads;
+    const int row = e / (D / 4), c4 = e - row * (D / 4);
+    *reinterpret_cast<float4*>(&Qs[row * RS + 4 * c4]) = qv[i];
+    *reinterpret_cast<float4*>(&Ks[row * RS + 4 * c4]) = kv[i];
+  }
+  __syncthreads();
+  const int wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int kb_blk = 32 * (wave >> 1), q_blk = 32 * (wave & 1);
+  const float* ka = &Ks[(kb_blk + l32) * RS + hh * (D / 2)];
+  const float* qa = &Qs[(q_blk + l32) * RS + hh * (D / 2)];
+  f32x16_t acc = {};
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (kb0 + tc + j < pblk) dst[kb0 + tc + j] = acc[i][j];
+  for (int s = 0; s < D / 2; s += 4) {
+    const float4 a4 = *reinterpret_cast<const float4*>(ka + s);
+    const float4 b4 = *reinterpret_cast<const float4*>(qa + s);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.x, b4.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.y, b4.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.z, b4.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.w, b4.w, acc, 0, 0, 0);
+  }
+  const int r = r0 + q_blk + l32;
+  if (r >= n_rows) return;
+  float* dst = scores + row_index(r) * NKB_max;
+  const bool vec = (NKB_max & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int kb = kb0 + kb_blk + 8 * j + 4 * hh;  // results 4j .. 4j+3: four consecutive blocks
+    if (vec && kb + 3 < pblk) {
+      *reinterpret_cast<float4*>(dst + kb) =
+          make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (kb + k < pblk) dst[kb + k] = acc[4 * j + k];
+    }
   }
 }
 

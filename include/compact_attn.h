@@ -358,7 +358,7 @@ CA_EXPORT ca_status ca_pool_blocks(const void* X, ca_dtype dtype, int B, int H, 
  * P = prior_len[b]/64, nq = chunk_len[b]/64, g = h / (H_q/H_kv):
  *
  *   scores[b,h,qb,kb] = sum_d qbar[b,h,qb,d] * kbar[b,g,kb,d]  (qb < nq, kb < P;
- *                       fp32 fused multiply-adds in ascending d)
+ *                       fp32, on the fp32 matrix cores)
  *   mask[b,h,qb,kb]   = 1 for kb = 0 (when P > 0), for P - local <= kb < P,
  *                       for P <= kb <= P + qb (causal block triangle), and for
  *                       the `budget` candidates 1 <= kb < max(P - local, 1)
