@@ -180,15 +180,17 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 }
 
 // One workgroup per mask row (b, h, qb).  The budget-th largest candidate key
-// is found by a most-significant-digit-first radix select (four 8-bit passes
-// over the row, histograms in LDS); the row is then written in ascending kb,
-// taking keys above the threshold and, of the keys equal to it, the lowest
-// kb first.
+// is found by a most-significant-digit-first radix select (up to four 8-bit
+// passes over the row, histograms in LDS).  When the digit bin that holds it
+// is taken whole (the usual case once the bin is one key), the select stops
+// and every thread decides its blocks alone; otherwise (equal keys straddle
+// the budget) the row is written in ascending kb, taking keys above the
+// threshold and, of the keys equal to it, the lowest kb first.
 __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
     const float* __restrict__ scores, int H_q, int NQ_max, int NKB_max, SeqInfo seq,
     int budget, int local, uint8_t* __restrict__ mask) {
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh_prefix, sh_need;
+  __shared__ uint32_t sh_prefix, sh_need, sh_bin;
   __shared__ int wave_eq[kMaskThreads / 64];
   const size_t row = blockIdx.x;
   const int b = static_cast<int>(row / (static_cast<size_t>(H_q) * NQ_max));
@@ -209,6 +211,8 @@ __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
   const float* srow = scores + row * NKB_max;
 
   uint32_t prefix = 0u, need = kk;
+  uint32_t lvl_mask = 0u;  // key bits the passes have fixed
+  bool whole_bin = true;   // every candidate in prefix's bin is taken
   if (kk > 0u) {
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
@@ -244,6 +248,7 @@ __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
             if (cum + h[j] >= need) {
               sh_prefix = prefix | (static_cast<uint32_t>(255 - 4 * lane - j) << shift);
               sh_need = need - cum;
+              sh_bin = h[j];
               break;
             }
             cum += h[j];
@@ -253,9 +258,25 @@ __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
       __syncthreads();
       prefix = sh_prefix;
       need = sh_need;
+      lvl_mask = 0xFFFFFFFFu << shift;
+      whole_bin = need == sh_bin;
+      // the digit's bin is taken whole: the budget is exactly the candidates
+      // whose fixed bits are at least prefix, and the lower bits need no pass
+      if (whole_bin) break;
     }
   }
-  // prefix = key of the budget-th largest candidate; take `need` of its equals
+  // prefix = the fixed bits of the budget-th largest candidate's key; take the
+  // candidates above it, and `need` of those equal to it (lowest kb first)
+
+  if (whole_bin) {  // no equal key is left out: no ordering across the row
+    for (int kb = tid; kb < NKB_max; kb += kMaskThreads) {
+      bool sel = (pblk > 0 && kb == 0) || (kb >= lo_local && kb < pblk) ||
+                 (kb >= pblk && kb <= pblk + qb);
+      if (kk > 0u && kb >= 1 && kb < lo_local) sel = sel || (score_key(srow[kb]) & lvl_mask) >= prefix;
+      mrow[kb] = sel ? 1 : 0;
+    }
+    return;
+  }
 
   uint32_t taken = 0u;  // equals already taken (uniform)
   for (int base = 0; base < NKB_max; base += kMaskThreads) {
