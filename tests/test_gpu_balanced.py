@@ -12,7 +12,9 @@ here:
   once, piece counts consistent, size classes non-increasing, the count within
   the launch grid;
 * NaN outside the selected blocks changes nothing; one workspace serves calls
-  of different shapes in a row; fp32 runs the unplanned kernel.
+  of different shapes in a row; fp32 runs the unplanned kernel;
+* more tiles than the planner keeps in LDS (its walks then pass through the
+  workspace).
 """
 import zlib
 
@@ -234,3 +236,32 @@ def test_balanced_fp32_runs_plain_kernel():
     assert torch.equal(Ob, Op) and torch.equal(lb, lp)
     Or, _ = oracle_full(w)
     assert float(np.abs(to_np(Ob) - Or).max()) <= F32_MAX_ABS
+
+
+def test_balanced_many_tiles_plan_in_global_scratch():
+    # more tiles (B * H_kv * tiles per group = 17 * 8 * 64) than the planner
+    # keeps in LDS: the walks go through the pieces array between its passes
+    B, H_q, H_kv, D, C_max = 17, 64, 8, 64, 2048
+    rng = np.random.default_rng(91)
+    prior = [64 * int(x) for x in rng.integers(0, 12, B)]
+    chunk = [64 * int(x) for x in rng.integers(1, 33, B)]
+    chunk[0] = C_max
+    w = gen.make_custom(B, H_q, H_kv, D, prior, chunk, "bf16", 92,
+                        _by_group([1.0, 0.1, 0.5, 0.0, 0.3, 1.0, 0.05, 0.7], H_q // H_kv),
+                        C_max=C_max, name="balanced_many_tiles")
+    assert B * H_kv * _n_t(w) > 8192
+    say(f"balanced with {B * H_kv * _n_t(w)} tiles")
+    d = Dev(w)
+    T, lens = d.tables()
+    ws = torch.empty(ca.balanced_workspace_size(B, H_q, H_kv, C_max, D), dtype=torch.uint8,
+                     device="cuda")
+    O, lse = _balanced(d, T, lens, ws)
+    torch.cuda.synchronize()
+    _check_plan(ws, w, T, lens)
+    rows = sample_rows(w, seed=93, heads_per_group=1, extra=2)
+    Or, lr = oracle_rows(w, rows)
+    r = torch.from_numpy(rows).cuda()
+    compare_bf16(to_np(O[r[:, 0], r[:, 1], r[:, 2]]), Or, f"{len(rows)} sampled rows")
+    np.testing.assert_allclose(to_np(lse[r[:, 0], r[:, 1], r[:, 2]]), lr, rtol=0, atol=LSE_ABS)
+    for b in range(B):
+        assert bool((O[b, :, chunk[b]:] == 0).all())
