@@ -16,7 +16,7 @@ from tests.gpu_util import (F32_MAX_ABS, LSE_ABS, Dev, compare_bf16, oracle_full
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 80
+N_CASES = 120
 
 
 def _case(seed):
