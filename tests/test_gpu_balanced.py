@@ -149,6 +149,8 @@ def test_balanced_small_full_parity(B, H_q, H_kv, D, prior, chunk, C_max, dens):
 def test_balanced_equals_plain_when_even():
     # dense tables of equal length: the walks already balance, nothing is cut,
     # and the planned kernel does the plain kernel's arithmetic
+    if torch.cuda.get_device_properties(0).multi_processor_count > 256:
+        pytest.skip("the plain kernel takes 8-wave workgroups here only up to 256 CUs")
     w = gen.make_custom(1, 32, 8, 128, [8192], [2048], "bf16", 41,
                         lambda rng, b, H, nq, pb: np.ones((H, nq, pb), np.uint8),
                         name="balanced_even")
