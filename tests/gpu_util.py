@@ -14,11 +14,45 @@ from oracle import chunk_attention_ref, chunk_attention_rows_ref, union_tables_r
 F32_MAX_ABS = 1e-5
 BF16_MAX_ABS = 2e-2
 BF16_MEAN_ABS = 2e-3
-# The bf16 path sums the bf16-rounded probabilities in the softmax denominator.
-# bf16 carries 8 significant bits, so round-to-nearest-even leaves each within a
-# relative 2^-8 of the exact value; log(l) is then within log(1 + 2^-8) ~= 3.9e-3
-# of the exact LSE, plus fp32 rounding of the scores and the exponentials.
-LSE_ABS = 4.5e-3
+# LSE bounds.  Both kernels return lse = m * scale + log(l), where l sums the fp32
+# exponentials before any rounding to bf16 (the bf16 path rounds the probabilities
+# only for the P.V product), so no bf16 rounding reaches lse: only fp32 rounding
+# does.
+#  * Scores: fp32 accumulation of exact products of bf16 (or fp32) inputs.  Their
+#    rounding grows with sum_d |q_d k_d|, which is of the order of the largest
+#    logits and so of |lse|: a relative term, 2^-18 of |lse| (about eight
+#    accumulations at 2^-24 each, times the ratio of sum |q_d k_d| to the largest
+#    logit, which is below 2 for Gaussian rows).
+#  * Exponentials, the log and the two final roundings: a few fp32 ulps.
+#  * The fp32 sum of the denominator: one add per staged block and row (up to
+#    2048 at 128K), plus the split or piece merge.  Rounded at random its
+#    relative error stays near sqrt(2048) * 2^-25 ~= 1.3e-6.
+# The absolute term, 1e-4, leaves room for those; a merge that weighted one split
+# or piece wrong by 0.02% of the row's mass would already exceed it.  The fp32
+# path has no bf16 inputs and short tables: 1e-5.
+LSE_ABS = 1e-4
+LSE_REL = 2.0 ** -18
+F32_LSE_ABS = 1e-5
+
+
+def check_lse(got, ref, what="lse", fp32=False):
+    """got/ref: lse arrays of the same shape.  -inf exactly where the reference
+    has no admissible key, elsewhere |got - ref| <= abs + 2^-18 |ref|."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    live = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), live), f"{what}: finite pattern differs"
+    assert np.all(got[~live] == -np.inf) and np.all(ref[~live] == -np.inf), \
+        f"{what}: non-finite entries other than -inf"
+    if not live.any():
+        return 0.0
+    err = np.abs(got[live] - ref[live])
+    bound = (F32_LSE_ABS if fp32 else LSE_ABS) + LSE_REL * np.abs(ref[live])
+    ratio = float((err / bound).max())
+    say(f"  {what}: lse max-abs {float(err.max()):.3e} (max |lse| {float(np.abs(ref[live]).max()):.2f}), "
+        f"{ratio:.3f} of the bound")
+    assert ratio <= 1.0, f"{what}: lse error {float(err.max())} exceeds its bound"
+    return float(err.max())
 
 
 def say(*a):
@@ -54,6 +88,45 @@ def oracle_full(w):
     T, ln = oracle_tables(w)
     q, k, v = (gen.tensor_to_f32(x) for x in (w.q, w.k, w.v))
     return chunk_attention_ref(q, k, v, T, ln, w.prior, w.chunk, w.scale)
+
+
+def oracle_full_parallel(w, arrays=None, workers=4):
+    """oracle_full, run as independent slices: attention of KV group g of
+    sequence b reads only that group's queries, cache rows and table, so each
+    (b, g) slice goes through chunk_attention_ref on its own, on a few threads
+    (NumPy's element-wise loops release the GIL; BLAS threads are shared out)."""
+    import concurrent.futures as cf
+    import os
+    T, ln = oracle_tables(w)
+    q, k, v = arrays if arrays is not None else f32_arrays(w)
+    G = w.G
+    O = np.zeros(q.shape, np.float32)
+    lse = np.full(q.shape[:3], -np.inf, np.float32)
+
+    def one(bg):
+        b, g = bg
+        sl = slice(b, b + 1)
+        o, l_ = chunk_attention_ref(q[sl, g * G:(g + 1) * G], k[sl, g:g + 1], v[sl, g:g + 1],
+                                    T[sl, g:g + 1], ln[sl, g:g + 1], w.prior[b:b + 1],
+                                    w.chunk[b:b + 1], w.scale)
+        O[b, g * G:(g + 1) * G] = o[0]
+        lse[b, g * G:(g + 1) * G] = l_[0]
+
+    jobs = [(b, g) for b in range(w.B) for g in range(w.H_kv)]
+    n = max(1, min(workers, len(jobs)))
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=max(1, cores // n), user_api="blas")
+    except Exception:  # threadpoolctl missing: BLAS keeps its own threads
+        limit = None
+    try:
+        with cf.ThreadPoolExecutor(max_workers=n) as ex:
+            list(ex.map(one, jobs))
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
+    return O, lse
 
 
 def f32_arrays(w):

@@ -24,7 +24,7 @@ import torch
 
 import gen
 import chunked_prefill_sparse_amd as ca
-from tests.gpu_util import (F32_MAX_ABS, LSE_ABS, Dev, compare_bf16, oracle_full, oracle_rows,
+from tests.gpu_util import (F32_MAX_ABS, check_lse, Dev, compare_bf16, oracle_full, oracle_rows,
                             sample_rows, say, to_np)
 
 pytestmark = pytest.mark.gpu
@@ -141,7 +141,7 @@ def test_balanced_small_full_parity(B, H_q, H_kv, D, prior, chunk, C_max, dens):
     live = np.isfinite(lr)
     gl = to_np(lse)
     assert np.array_equal(np.isfinite(gl), live)
-    np.testing.assert_allclose(gl[live], lr[live], rtol=0, atol=LSE_ABS)
+    check_lse(gl[live], lr[live])
     for b in range(B):
         assert bool((O[b, :, chunk[b]:] == 0).all())
 
@@ -186,7 +186,7 @@ def test_balanced_tp_shard_128k_sampled(variant):
     Or, lr = oracle_rows(w, rows)
     r = torch.from_numpy(rows).cuda()
     compare_bf16(to_np(O[r[:, 0], r[:, 1], r[:, 2]]), Or, f"{len(rows)} sampled rows")
-    np.testing.assert_allclose(to_np(lse[r[:, 0], r[:, 1], r[:, 2]]), lr, rtol=0, atol=LSE_ABS)
+    check_lse(to_np(lse[r[:, 0], r[:, 1], r[:, 2]]), lr)
     assert bool(torch.isfinite(O).all())
 
 
@@ -223,7 +223,7 @@ def test_balanced_poison_and_workspace_reuse():
     Or, lr = oracle_full(w2)
     compare_bf16(to_np(O3), Or, "second call")
     live = np.isfinite(lr)
-    np.testing.assert_allclose(to_np(lse3)[live], lr[live], rtol=0, atol=LSE_ABS)
+    check_lse(to_np(lse3)[live], lr[live])
 
 
 def test_balanced_fp32_runs_plain_kernel():
@@ -264,6 +264,6 @@ def test_balanced_many_tiles_plan_in_global_scratch():
     Or, lr = oracle_rows(w, rows)
     r = torch.from_numpy(rows).cuda()
     compare_bf16(to_np(O[r[:, 0], r[:, 1], r[:, 2]]), Or, f"{len(rows)} sampled rows")
-    np.testing.assert_allclose(to_np(lse[r[:, 0], r[:, 1], r[:, 2]]), lr, rtol=0, atol=LSE_ABS)
+    check_lse(to_np(lse[r[:, 0], r[:, 1], r[:, 2]]), lr)
     for b in range(B):
         assert bool((O[b, :, chunk[b]:] == 0).all())

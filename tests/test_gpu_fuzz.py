@@ -11,7 +11,7 @@ import torch
 import gen
 import chunked_prefill_sparse_amd as ca
 from oracle import sparse_attention_ref
-from tests.gpu_util import (F32_MAX_ABS, LSE_ABS, Dev, compare_bf16, oracle_full, oracle_tables,
+from tests.gpu_util import (F32_MAX_ABS, check_lse, Dev, compare_bf16, oracle_full, oracle_tables,
                             say, to_np)
 
 pytestmark = pytest.mark.gpu
@@ -45,11 +45,7 @@ def _compare(w, O, lse, Or, lr, what):
     else:
         err = float(np.abs(to_np(O) - Or).max())
         assert err <= F32_MAX_ABS, (what, err)
-    fin = np.isfinite(lr)
-    gl = to_np(lse)
-    assert np.array_equal(np.isfinite(gl), fin), what
-    np.testing.assert_allclose(gl[fin], lr[fin], rtol=0,
-                               atol=LSE_ABS if w.dtype == "bf16" else 1e-5, err_msg=what)
+    check_lse(to_np(lse), lr, what, fp32=w.dtype != "bf16")
     for b in range(w.B):
         assert np.all(to_np(O)[b, :, w.chunk[b]:] == 0), what
 

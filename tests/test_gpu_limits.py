@@ -20,7 +20,7 @@ import gen
 import chunked_prefill_sparse_amd as ca
 from chunked_prefill_sparse_amd._lib import CA_MAX_BATCH
 from oracle import chunk_attention_ref, union_tables_ref
-from tests.gpu_util import (F32_MAX_ABS, LSE_ABS, Dev, compare_bf16, oracle_full, oracle_tables,
+from tests.gpu_util import (F32_MAX_ABS, check_lse, Dev, compare_bf16, oracle_full, oracle_tables,
                             say, to_np)
 
 pytestmark = pytest.mark.gpu
@@ -53,7 +53,7 @@ def test_max_batch_ragged(dtype):
         assert np.abs(to_np(O) - Or).max() <= F32_MAX_ABS
     live = np.isfinite(lser)
     assert np.array_equal(np.isfinite(to_np(lse)), live)
-    np.testing.assert_allclose(to_np(lse)[live], lser[live], rtol=0, atol=LSE_ABS)
+    check_lse(to_np(lse)[live], lser[live])
     for b in range(B):
         assert np.all(to_np(O)[b, :, chunk[b]:] == 0)
 
@@ -128,11 +128,11 @@ def test_bf16_cache_slice_at_32bit_offset_limit():
     say(f"bf16 cache slice of {L * 256} bytes")
     O, lse, Or, lser = _large_cache_case("bf16", L, 32)
     compare_bf16(to_np(O), Or, "O")
-    np.testing.assert_allclose(to_np(lse), lser, rtol=0, atol=LSE_ABS)
+    check_lse(to_np(lse), lser)
 
 
 def test_f32_cache_slice_past_4gib():
     L = 9 * (1 << 20)  # 9 Mi tokens * 128 * 4 bytes = 4.5 GiB per (b, g) slice
     O, lse, Or, lser = _large_cache_case("f32", L, 33)
     assert np.abs(to_np(O) - Or).max() <= F32_MAX_ABS
-    np.testing.assert_allclose(to_np(lse), lser, rtol=0, atol=1e-5)
+    check_lse(to_np(lse), lser, fp32=True)
