@@ -24,7 +24,7 @@ from ._lib import CA_BLOCK, CA_MAX_BATCH, CompactAttnError  # noqa: F401
 __all__ = ["build_union_tables", "chunk_attention", "tables_to_csr", "check_tables",
            "compact_kv",
            "build_row_tables", "chunk_attention_rows", "pool_blocks", "block_mask_topk",
-           "workspace_size", "balanced_workspace_size",
+           "workspace_size", "balanced_workspace_size", "chunk_attention_split_noalloc",
            "CompactAttnError", "library_path"]
 
 
@@ -276,6 +276,32 @@ def chunk_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
         B, H_q, H_kv, C_max, L, D, CA_BLOCK, float(scale), dt, out.data_ptr(),
         lse.data_ptr() if lse is not None else None, _stream_ptr(stream))
     _lib.check(st, "ca_chunk_attention")
+    return (out, lse) if return_lse else out
+
+
+def chunk_attention_split_noalloc(q: torch.Tensor, k_cache: torch.Tensor,
+                                  v_cache: torch.Tensor, T: torch.Tensor, lens: torch.Tensor,
+                                  prior_len: Sequence[int], chunk_len: Sequence[int],
+                                  n_splits: int, scale: Optional[float] = None,
+                                  out: Optional[torch.Tensor] = None,
+                                  lse: Optional[torch.Tensor] = None, return_lse: bool = False,
+                                  stream: Optional[torch.cuda.Stream] = None):
+    """Split-KV chunk attention whose partials live in the library's static device
+    array (``ca_chunk_attention_split_noalloc``): the library allocates nothing.
+    Pass ``out`` (and ``lse``) to allocate nothing here either.  Calls that
+    overlap on one device race on the shared array."""
+    B, H_q, H_kv, C_max, L, D, scale, out, lse, dt = _attention_args(
+        q, k_cache, v_cache, scale, out, lse, return_lse)
+    _need_cuda("T", T, torch.int32)
+    _need_cuda("lens", lens, torch.int32)
+    if T.dim() != 3 or tuple(T.shape[:2]) != (B, H_kv) or tuple(lens.shape) != (B, H_kv):
+        raise ValueError("T must be [B, H_kv, NKB_max] and lens [B, H_kv]")
+    st = _lib.lib().ca_chunk_attention_split_noalloc(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), T.data_ptr(), lens.data_ptr(),
+        T.shape[2], _host_ints("prior_len", prior_len, B), _host_ints("chunk_len", chunk_len, B),
+        B, H_q, H_kv, C_max, L, D, CA_BLOCK, scale, dt, int(n_splits), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, _stream_ptr(stream))
+    _lib.check(st, "ca_chunk_attention_split_noalloc")
     return (out, lse) if return_lse else out
 
 

@@ -17,12 +17,15 @@ CA_BF16 = 1
 CA_BLOCK = 64
 CA_MAX_BATCH = 128
 CA_MAX_SPLITS = 16
+CA_STATIC_SCRATCH_BYTES = 64 << 20
+CA_ERR_TOO_LARGE = 6
 
 EXPORTED = (
     "ca_build_union_tables",
     "ca_chunk_attention",
     "ca_chunk_attention_rows",
     "ca_chunk_attention_split",
+    "ca_chunk_attention_split_noalloc",
     "ca_chunk_attention_workspace_size",
     "ca_chunk_attention_balanced",
     "ca_chunk_attention_balanced_workspace_size",
@@ -60,6 +63,10 @@ def _declare(lib):
                                              _i32, _i32, _i32, _i64, _i32, _i32, ctypes.c_float,
                                              _i32, _i32, _vp, ctypes.c_size_t, _vp, _vp, _vp]
     lib.ca_chunk_attention_split.restype = _i32
+    lib.ca_chunk_attention_split_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32p, _i32p,
+                                                     _i32, _i32, _i32, _i32, _i64, _i32, _i32,
+                                                     ctypes.c_float, _i32, _i32, _vp, _vp, _vp]
+    lib.ca_chunk_attention_split_noalloc.restype = _i32
     lib.ca_chunk_attention_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
     lib.ca_chunk_attention_workspace_size.restype = ctypes.c_size_t
     lib.ca_chunk_attention_balanced.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32p, _i32p, _i32,

@@ -1,7 +1,8 @@
 // C ABI of the CompactAttention chunked-prefill path: host-side validation,
 // scheduling metadata and kernel launches.  The library allocates nothing and
 // keeps no state beyond a per-thread copy of the last HIP error text and a
-// per-device cache of the compute-unit count.
+// per-device cache of the compute-unit count (the static scratch array of
+// ca_chunk_attention_split_noalloc lives in static_scratch.hip).
 
 #include <math.h>
 #include <stdio.h>
@@ -57,6 +58,8 @@ CA_EXPORT const char* ca_status_string(ca_status s) {
     case CA_ERR_DTYPE: return "CA_ERR_DTYPE: unknown element type";
     case CA_ERR_UNSUPPORTED: return "CA_ERR_UNSUPPORTED: request this library does not run";
     case CA_ERR_HIP: return "CA_ERR_HIP: the HIP runtime reported an error";
+    case CA_ERR_TOO_LARGE:
+      return "CA_ERR_TOO_LARGE: the call needs more than the library's static scratch memory";
   }
   return "unknown ca_status";
 }
@@ -147,7 +150,7 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
                     const int32_t* chunk_len, int B, int H_q, int H_kv, int C_max, int64_t L,
                     int D, int block, float scale, ca_dtype dtype, void* O, float* lse,
                     bool row_tables, int n_split, void* workspace, size_t workspace_bytes,
-                    hipStream_t stream, bool balanced = false) {
+                    hipStream_t stream, bool balanced = false, bool static_scratch = false) {
   if (!Q || !K_cache || !V_cache || !T || !len || !prior_len || !chunk_len || !O)
     return CA_ERR_NULL;
   if (dtype != CA_F32 && dtype != CA_BF16) return CA_ERR_DTYPE;
@@ -164,7 +167,8 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
   int64_t work[CA_MAX_BATCH];
   for (int b = 0; b < B; ++b) {
     const int64_t P = prior_len[b], C = chunk_len[b];
-    if (P < 0 || C < 0 || C > C_max || P + C > L || P + C > static_cast<int64_t>(NKB_max) * CA_BLOCK)
+    if (P < 0 || C < 0 || C > C_max || P + C > L ||
+        P + C > static_cast<int64_t>(NKB_max) * CA_BLOCK)
       return CA_ERR_SHAPE;
     if (P % CA_BLOCK != 0 || C % CA_BLOCK != 0) return CA_ERR_UNSUPPORTED;
     seq.prior[b] = static_cast<int32_t>(P);
@@ -228,6 +232,11 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
     p.xcd = (n_bg % 8 == 0) ? 1 : 0;
     if (n_bg * p.n_t * n_split > INT32_MAX) return CA_ERR_SHAPE;
     if (n_split > 1) {
+      if (static_scratch) {  // every argument checked: now look up the array
+        hipError_t e = hipSuccess;
+        workspace = ca::static_scratch_address(&e);
+        if (workspace == nullptr) return hip_status(e);
+      }
       float* part_o = static_cast<float*>(workspace);
       float* part_ml = part_o + static_cast<size_t>(n_split) * p.rows_total * D;
       return hip_status(ca::launch_chunk_attn_bf16_split(Q, K_cache, V_cache, T, len, O, lse, B,
@@ -244,6 +253,11 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
   const float* k = static_cast<const float*>(K_cache);
   const float* v = static_cast<const float*>(V_cache);
   if (n_split > 1) {
+    if (static_scratch) {
+      hipError_t e = hipSuccess;
+      workspace = ca::static_scratch_address(&e);
+      if (workspace == nullptr) return hip_status(e);
+    }
     float* part_o = static_cast<float*>(workspace);
     float* part_ml = part_o + static_cast<size_t>(n_split) * p.rows_total * D;
     return hip_status(ca::launch_chunk_attn_f32_split(q, k, v, T, len, static_cast<float*>(O),
@@ -296,6 +310,27 @@ CA_EXPORT ca_status ca_chunk_attention_split(const void* Q, const void* K_cache,
   return attention(Q, K_cache, V_cache, T, len, 0, NKB_max, prior_len, chunk_len, B, H_q, H_kv,
                    C_max, L, D, block, scale, dtype, O, lse, false, n_splits, workspace,
                    workspace_bytes, stream);
+}
+
+CA_EXPORT ca_status ca_chunk_attention_split_noalloc(
+    const void* Q, const void* K_cache, const void* V_cache, const int32_t* T,
+    const int32_t* len, int NKB_max, const int32_t* prior_len, const int32_t* chunk_len, int B,
+    int H_q, int H_kv, int C_max, int64_t L, int D, int block, float scale, ca_dtype dtype,
+    int n_splits, void* O, float* lse, hipStream_t stream) {
+  if (n_splits < 1 || n_splits > CA_MAX_SPLITS) return CA_ERR_SHAPE;
+  if (n_splits == 1)
+    return attention(Q, K_cache, V_cache, T, len, 0, NKB_max, prior_len, chunk_len, B, H_q,
+                     H_kv, C_max, L, D, block, scale, dtype, O, lse, false, 1, nullptr, 0, stream);
+  // the partials must fit the static array; checked before anything touches the device
+  if (B >= 1 && H_q >= 1 && C_max >= 1 && (D == 64 || D == 128) &&
+      ca_chunk_attention_workspace_size(B, H_q, C_max, D, n_splits) > CA_STATIC_SCRATCH_BYTES)
+    return CA_ERR_TOO_LARGE;
+  // every split writes its partials for every live row before the merge reads
+  // them, so nothing in the array needs clearing between calls; the array's
+  // address is looked up only once the arguments have passed every check
+  return attention(Q, K_cache, V_cache, T, len, 0, NKB_max, prior_len, chunk_len, B, H_q, H_kv,
+                   C_max, L, D, block, scale, dtype, O, lse, false, n_splits, nullptr,
+                   CA_STATIC_SCRATCH_BYTES, stream, false, true);
 }
 
 CA_EXPORT size_t ca_chunk_attention_balanced_workspace_size(int B, int H_q, int H_kv, int C_max,

@@ -58,6 +58,11 @@ struct AttnParams {
   const int32_t* plan_pieces;
 };
 
+// Device address of the library's static scratch array (CA_STATIC_SCRATCH_BYTES)
+// on the current device, looked up once per device; nullptr, with the HIP
+// error in *err, if the lookup fails.
+void* static_scratch_address(hipError_t* err);
+
 hipError_t launch_union_tables(const uint8_t* mask, int B, int H_q, int H_kv, int NQ_max,
                                int NKB_max, const UnionExtents& ext, int32_t* T,
                                int32_t* len, hipStream_t stream);

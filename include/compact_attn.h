@@ -22,7 +22,8 @@
  *
  * Conventions shared by every call
  *   - Ownership: the caller allocates and frees every buffer.  The library
- *     never allocates or frees device memory and keeps no mutable state.
+ *     never allocates or frees device memory and keeps no mutable state,
+ *     except the static device array of ca_chunk_attention_split_noalloc.
  *   - Device pointers point to device memory of the current HIP device.  Host
  *     arrays are read during the call only.
  *   - Asynchrony: every call enqueues its kernels on `stream` (0 = the null
@@ -52,6 +53,9 @@ extern "C" {
 #define CA_BLOCK 64      /* tokens per KV block and per Q-block */
 #define CA_MAX_BATCH 128 /* sequences per call */
 #define CA_MAX_SPLITS 16 /* split-KV ranges per (sequence, KV head) */
+/* Bytes of the library's static device array behind
+ * ca_chunk_attention_split_noalloc: 64 MiB, one copy per device. */
+#define CA_STATIC_SCRATCH_BYTES (64u << 20)
 
 typedef enum {
   CA_OK = 0,
@@ -59,7 +63,8 @@ typedef enum {
   CA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
   CA_ERR_DTYPE = 3,       /* unknown element type */
   CA_ERR_UNSUPPORTED = 4, /* valid request this library does not run (see each call) */
-  CA_ERR_HIP = 5          /* the HIP runtime reported an error */
+  CA_ERR_HIP = 5,         /* the HIP runtime reported an error */
+  CA_ERR_TOO_LARGE = 6    /* needs more than CA_STATIC_SCRATCH_BYTES (no-alloc call only) */
 } ca_status;
 
 typedef enum { CA_F32 = 0, CA_BF16 = 1 } ca_dtype;
@@ -178,6 +183,39 @@ CA_EXPORT ca_status ca_chunk_attention_split(const void* Q, const void* K_cache,
  * n_splits < 2 or nonpositive sizes. */
 CA_EXPORT size_t ca_chunk_attention_workspace_size(int B, int H_q, int C_max, int D,
                                          int n_splits);
+
+/*
+ * ca_chunk_attention_split_noalloc -- ca_chunk_attention_split for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The split partials live in
+ * a static device array of CA_STATIC_SCRATCH_BYTES inside the library (one
+ * copy per device, held until the process ends) instead of a caller
+ * workspace; the caller still passes every input and output.  The call makes
+ * no hipMalloc, hipFree or other allocating call.  The array's device address
+ * is looked up (hipGetSymbolAddress) on the first call on each device, after
+ * the arguments have been checked.
+ *
+ * Same kernels, arguments, layouts and result as ca_chunk_attention_split
+ * with n_splits, bit for bit.  n_splits == 1 runs ca_chunk_attention (the
+ * array is not used).
+ * Limit: ca_chunk_attention_workspace_size(B, H_q, C_max, D, n_splits) must
+ * not exceed CA_STATIC_SCRATCH_BYTES, else CA_ERR_TOO_LARGE (nothing is
+ * enqueued).  For example one GPU's tensor-parallel share of a 2048-token
+ * chunk (H_q = 4, D = 128) at n_splits = 8 needs 32.5 MiB.
+ * Every call on one device shares that device's array and leaves its partials
+ * there: calls that overlap on one device (different streams, or threads
+ * without ordering) race and give wrong results; order them on one stream.
+ * Nothing in the array needs to start at zero.
+ * Errors: those of ca_chunk_attention_split, and CA_ERR_TOO_LARGE.
+ */
+CA_EXPORT ca_status ca_chunk_attention_split_noalloc(const void* Q, const void* K_cache,
+                                           const void* V_cache, const int32_t* T,
+                                           const int32_t* len, int NKB_max,
+                                           const int32_t* prior_len, const int32_t* chunk_len,
+                                           int B, int H_q, int H_kv, int C_max, int64_t L,
+                                           int D, int block, float scale, ca_dtype dtype,
+                                           int n_splits, void* O, float* lse,
+                                           hipStream_t stream);
 
 /*
  * ca_chunk_attention_balanced -- ca_chunk_attention with the work spread

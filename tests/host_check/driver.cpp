@@ -94,6 +94,30 @@ int main() {
     EXPECT(strcmp(stub::last.what, "attn_f32_split") == 0 && stub::last.p.n_split == 4);
     EXPECT((char*)stub::last.ptrs[1] - (char*)stub::last.ptrs[0] ==
            (ptrdiff_t)(4LL * 3 * 32 * 256 * 128 * 4));
+    // no-alloc split: the partials go to the static array (its stand-in address),
+    // same layout; a split past the array's size is refused before any launch
+    {
+      char* const sa = reinterpret_cast<char*>(static_cast<uintptr_t>(0x5c7a7c400000ull));
+      stub::last = stub::Record{};
+      EXPECT(ca_chunk_attention_split_noalloc(FAKE, FAKE, FAKE, (const int32_t*)FAKE,
+                                              (const int32_t*)FAKE, 200, prior, chunk, 3, 32, 8,
+                                              256, 8448, 128, 64, 0.125f, CA_BF16, 4, FAKE,
+                                              nullptr, 0) == CA_OK);
+      EXPECT(strcmp(stub::last.what, "attn_bf16_split") == 0 && stub::last.p.n_split == 4);
+      EXPECT((char*)stub::last.ptrs[0] == sa);
+      EXPECT((char*)stub::last.ptrs[1] - sa == (ptrdiff_t)(4LL * 3 * 32 * 256 * 128 * 4));
+      EXPECT(ca_chunk_attention_split_noalloc(FAKE, FAKE, FAKE, (const int32_t*)FAKE,
+                                              (const int32_t*)FAKE, 200, prior, chunk, 3, 32, 8,
+                                              256, 8448, 128, 64, 0.125f, CA_F32, 4, FAKE,
+                                              nullptr, 0) == CA_OK);
+      EXPECT(strcmp(stub::last.what, "attn_f32_split") == 0 && (char*)stub::last.ptrs[0] == sa);
+      stub::last = stub::Record{};
+      EXPECT(ca_chunk_attention_split_noalloc(FAKE, FAKE, FAKE, (const int32_t*)FAKE,
+                                              (const int32_t*)FAKE, 200, prior, chunk, 3, 32, 8,
+                                              256, 8448, 128, 64, 0.125f, CA_BF16, 8, FAKE,
+                                              nullptr, 0) == CA_ERR_TOO_LARGE);
+      EXPECT(strcmp(stub::last.what, "") == 0);
+    }
     // balanced: workspace layout (partials for 8 pieces, then the plan and the
     // pieces per tile), size check, 8-wave tiles, fp32 runs unplanned
     const size_t bneed = ca_chunk_attention_balanced_workspace_size(3, 32, 8, 256, 128);

@@ -10,6 +10,13 @@ Record last;
 
 namespace ca {
 
+// Stand-in for the static scratch array's address: a recognisable fake
+// pointer, never dereferenced (the launcher stand-ins only record it).
+void* static_scratch_address(hipError_t* err) {
+  *err = hipSuccess;
+  return reinterpret_cast<void*>(static_cast<uintptr_t>(0x5c7a7c400000ull));
+}
+
 hipError_t launch_union_tables(const uint8_t*, int B, int H_q, int H_kv, int NQ_max, int NKB_max,
                                const UnionExtents& ext, int32_t*, int32_t*, hipStream_t) {
   stub::last = stub::Record{};

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = _lib.lib()
-    for s in range(6):
+    for s in range(7):
         assert lib.ca_status_string(s).decode().startswith("CA_")
     assert lib.ca_status_string(99).decode() == "unknown ca_status"
     assert lib.ca_last_hip_error().decode() == ""
@@ -190,3 +190,31 @@ def test_balanced_validation_and_workspace_size():
     assert lib.ca_chunk_attention_balanced(*base, 7, FAKE, need, FAKE, None, None) == 3
     bad = base[:10] + (3,) + base[11:]  # H_q = 4 over H_kv = 3
     assert lib.ca_chunk_attention_balanced(*bad, 1, FAKE, need, FAKE, None, None) == 2
+
+
+def test_split_noalloc_validation():
+    # Sizes past the static array and bad arguments are refused on the host,
+    # before the array's address is looked up (no GPU is touched here).
+    lib = _lib.lib()
+    base = (FAKE, FAKE, FAKE, FAKE, FAKE, 20, _ints(1024), _ints(256), 1, 4, 1, 256, 1280, 64, 64,
+            0.125)
+    assert lib.ca_chunk_attention_split_noalloc(*base, 1, 17, FAKE, None, None) == 2
+    assert lib.ca_chunk_attention_split_noalloc(*base, 1, 0, FAKE, None, None) == 2
+    assert lib.ca_chunk_attention_split_noalloc(None, *base[1:], 1, 4, FAKE, None, None) == 1
+    assert lib.ca_chunk_attention_split_noalloc(*base, 9, 4, FAKE, None, None) == 3
+    assert lib.ca_chunk_attention_split_noalloc(*base[:13], 96, *base[14:], 1, 4, FAKE, None,
+                                                None) == 4
+    # one GPU's tensor-parallel share of a 2048-row chunk (4 heads, D = 128: 130 floats per
+    # row and split) fits at 15 splits and not at 16
+    cap = _lib.CA_STATIC_SCRATCH_BYTES
+    assert lib.ca_chunk_attention_workspace_size(1, 4, 2048, 128, 15) == 15 * 4259840 <= cap
+    assert lib.ca_chunk_attention_workspace_size(1, 4, 2048, 128, 16) > cap
+    tp = (FAKE, FAKE, FAKE, FAKE, FAKE, 2048, _ints(129024), _ints(2048), 1, 4, 1, 2048,
+          131072, 128, 64, 0.088)
+    assert lib.ca_chunk_attention_split_noalloc(*tp, 1, 16, FAKE, None, None) == \
+        _lib.CA_ERR_TOO_LARGE
+    # the whole 32-head chunk fits no split at all (65 MiB at 2)
+    big = tp[:9] + (32, 8) + tp[11:]
+    assert lib.ca_chunk_attention_split_noalloc(*big, 1, 2, FAKE, None, None) == \
+        _lib.CA_ERR_TOO_LARGE
+    assert lib.ca_status_string(_lib.CA_ERR_TOO_LARGE).decode().startswith("CA_ERR_TOO_LARGE")
