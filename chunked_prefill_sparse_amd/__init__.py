@@ -22,6 +22,7 @@ from . import _lib
 from ._lib import CA_BLOCK, CA_MAX_BATCH, CompactAttnError  # noqa: F401
 
 __all__ = ["build_union_tables", "chunk_attention", "tables_to_csr", "check_tables",
+           "build_union_tables_devlen", "chunk_attention_devlen",
            "compact_kv",
            "build_row_tables", "chunk_attention_rows", "pool_blocks", "block_mask_topk",
            "workspace_size", "balanced_workspace_size", "chunk_attention_split_noalloc",
@@ -82,6 +83,67 @@ def build_union_tables(mask: torch.Tensor, H_kv: int, n_q_blocks: Sequence[int],
         _stream_ptr(stream))
     _lib.check(st, "ca_build_union_tables")
     return T, lens
+
+
+def _dev_ints(name: str, t: torch.Tensor, B: int):
+    _need_cuda(name, t, torch.int32)
+    if t.dim() != 1 or t.shape[0] != B:
+        raise ValueError(f"{name} must be a device int32 tensor of {B} entries")
+    return t.data_ptr()
+
+
+def build_union_tables_devlen(mask: torch.Tensor, H_kv: int, n_q_blocks: torch.Tensor,
+                              n_kv_blocks: torch.Tensor, T: Optional[torch.Tensor] = None,
+                              lens: Optional[torch.Tensor] = None,
+                              stream: Optional[torch.cuda.Stream] = None
+                              ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """``build_union_tables`` with the extents n_q_blocks / n_kv_blocks as device
+    int32 [B] tensors, read by the kernel when it runs (graph replay with new
+    extents)."""
+    _need_cuda("mask", mask, torch.uint8)
+    if mask.dim() != 4:
+        raise ValueError("mask must be [B, H_q, NQ_max, NKB_max]")
+    B, H_q, NQ_max, NKB_max = mask.shape
+    if H_kv < 1 or H_q % H_kv:
+        raise ValueError("H_q must be a positive multiple of H_kv")
+    if T is None:
+        T = torch.empty((B, H_kv, NKB_max), dtype=torch.int32, device=mask.device)
+    if lens is None:
+        lens = torch.empty((B, H_kv), dtype=torch.int32, device=mask.device)
+    _need_cuda("T", T, torch.int32)
+    _need_cuda("lens", lens, torch.int32)
+    if tuple(T.shape) != (B, H_kv, NKB_max) or tuple(lens.shape) != (B, H_kv):
+        raise ValueError("T / lens have the wrong shape")
+    st = _lib.lib().ca_build_union_tables_devlen(
+        mask.data_ptr(), B, H_q, H_kv, NQ_max, NKB_max, _dev_ints("n_q_blocks", n_q_blocks, B),
+        _dev_ints("n_kv_blocks", n_kv_blocks, B), T.data_ptr(), lens.data_ptr(),
+        _stream_ptr(stream))
+    _lib.check(st, "ca_build_union_tables_devlen")
+    return T, lens
+
+
+def chunk_attention_devlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           T: torch.Tensor, lens: torch.Tensor, prior_len: torch.Tensor,
+                           chunk_len: torch.Tensor, scale: Optional[float] = None,
+                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                           return_lse: bool = False, stream: Optional[torch.cuda.Stream] = None):
+    """``chunk_attention`` with prior_len / chunk_len as device int32 [B] tensors,
+    read by the kernels when they run: one captured graph serves every chunk
+    offset.  Lengths that break the call's limits give that sequence O = 0 and
+    lse = -inf."""
+    B, H_q, H_kv, C_max, L, D, scale, out, lse, dt = _attention_args(
+        q, k_cache, v_cache, scale, out, lse, return_lse)
+    _need_cuda("T", T, torch.int32)
+    _need_cuda("lens", lens, torch.int32)
+    if T.dim() != 3 or tuple(T.shape[:2]) != (B, H_kv) or tuple(lens.shape) != (B, H_kv):
+        raise ValueError("T must be [B, H_kv, NKB_max] and lens [B, H_kv]")
+    st = _lib.lib().ca_chunk_attention_devlen(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), T.data_ptr(), lens.data_ptr(),
+        T.shape[2], _dev_ints("prior_len", prior_len, B), _dev_ints("chunk_len", chunk_len, B),
+        B, H_q, H_kv, C_max, L, D, CA_BLOCK, scale, dt, out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, _stream_ptr(stream))
+    _lib.check(st, "ca_chunk_attention_devlen")
+    return (out, lse) if return_lse else out
 
 
 def check_tables(T: torch.Tensor, lens: torch.Tensor, n_kv_blocks: Sequence[int],

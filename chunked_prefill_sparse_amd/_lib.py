@@ -22,7 +22,9 @@ CA_ERR_TOO_LARGE = 6
 
 EXPORTED = (
     "ca_build_union_tables",
+    "ca_build_union_tables_devlen",
     "ca_chunk_attention",
+    "ca_chunk_attention_devlen",
     "ca_chunk_attention_rows",
     "ca_chunk_attention_split",
     "ca_chunk_attention_split_noalloc",
@@ -51,10 +53,17 @@ def _declare(lib):
     lib.ca_build_union_tables.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _i32p, _i32p,
                                           _vp, _vp, _vp]
     lib.ca_build_union_tables.restype = _i32
+    lib.ca_build_union_tables_devlen.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                                 _vp, _vp, _vp]
+    lib.ca_build_union_tables_devlen.restype = _i32
     lib.ca_chunk_attention.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32p, _i32p, _i32, _i32,
                                        _i32, _i32, _i64, _i32, _i32, ctypes.c_float, _i32, _vp,
                                        _vp, _vp]
     lib.ca_chunk_attention.restype = _i32
+    lib.ca_chunk_attention_devlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
+                                              _i32, _i32, _i32, _i64, _i32, _i32, ctypes.c_float,
+                                              _i32, _vp, _vp, _vp]
+    lib.ca_chunk_attention_devlen.restype = _i32
     lib.ca_chunk_attention_rows.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32p, _i32p,
                                             _i32, _i32, _i32, _i32, _i64, _i32, _i32,
                                             ctypes.c_float, _i32, _vp, _vp, _vp]

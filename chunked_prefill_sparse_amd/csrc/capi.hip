@@ -84,8 +84,26 @@ CA_EXPORT ca_status ca_build_union_tables(const uint8_t* mask, int B, int H_q, i
     ext.nq[b] = n_q_blocks[b];
     ext.nkb[b] = n_kv_blocks[b];
   }
-  return hip_status(
-      ca::launch_union_tables(mask, B, H_q, H_kv, NQ_max, NKB_max, ext, T, len, stream));
+  return hip_status(ca::launch_union_tables(mask, B, H_q, H_kv, NQ_max, NKB_max, ext, nullptr,
+                                            nullptr, T, len, stream));
+}
+
+CA_EXPORT ca_status ca_build_union_tables_devlen(const uint8_t* mask, int B, int H_q, int H_kv,
+                                                 int NQ_max, int NKB_max,
+                                                 const int32_t* n_q_blocks,
+                                                 const int32_t* n_kv_blocks, int32_t* T,
+                                                 int32_t* len, hipStream_t stream) {
+  if (!mask || !n_q_blocks || !n_kv_blocks || !T || !len) return CA_ERR_NULL;
+  if (B < 1 || B > CA_MAX_BATCH || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || NQ_max < 1 ||
+      NKB_max < 1 || NKB_max > kMaxUnionBlocks)
+    return CA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H_kv > (1 << 30)) return CA_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(n_q_blocks) | reinterpret_cast<uintptr_t>(n_kv_blocks)) & 3u)
+    return CA_ERR_UNSUPPORTED;
+  ca::UnionExtents ext;  // unused: the kernel reads the extents from device memory
+  memset(&ext, 0, sizeof(ext));
+  return hip_status(ca::launch_union_tables(mask, B, H_q, H_kv, NQ_max, NKB_max, ext,
+                                            n_q_blocks, n_kv_blocks, T, len, stream));
 }
 
 CA_EXPORT ca_status ca_check_tables(const int32_t* T, const int32_t* len, int B, int H_kv,
@@ -150,7 +168,8 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
                     const int32_t* chunk_len, int B, int H_q, int H_kv, int C_max, int64_t L,
                     int D, int block, float scale, ca_dtype dtype, void* O, float* lse,
                     bool row_tables, int n_split, void* workspace, size_t workspace_bytes,
-                    hipStream_t stream, bool balanced = false, bool static_scratch = false) {
+                    hipStream_t stream, bool balanced = false, bool static_scratch = false,
+                    bool dev_lengths = false) {
   if (!Q || !K_cache || !V_cache || !T || !len || !prior_len || !chunk_len || !O)
     return CA_ERR_NULL;
   if (dtype != CA_F32 && dtype != CA_BF16) return CA_ERR_DTYPE;
@@ -164,21 +183,28 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
     return CA_ERR_UNSUPPORTED;
   ca::SeqInfo seq;
   memset(&seq, 0, sizeof(seq));
-  int64_t work[CA_MAX_BATCH];
-  for (int b = 0; b < B; ++b) {
-    const int64_t P = prior_len[b], C = chunk_len[b];
-    if (P < 0 || C < 0 || C > C_max || P + C > L ||
-        P + C > static_cast<int64_t>(NKB_max) * CA_BLOCK)
-      return CA_ERR_SHAPE;
-    if (P % CA_BLOCK != 0 || C % CA_BLOCK != 0) return CA_ERR_UNSUPPORTED;
-    seq.prior[b] = static_cast<int32_t>(P);
-    seq.chunk[b] = static_cast<int32_t>(C);
-    work[b] = (P + C) * C;  // dense upper bound of the sequence's attention work
+  if (dev_lengths) {
+    // lengths stay on the device (the kernels check them); sequences in order
+    if ((reinterpret_cast<uintptr_t>(prior_len) | reinterpret_cast<uintptr_t>(chunk_len)) & 3u)
+      return CA_ERR_UNSUPPORTED;
+    for (int r = 0; r < B; ++r) seq.order[r] = r;
+  } else {
+    int64_t work[CA_MAX_BATCH];
+    for (int b = 0; b < B; ++b) {
+      const int64_t P = prior_len[b], C = chunk_len[b];
+      if (P < 0 || C < 0 || C > C_max || P + C > L ||
+          P + C > static_cast<int64_t>(NKB_max) * CA_BLOCK)
+        return CA_ERR_SHAPE;
+      if (P % CA_BLOCK != 0 || C % CA_BLOCK != 0) return CA_ERR_UNSUPPORTED;
+      seq.prior[b] = static_cast<int32_t>(P);
+      seq.chunk[b] = static_cast<int32_t>(C);
+      work[b] = (P + C) * C;  // dense upper bound of the sequence's attention work
+    }
+    int order[CA_MAX_BATCH];
+    std::iota(order, order + B, 0);
+    std::stable_sort(order, order + B, [&](int a, int c) { return work[a] > work[c]; });
+    for (int r = 0; r < B; ++r) seq.order[r] = order[r];
   }
-  int order[CA_MAX_BATCH];
-  std::iota(order, order + B, 0);
-  std::stable_sort(order, order + B, [&](int a, int c) { return work[a] > work[c]; });
-  for (int r = 0; r < B; ++r) seq.order[r] = order[r];
 
   ca::AttnParams p;
   p.H_q = H_q;
@@ -197,6 +223,8 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
   p.cus = device_cus();
   p.plan_items = nullptr;
   p.plan_pieces = nullptr;
+  p.dev_prior = dev_lengths ? prior_len : nullptr;
+  p.dev_chunk = dev_lengths ? chunk_len : nullptr;
   const int64_t n_bg = static_cast<int64_t>(B) * H_kv;
   if (dtype == CA_BF16) {
     // the bf16 kernels address one (b, g) cache slice through a buffer
@@ -281,6 +309,18 @@ CA_EXPORT ca_status ca_chunk_attention(const void* Q, const void* K_cache, const
                                        float* lse, hipStream_t stream) {
   return attention(Q, K_cache, V_cache, T, len, 0, NKB_max, prior_len, chunk_len, B, H_q, H_kv,
                    C_max, L, D, block, scale, dtype, O, lse, false, 1, nullptr, 0, stream);
+}
+
+CA_EXPORT ca_status ca_chunk_attention_devlen(const void* Q, const void* K_cache,
+                                              const void* V_cache, const int32_t* T,
+                                              const int32_t* len, int NKB_max,
+                                              const int32_t* prior_len, const int32_t* chunk_len,
+                                              int B, int H_q, int H_kv, int C_max, int64_t L,
+                                              int D, int block, float scale, ca_dtype dtype,
+                                              void* O, float* lse, hipStream_t stream) {
+  return attention(Q, K_cache, V_cache, T, len, 0, NKB_max, prior_len, chunk_len, B, H_q, H_kv,
+                   C_max, L, D, block, scale, dtype, O, lse, false, 1, nullptr, 0, stream, false,
+                   false, true);
 }
 
 CA_EXPORT size_t ca_chunk_attention_workspace_size(int B, int H_q, int C_max, int D,

@@ -186,8 +186,8 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
     b = seq.order[rank];
   }
   const bool partials = kSplit != 0 && n_split > 1;  // else O and lse written here
-  const int P = seq.prior[b];
-  const int C = seq.chunk[b];
+  int P, C;
+  seq_lengths(p, seq, b, P, C);
   const int bg = b * p.H_kv + g;
 
   const int n_pb = (p.C_max + kRowsPerWave - 1) / kRowsPerWave;
@@ -573,8 +573,10 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const float* __restr
   const int64_t per_b = static_cast<int64_t>(p.H_q) * p.C_max;
   const int b = static_cast<int>(r / per_b);
   const int i = static_cast<int>(r % p.C_max);
+  int P_b, C_b;
+  seq_lengths(p, seq, b, P_b, C_b);
   float M = -INFINITY;
-  if (i < seq.chunk[b])
+  if (i < C_b)
     for (int sp = 0; sp < p.n_split; ++sp)
       M = fmaxf(M, part_ml[2 * (static_cast<size_t>(sp) * p.rows_total + r)]);
   float acc[E], l = 0.f;

@@ -68,8 +68,8 @@ __global__ __launch_bounds__(kThreadsF) void chunk_attn_f32_kernel(
   const int h = bh - rank * p.H_q;
   const int b = seq.order[rank];
   const int g = h / p.G;
-  const int P = seq.prior[b];
-  const int C = seq.chunk[b];
+  int P, C;
+  seq_lengths(p, seq, b, P, C);
   const int bg = b * p.H_kv + g;
 
   const int row = tile * kRowsF + tid / kTpr;

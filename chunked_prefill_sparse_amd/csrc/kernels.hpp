@@ -56,16 +56,46 @@ struct AttnParams {
   // plan_pieces[(b * H_kv + g) * n_t + tile] = n
   const int32_t* plan_items;
   const int32_t* plan_pieces;
+  // device-length calls: prior and chunk lengths read from device int32 [B]
+  // arrays (nullptr: the host values in SeqInfo)
+  const int32_t* dev_prior;
+  const int32_t* dev_chunk;
 };
+
+// Prior and chunk length of sequence b in a kernel.  Host-length calls pass
+// values the host has already checked.  Device-length calls read them from
+// device memory and check them here against the call's limits: a sequence
+// whose lengths are negative, not multiples of 64, a chunk past C_max, or a
+// total past the cache capacity or the table length runs as an empty chunk
+// (its rows give O = 0 and lse = -inf; nothing else is read).
+__device__ __forceinline__ void seq_lengths(const AttnParams& p, const SeqInfo& seq, int b,
+                                            int& P, int& C) {
+  if (p.dev_prior == nullptr) {
+    P = seq.prior[b];
+    C = seq.chunk[b];
+    return;
+  }
+  const int P_ = p.dev_prior[b];
+  const int C_ = p.dev_chunk[b];
+  const int64_t cap = p.L < 64 * static_cast<int64_t>(p.NKB_max)
+                          ? p.L : 64 * static_cast<int64_t>(p.NKB_max);
+  const bool ok = P_ >= 0 && C_ >= 0 && ((P_ | C_) & 63) == 0 && C_ <= p.C_max &&
+                  static_cast<int64_t>(P_) + C_ <= cap;
+  P = ok ? P_ : 0;
+  C = ok ? C_ : 0;
+}
 
 // Device address of the library's static scratch array (CA_STATIC_SCRATCH_BYTES)
 // on the current device, looked up once per device; nullptr, with the HIP
 // error in *err, if the lookup fails.
 void* static_scratch_address(hipError_t* err);
 
+// dev_nq / dev_nkb: device int32 [B] extents (device-length call), or nullptr
+// to use ext.
 hipError_t launch_union_tables(const uint8_t* mask, int B, int H_q, int H_kv, int NQ_max,
-                               int NKB_max, const UnionExtents& ext, int32_t* T,
-                               int32_t* len, hipStream_t stream);
+                               int NKB_max, const UnionExtents& ext, const int32_t* dev_nq,
+                               const int32_t* dev_nkb, int32_t* T, int32_t* len,
+                               hipStream_t stream);
 
 hipError_t launch_check_tables(const int32_t* T, const int32_t* len, int n_bg, int H_kv,
                                int NKB_max, const UnionExtents& ext, int32_t* row_bad,

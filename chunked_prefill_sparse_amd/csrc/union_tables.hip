@@ -48,7 +48,8 @@ __device__ inline uint32_t nonzero_bytes4(uint32_t x) {
 template <int VW>  // bytes per load: 16 (rows 16-byte aligned) or 1
 __global__ __launch_bounds__(kUnionThreads) void union_tables_kernel(
     const uint8_t* __restrict__ mask, int H_q, int H_kv, int NQ_max, int NKB_max,
-    UnionExtents ext, int32_t* __restrict__ T, int32_t* __restrict__ len) {
+    UnionExtents ext, const int32_t* __restrict__ dev_nq, const int32_t* __restrict__ dev_nkb,
+    int32_t* __restrict__ T, int32_t* __restrict__ len) {
   extern __shared__ uint32_t bitmap[];  // ceil(NKB_max / 32) words
   __shared__ int wave_total[kUnionWaves];
 
@@ -56,8 +57,13 @@ __global__ __launch_bounds__(kUnionThreads) void union_tables_kernel(
   const int b = bg / H_kv;
   const int g = bg - b * H_kv;
   const int G = H_q / H_kv;
-  const int nq = ext.nq[b];
-  const int nkb = ext.nkb[b];
+  int nq = ext.nq[b];
+  int nkb = ext.nkb[b];
+  if (dev_nq != nullptr) {  // device extents: out of range -> an empty table
+    nq = dev_nq[b];
+    nkb = dev_nkb[b];
+    if (nq < 0 || nq > NQ_max || nkb < 0 || nkb > NKB_max) nq = nkb = 0;
+  }
   const int tid = threadIdx.x;
   const int nwords = (NKB_max + 31) >> 5;
 
@@ -218,17 +224,18 @@ __global__ __launch_bounds__(kCheckThreads) void check_tables_kernel(
 }  // namespace
 
 hipError_t launch_union_tables(const uint8_t* mask, int B, int H_q, int H_kv, int NQ_max,
-                               int NKB_max, const UnionExtents& ext, int32_t* T,
-                               int32_t* len, hipStream_t stream) {
+                               int NKB_max, const UnionExtents& ext, const int32_t* dev_nq,
+                               const int32_t* dev_nkb, int32_t* T, int32_t* len,
+                               hipStream_t stream) {
   const size_t lds = static_cast<size_t>((NKB_max + 31) / 32) * sizeof(uint32_t);
   const bool vec = (NKB_max % 16 == 0) && (reinterpret_cast<uintptr_t>(mask) % 16 == 0);
   dim3 grid(B * H_kv), block(kUnionThreads);
   if (vec)
     hipLaunchKernelGGL(union_tables_kernel<16>, grid, block, lds, stream, mask, H_q, H_kv,
-                       NQ_max, NKB_max, ext, T, len);
+                       NQ_max, NKB_max, ext, dev_nq, dev_nkb, T, len);
   else
     hipLaunchKernelGGL(union_tables_kernel<1>, grid, block, lds, stream, mask, H_q, H_kv,
-                       NQ_max, NKB_max, ext, T, len);
+                       NQ_max, NKB_max, ext, dev_nq, dev_nkb, T, len);
   return hipGetLastError();
 }
 

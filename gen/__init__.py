@@ -9,6 +9,7 @@ from .workloads import (  # noqa: F401
     BLOCK,
     WORKLOADS,
     VSLASH_DENSITIES,
+    VSLASH_HEAD_MODES,
     Workload,
     bf16_bits_to_f32,
     make_custom,

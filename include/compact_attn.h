@@ -103,6 +103,22 @@ CA_EXPORT ca_status ca_build_union_tables(const uint8_t* mask, int B, int H_q, i
                                 hipStream_t stream);
 
 /*
+ * ca_build_union_tables_devlen -- ca_build_union_tables with the per-sequence
+ * extents in device memory, so that a captured HIP graph can be replayed for
+ * a new chunk after only those device values change.
+ *
+ * n_q_blocks, n_kv_blocks  device int32 [B], 4-byte aligned (else
+ *             CA_ERR_UNSUPPORTED), read by the kernel when it runs.  A
+ *             sequence with n_q_blocks[b] outside [0, NQ_max] or n_kv_blocks[b]
+ *             outside [0, NKB_max] gets an empty table (len 0, T all -1).
+ * Every other argument, the result and the errors as for ca_build_union_tables.
+ */
+CA_EXPORT ca_status ca_build_union_tables_devlen(const uint8_t* mask, int B, int H_q, int H_kv,
+                                       int NQ_max, int NKB_max, const int32_t* n_q_blocks,
+                                       const int32_t* n_kv_blocks, int32_t* T, int32_t* len,
+                                       hipStream_t stream);
+
+/*
  * ca_chunk_attention -- zero-copy paged chunk attention (execution stage).
  *
  * For sequence b, query head h (group g = h / (H_q/H_kv)) and chunk row
@@ -147,6 +163,32 @@ CA_EXPORT ca_status ca_chunk_attention(const void* Q, const void* K_cache, const
                              int H_q, int H_kv, int C_max, int64_t L, int D, int block,
                              float scale, ca_dtype dtype, void* O, float* lse,
                              hipStream_t stream);
+
+/*
+ * ca_chunk_attention_devlen -- ca_chunk_attention with prior_len and
+ * chunk_len in device memory (CompactAttention, execution stage: the tables
+ * and the per-request lengths travel to the paged dense kernel as device
+ * metadata).  The grid depends only on B, H_q, H_kv and C_max, so one
+ * captured HIP graph serves every chunk offset: between replays only the
+ * device lengths (and the inputs' contents) change.
+ *
+ * prior_len,  device int32 [B], 4-byte aligned (else CA_ERR_UNSUPPORTED),
+ * chunk_len   read by the kernels when they run.  The conditions of
+ *             ca_chunk_attention (multiples of 64, chunk_len <= C_max,
+ *             prior_len + chunk_len <= L and <= 64 * NKB_max) are checked
+ *             there: a sequence that breaks them is computed as an empty chunk
+ *             (every row O = 0, lse = -inf) and reads nothing from the cache.
+ * Sequences run in index order (the host does not see the lengths, so the
+ * longest-first order of ca_chunk_attention is not applied).  With valid
+ * lengths the result equals ca_chunk_attention's bit for bit.
+ * Every other argument and the errors as for ca_chunk_attention.
+ */
+CA_EXPORT ca_status ca_chunk_attention_devlen(const void* Q, const void* K_cache,
+                                    const void* V_cache, const int32_t* T, const int32_t* len,
+                                    int NKB_max, const int32_t* prior_len,
+                                    const int32_t* chunk_len, int B, int H_q, int H_kv,
+                                    int C_max, int64_t L, int D, int block, float scale,
+                                    ca_dtype dtype, void* O, float* lse, hipStream_t stream);
 
 /*
  * ca_chunk_attention_split -- ca_chunk_attention with each (b, g) table cut

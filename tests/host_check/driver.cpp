@@ -94,6 +94,27 @@ int main() {
     EXPECT(strcmp(stub::last.what, "attn_f32_split") == 0 && stub::last.p.n_split == 4);
     EXPECT((char*)stub::last.ptrs[1] - (char*)stub::last.ptrs[0] ==
            (ptrdiff_t)(4LL * 3 * 32 * 256 * 128 * 4));
+    // device lengths: the host reads none of them; sequences in index order, the
+    // kernels get the device pointers
+    {
+      const int32_t* dp = reinterpret_cast<const int32_t*>(static_cast<uintptr_t>(0x7000100));
+      const int32_t* dc = reinterpret_cast<const int32_t*>(static_cast<uintptr_t>(0x7000200));
+      EXPECT(ca_chunk_attention_devlen(FAKE, FAKE, FAKE, (const int32_t*)FAKE,
+                                       (const int32_t*)FAKE, 200, dp, dc, 3, 32, 8, 256, 8448,
+                                       128, 64, 0.125f, CA_BF16, FAKE, nullptr, 0) == CA_OK);
+      EXPECT(strcmp(stub::last.what, "attn_bf16") == 0);
+      EXPECT(stub::last.p.dev_prior == dp && stub::last.p.dev_chunk == dc);
+      EXPECT(stub::last.seq.order[0] == 0 && stub::last.seq.order[1] == 1 &&
+             stub::last.seq.order[2] == 2);
+      EXPECT(ca_chunk_attention(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE,
+                                200, prior, chunk, 3, 32, 8, 256, 8448, 128, 64, 0.125f, CA_BF16,
+                                FAKE, nullptr, 0) == CA_OK);
+      EXPECT(stub::last.p.dev_prior == nullptr && stub::last.p.dev_chunk == nullptr);
+      EXPECT(ca_build_union_tables_devlen((const uint8_t*)FAKE, 2, 8, 2, 4, 64, dp, dc,
+                                          (int32_t*)FAKE, (int32_t*)FAKE, 0) == CA_OK);
+      EXPECT(strcmp(stub::last.what, "union") == 0 && stub::last.ptrs[0] == (void*)dp &&
+             stub::last.ptrs[1] == (void*)dc);
+    }
     // no-alloc split: the partials go to the static array (its stand-in address),
     // same layout; a split past the array's size is refused before any launch
     {

@@ -18,7 +18,8 @@ void* static_scratch_address(hipError_t* err) {
 }
 
 hipError_t launch_union_tables(const uint8_t*, int B, int H_q, int H_kv, int NQ_max, int NKB_max,
-                               const UnionExtents& ext, int32_t*, int32_t*, hipStream_t) {
+                               const UnionExtents& ext, const int32_t* dev_nq,
+                               const int32_t* dev_nkb, int32_t*, int32_t*, hipStream_t) {
   stub::last = stub::Record{};
   stub::last.what = "union";
   stub::last.B = B;
@@ -28,6 +29,8 @@ hipError_t launch_union_tables(const uint8_t*, int B, int H_q, int H_kv, int NQ_
   stub::last.ints[3] = NKB_max;
   stub::last.ints[4] = ext.nq[B - 1];
   stub::last.ints[5] = ext.nkb[B - 1];
+  stub::last.ptrs[0] = const_cast<int32_t*>(dev_nq);
+  stub::last.ptrs[1] = const_cast<int32_t*>(dev_nkb);
   return hipSuccess;
 }
 

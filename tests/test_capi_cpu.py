@@ -218,3 +218,32 @@ def test_split_noalloc_validation():
     assert lib.ca_chunk_attention_split_noalloc(*big, 1, 2, FAKE, None, None) == \
         _lib.CA_ERR_TOO_LARGE
     assert lib.ca_status_string(_lib.CA_ERR_TOO_LARGE).decode().startswith("CA_ERR_TOO_LARGE")
+
+
+def test_devlen_validation():
+    # the device-length calls check everything the host can see; their length
+    # arrays are device pointers that the host never reads
+    lib = _lib.lib()
+    ua = lib.ca_build_union_tables_devlen
+    assert ua(None, 1, 4, 1, 1, 4, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert ua(FAKE, 1, 4, 1, 1, 4, None, FAKE, FAKE, FAKE, None) == 1
+    assert ua(FAKE, 0, 4, 1, 1, 4, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert ua(FAKE, 1, 4, 3, 1, 4, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert ua(FAKE, 1, 4, 1, 1, 1 << 20, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert ua(FAKE, 1, 4, 1, 1, 4, FAKE + 2, FAKE, FAKE, FAKE, None) == 4  # misaligned
+    at = lib.ca_chunk_attention_devlen
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 20, FAKE, FAKE, 1, 4, 1, 256, 1280, 64, 64, 0.125, 1,
+            FAKE, None, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return at(*a)
+
+    assert call(a0=None) == 1 and call(a6=None) == 1 and call(a17=None) == 1
+    assert call(a16=7) == 3
+    assert call(a8=0) == 2 and call(a10=3) == 2 and call(a15=0.0) == 2
+    assert call(a13=96) == 4 and call(a14=32) == 4
+    assert call(a7=FAKE + 2) == 4  # misaligned device lengths
+    assert call(a12=1 << 24, a13=128) == 4  # bf16 slice past 32-bit offsets
