@@ -24,6 +24,10 @@ Contents (each function cites the passage it follows):
   strict ascent, -1 padding), checked row by row.  Pinned by the tables of
   ``union_tables_ref`` (all rows pass) and by planted single violations,
   each giving exactly its own flag.
+* ``append_kv_ref`` -- the append step of chunked prefill: a chunk's keys and
+  values written into the cache after the prior tokens.  Pinned by a
+  hand-worked case and by rebuilding a whole prompt chunk by chunk, in any
+  order.
 * ``compact_kv_ref`` -- explicit KV compaction (the copy zero-copy execution
   avoids): selected prior blocks packed to end where the chunk starts.  Pinned
   by a hand-worked case and by the invariant that attention over the
@@ -48,6 +52,7 @@ from .attention_ref import (  # noqa: F401
     chunk_attention_ref,
     chunk_attention_rows_ref,
 )
+from .append_ref import append_kv_ref  # noqa: F401
 from .compact_ref import compact_kv_ref  # noqa: F401
 from .sparse_ref import sparse_attention_ref, sparse_attention_rows_ref  # noqa: F401
 from .producer_ref import (block_scores_ref, pool_blocks_ref, producer_mask_ref,  # noqa: F401
