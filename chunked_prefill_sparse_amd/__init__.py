@@ -23,7 +23,7 @@ from ._lib import CA_BLOCK, CA_MAX_BATCH, CompactAttnError  # noqa: F401
 
 __all__ = ["build_union_tables", "chunk_attention", "tables_to_csr", "check_tables",
            "build_union_tables_devlen", "chunk_attention_devlen",
-           "compact_kv",
+           "compact_kv", "append_kv",
            "build_row_tables", "chunk_attention_rows", "pool_blocks", "block_mask_topk",
            "workspace_size", "balanced_workspace_size", "chunk_attention_split_noalloc",
            "CompactAttnError", "library_path"]
@@ -380,6 +380,31 @@ def tables_to_csr(T: torch.Tensor, lens: torch.Tensor, L: int,
                                      indptr.data_ptr(), indices.data_ptr(), _stream_ptr(stream))
     _lib.check(st, "ca_tables_to_csr")
     return indptr, indices
+
+
+def append_kv(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+              v_cache: torch.Tensor, prior_len: Sequence[int], chunk_len: Sequence[int],
+              stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Write a chunk's keys and values (k_new, v_new [B, H_kv, C_max, D], rows
+    [0, chunk_len[b]) used) into the caches [B, H_kv, L, D] at rows
+    [prior_len[b], prior_len[b] + chunk_len[b]) (``ca_append_kv``)."""
+    _need_cuda("k_new", k_new)
+    if k_new.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("k_new must be bfloat16 or float32")
+    for name, t in (("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _need_cuda(name, t, k_new.dtype)
+    if k_new.dim() != 4 or v_new.shape != k_new.shape or k_cache.dim() != 4 or \
+            v_cache.shape != k_cache.shape:
+        raise ValueError("k_new/v_new must be [B, H_kv, C_max, D] and the caches [B, H_kv, L, D]")
+    B, H_kv, C_max, D = k_new.shape
+    if tuple(k_cache.shape[:2]) != (B, H_kv) or k_cache.shape[3] != D:
+        raise ValueError("cache batch / heads / head dim do not match the new rows")
+    dt = _lib.CA_BF16 if k_new.dtype == torch.bfloat16 else _lib.CA_F32
+    st = _lib.lib().ca_append_kv(k_new.data_ptr(), v_new.data_ptr(), B, H_kv, C_max,
+                                 k_cache.shape[2], D, dt, _host_ints("prior_len", prior_len, B),
+                                 _host_ints("chunk_len", chunk_len, B), k_cache.data_ptr(),
+                                 v_cache.data_ptr(), _stream_ptr(stream))
+    _lib.check(st, "ca_append_kv")
 
 
 def compact_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, T: torch.Tensor,

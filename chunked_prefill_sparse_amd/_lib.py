@@ -34,6 +34,7 @@ EXPORTED = (
     "ca_tables_to_csr",
     "ca_check_tables",
     "ca_compact_kv",
+    "ca_append_kv",
     "ca_pool_blocks",
     "ca_block_mask_topk",
     "ca_status_string",
@@ -92,6 +93,9 @@ def _declare(lib):
     lib.ca_compact_kv.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32p, _i32p, _i32, _i32, _i64, _i32,
                                   _i32, _vp, _vp, _vp, _vp]
     lib.ca_compact_kv.restype = _i32
+    lib.ca_append_kv.argtypes = [_vp, _vp, _i32, _i32, _i32, _i64, _i32, _i32, _i32p, _i32p, _vp,
+                                 _vp, _vp]
+    lib.ca_append_kv.restype = _i32
     lib.ca_pool_blocks.argtypes = [_vp, _i32, _i32, _i32, _i64, _i32, _i32p, _i32p, _vp, _i32,
                                    _vp]
     lib.ca_pool_blocks.restype = _i32

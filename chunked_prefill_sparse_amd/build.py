@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcompact_attn.so")
 SOURCES = ("capi.hip", "union_tables.hip", "chunk_attn_bf16.hip", "chunk_attn_f32.hip",
-           "compact_kv.hip", "block_mask.hip", "static_scratch.hip")
+           "compact_kv.hip", "block_mask.hip", "static_scratch.hip", "append_kv.hip")
 ARCH = "gfx950"
 
 

@@ -85,7 +85,7 @@ CA_EXPORT ca_status ca_build_union_tables(const uint8_t* mask, int B, int H_q, i
     ext.nkb[b] = n_kv_blocks[b];
   }
   return hip_status(ca::launch_union_tables(mask, B, H_q, H_kv, NQ_max, NKB_max, ext, nullptr,
-                                            nullptr, T, len, stream));
+                                            nullptr, T, len, device_cus(), stream));
 }
 
 CA_EXPORT ca_status ca_build_union_tables_devlen(const uint8_t* mask, int B, int H_q, int H_kv,
@@ -103,7 +103,8 @@ CA_EXPORT ca_status ca_build_union_tables_devlen(const uint8_t* mask, int B, int
   ca::UnionExtents ext;  // unused: the kernel reads the extents from device memory
   memset(&ext, 0, sizeof(ext));
   return hip_status(ca::launch_union_tables(mask, B, H_q, H_kv, NQ_max, NKB_max, ext,
-                                            n_q_blocks, n_kv_blocks, T, len, stream));
+                                            n_q_blocks, n_kv_blocks, T, len, device_cus(),
+                                            stream));
 }
 
 CA_EXPORT ca_status ca_check_tables(const int32_t* T, const int32_t* len, int B, int H_kv,
@@ -411,6 +412,32 @@ CA_EXPORT ca_status ca_chunk_attention_rows(const void* Q, const void* K_cache,
   return attention(Q, K_cache, V_cache, T_rows, len_rows, NQ_max, NKB_max, prior_len, chunk_len,
                    B, H_q, H_kv, C_max, L, D, block, scale, dtype, O, lse, true, 1, nullptr, 0,
                    stream);
+}
+
+CA_EXPORT ca_status ca_append_kv(const void* K_new, const void* V_new, int B, int H_kv,
+                                 int C_max, int64_t L, int D, ca_dtype dtype,
+                                 const int32_t* prior_len, const int32_t* chunk_len,
+                                 void* K_cache, void* V_cache, hipStream_t stream) {
+  if (!K_new || !V_new || !prior_len || !chunk_len || !K_cache || !V_cache) return CA_ERR_NULL;
+  if (dtype != CA_F32 && dtype != CA_BF16) return CA_ERR_DTYPE;
+  if (B < 1 || B > CA_MAX_BATCH || H_kv < 1 || C_max < 1 || L < 1 ||
+      static_cast<int64_t>(B) * H_kv > (1 << 24))
+    return CA_ERR_SHAPE;
+  if (D != 64 && D != 128) return CA_ERR_UNSUPPORTED;
+  if (!aligned16(K_new) || !aligned16(V_new) || !aligned16(K_cache) || !aligned16(V_cache))
+    return CA_ERR_UNSUPPORTED;
+  ca::SeqInfo seq;
+  memset(&seq, 0, sizeof(seq));
+  for (int b = 0; b < B; ++b) {
+    const int64_t P = prior_len[b], C = chunk_len[b];
+    if (P < 0 || C < 0 || C > C_max || P + C > L) return CA_ERR_SHAPE;
+    seq.prior[b] = static_cast<int32_t>(P);
+    seq.chunk[b] = static_cast<int32_t>(C);
+    seq.order[b] = b;
+  }
+  const int esz = dtype == CA_BF16 ? 2 : 4;
+  return hip_status(ca::launch_append_kv(K_new, V_new, B, H_kv, C_max, L, D, esz, seq, K_cache,
+                                         V_cache, stream));
 }
 
 CA_EXPORT ca_status ca_compact_kv(const void* K_cache, const void* V_cache, const int32_t* T,

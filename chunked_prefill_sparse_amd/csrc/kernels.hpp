@@ -91,10 +91,12 @@ __device__ __forceinline__ void seq_lengths(const AttnParams& p, const SeqInfo& 
 void* static_scratch_address(hipError_t* err);
 
 // dev_nq / dev_nkb: device int32 [B] extents (device-length call), or nullptr
-// to use ext.
+// to use ext.  cus: compute units of the device (how finely the OR step is
+// spread when there are few pseudo-requests; T then also holds intermediate
+// bitmap words during the call).
 hipError_t launch_union_tables(const uint8_t* mask, int B, int H_q, int H_kv, int NQ_max,
                                int NKB_max, const UnionExtents& ext, const int32_t* dev_nq,
-                               const int32_t* dev_nkb, int32_t* T, int32_t* len,
+                               const int32_t* dev_nkb, int32_t* T, int32_t* len, int cus,
                                hipStream_t stream);
 
 hipError_t launch_check_tables(const int32_t* T, const int32_t* len, int n_bg, int H_kv,
@@ -148,6 +150,12 @@ hipError_t launch_chunk_attn_f32_split(const float* Q, const float* K, const flo
 hipError_t launch_split_combine(const float* part_o, const float* part_ml, int D, bool f32_out,
                                 void* O, float* lse, const AttnParams& p, const SeqInfo& seq,
                                 hipStream_t stream);
+
+// Append of a chunk's K/V ([B, H_kv, C_max, D], rows [0, chunk)) to the cache
+// rows [prior, prior + chunk); esz = element size in bytes.
+hipError_t launch_append_kv(const void* k_new, const void* v_new, int B, int H_kv, int C_max,
+                            int64_t L, int D, int esz, const SeqInfo& seq, void* k_cache,
+                            void* v_cache, hipStream_t stream);
 
 // Explicit KV compaction (baseline); esz = element size in bytes.
 hipError_t launch_compact_kv(const void* K, const void* V, const int32_t* T, const int32_t* len,

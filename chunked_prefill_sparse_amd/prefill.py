@@ -2,7 +2,7 @@
 
 Chunked prefill (CompactAttention, problem statement and "Methodology" of the
 technical summaries): a long prompt is processed in fixed-size chunks; for
-each one the chunk's keys and values are already appended to the cache, a
+each one the chunk's keys and values are appended to the cache, a
 lightweight search makes the per-head block mask over the cache so far, the
 union turns it into per-group tables, and zero-copy attention runs the
 chunk's queries over the selected blocks.  Every step is a call into the HIP
@@ -16,22 +16,25 @@ from typing import Optional
 
 import torch
 
-from . import (balanced_workspace_size, block_mask_topk, build_union_tables, chunk_attention,
-               pool_blocks)
+from . import (append_kv, balanced_workspace_size, block_mask_topk, build_union_tables,
+               chunk_attention, pool_blocks)
 from ._lib import CA_BLOCK
 
 
 class ChunkedPrefill:
-    """Per-prompt state: caches [B, H_kv, L, D] (device, bf16 or fp32; the
-    prompt's keys/values up to the current chunk must be in place), pooled
+    """Per-prompt state: caches [B, H_kv, L, D] (device, bf16 or fp32), pooled
     keys kept across chunks, and the mask / table / output buffers.
 
-    ``step(q_chunk, prior)`` runs one chunk of C tokens at absolute offset
-    ``prior``; ``step_dense`` runs the same attention over every block (the
-    dense baseline).  ``balanced`` runs the sparse attention through
-    ``chunk_attention(..., balanced=True)``: the union's per-group tables differ
-    in length from group to group, and the plan spreads that work evenly over
-    the compute units (the workspace is allocated here, once)."""
+    ``step(q_chunk, prior, k_chunk, v_chunk)`` runs one chunk of C tokens at
+    absolute offset ``prior``: it appends the chunk's keys and values
+    ([B, H_kv, C, D]) to the caches at rows [prior, prior + C), then selects
+    and attends.  Without k_chunk / v_chunk the caches must already hold those
+    rows.  ``step_dense`` runs the same attention over every block (the dense
+    baseline), with the same optional append.  ``balanced`` runs the sparse
+    attention through ``chunk_attention(..., balanced=True)``: the union's
+    per-group tables differ in length from group to group, and the plan spreads
+    that work evenly over the compute units (the workspace is allocated here,
+    once)."""
 
     def __init__(self, k_cache: torch.Tensor, v_cache: torch.Tensor, H_q: int, C: int,
                  budget: int, local: int, scale: Optional[float] = None,
@@ -61,6 +64,13 @@ class ChunkedPrefill:
             self.ws = torch.empty(balanced_workspace_size(B, H_q, H_kv, C, D), dtype=torch.uint8,
                                   device=dev)
 
+    def append(self, k_chunk: torch.Tensor, v_chunk: torch.Tensor, prior: int,
+               stream=None) -> None:
+        """Write the chunk's keys and values [B, H_kv, C, D] into the caches at
+        rows [prior, prior + C) (``ca_append_kv``)."""
+        append_kv(k_chunk, v_chunk, self.k, self.v, [prior] * self.B, [self.C] * self.B,
+                  stream=stream)
+
     def select(self, q_chunk: torch.Tensor, prior: int, stream=None) -> None:
         """Pool the chunk's new key blocks and its queries, make the mask and
         build the union tables (into self.mask / self.T / self.lens)."""
@@ -79,35 +89,45 @@ class ChunkedPrefill:
                                [self.C] * self.B, self.scale, out=out, stream=stream,
                                balanced=self.balanced, workspace=self.ws)
 
-    def step(self, q_chunk: torch.Tensor, prior: int, out=None, stream=None) -> torch.Tensor:
+    def step(self, q_chunk: torch.Tensor, prior: int, out=None, stream=None,
+             k_chunk: Optional[torch.Tensor] = None,
+             v_chunk: Optional[torch.Tensor] = None) -> torch.Tensor:
+        if k_chunk is not None:
+            self.append(k_chunk, v_chunk, prior, stream)
         self.select(q_chunk, prior, stream)
         return self.attend(q_chunk, prior, out, stream)
 
     def capture(self, q_chunks, priors, outs=None, dense: bool = False,
-                select_only: bool = False) -> torch.cuda.CUDAGraph:
+                select_only: bool = False, kv_chunks=None) -> torch.cuda.CUDAGraph:
         """Record ``step`` (or ``step_dense``, or only ``select``) for a
         sequence of chunks into one HIP graph; ``replay()`` then reissues every
         kernel with the same arguments and buffers, without the per-call host
         work.  ``outs[i]`` receives chunk i's output (default: the shared
-        ``self.out``, which the last chunk leaves).  The library records no
-        memset, copy, allocation or synchronisation, so the whole call
-        sequence can be captured; inputs must stay at the same addresses
-        between replays."""
+        ``self.out``, which the last chunk leaves); ``kv_chunks[i]`` =
+        (k_chunk, v_chunk) makes chunk i append its keys and values first.
+        The library records no memset, copy, allocation or synchronisation, so
+        the whole call sequence can be captured; inputs must stay at the same
+        addresses between replays."""
         if outs is not None and len(outs) != len(q_chunks):
             raise ValueError("outs must give one output per chunk")
         if len(priors) != len(q_chunks):
             raise ValueError("priors must give one offset per chunk")
+        if kv_chunks is not None and len(kv_chunks) != len(q_chunks):
+            raise ValueError("kv_chunks must give one (k, v) pair per chunk")
         lens = [self.dense_lens(p) for p in priors] if dense else None
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i, (q, p) in enumerate(zip(q_chunks, priors)):
                 o = outs[i] if outs is not None else None
+                kc, vc = kv_chunks[i] if kv_chunks is not None else (None, None)
                 if select_only:
+                    if kc is not None:
+                        self.append(kc, vc, p)
                     self.select(q, p)
                 elif dense:
-                    self.step_dense(q, p, lens[i], out=o)
+                    self.step_dense(q, p, lens[i], out=o, k_chunk=kc, v_chunk=vc)
                 else:
-                    self.step(q, p, out=o)
+                    self.step(q, p, out=o, k_chunk=kc, v_chunk=vc)
         g.ca_dense_lens = lens  # device buffers the graph reads: keep them alive
         return g
 
@@ -116,9 +136,12 @@ class ChunkedPrefill:
         return torch.full((self.B, self.H_kv), n, dtype=torch.int32, device=self.k.device)
 
     def step_dense(self, q_chunk: torch.Tensor, prior: int, lens: torch.Tensor, out=None,
-                   stream=None) -> torch.Tensor:
+                   stream=None, k_chunk: Optional[torch.Tensor] = None,
+                   v_chunk: Optional[torch.Tensor] = None) -> torch.Tensor:
         """Dense baseline: the same attention kernel over every block up to the
-        chunk (lens from ``dense_lens``)."""
+        chunk (lens from ``dense_lens``), after the same optional append."""
+        if k_chunk is not None:
+            self.append(k_chunk, v_chunk, prior, stream)
         out = self.out if out is None else out
         return chunk_attention(q_chunk, self.k, self.v, self.T_dense, lens, [prior] * self.B,
                                [self.C] * self.B, self.scale, out=out, stream=stream)

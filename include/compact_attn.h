@@ -373,6 +373,30 @@ CA_EXPORT ca_status ca_tables_to_csr(const int32_t* T, const int32_t* len, int B
                            hipStream_t stream);
 
 /*
+ * ca_append_kv -- the append step of chunked prefill (problem statement of
+ * the technical summaries: chunks are processed in sequence, and each attends
+ * to the cache accumulated so far plus itself, so its own keys and values are
+ * written into the cache before ca_chunk_attention runs).
+ *
+ *   K_cache[b, g, prior_len[b] + i, :] = K_new[b, g, i, :]   (i < chunk_len[b]),
+ *   V_cache likewise; every other cache row is left as it was.
+ *
+ * K_new, V_new      device [B, H_kv, C_max, D] (dtype), 16-byte aligned: the
+ *                   chunk's keys and values, rows [0, chunk_len[b]) used.
+ * K_cache, V_cache  device [B, H_kv, L, D] (dtype), 16-byte aligned (in/out).
+ * prior_len, chunk_len  host int32 [B]; 0 <= chunk_len[b] <= C_max,
+ *                   prior_len[b] >= 0, prior_len[b] + chunk_len[b] <= L (else
+ *                   CA_ERR_SHAPE).  Any row offsets (no multiple of 64 needed).
+ * B in [1, CA_MAX_BATCH], B*H_kv <= 2^24, D in {64, 128}.  The new rows must
+ * not overlap the cache.  Asynchronous on `stream`.
+ * Errors: CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_DTYPE, CA_ERR_UNSUPPORTED, CA_ERR_HIP.
+ */
+CA_EXPORT ca_status ca_append_kv(const void* K_new, const void* V_new, int B, int H_kv, int C_max,
+                                 int64_t L, int D, ca_dtype dtype, const int32_t* prior_len,
+                                 const int32_t* chunk_len, void* K_cache, void* V_cache,
+                                 hipStream_t stream);
+
+/*
  * ca_compact_kv -- explicit KV compaction: the selected blocks are gathered
  * into a compact buffer before a dense kernel runs.  CompactAttention,
  * abstract: its block tables let the attention read the selected blocks in

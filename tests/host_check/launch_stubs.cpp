@@ -19,7 +19,8 @@ void* static_scratch_address(hipError_t* err) {
 
 hipError_t launch_union_tables(const uint8_t*, int B, int H_q, int H_kv, int NQ_max, int NKB_max,
                                const UnionExtents& ext, const int32_t* dev_nq,
-                               const int32_t* dev_nkb, int32_t*, int32_t*, hipStream_t) {
+                               const int32_t* dev_nkb, int32_t*, int32_t*, int cus,
+                               hipStream_t) {
   stub::last = stub::Record{};
   stub::last.what = "union";
   stub::last.B = B;
@@ -31,6 +32,7 @@ hipError_t launch_union_tables(const uint8_t*, int B, int H_q, int H_kv, int NQ_
   stub::last.ints[5] = ext.nkb[B - 1];
   stub::last.ptrs[0] = const_cast<int32_t*>(dev_nq);
   stub::last.ptrs[1] = const_cast<int32_t*>(dev_nkb);
+  stub::last.ints[6] = cus;
   return hipSuccess;
 }
 
@@ -105,6 +107,20 @@ hipError_t launch_chunk_attn_f32_split(const float*, const float*, const float*,
   record_attn("attn_f32_split", B, D, p, seq);
   stub::last.ptrs[0] = part_o;
   stub::last.ptrs[1] = part_ml;
+  return hipSuccess;
+}
+
+hipError_t launch_append_kv(const void*, const void*, int B, int H_kv, int C_max, int64_t L,
+                            int D, int esz, const SeqInfo& seq, void*, void*, hipStream_t) {
+  stub::last = stub::Record{};
+  stub::last.what = "append";
+  stub::last.B = B;
+  stub::last.D = D;
+  stub::last.ints[0] = H_kv;
+  stub::last.ints[1] = C_max;
+  stub::last.ints[2] = static_cast<int>(L);
+  stub::last.ints[3] = esz;
+  stub::last.seq = seq;
   return hipSuccess;
 }
 

@@ -247,3 +247,23 @@ def test_devlen_validation():
     assert call(a13=96) == 4 and call(a14=32) == 4
     assert call(a7=FAKE + 2) == 4  # misaligned device lengths
     assert call(a12=1 << 24, a13=128) == 4  # bf16 slice past 32-bit offsets
+
+
+def test_append_validation():
+    lib = _lib.lib()
+    # K_new, V_new, B, H_kv, C_max, L, D, dtype, prior, chunk, K_cache, V_cache
+    base = [FAKE, FAKE, 1, 2, 128, 1024, 64, 1, _ints(896), _ints(128), FAKE, FAKE]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.ca_append_kv(*a, None)
+
+    assert call(a0=None) == 1 and call(a8=None) == 1 and call(a11=None) == 1
+    assert call(a7=5) == 3
+    assert call(a2=0) == 2 and call(a3=0) == 2
+    assert call(a9=_ints(129)) == 2               # chunk > C_max
+    assert call(a8=_ints(897)) == 2               # prior + chunk > L
+    assert call(a8=_ints(-1)) == 2
+    assert call(a6=96) == 4 and call(a10=FAKE + 8) == 4
