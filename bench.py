@@ -193,6 +193,257 @@ def cpu_baseline(w, seconds_budget=20.0):
     }
 
 
+# --------------------------------------------------------------------------- every config
+
+
+def dense_tables(w, dev):
+    """The all-blocks table of a workload (every block of each sequence, the
+    dense baseline the same kernel runs) and its lengths."""
+    import torch
+    T = torch.full((w.B, w.H_kv, w.NKB_max), -1, dtype=torch.int32)
+    ln = torch.zeros((w.B, w.H_kv), dtype=torch.int32)
+    for b, n in enumerate(w.n_kv_blocks):
+        T[b, :, :n] = torch.arange(n, dtype=torch.int32)
+        ln[b] = n
+    return T.to(dev), ln.to(dev)
+
+
+def union_kernel_us(fn, calls=50):
+    """Kernel time of one union call: ``calls`` calls recorded into a HIP graph,
+    replayed, and timed with HIP events (no per-call host launch work)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = []
+    for _ in range(5):
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        reps.append(a.elapsed_time(b) * 1e3 / calls)
+    del g
+    return statistics.median(reps)
+
+
+def blocks_summary(w, lh):
+    """[sum of len, mean len per (sequence, KV group), mean per-head Q-block
+    union, mean blocks per sequence] (+ the achieved density of the prior cells
+    for vertical-slash masks)."""
+    per_head = []
+    for b in range(w.B):
+        nq, nkb = w.n_q_blocks[b], w.n_kv_blocks[b]
+        per_head.append(w.mask[b, :, :nq, :nkb].any(axis=1).sum(axis=-1).mean())
+    all_blocks = float(np.mean([n for n in w.n_kv_blocks]))
+    r = [int(lh.sum()), round(float(lh.mean()), 1), round(float(np.mean(per_head)), 1),
+         round(all_blocks, 1)]
+    if w.meta.get("mask") == "vertical_slash":
+        pb = w.prior[0] // 64
+        r.append(round(float(w.mask[:, :, :w.n_q_blocks[0], :pb].mean()), 4))
+    return r
+
+
+def measure_config(w, dev, stream, reps, q=None, k=None, v=None, dense_ms=None):
+    """One workload on the GPU: union tables (per call and kernel only), chunk
+    attention (median, p10, p90 of ``reps`` HIP-event-timed calls), the same
+    kernel over every block (x vs dense), and the work accounting."""
+    import torch
+    import chunked_prefill_sparse_amd as ca
+    q = w.q.to(dev) if q is None else q
+    k = w.k.to(dev) if k is None else k
+    v = w.v.to(dev) if v is None else v
+    mask = torch.from_numpy(w.mask).to(dev)
+    T = torch.empty((w.B, w.H_kv, w.NKB_max), dtype=torch.int32, device=dev)
+    lens = torch.empty((w.B, w.H_kv), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+
+    def tables():
+        ca.build_union_tables(mask, w.H_kv, w.n_q_blocks, w.n_kv_blocks, T=T, lens=lens)
+
+    def attn(T_=T, l_=lens, **kw):
+        ca.chunk_attention(q, k, v, T_, l_, w.prior, w.chunk, w.scale, out=out, **kw)
+
+    tables()
+    torch.cuda.synchronize()
+    Th, lh = T.cpu().numpy(), lens.cpu().numpy()
+    flops, bytes_alg, pairs = algorithmic(w, Th, lh)
+    attn()
+    a_ms = time_calls(attn, reps, stream)
+    u_ms = time_calls(tables, reps, stream)
+    u_kernel = union_kernel_us(tables)
+    med = statistics.median(a_ms)
+    eff = flops / (med * 1e-3) / 1e12
+    r = dict(
+        ms=[round(med, 4), round(pct(a_ms, 10), 4), round(pct(a_ms, 90), 4)],
+        union_us=[round(statistics.median(u_ms) * 1e3, 2), round(u_kernel, 2)],
+        tflops=round(eff, 2),
+        hbm_GBps=round(bytes_alg / (med * 1e-3) / 1e9, 1),
+        len=blocks_summary(w, lh),
+    )
+    if w.dtype == "bf16":
+        r["mfma"] = round(eff / PEAK_BF16_TFLOPS, 4)
+    else:  # fp32 on the vector ALUs: latency-bound, also run split 8 ways
+        ws = torch.empty(ca.workspace_size(w.B, w.H_q, w.C_max, w.D, 8), dtype=torch.uint8,
+                         device=dev)
+        attn(n_splits=8, workspace=ws)
+        s_ms = statistics.median(time_calls(lambda: attn(n_splits=8, workspace=ws), reps, stream))
+        r["split8_ms"] = round(s_ms, 4)
+        r["split8_tflops"] = round(flops / (s_ms * 1e-3) / 1e12, 3)
+    if dense_ms is None:
+        Td, ld = dense_tables(w, dev)
+        attn(Td, ld)
+        dense_ms = statistics.median(time_calls(lambda: attn(Td, ld), reps, stream))
+    r["dense_ms"] = round(dense_ms, 4)
+    r["x_dense"] = round(dense_ms / med, 3)
+    return r
+
+
+def oracle_seconds(w, arrays, full, runs=1):
+    """The oracle on this workload, timed on the host cores: the whole output
+    (``full``), else the slice of KV group 0 of every sequence, scaled to the
+    whole workload by its share of the admissible pairs."""
+    from oracle import chunk_attention_ref, union_tables_ref
+    q, k, v = arrays
+    t0 = time.perf_counter()
+    Tr, lr = union_tables_ref(w.mask, w.H_kv, w.n_q_blocks, w.n_kv_blocks)
+    t_union = time.perf_counter() - t0
+    if full:
+        ts = []
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            chunk_attention_ref(q, k, v, Tr, lr, w.prior, w.chunk, w.scale)
+            ts.append(time.perf_counter() - t0)
+        return dict(s=round(statistics.median(ts) + t_union, 3), runs=runs, sample="whole")
+    G = w.G
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        chunk_attention_ref(q[b:b + 1, :G], k[b:b + 1, :1], v[b:b + 1, :1], Tr[b:b + 1, :1],
+                            lr[b:b + 1, :1], w.prior[b:b + 1], w.chunk[b:b + 1], w.scale)
+    t_slice = time.perf_counter() - t0
+    part = admissible_pairs(Tr[:, :1], lr[:, :1], w.prior, w.chunk, G)
+    whole = admissible_pairs(Tr, lr, w.prior, w.chunk, G)
+    return dict(s=round(t_union + t_slice * whole / max(part, 1), 3),
+                measured_s=round(t_union + t_slice, 3),
+                sample=f"group 0 of each sequence ({part / whole:.3f} of the pairs), scaled")
+
+
+def configs_leg(stream, reps, base, base_dev, results, oracle_budget):
+    """Every synthetic config at one GPU: config 1 (fp32), config 2 (32K),
+    config 3 (128K: pairwise, colshared, groupshared, dense), config 4 (ragged
+    B=4) and the 12 points of config 5 (vertical-slash density sweep x heads
+    identical / independent), each with the oracle's time on the host cores
+    (whole output for configs 1 and 2, one KV group scaled for the rest, while
+    ``oracle_budget`` seconds last)."""
+    import torch
+    import gen
+    dev = base_dev[0].device
+    cores = len(os.sched_getaffinity(0))
+    out = {}
+    spent = [0.0]
+
+    def oracle(w, arrays, full, runs=1):
+        if spent[0] >= oracle_budget:
+            return dict(s=None, sample="skipped: oracle time budget spent")
+        t0 = time.perf_counter()
+        r = oracle_seconds(w, arrays, full, runs)
+        spent[0] += time.perf_counter() - t0
+        r["cores"] = cores
+        return r
+
+    def small(name, cfg, runs):
+        w = gen.make_workload(name)
+        r = measure_config(w, dev, stream, reps)
+        r = dict(cfg=cfg, dtype=w.dtype, **r)
+        r["oracle"] = oracle(w, tuple(gen.tensor_to_f32(x) for x in (w.q, w.k, w.v)), True, runs)
+        log(f"config {cfg} {name}: attention {r['ms'][0]:.4f} ms ({r['tflops']:.1f} TFLOP/s), "
+            f"union {r['union_us'][0]:.1f} us (kernel {r['union_us'][1]:.1f}), "
+            f"x{r['x_dense']:.2f} vs dense, oracle {r['oracle']['s']} s")
+        return r
+
+    out["tiny_f32"] = small("tiny_f32", 1, 5)
+    out["llama8b_32k"] = small("llama8b_32k", 2, 1)
+    torch.cuda.empty_cache()
+
+    q, k, v = base_dev
+    base_arrays = tuple(gen.tensor_to_f32(x) for x in (base.q, base.k, base.v))
+    dense_ms = results["dense"]["attn_ms_median"]
+    for variant in ("pairwise", "colshared", "groupshared", "dense"):
+        w = gen.make_workload("llama8b_128k", variant=variant, with_tensors=False)
+        r = measure_config(w, dev, stream, reps, q, k, v, dense_ms=dense_ms)
+        r = dict(cfg=3, dtype="bf16", **r)
+        r["oracle"] = oracle(w, base_arrays, False)
+        out[f"llama8b_128k.{variant}"] = r
+        log(f"config 3 {variant}: attention {r['ms'][0]:.3f} ms ({r['tflops']:.0f} TFLOP/s), "
+            f"union kernel {r['union_us'][1]:.1f} us, x{r['x_dense']:.2f} vs dense")
+    for dn in gen.VSLASH_DENSITIES:
+        for hm in gen.VSLASH_HEAD_MODES:
+            w = gen.make_workload("vslash_128k", density=dn, heads=hm, with_tensors=False)
+            r = measure_config(w, dev, stream, reps, q, k, v, dense_ms=dense_ms)
+            r = dict(cfg=5, dtype="bf16", **r)
+            r["oracle"] = oracle(w, base_arrays, False)
+            out[f"vslash_128k.d{dn}.{hm}"] = r
+            log(f"config 5 d={dn} {hm}: attention {r['ms'][0]:.3f} ms ({r['tflops']:.0f} "
+                f"TFLOP/s), mean len {r['len'][1]} vs per-head {r['len'][2]}, "
+                f"x{r['x_dense']:.2f} vs dense")
+    del base_arrays
+    w = gen.make_workload("ragged_b4")
+    r = measure_config(w, dev, stream, reps)
+    r = dict(cfg=4, dtype="bf16", **r)
+    r["oracle"] = oracle(w, tuple(gen.tensor_to_f32(x) for x in (w.q, w.k, w.v)), False)
+    out["ragged_b4"] = r
+    log(f"config 4 ragged_b4: attention {r['ms'][0]:.3f} ms ({r['tflops']:.0f} TFLOP/s), "
+        f"x{r['x_dense']:.2f} vs dense")
+    del w
+    torch.cuda.empty_cache()
+    return out
+
+
+def markdown_table(line):
+    """The benchmark's per-config table from a bench JSON line (``--table``)."""
+    rows = ["| config / mask | attention ms (median; p10–p90) | union µs (per call; kernel) "
+            "| eff. TFLOP/s | MFMA frac | alg. HBM GB/s | × vs dense "
+            "| mean len / per-head Q-union / all blocks | oracle s (cores) |",
+            "|---|---|---|---|---|---|---|---|---|"]
+    for key, r in line["configs"].items():
+        name, _, rest = key.partition(".")
+        label = f"{r['cfg']} {name}" + (f" {rest}" if rest else "") + \
+            (" (fp32)" if r["dtype"] == "f32" else "")
+        m, u, ln = r["ms"], r["union_us"], r["len"]
+        att = f"{m[0]:.3f}; {m[1]:.3f}–{m[2]:.3f}"
+        if "split8_ms" in r:
+            att += f" (8 splits: {r['split8_ms']:.3f})"
+        o = r.get("oracle") or {}
+        osec = "—" if o.get("s") is None else (
+            f"{o['s']:.3g} ({o['cores']})" + ("" if o.get("sample") == "whole" else " est."))
+        mf = f"{r['mfma']:.3f}" if "mfma" in r else "—"
+        rows.append(f"| {label} | {att} | {u[0]:.1f}; {u[1]:.1f} | {r['tflops']:.1f} | {mf} "
+                    f"| {r['hbm_GBps']:.0f} | {r['x_dense']:.2f} "
+                    f"| {ln[1]:.0f} / {ln[2]:.0f} / {ln[3]:.0f} | {osec} |")
+    return "\n".join(rows)
+
+
+def _bench_line(rec):
+    """The bench JSON line inside a record: the line itself, or a driver record
+    holding it in its stdout tail."""
+    if "configs" in rec:
+        return rec
+    for text in (rec.get("run", {}).get("stdout_tail", ""), rec.get("tail", "")):
+        for ln in text.splitlines():
+            if ln.startswith("{") and '"configs"' in ln:
+                return json.loads(ln)
+    raise SystemExit("no bench line with a configs object in that record")
+
+
 # --------------------------------------------------------------------------- one GPU's TP share
 
 
@@ -253,29 +504,36 @@ def tp_shard_leg(stream, reps):
 
 def prefill_leg(stream, budget=32, local=8):
     """A 128K prompt in 64 chunks of 2048 (planted-structure synthetic stream):
-    per chunk, pool the new key blocks and the queries, make the top-k block
-    mask, build the union tables and run zero-copy attention (also timed with
-    balanced attention, for reference); the dense baseline runs the same
-    attention over every block.  Cumulative times from
-    HIP events on the launch stream, for the Python loop of calls and for the
-    same calls recorded into HIP graphs and replayed."""
+    per chunk, append its keys and values to the cache, pool the new key
+    blocks and the queries, make the top-k block mask, build the union tables
+    and run zero-copy attention (also timed with balanced attention, for
+    reference); the dense baseline appends and runs the same attention over
+    every block.  The caches start empty.  Cumulative times from HIP events on
+    the launch stream, for the Python loop of calls and for the same calls
+    recorded into HIP graphs and replayed."""
     import torch
     import gen
     from chunked_prefill_sparse_amd.prefill import ChunkedPrefill
     log("generating prefill_128k stream ...")
     s = gen.make_prefill_stream("prefill_128k")
-    k, v = s.k.cuda(), s.v.cuda()
+    k_src, v_src = s.k.cuda(), s.v.cuda()
+    kv = [(k_src[:, :, c * s.C:(c + 1) * s.C].contiguous(),
+           v_src[:, :, c * s.C:(c + 1) * s.C].contiguous()) for c in range(s.n_chunks)]
+    del k_src, v_src
+    k = torch.zeros((1, s.H_kv, s.L, s.D), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(k)
     qs = [s.q_chunk(c).cuda() for c in range(s.n_chunks)]
     drv = ChunkedPrefill(k, v, s.H_q, s.C, budget=budget, local=local, balanced=False)
     drv_bal = ChunkedPrefill(k, v, s.H_q, s.C, budget=budget, local=local, balanced=True)
     dense_lens = [drv.dense_lens(c * s.C) for c in range(s.n_chunks)]
+    priors = [c * s.C for c in range(s.n_chunks)]
     torch.cuda.synchronize()
     # untimed pass: work accounting per chunk
     flops = flops_dense = 0
     frac = []
     for c in range(s.n_chunks):
         P = c * s.C
-        drv.step(qs[c], P)
+        drv.step(qs[c], P, k_chunk=kv[c][0], v_chunk=kv[c][1])
         T, ln = drv.T.cpu().numpy(), drv.lens.cpu().numpy()
         flops += 4 * s.D * admissible_pairs(T, ln, [P], [s.C], s.G)
         nkb = (P + s.C) // 64
@@ -293,67 +551,74 @@ def prefill_leg(stream, budget=32, local=8):
 
     def run_sparse():
         for c in range(s.n_chunks):
-            drv.step(qs[c], c * s.C)
+            drv.step(qs[c], priors[c], k_chunk=kv[c][0], v_chunk=kv[c][1])
+
+    def run_append():
+        for c in range(s.n_chunks):
+            drv.append(kv[c][0], kv[c][1], priors[c])
 
     def run_select():
         for c in range(s.n_chunks):
-            drv.select(qs[c], c * s.C)
+            drv.select(qs[c], priors[c])
 
     def run_dense():
         for c in range(s.n_chunks):
-            drv.step_dense(qs[c], c * s.C, dense_lens[c])
+            drv.step_dense(qs[c], priors[c], dense_lens[c], k_chunk=kv[c][0], v_chunk=kv[c][1])
+
+    def run_balanced():  # the same loop with balanced attention, for reference
+        for c in range(s.n_chunks):
+            drv_bal.step(qs[c], priors[c], k_chunk=kv[c][0], v_chunk=kv[c][1])
 
     reps = 3
     run_sparse()
     run_dense()
     sparse_ms = statistics.median(timed(run_sparse) for _ in range(reps))
+    append_ms = statistics.median(timed(run_append) for _ in range(reps))
     select_ms = statistics.median(timed(run_select) for _ in range(reps))
     dense_ms = statistics.median(timed(run_dense) for _ in range(reps))
-    attn_ms = sparse_ms - select_ms
-    def run_balanced():  # the same loop with balanced attention, for reference
-        for c in range(s.n_chunks):
-            drv_bal.step(qs[c], c * s.C)
-
+    attn_ms = sparse_ms - select_ms - append_ms
     run_balanced()
     bal_ms = statistics.median(timed(run_balanced) for _ in range(reps))
     # the same call sequences recorded once into HIP graphs and replayed: the
     # GPU time without the per-call host work of the loop above
-    priors = [c * s.C for c in range(s.n_chunks)]
-    g_sparse = drv.capture(qs, priors)
+    g_sparse = drv.capture(qs, priors, kv_chunks=kv)
     g_select = drv.capture(qs, priors, select_only=True)
-    g_dense = drv.capture(qs, priors, dense=True)
+    g_dense = drv.capture(qs, priors, dense=True, kv_chunks=kv)
     g_sparse.replay()
     g_dense.replay()
     gs_ms = statistics.median(timed(g_sparse.replay) for _ in range(reps))
     gsel_ms = statistics.median(timed(g_select.replay) for _ in range(reps))
     gd_ms = statistics.median(timed(g_dense.replay) for _ in range(reps))
+    moved = 2 * 2 * s.n_chunks * s.H_kv * s.C * s.D * 2  # K and V, read once and written once
     r = dict(
         chunks=s.n_chunks, chunk=s.C, prompt=s.L, budget_blocks=budget, local_blocks=local,
-        total_ms=round(sparse_ms, 3), select_ms=round(select_ms, 3),
-        attention_ms=round(attn_ms, 3), dense_attention_ms=round(dense_ms, 3),
+        total_ms=round(sparse_ms, 3), append_ms=round(append_ms, 3),
+        append_GBps=round(moved / (append_ms * 1e-3) / 1e9, 1), select_ms=round(select_ms, 3),
+        attention_ms=round(attn_ms, 3), dense_total_ms=round(dense_ms, 3),
         x_vs_dense=round(dense_ms / sparse_ms, 3),
         attention_eff_tflops=round(flops / (attn_ms * 1e-3) / 1e12, 1),
-        dense_eff_tflops=round(flops_dense / (dense_ms * 1e-3) / 1e12, 1),
+        dense_eff_tflops=round(flops_dense / ((dense_ms - append_ms) * 1e-3) / 1e12, 1),
         work_frac_of_dense=round(flops / flops_dense, 4),
         union_block_frac_first_mid_last=[round(frac[0], 3), round(frac[len(frac) // 2], 3),
                                          round(frac[-1], 3)],
-        balanced=dict(total_ms=round(bal_ms, 3), attention_ms=round(bal_ms - select_ms, 3),
+        balanced=dict(total_ms=round(bal_ms, 3),
+                      attention_ms=round(bal_ms - select_ms - append_ms, 3),
                       x_vs_dense=round(dense_ms / bal_ms, 3),
-                      attention_eff_tflops=round(flops / ((bal_ms - select_ms) * 1e-3) / 1e12, 1)),
+                      attention_eff_tflops=round(
+                          flops / ((bal_ms - select_ms - append_ms) * 1e-3) / 1e12, 1)),
         graph=dict(total_ms=round(gs_ms, 3), select_ms=round(gsel_ms, 3),
-                   attention_ms=round(gs_ms - gsel_ms, 3), dense_attention_ms=round(gd_ms, 3),
-                   x_vs_dense=round(gd_ms / gs_ms, 3)),
+                   dense_total_ms=round(gd_ms, 3), x_vs_dense=round(gd_ms / gs_ms, 3)),
         data=("synthetic planted-structure stream: K, V, Q ~ N(0,1), 3% salient KV blocks per "
-              "KV head shifted along a per-head direction that the group's queries share"),
+              "KV head shifted along a per-head direction that the group's queries share; the "
+              "caches start empty and each chunk appends its own K/V"),
     )
-    log(f"prefill_128k: total {sparse_ms:.2f} ms (select {select_ms:.2f}, attention "
-        f"{attn_ms:.2f}) vs dense attention {dense_ms:.2f} ms -> x{dense_ms / sparse_ms:.2f}; "
+    log(f"prefill_128k: total {sparse_ms:.2f} ms (append {append_ms:.2f}, select {select_ms:.2f}, "
+        f"attention {attn_ms:.2f}) vs dense {dense_ms:.2f} ms -> x{dense_ms / sparse_ms:.2f}; "
         f"union fraction first/mid/last {r['union_block_frac_first_mid_last']}")
-    log(f"prefill_128k with balanced attention: total {bal_ms:.2f} ms (attention "
-        f"{bal_ms - select_ms:.2f}) -> x{dense_ms / bal_ms:.2f}")
+    log(f"prefill_128k with balanced attention: total {bal_ms:.2f} ms -> x{dense_ms / bal_ms:.2f}")
     log(f"prefill_128k as HIP graphs: total {gs_ms:.2f} ms (select {gsel_ms:.2f}) vs dense "
         f"{gd_ms:.2f} ms -> x{gd_ms / gs_ms:.2f}")
-    del qs, k, v, drv, drv_bal, g_sparse, g_select, g_dense
+    del qs, k, v, kv, drv, drv_bal, g_sparse, g_select, g_dense
     torch.cuda.empty_cache()
     return r
 
@@ -408,7 +673,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-prefill", action="store_true", help="skip the 64-chunk prefill leg")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the leg that measures every config (1-5)")
+    ap.add_argument("--config-oracle-seconds", type=float, default=120.0,
+                    help="host time the configs leg may spend timing the oracle")
+    ap.add_argument("--table", metavar="JSON",
+                    help="print BASELINE.md's per-config table from a bench JSON line (a file "
+                         "holding the line, or a driver record with it in its stdout tail) and exit")
     args = ap.parse_args()
+
+    if args.table:
+        print(markdown_table(_bench_line(json.load(open(args.table)))))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -614,6 +890,10 @@ def main():
         "reread_factor": round(traffic / main_r["bytes_alg"], 4) if traffic else None,
     }
     del k_out, v_out
+    configs = None
+    if not args.no_configs:
+        configs = configs_leg(stream, max(args.reps // 2, 20), w, (q, k, v), results,
+                              args.config_oracle_seconds)
     tp_shard = tp_shard_leg(stream, args.reps)
     prefill = None if args.no_prefill else prefill_leg(stream)
 
@@ -648,6 +928,7 @@ def main():
                      for n_, r in results.items()},
         "compaction": compaction,
         "block_sparse": sparse,
+        "configs": configs,
         "tp_shard_128k": tp_shard,
         "prefill_128k": prefill,
         "roofline": roofline,

@@ -78,3 +78,37 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
     assert not r.stdout.strip().startswith("{")
+
+
+def test_blocks_summary_and_table():
+    # the union-size summary of a tiny workload, by hand, and the per-config table
+    import gen
+    w = gen.make_custom(1, 4, 2, 64, [128], [128], "bf16", 3,
+                        lambda rng, b, H, nq, pb: np.zeros((H, nq, pb), np.uint8),
+                        with_tensors=False)
+    w.mask[0, 0, 0, 0] = 1  # head 0 (group 0), Q-block 0 selects prior block 0
+    T, ln = union_tables_ref(w.mask, w.H_kv, w.n_q_blocks, w.n_kv_blocks)
+    # group 0: block 0 + the chunk's two blocks; group 1: the chunk's two blocks
+    assert ln.tolist() == [[3, 2]]
+    # per head: heads 0 sees {0, 2, 3}, the others {2, 3}
+    assert bench.blocks_summary(w, ln) == [5, 2.5, 2.2, 4.0]
+    rec = {"configs": {"tiny_f32": dict(cfg=1, dtype="f32", ms=[0.1, 0.09, 0.11],
+                                        union_us=[10.0, 3.5], tflops=2.5, hbm_GBps=10.0,
+                                        len=[19, 19.0, 14.0, 20.0], split8_ms=0.026,
+                                        dense_ms=0.105, x_dense=1.05,
+                                        oracle=dict(s=0.005, sample="whole", cores=16)),
+                       "vslash_128k.d0.02.identical": dict(
+                           cfg=5, dtype="bf16", ms=[1.0, 0.99, 1.01], union_us=[12.0, 9.0],
+                           tflops=1200.0, hbm_GBps=180.0, mfma=0.48,
+                           len=[4848, 606.0, 606.0, 2048.0, 0.0195], dense_ms=3.5, x_dense=3.5,
+                           oracle=dict(s=None, sample="skipped"))}}
+    table = bench.markdown_table(rec).splitlines()
+    assert len(table) == 4
+    assert table[2].startswith("| 1 tiny_f32 (fp32) | 0.100; 0.090–0.110 (8 splits: 0.026) |")
+    assert "| 0.005 (16) |" in table[2] and "| — | 10 | 1.05 |" in table[2]
+    assert table[3].startswith("| 5 vslash_128k d0.02.identical | 1.000;")
+    assert table[3].endswith("| 606 / 606 / 2048 | — |")
+    # a driver record holding the line in its stdout tail
+    import json
+    drv = {"parsed": {"value": 1}, "run": {"stdout_tail": json.dumps(rec) + "\n\n---- stderr"}}
+    assert bench._bench_line(drv) == rec
