@@ -45,6 +45,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published)
+PEAK_CLOCK_GHZ = 2.4       # the engine clock the published matrix peak assumes
 WORKLOAD = "llama8b_128k"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "chunk_attn_bf16_llama8b_128k_pmc.txt")
 KERNEL_SRC = os.path.join(ROOT, "chunked_prefill_sparse_amd", "csrc", "chunk_attn_bf16.hip")
@@ -875,6 +876,20 @@ def main():
     main_r = results["pairwise"]
     traffic, pmc = stored_traffic()
     achieved = main_r["flops"] / (main_r["attn_ms_mean"] * 1e-3) / 1e12
+    # the shader clock the attention kernel ran at, from its own per-workgroup
+    # records (real-time ticks and shader cycles), over 20 calls after the timed ones
+    T, lens = tables("pairwise")
+    stamps = None
+    clocks = []
+    for _ in range(20):
+        _, stamps = ca.chunk_attention_stamped(q, k, v, T, lens, w.prior, w.chunk, w.scale,
+                                               out=out, stamps=stamps)
+        torch.cuda.synchronize()
+        clocks.append(ca.stamps_summary(stamps))
+    clock = statistics.median(c["clock_GHz"] for c in clocks)
+    by_xcc = {x: round(statistics.median(c["clock_GHz_by_xcc"][x] for c in clocks), 3)
+              for x in clocks[-1]["clock_GHz_by_xcc"]}
+    log(f"shader clock during attention: {clock:.3f} GHz (by XCC {by_xcc})")
     roofline = {
         "bound": "mfma",
         "kernel": "chunk_attn_bf16_kernel<128, 8, false, 0>",
@@ -888,6 +903,10 @@ def main():
         "hbm_frac": (round(traffic / (main_r["attn_ms_mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
                      if traffic else None),
         "reread_factor": round(traffic / main_r["bytes_alg"], 4) if traffic else None,
+        "clock_GHz": round(clock, 4),
+        "clock_GHz_by_xcc": by_xcc,
+        "peak_at_clock": round(PEAK_BF16_TFLOPS * clock / PEAK_CLOCK_GHZ, 1),
+        "frac_at_clock": round(achieved / (PEAK_BF16_TFLOPS * clock / PEAK_CLOCK_GHZ), 4),
     }
     del k_out, v_out
     configs = None

@@ -13,6 +13,7 @@ a KV-head-major cache) are separate calls, as in the method.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 from typing import Optional, Sequence, Tuple
 
@@ -22,7 +23,8 @@ from . import _lib
 from ._lib import CA_BLOCK, CA_MAX_BATCH, CompactAttnError  # noqa: F401
 
 __all__ = ["build_union_tables", "chunk_attention", "tables_to_csr", "check_tables",
-           "build_union_tables_devlen", "chunk_attention_devlen",
+           "build_union_tables_devlen", "chunk_attention_devlen", "chunk_attention_stamped",
+           "stamps_summary",
            "compact_kv", "append_kv",
            "build_row_tables", "chunk_attention_rows", "pool_blocks", "block_mask_topk",
            "workspace_size", "balanced_workspace_size", "chunk_attention_split_noalloc",
@@ -365,6 +367,55 @@ def chunk_attention_split_noalloc(q: torch.Tensor, k_cache: torch.Tensor,
         lse.data_ptr() if lse is not None else None, _stream_ptr(stream))
     _lib.check(st, "ca_chunk_attention_split_noalloc")
     return (out, lse) if return_lse else out
+
+
+def chunk_attention_stamped(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            T: torch.Tensor, lens: torch.Tensor, prior_len: Sequence[int],
+                            chunk_len: Sequence[int], scale: Optional[float] = None,
+                            out: Optional[torch.Tensor] = None,
+                            stamps: Optional[torch.Tensor] = None,
+                            stream: Optional[torch.cuda.Stream] = None):
+    """``chunk_attention`` (bf16) that also records per-workgroup timing words
+    (``ca_chunk_attention_stamped``).  Returns (O, stamps int32 [n_wg, 4]);
+    ``stamps_summary`` turns them into durations and the shader clock."""
+    B, H_q, H_kv, C_max, L, D, scale, out, _, dt = _attention_args(
+        q, k_cache, v_cache, scale, out, None, False)
+    _need_cuda("T", T, torch.int32)
+    _need_cuda("lens", lens, torch.int32)
+    if T.dim() != 3 or tuple(T.shape[:2]) != (B, H_kv) or tuple(lens.shape) != (B, H_kv):
+        raise ValueError("T must be [B, H_kv, NKB_max] and lens [B, H_kv]")
+    n = ctypes.c_int(0)
+    for _ in range(2):  # a first call without a large enough buffer reports the count
+        cap = 0 if stamps is None else stamps.numel() // 4
+        st = _lib.lib().ca_chunk_attention_stamped(
+            q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), T.data_ptr(), lens.data_ptr(),
+            T.shape[2], _host_ints("prior_len", prior_len, B),
+            _host_ints("chunk_len", chunk_len, B), B, H_q, H_kv, C_max, L, D, CA_BLOCK, scale,
+            dt, out.data_ptr(), None, 0 if stamps is None else stamps.data_ptr(), cap,
+            ctypes.byref(n), _stream_ptr(stream))
+        if st == _lib.CA_OK:
+            return out, stamps[:n.value]
+        if stamps is not None and n.value <= cap:
+            break
+        stamps = torch.zeros((max(n.value, 1), 4), dtype=torch.int32, device=q.device)
+    _lib.check(st, "ca_chunk_attention_stamped")
+
+
+def stamps_summary(stamps: torch.Tensor) -> dict:
+    """Durations (us) and shader clock (GHz) from ``chunk_attention_stamped``'s
+    records: overall, and the clock per XCC."""
+    import numpy as np
+    a = stamps.cpu().numpy().view(np.uint32).astype(np.float64)
+    ticks, cycles = a[:, 1], a[:, 2]
+    xcc = (a[:, 3].astype(np.int64) & 0xF)
+    ghz = cycles / np.maximum(ticks, 1) * 0.1
+    per = {int(x): round(float(ghz[xcc == x].mean()), 4) for x in np.unique(xcc)}
+    start = a[:, 0]
+    span_us = float(((start + ticks).max() - start.min()) / 100.0)
+    return dict(workgroups=int(a.shape[0]), clock_GHz=round(float(cycles.sum() / ticks.sum() * 0.1), 4),
+                clock_GHz_by_xcc=per, wg_us_mean=round(float(ticks.mean() / 100.0), 2),
+                wg_us_max=round(float(ticks.max() / 100.0), 2), span_us=round(span_us, 2),
+                cycles_per_wg_mean=round(float(cycles.mean()), 1))
 
 
 def tables_to_csr(T: torch.Tensor, lens: torch.Tensor, L: int,

@@ -25,6 +25,7 @@ EXPORTED = (
     "ca_build_union_tables_devlen",
     "ca_chunk_attention",
     "ca_chunk_attention_devlen",
+    "ca_chunk_attention_stamped",
     "ca_chunk_attention_rows",
     "ca_chunk_attention_split",
     "ca_chunk_attention_split_noalloc",
@@ -65,6 +66,11 @@ def _declare(lib):
                                               _i32, _i32, _i32, _i64, _i32, _i32, ctypes.c_float,
                                               _i32, _vp, _vp, _vp]
     lib.ca_chunk_attention_devlen.restype = _i32
+    lib.ca_chunk_attention_stamped.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32p, _i32p, _i32,
+                                               _i32, _i32, _i32, _i64, _i32, _i32,
+                                               ctypes.c_float, _i32, _vp, _vp, _vp, _i32,
+                                               ctypes.POINTER(ctypes.c_int), _vp]
+    lib.ca_chunk_attention_stamped.restype = _i32
     lib.ca_chunk_attention_rows.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32p, _i32p,
                                             _i32, _i32, _i32, _i32, _i64, _i32, _i32,
                                             ctypes.c_float, _i32, _vp, _vp, _vp]

@@ -170,7 +170,8 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
                     int D, int block, float scale, ca_dtype dtype, void* O, float* lse,
                     bool row_tables, int n_split, void* workspace, size_t workspace_bytes,
                     hipStream_t stream, bool balanced = false, bool static_scratch = false,
-                    bool dev_lengths = false) {
+                    bool dev_lengths = false, uint32_t* stamps = nullptr,
+                    int max_stamped = 0, int* n_stamped = nullptr) {
   if (!Q || !K_cache || !V_cache || !T || !len || !prior_len || !chunk_len || !O)
     return CA_ERR_NULL;
   if (dtype != CA_F32 && dtype != CA_BF16) return CA_ERR_DTYPE;
@@ -226,6 +227,7 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
   p.plan_pieces = nullptr;
   p.dev_prior = dev_lengths ? prior_len : nullptr;
   p.dev_chunk = dev_lengths ? chunk_len : nullptr;
+  p.stamps = nullptr;
   const int64_t n_bg = static_cast<int64_t>(B) * H_kv;
   if (dtype == CA_BF16) {
     // the bf16 kernels address one (b, g) cache slice through a buffer
@@ -260,6 +262,12 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
                        : static_cast<int>((p.G * n_pb + p.waves - 1) / p.waves);
     p.xcd = (n_bg % 8 == 0) ? 1 : 0;
     if (n_bg * p.n_t * n_split > INT32_MAX) return CA_ERR_SHAPE;
+    if (n_stamped != nullptr) {  // stamped call: one record per workgroup
+      const int64_t n_wg = n_bg * p.n_t;
+      *n_stamped = static_cast<int>(n_wg);
+      if (n_wg > max_stamped) return CA_ERR_SHAPE;
+      p.stamps = stamps;
+    }
     if (n_split > 1) {
       if (static_scratch) {  // every argument checked: now look up the array
         hipError_t e = hipSuccess;
@@ -322,6 +330,24 @@ CA_EXPORT ca_status ca_chunk_attention_devlen(const void* Q, const void* K_cache
   return attention(Q, K_cache, V_cache, T, len, 0, NKB_max, prior_len, chunk_len, B, H_q, H_kv,
                    C_max, L, D, block, scale, dtype, O, lse, false, 1, nullptr, 0, stream, false,
                    false, true);
+}
+
+CA_EXPORT ca_status ca_chunk_attention_stamped(const void* Q, const void* K_cache,
+                                               const void* V_cache, const int32_t* T,
+                                               const int32_t* len, int NKB_max,
+                                               const int32_t* prior_len,
+                                               const int32_t* chunk_len, int B, int H_q,
+                                               int H_kv, int C_max, int64_t L, int D, int block,
+                                               float scale, ca_dtype dtype, void* O, float* lse,
+                                               uint32_t* stamps, int max_workgroups,
+                                               int* n_workgroups, hipStream_t stream) {
+  if (!n_workgroups || (!stamps && max_workgroups > 0)) return CA_ERR_NULL;
+  if (dtype != CA_BF16) return CA_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(stamps) & 3u) return CA_ERR_UNSUPPORTED;
+  *n_workgroups = 0;
+  return attention(Q, K_cache, V_cache, T, len, 0, NKB_max, prior_len, chunk_len, B, H_q, H_kv,
+                   C_max, L, D, block, scale, dtype, O, lse, false, 1, nullptr, 0, stream, false,
+                   false, false, stamps, max_workgroups, n_workgroups);
 }
 
 CA_EXPORT size_t ca_chunk_attention_workspace_size(int B, int H_q, int C_max, int D,

@@ -152,6 +152,12 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
+  // stamped calls: the counters at the start (uniform; a scalar read each)
+  uint64_t t_start = 0, c_start = 0;
+  if (kSplit == 0 && !kRows && p.stamps != nullptr) {
+    t_start = __builtin_amdgcn_s_memrealtime();
+    c_start = __builtin_amdgcn_s_memtime();
+  }
   // ---- workgroup -> (sequence, group, tile[, split])
   const int wg = blockIdx.x;
   int b, g, t;
@@ -471,6 +477,18 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
     __syncthreads();
   }
 
+  if (kSplit == 0 && !kRows && p.stamps != nullptr && tid == 0) {
+    const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
+    const uint64_t c_end = __builtin_amdgcn_s_memtime();
+    constexpr uint32_t kHwId = 4 | (31 << 11);    // HW_REG_HW_ID, bits 0..31
+    constexpr uint32_t kXccId = 20 | (31 << 11);  // HW_REG_XCC_ID
+    uint32_t* st = p.stamps + static_cast<size_t>(wg) * kStampWords;
+    st[0] = static_cast<uint32_t>(t_start);
+    st[1] = static_cast<uint32_t>(t_end - t_start);
+    st[2] = static_cast<uint32_t>(c_end - c_start);
+    st[3] = (__builtin_amdgcn_s_getreg(kXccId) & 0xFu) |
+            (((__builtin_amdgcn_s_getreg(kHwId) >> 8) & 0xFFu) << 8);
+  }
   // ---- epilogue: O = acc / l, rows >= C written as 0
   const LaneHalves lh = lane_halves(ws.l_part);
   const float l_tot = lh.lo + lh.hi;

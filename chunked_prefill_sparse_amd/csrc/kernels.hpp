@@ -60,7 +60,16 @@ struct AttnParams {
   // arrays (nullptr: the host values in SeqInfo)
   const int32_t* dev_prior;
   const int32_t* dev_chunk;
+  // stamped calls (bf16 union tables, no split): per-workgroup timing words,
+  // kStampWords per workgroup (nullptr: none written)
+  uint32_t* stamps;
 };
+
+// Timing words per workgroup of a stamped call: start of the 100 MHz
+// real-time counter (low 32 bits), its ticks until the epilogue, the
+// shader-clock cycles over the same span, and the hardware ids (XCC in bits
+// 0..3, the HW_ID register's CU / SH / SE fields in bits 8..15).
+constexpr int kStampWords = 4;
 
 // Prior and chunk length of sequence b in a kernel.  Host-length calls pass
 // values the host has already checked.  Device-length calls read them from

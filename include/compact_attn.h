@@ -191,6 +191,35 @@ CA_EXPORT ca_status ca_chunk_attention_devlen(const void* Q, const void* K_cache
                                     ca_dtype dtype, void* O, float* lse, hipStream_t stream);
 
 /*
+ * ca_chunk_attention_stamped -- ca_chunk_attention (bf16) that also records,
+ * per workgroup, when it ran and at what shader clock: a measurement aid for
+ * the execution stage's kernel (how long each workgroup's table walk takes,
+ * on which XCD, at which clock).  Same result as ca_chunk_attention, bit for
+ * bit.
+ *
+ * stamps          device uint32 [max_workgroups, 4] (out), 4-byte aligned.
+ *                 Record w: [0] start of the 100 MHz real-time counter (low 32
+ *                 bits); [1] its ticks until the workgroup's epilogue; [2]
+ *                 shader-clock cycles over the same span (so the clock is
+ *                 [2] / [1] * 100 MHz); [3] XCC id in bits 0..3, the HW_ID
+ *                 register's CU / SH / SE fields in bits 8..15.
+ * max_workgroups  records the buffer holds; stamps may be NULL with
+ *                 max_workgroups = 0, to learn the count.
+ * n_workgroups    host int (out): the workgroups the call launches (set even
+ *                 when the buffer is too small, which gives CA_ERR_SHAPE and
+ *                 launches nothing).
+ * dtype           CA_BF16 only (else CA_ERR_UNSUPPORTED).
+ * Other arguments, layouts and errors as for ca_chunk_attention.
+ */
+CA_EXPORT ca_status ca_chunk_attention_stamped(const void* Q, const void* K_cache,
+                                     const void* V_cache, const int32_t* T, const int32_t* len,
+                                     int NKB_max, const int32_t* prior_len,
+                                     const int32_t* chunk_len, int B, int H_q, int H_kv,
+                                     int C_max, int64_t L, int D, int block, float scale,
+                                     ca_dtype dtype, void* O, float* lse, uint32_t* stamps,
+                                     int max_workgroups, int* n_workgroups, hipStream_t stream);
+
+/*
  * ca_chunk_attention_split -- ca_chunk_attention with each (b, g) table cut
  * into n_splits contiguous ranges processed by separate workgroups, then
  * merged.  For shapes with few (sequence, KV head) pairs, such as one GPU's

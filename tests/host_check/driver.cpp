@@ -115,6 +115,28 @@ int main() {
       EXPECT(strcmp(stub::last.what, "union") == 0 && stub::last.ptrs[0] == (void*)dp &&
              stub::last.ptrs[1] == (void*)dc);
     }
+    // stamped call: the launch gets the record buffer; too small a buffer is
+    // refused with the workgroup count reported
+    {
+      uint32_t* sb = reinterpret_cast<uint32_t*>(static_cast<uintptr_t>(0x7000400));
+      const int32_t p1[1] = {129024}, c1[1] = {2048};
+      int n_wg = -1;
+      EXPECT(ca_chunk_attention_stamped(FAKE, FAKE, FAKE, (const int32_t*)FAKE,
+                                        (const int32_t*)FAKE, 2048, p1, c1, 1, 32, 8, 2048,
+                                        131072, 128, 64, 0.088f, CA_BF16, FAKE, nullptr, sb, 256,
+                                        &n_wg, 0) == CA_OK);
+      EXPECT(n_wg == 256 && stub::last.p.stamps == sb);
+      stub::last = stub::Record{};
+      EXPECT(ca_chunk_attention_stamped(FAKE, FAKE, FAKE, (const int32_t*)FAKE,
+                                        (const int32_t*)FAKE, 2048, p1, c1, 1, 32, 8, 2048,
+                                        131072, 128, 64, 0.088f, CA_BF16, FAKE, nullptr, sb, 255,
+                                        &n_wg, 0) == CA_ERR_SHAPE);
+      EXPECT(n_wg == 256 && strcmp(stub::last.what, "") == 0);
+      EXPECT(ca_chunk_attention(FAKE, FAKE, FAKE, (const int32_t*)FAKE, (const int32_t*)FAKE,
+                                2048, p1, c1, 1, 32, 8, 2048, 131072, 128, 64, 0.088f, CA_BF16,
+                                FAKE, nullptr, 0) == CA_OK);
+      EXPECT(stub::last.p.stamps == nullptr);
+    }
     // no-alloc split: the partials go to the static array (its stand-in address),
     // same layout; a split past the array's size is refused before any launch
     {

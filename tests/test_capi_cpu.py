@@ -267,3 +267,18 @@ def test_append_validation():
     assert call(a8=_ints(897)) == 2               # prior + chunk > L
     assert call(a8=_ints(-1)) == 2
     assert call(a6=96) == 4 and call(a10=FAKE + 8) == 4
+
+
+def test_stamped_validation():
+    lib = _lib.lib()
+    n = ctypes.c_int(-1)
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 20, _ints(1024), _ints(256), 1, 4, 1, 256, 1280, 64, 64,
+            0.125, 1, FAKE, None]
+    st = lib.ca_chunk_attention_stamped
+    assert st(*base, None, 16, ctypes.byref(n), None) == 1
+    # no buffer: the count only (4 heads x 256 rows in 32-row tiles, 4 per workgroup)
+    assert st(*base, None, 0, ctypes.byref(n), None) == 2 and n.value == 8
+    assert st(*base, FAKE, 16, None, None) == 1
+    assert st(*base[:16], 0, *base[17:], FAKE, 16, ctypes.byref(n), None) == 4  # fp32
+    assert st(*base, FAKE + 2, 16, ctypes.byref(n), None) == 4
+    assert st(*base[:6], _ints(1000), *base[7:], FAKE, 16, ctypes.byref(n), None) == 4
