@@ -29,6 +29,16 @@ __global__ __launch_bounds__(kAppendThreads) void append_kv_kernel(
   uint4* dst = (blockIdx.z == 0 ? k_cache : v_cache) + static_cast<int64_t>(u) * cache_slice_vec +
                static_cast<int64_t>(seq.prior[b]) * row_vec;
   uint4 x[kAppendVec];
+  const int64_t wg_end = (static_cast<int64_t>(blockIdx.y) + 1) * kAppendThreads * kAppendVec;
+  if (wg_end <= n) {
+    // whole workgroup in range (uniform): unguarded loads, so all four are in
+    // flight before the first wait (guarded ones each wait on their own)
+#pragma unroll
+    for (int k = 0; k < kAppendVec; ++k) x[k] = src[i0 + static_cast<int64_t>(k) * kAppendThreads];
+#pragma unroll
+    for (int k = 0; k < kAppendVec; ++k) dst[i0 + static_cast<int64_t>(k) * kAppendThreads] = x[k];
+    return;
+  }
 #pragma unroll
   for (int k = 0; k < kAppendVec; ++k) {
     const int64_t i = i0 + static_cast<int64_t>(k) * kAppendThreads;
