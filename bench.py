@@ -562,6 +562,10 @@ def prefill_leg(stream, budget=32, local=8):
         for c in range(s.n_chunks):
             drv.select(qs[c], priors[c])
 
+    def run_select_separate():  # the same selection through the six separate launches
+        for c in range(s.n_chunks):
+            drv.select_separate(qs[c], priors[c])
+
     def run_dense():
         for c in range(s.n_chunks):
             drv.step_dense(qs[c], priors[c], dense_lens[c], k_chunk=kv[c][0], v_chunk=kv[c][1])
@@ -576,6 +580,7 @@ def prefill_leg(stream, budget=32, local=8):
     sparse_ms = statistics.median(timed(run_sparse) for _ in range(reps))
     append_ms = statistics.median(timed(run_append) for _ in range(reps))
     select_ms = statistics.median(timed(run_select) for _ in range(reps))
+    select_sep_ms = statistics.median(timed(run_select_separate) for _ in range(reps))
     dense_ms = statistics.median(timed(run_dense) for _ in range(reps))
     attn_ms = sparse_ms - select_ms - append_ms
     run_balanced()
@@ -584,17 +589,22 @@ def prefill_leg(stream, budget=32, local=8):
     # GPU time without the per-call host work of the loop above
     g_sparse = drv.capture(qs, priors, kv_chunks=kv)
     g_select = drv.capture(qs, priors, select_only=True)
+    g_select_sep = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_select_sep):
+        run_select_separate()
     g_dense = drv.capture(qs, priors, dense=True, kv_chunks=kv)
     g_sparse.replay()
     g_dense.replay()
     gs_ms = statistics.median(timed(g_sparse.replay) for _ in range(reps))
     gsel_ms = statistics.median(timed(g_select.replay) for _ in range(reps))
+    gsel_sep_ms = statistics.median(timed(g_select_sep.replay) for _ in range(reps))
     gd_ms = statistics.median(timed(g_dense.replay) for _ in range(reps))
     moved = 2 * 2 * s.n_chunks * s.H_kv * s.C * s.D * 2  # K and V, read once and written once
     r = dict(
         chunks=s.n_chunks, chunk=s.C, prompt=s.L, budget_blocks=budget, local_blocks=local,
         total_ms=round(sparse_ms, 3), append_ms=round(append_ms, 3),
         append_GBps=round(moved / (append_ms * 1e-3) / 1e9, 1), select_ms=round(select_ms, 3),
+        select_separate_ms=round(select_sep_ms, 3),
         attention_ms=round(attn_ms, 3), dense_total_ms=round(dense_ms, 3),
         x_vs_dense=round(dense_ms / sparse_ms, 3),
         attention_eff_tflops=round(flops / (attn_ms * 1e-3) / 1e12, 1),
@@ -608,6 +618,7 @@ def prefill_leg(stream, budget=32, local=8):
                       attention_eff_tflops=round(
                           flops / ((bal_ms - select_ms - append_ms) * 1e-3) / 1e12, 1)),
         graph=dict(total_ms=round(gs_ms, 3), select_ms=round(gsel_ms, 3),
+                   select_separate_ms=round(gsel_sep_ms, 3),
                    dense_total_ms=round(gd_ms, 3), x_vs_dense=round(gd_ms / gs_ms, 3)),
         data=("synthetic planted-structure stream: K, V, Q ~ N(0,1), 3% salient KV blocks per "
               "KV head shifted along a per-head direction that the group's queries share; the "
@@ -617,9 +628,9 @@ def prefill_leg(stream, budget=32, local=8):
         f"attention {attn_ms:.2f}) vs dense {dense_ms:.2f} ms -> x{dense_ms / sparse_ms:.2f}; "
         f"union fraction first/mid/last {r['union_block_frac_first_mid_last']}")
     log(f"prefill_128k with balanced attention: total {bal_ms:.2f} ms -> x{dense_ms / bal_ms:.2f}")
-    log(f"prefill_128k as HIP graphs: total {gs_ms:.2f} ms (select {gsel_ms:.2f}) vs dense "
-        f"{gd_ms:.2f} ms -> x{gd_ms / gs_ms:.2f}")
-    del qs, k, v, kv, drv, drv_bal, g_sparse, g_select, g_dense
+    log(f"prefill_128k as HIP graphs: total {gs_ms:.2f} ms (select {gsel_ms:.2f}, through the "
+        f"separate calls {gsel_sep_ms:.2f}) vs dense {gd_ms:.2f} ms -> x{gd_ms / gs_ms:.2f}")
+    del qs, k, v, kv, drv, drv_bal, g_sparse, g_select, g_select_sep, g_dense
     torch.cuda.empty_cache()
     return r
 

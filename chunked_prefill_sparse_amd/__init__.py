@@ -26,7 +26,7 @@ __all__ = ["build_union_tables", "chunk_attention", "tables_to_csr", "check_tabl
            "build_union_tables_devlen", "chunk_attention_devlen", "chunk_attention_stamped",
            "stamps_summary",
            "compact_kv", "append_kv",
-           "build_row_tables", "chunk_attention_rows", "pool_blocks", "block_mask_topk",
+           "build_row_tables", "chunk_attention_rows", "pool_blocks", "block_mask_topk", "select_chunk",
            "workspace_size", "balanced_workspace_size", "chunk_attention_split_noalloc",
            "CompactAttnError", "library_path"]
 
@@ -558,3 +558,38 @@ def block_mask_topk(qbar: torch.Tensor, kbar: torch.Tensor, prior_len: Sequence[
         int(budget), int(local), scores.data_ptr(), mask.data_ptr(), _stream_ptr(stream))
     _lib.check(st, "ca_block_mask_topk")
     return mask, scores
+
+
+def select_chunk(q_chunk: torch.Tensor, k_cache: torch.Tensor, prior_len: Sequence[int],
+                 chunk_len: Sequence[int], budget: int, local: int, qbar: torch.Tensor,
+                 kbar: torch.Tensor, scores: torch.Tensor, mask: torch.Tensor, T: torch.Tensor,
+                 lens: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """A chunk's whole selection step (``ca_select_chunk``): pool the chunk's new
+    key blocks into kbar and its Q-blocks into qbar, score, take the top-k
+    mask and build the union tables T / lens, in four launches; every output
+    buffer is the caller's (qbar [B, H_q, NQ, D], kbar [B, H_kv, NKB, D] kept
+    across chunks, scores / mask [B, H_q, NQ, NKB], T [B, H_kv, NKB], lens [B, H_kv])."""
+    _need_cuda("q_chunk", q_chunk)
+    if q_chunk.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q_chunk must be bfloat16 or float32")
+    _need_cuda("k_cache", k_cache, q_chunk.dtype)
+    for name, t, dt in (("qbar", qbar, torch.float32), ("kbar", kbar, torch.float32),
+                        ("scores", scores, torch.float32), ("mask", mask, torch.uint8),
+                        ("T", T, torch.int32), ("lens", lens, torch.int32)):
+        _need_cuda(name, t, dt)
+    if q_chunk.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q_chunk must be [B, H_q, C_max, D] and k_cache [B, H_kv, L, D]")
+    B, H_q, C_max, D = q_chunk.shape
+    H_kv, L = k_cache.shape[1], k_cache.shape[2]
+    NQ, NKB = qbar.shape[2], kbar.shape[2]
+    if tuple(qbar.shape) != (B, H_q, NQ, D) or tuple(kbar.shape) != (B, H_kv, NKB, D) or \
+            tuple(scores.shape) != (B, H_q, NQ, NKB) or tuple(mask.shape) != (B, H_q, NQ, NKB) or \
+            tuple(T.shape) != (B, H_kv, NKB) or tuple(lens.shape) != (B, H_kv):
+        raise ValueError("qbar / kbar / scores / mask / T / lens shapes do not match")
+    dt = _lib.CA_BF16 if q_chunk.dtype == torch.bfloat16 else _lib.CA_F32
+    st = _lib.lib().ca_select_chunk(
+        q_chunk.data_ptr(), k_cache.data_ptr(), dt, B, H_q, H_kv, C_max, L, D,
+        _host_ints("prior_len", prior_len, B), _host_ints("chunk_len", chunk_len, B),
+        int(budget), int(local), qbar.data_ptr(), NQ, kbar.data_ptr(), NKB, scores.data_ptr(),
+        mask.data_ptr(), T.data_ptr(), lens.data_ptr(), _stream_ptr(stream))
+    _lib.check(st, "ca_select_chunk")

@@ -38,6 +38,7 @@ EXPORTED = (
     "ca_append_kv",
     "ca_pool_blocks",
     "ca_block_mask_topk",
+    "ca_select_chunk",
     "ca_status_string",
     "ca_last_hip_error",
 )
@@ -108,6 +109,10 @@ def _declare(lib):
     lib.ca_block_mask_topk.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32p, _i32p,
                                        _i32, _i32, _vp, _vp, _vp]
     lib.ca_block_mask_topk.restype = _i32
+    lib.ca_select_chunk.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32p,
+                                    _i32p, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp,
+                                    _vp]
+    lib.ca_select_chunk.restype = _i32
     lib.ca_status_string.argtypes = [_i32]
     lib.ca_status_string.restype = ctypes.c_char_p
     lib.ca_last_hip_error.argtypes = []

@@ -17,43 +17,39 @@
 // each new block once; the scores read kbar once per KV group; the selection
 // reads each score row a few times from L2 and writes one mask byte per cell.
 
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace ca {
 namespace {
 
 constexpr int kMaskThreads = 256;
+constexpr int kSelectReplicas = 16;  // union bitmap copies of the fused selection
+constexpr int kTopkStage = 8;        // score loads in flight per thread when staging keys
+constexpr int kTopkLdsMax = 15360;   // rows up to this many blocks stage keys in LDS (60 KiB)
 
 // ---------------------------------------------------------------- pooling
 
-// Workgroup (b*H + h, y) pools block kb = begin[b] + y.  Each thread sums a
-// 16-byte column slice over every RPI-th row of the block; the RPI partial
-// sums of a column are then added in row-group order.
+// Mean of the 64 rows of one block (src points at its first row, row stride
+// D) into out[0 .. D): each thread sums a 16-byte column slice over every
+// RPI-th row; the RPI partial sums of a column are then added in row-group
+// order.  All of a thread's row loads are in flight before the sums.
 template <typename TIn, int D>
-__global__ __launch_bounds__(kMaskThreads) void pool_blocks_kernel(const TIn* __restrict__ X,
-                                                                   int H, int64_t R,
-                                                                   BlockRange rng,
-                                                                   float* __restrict__ out,
-                                                                   int NB_out) {
+__device__ __forceinline__ void pool_one_block(const TIn* __restrict__ src,
+                                               float* __restrict__ out, float* part) {
   constexpr int V = 16 / static_cast<int>(sizeof(TIn));  // elements per 16-byte load
   constexpr int TPR = D / V;                              // threads per row
   constexpr int RPI = kMaskThreads / TPR;                 // rows per iteration
   static_assert(64 % RPI == 0, "rows of a block split evenly over the row groups");
-  __shared__ float part[RPI * D];
-  const int bh = blockIdx.x;
-  const int b = bh / H;
-  const int kb = rng.begin[b] + static_cast<int>(blockIdx.y);
-  if (kb >= rng.end[b]) return;
   const int tid = threadIdx.x;
   const int col = (tid % TPR) * V;
   const int rsub = tid / TPR;
-  const TIn* src = X + (static_cast<size_t>(bh) * R + static_cast<size_t>(kb) * 64) * D + col;
-  // all of this thread's row loads in flight before the sums (in row order)
   constexpr int NR = 64 / RPI;
   uint4 raw[NR];
 #pragma unroll
   for (int k = 0; k < NR; ++k)
-    raw[k] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(rsub + k * RPI) * D);
+    raw[k] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(rsub + k * RPI) * D + col);
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
@@ -69,8 +65,63 @@ __global__ __launch_bounds__(kMaskThreads) void pool_blocks_kernel(const TIn* __
   if (tid < D) {
     float s = 0.f;
     for (int k = 0; k < RPI; ++k) s += part[k * D + tid];
-    out[(static_cast<size_t>(bh) * NB_out + kb) * D + tid] = s * (1.f / 64.f);
+    out[tid] = s * (1.f / 64.f);
   }
+}
+
+template <typename TIn, int D>
+constexpr int kPoolPart = (kMaskThreads / (D / (16 / static_cast<int>(sizeof(TIn))))) * D;
+
+// Workgroup (b*H + h, y) pools block kb = begin[b] + y.
+template <typename TIn, int D>
+__global__ __launch_bounds__(kMaskThreads) void pool_blocks_kernel(const TIn* __restrict__ X,
+                                                                   int H, int64_t R,
+                                                                   BlockRange rng,
+                                                                   float* __restrict__ out,
+                                                                   int NB_out) {
+  __shared__ float part[kPoolPart<TIn, D>];
+  const int bh = blockIdx.x;
+  const int b = bh / H;
+  const int kb = rng.begin[b] + static_cast<int>(blockIdx.y);
+  if (kb >= rng.end[b]) return;
+  pool_one_block<TIn, D>(X + (static_cast<size_t>(bh) * R + static_cast<size_t>(kb) * 64) * D,
+                         out + (static_cast<size_t>(bh) * NB_out + kb) * D, part);
+}
+
+// First launch of a chunk's selection: workgroup w < nK pools the chunk's new
+// key block (b, g, P/64 + y) into kbar; the next nQ workgroups pool its
+// Q-block (b, h, y) into qbar; the last B * H_kv workgroups clear the union
+// bitmaps at the tail of each T[b,g] row (n_rep copies of ceil(NKB_max / 32)
+// words), which the selection then ORs into.
+template <typename TIn, int D>
+__global__ __launch_bounds__(kMaskThreads) void select_pool_kernel(
+    const TIn* __restrict__ K, const TIn* __restrict__ Q, int H_q, int H_kv, int64_t L,
+    int C_max, int NQ_max, int NKB_max, int span, int n_k, int n_q, int n_rep, SeqInfo seq,
+    float* __restrict__ kbar, float* __restrict__ qbar, int32_t* __restrict__ T) {
+  __shared__ float part[kPoolPart<TIn, D>];
+  int w = blockIdx.x;  // n_k = B * H_kv * span key blocks, n_q = B * H_q * span Q-blocks
+  if (w < n_k) {
+    const int bg = w / span, y = w - bg * span;
+    const int b = bg / H_kv;
+    const int kb = seq.prior[b] / 64 + y;
+    if (y >= seq.chunk[b] / 64) return;
+    pool_one_block<TIn, D>(K + (static_cast<size_t>(bg) * L + static_cast<size_t>(kb) * 64) * D,
+                           kbar + (static_cast<size_t>(bg) * NKB_max + kb) * D, part);
+    return;
+  }
+  w -= n_k;
+  if (w < n_q) {
+    const int bh = w / span, y = w - bh * span;
+    const int b = bh / H_q;
+    if (y >= seq.chunk[b] / 64) return;
+    pool_one_block<TIn, D>(Q + (static_cast<size_t>(bh) * C_max + static_cast<size_t>(y) * 64) * D,
+                           qbar + (static_cast<size_t>(bh) * NQ_max + y) * D, part);
+    return;
+  }
+  w -= n_q;  // one row of T per workgroup
+  const int nw = n_rep * ((NKB_max + 31) >> 5);
+  int32_t* tail = T + static_cast<size_t>(w) * NKB_max + (NKB_max - nw);
+  for (int i = threadIdx.x; i < nw; i += kMaskThreads) tail[i] = 0;
 }
 
 // ---------------------------------------------------------------- scores
@@ -186,9 +237,24 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 // and every thread decides its blocks alone; otherwise (equal keys straddle
 // the budget) the row is written in ascending kb, taking keys above the
 // threshold and, of the keys equal to it, the lowest kb first.
+//
+// kUnion: the fused selection also ORs each selected cell into its group's
+// union bitmap at the tail of the T[b,g] row (cleared by select_pool_kernel):
+// per wave, one ballot over 64 consecutive blocks and up to two device-scope
+// atomicOr.  The 128 rows of a group would all hit the same words, and
+// atomics on one address serialize, so row r ORs into copy r % n_rep of the
+// bitmap (n_rep copies side by side; the compaction ORs them together).  What
+// is ORed is exactly the union over the chunk's Q-blocks and the group's heads
+// (rows past the chunk select nothing).
+// kLds: the row's candidate keys are read from the scores once (kTopkStage
+// loads in flight per thread) into dynamic LDS (NKB_max words), and every pass
+// reads them there; without it each pass re-reads the scores row.
+template <bool kUnion, bool kLds>
 __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
     const float* __restrict__ scores, int H_q, int NQ_max, int NKB_max, SeqInfo seq,
-    int budget, int local, uint8_t* __restrict__ mask) {
+    int budget, int local, uint8_t* __restrict__ mask, int H_kv, int32_t* __restrict__ T,
+    int n_rep) {
+  extern __shared__ uint32_t keys[];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh_prefix, sh_need, sh_bin;
   __shared__ int wave_eq[kMaskThreads / 64];
@@ -201,6 +267,26 @@ __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
   uint8_t* mrow = mask + row * NKB_max;
   const int pblk = seq.prior[b] / 64;
   const int nq = seq.chunk[b] / 64;
+  // union bitmap of this row's group (kUnion): words at the tail of T[b,g]
+  const int nwords = (NKB_max + 31) >> 5;
+  uint32_t* ubits = nullptr;
+  if (kUnion) {
+    const int h = static_cast<int>((row / NQ_max) % H_q);
+    const int g = h / (H_q / H_kv);
+    ubits = reinterpret_cast<uint32_t*>(T + (static_cast<size_t>(b) * H_kv + g) * NKB_max +
+                                        (NKB_max - n_rep * nwords) +
+                                        static_cast<size_t>(row % n_rep) * nwords);
+  }
+  // OR the selections of blocks base + 64 * wave .. + 63 into the bitmap
+  auto or_bits = [&](int base, bool sel) {
+    const uint64_t bal = __ballot(sel);
+    if (lane == 0 && bal != 0ull) {
+      const int w0 = (base + 64 * wave) >> 5;
+      const uint32_t lo = static_cast<uint32_t>(bal), hi = static_cast<uint32_t>(bal >> 32);
+      if (lo != 0u && w0 < nwords) atomicOr(&ubits[w0], lo);
+      if (hi != 0u && w0 + 1 < nwords) atomicOr(&ubits[w0 + 1], hi);
+    }
+  };
   if (qb >= nq) {
     for (int kb = tid; kb < NKB_max; kb += kMaskThreads) mrow[kb] = 0;
     return;
@@ -209,6 +295,23 @@ __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
   const int n_cand = lo_local - 1 > 0 ? lo_local - 1 : 0;
   const uint32_t kk = static_cast<uint32_t>(budget < n_cand ? budget : n_cand);
   const float* srow = scores + row * NKB_max;
+  if (kLds && kk > 0u) {  // kk is uniform; candidates are [1, lo_local), lo_local >= 2
+    for (int base = 1; base < lo_local; base += kMaskThreads * kTopkStage) {
+      float v[kTopkStage];
+#pragma unroll
+      for (int j = 0; j < kTopkStage; ++j) {  // clamped, so no load waits on a branch
+        const int kb = base + j * kMaskThreads + tid;
+        v[j] = srow[kb < lo_local ? kb : lo_local - 1];
+      }
+#pragma unroll
+      for (int j = 0; j < kTopkStage; ++j) {
+        const int kb = base + j * kMaskThreads + tid;
+        if (kb < lo_local) keys[kb] = score_key(v[j]);
+      }
+    }
+    __syncthreads();
+  }
+  auto key_at = [&](int kb) -> uint32_t { return kLds ? keys[kb] : score_key(srow[kb]); };
 
   uint32_t prefix = 0u, need = kk;
   uint32_t lvl_mask = 0u;  // key bits the passes have fixed
@@ -220,7 +323,7 @@ __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
       hist[tid] = 0u;
       __syncthreads();
       for (int kb = 1 + tid; kb < lo_local; kb += kMaskThreads) {
-        const uint32_t key = score_key(srow[kb]);
+        const uint32_t key = key_at(kb);
         if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
@@ -269,11 +372,17 @@ __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
   // candidates above it, and `need` of those equal to it (lowest kb first)
 
   if (whole_bin) {  // no equal key is left out: no ordering across the row
-    for (int kb = tid; kb < NKB_max; kb += kMaskThreads) {
-      bool sel = (pblk > 0 && kb == 0) || (kb >= lo_local && kb < pblk) ||
-                 (kb >= pblk && kb <= pblk + qb);
-      if (kk > 0u && kb >= 1 && kb < lo_local) sel = sel || (score_key(srow[kb]) & lvl_mask) >= prefix;
-      mrow[kb] = sel ? 1 : 0;
+    for (int base = 0; base < NKB_max; base += kMaskThreads) {
+      const int kb = base + tid;
+      bool sel = false;
+      if (kb < NKB_max) {
+        sel = (pblk > 0 && kb == 0) || (kb >= lo_local && kb < pblk) ||
+              (kb >= pblk && kb <= pblk + qb);
+        if (kk > 0u && kb >= 1 && kb < lo_local)
+          sel = sel || (key_at(kb) & lvl_mask) >= prefix;
+        mrow[kb] = sel ? 1 : 0;
+      }
+      if (kUnion) or_bits(base, sel);
     }
     return;
   }
@@ -286,7 +395,7 @@ __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
       sel = (pblk > 0 && kb == 0) || (kb >= lo_local && kb < pblk) ||
             (kb >= pblk && kb <= pblk + qb);
       if (kk > 0u && kb >= 1 && kb < lo_local) {
-        const uint32_t key = score_key(srow[kb]);
+        const uint32_t key = key_at(kb);
         sel = sel || key > prefix;
         eq = key == prefix;
       }
@@ -300,9 +409,24 @@ __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
     for (int w = 0; w < wave; ++w) off += wave_eq[w];
     if (eq && off + below < need) sel = true;
     if (kb < NKB_max) mrow[kb] = sel ? 1 : 0;
+    if (kUnion) or_bits(base, sel);
     for (int w = 0; w < kMaskThreads / 64; ++w) taken += wave_eq[w];
     __syncthreads();
   }
+}
+
+template <bool kUnion>
+void launch_topk(const float* scores, int B, int H_q, int NQ_max, int NKB_max, const SeqInfo& seq,
+                 int budget, int local, uint8_t* mask, int H_kv, int32_t* T, int n_rep,
+                 hipStream_t stream) {
+  const dim3 grid(B * H_q * NQ_max);
+  if (NKB_max <= kTopkLdsMax)
+    hipLaunchKernelGGL((topk_mask_kernel<kUnion, true>), grid, dim3(kMaskThreads),
+                       static_cast<size_t>(NKB_max) * sizeof(uint32_t), stream, scores, H_q,
+                       NQ_max, NKB_max, seq, budget, local, mask, H_kv, T, n_rep);
+  else
+    hipLaunchKernelGGL((topk_mask_kernel<kUnion, false>), grid, dim3(kMaskThreads), 0, stream,
+                       scores, H_q, NQ_max, NKB_max, seq, budget, local, mask, H_kv, T, n_rep);
 }
 
 }  // namespace
@@ -332,26 +456,80 @@ hipError_t launch_pool_blocks(const void* X, int esz, int B, int H, int64_t R, i
   return hipGetLastError();
 }
 
+namespace {
+
+hipError_t launch_scores(const float* qbar, const float* kbar, int B, int H_q, int H_kv,
+                         int NQ_max, int NKB_max, int D, const SeqInfo& seq, int max_pblk,
+                         float* scores, hipStream_t stream) {
+  if (max_pblk <= 0) return hipSuccess;
+  const int ny = (max_pblk + kScoreTile - 1) / kScoreTile;
+  const int nz = ((H_q / H_kv) * NQ_max + kScoreTile - 1) / kScoreTile;
+  const dim3 grid(B * H_kv, ny, nz);
+  if (D == 128)
+    hipLaunchKernelGGL(block_scores_kernel<128>, grid, dim3(kMaskThreads), 0, stream, qbar, kbar,
+                       H_q, H_kv, NQ_max, NKB_max, seq, scores);
+  else
+    hipLaunchKernelGGL(block_scores_kernel<64>, grid, dim3(kMaskThreads), 0, stream, qbar, kbar,
+                       H_q, H_kv, NQ_max, NKB_max, seq, scores);
+  return hipGetLastError();
+}
+
+template <typename TIn>
+void launch_select_pool(const void* Q, const void* K, int B, int H_q, int H_kv, int C_max,
+                        int64_t L, int D, const SeqInfo& seq, int span, float* qbar, int NQ_max,
+                        float* kbar, int NKB_max, int32_t* T, int n_rep, hipStream_t stream) {
+  const int n_k = B * H_kv * span, n_q = B * H_q * span;
+  const dim3 grid(n_k + n_q + B * H_kv);
+  const TIn* k = static_cast<const TIn*>(K);
+  const TIn* q = static_cast<const TIn*>(Q);
+  if (D == 128)
+    hipLaunchKernelGGL((select_pool_kernel<TIn, 128>), grid, dim3(kMaskThreads), 0, stream, k, q,
+                       H_q, H_kv, L, C_max, NQ_max, NKB_max, span, n_k, n_q, n_rep, seq, kbar,
+                       qbar, T);
+  else
+    hipLaunchKernelGGL((select_pool_kernel<TIn, 64>), grid, dim3(kMaskThreads), 0, stream, k, q,
+                       H_q, H_kv, L, C_max, NQ_max, NKB_max, span, n_k, n_q, n_rep, seq, kbar,
+                       qbar, T);
+}
+
+}  // namespace
+
 hipError_t launch_block_mask(const float* qbar, const float* kbar, int B, int H_q, int H_kv,
                              int NQ_max, int NKB_max, int D, const SeqInfo& seq, int max_pblk,
                              int budget, int local, float* scores, uint8_t* mask,
                              hipStream_t stream) {
-  if (max_pblk > 0) {
-    const int ny = (max_pblk + kScoreTile - 1) / kScoreTile;
-    const int nz = ((H_q / H_kv) * NQ_max + kScoreTile - 1) / kScoreTile;
-    const dim3 grid(B * H_kv, ny, nz);
-    if (D == 128)
-      hipLaunchKernelGGL(block_scores_kernel<128>, grid, dim3(kMaskThreads), 0, stream, qbar,
-                         kbar, H_q, H_kv, NQ_max, NKB_max, seq, scores);
-    else
-      hipLaunchKernelGGL(block_scores_kernel<64>, grid, dim3(kMaskThreads), 0, stream, qbar, kbar,
-                         H_q, H_kv, NQ_max, NKB_max, seq, scores);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(topk_mask_kernel, dim3(B * H_q * NQ_max), dim3(kMaskThreads), 0, stream,
-                     scores, H_q, NQ_max, NKB_max, seq, budget, local, mask);
+  const hipError_t e = launch_scores(qbar, kbar, B, H_q, H_kv, NQ_max, NKB_max, D, seq, max_pblk,
+                                     scores, stream);
+  if (e != hipSuccess) return e;
+  launch_topk<false>(scores, B, H_q, NQ_max, NKB_max, seq, budget, local, mask, H_kv, nullptr, 1,
+                     stream);
   return hipGetLastError();
+}
+
+hipError_t launch_select_chunk(const void* Q, const void* K, int esz, int B, int H_q, int H_kv,
+                               int C_max, int64_t L, int D, const SeqInfo& seq, int max_nq,
+                               int max_pblk, int budget, int local, float* qbar, int NQ_max,
+                               float* kbar, int NKB_max, float* scores, uint8_t* mask,
+                               int32_t* T, int32_t* len, hipStream_t stream) {
+  // copies of the union bitmap the top-k rows spread their atomics over (as many
+  // as the T row's tail holds, up to 16)
+  const int nwords = (NKB_max + 31) / 32;
+  const int n_rep = std::max(1, std::min(kSelectReplicas, NKB_max / nwords));
+  if (esz == 2)
+    launch_select_pool<__bf16>(Q, K, B, H_q, H_kv, C_max, L, D, seq, max_nq, qbar, NQ_max, kbar,
+                               NKB_max, T, n_rep, stream);
+  else
+    launch_select_pool<float>(Q, K, B, H_q, H_kv, C_max, L, D, seq, max_nq, qbar, NQ_max, kbar,
+                              NKB_max, T, n_rep, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_scores(qbar, kbar, B, H_q, H_kv, NQ_max, NKB_max, D, seq, max_pblk, scores, stream);
+  if (e != hipSuccess) return e;
+  launch_topk<true>(scores, B, H_q, NQ_max, NKB_max, seq, budget, local, mask, H_kv, T, n_rep,
+                    stream);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_union_compact(B * H_kv, NKB_max, n_rep, T, len, stream);
 }
 
 }  // namespace ca

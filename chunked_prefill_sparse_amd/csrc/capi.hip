@@ -553,4 +553,46 @@ CA_EXPORT ca_status ca_block_mask_topk(const float* qbar, const float* kbar, int
                                           max_pblk, budget, local, scores, mask, stream));
 }
 
+CA_EXPORT ca_status ca_select_chunk(const void* Q_chunk, const void* K_cache, ca_dtype dtype,
+                                    int B, int H_q, int H_kv, int C_max, int64_t L, int D,
+                                    const int32_t* prior_len, const int32_t* chunk_len,
+                                    int budget, int local, float* qbar, int NQ_max, float* kbar,
+                                    int NKB_max, float* scores, uint8_t* mask, int32_t* T,
+                                    int32_t* len, hipStream_t stream) {
+  if (!Q_chunk || !K_cache || !prior_len || !chunk_len || !qbar || !kbar || !scores || !mask ||
+      !T || !len)
+    return CA_ERR_NULL;
+  if (dtype != CA_F32 && dtype != CA_BF16) return CA_ERR_DTYPE;
+  if (B < 1 || B > CA_MAX_BATCH || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || C_max < 1 ||
+      L < 1 || NQ_max < 1 || NKB_max < 1 || NKB_max > kMaxUnionBlocks || budget < 0 || local < 0)
+    return CA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H_q * NQ_max > INT32_MAX ||
+      static_cast<int64_t>(B) * H_kv > 65535)
+    return CA_ERR_SHAPE;
+  if (D != 64 && D != 128) return CA_ERR_UNSUPPORTED;
+  if (!aligned16(Q_chunk) || !aligned16(K_cache) || !aligned16(qbar) || !aligned16(kbar))
+    return CA_ERR_UNSUPPORTED;
+  ca::SeqInfo seq;
+  memset(&seq, 0, sizeof(seq));
+  int max_pblk = 0, max_nq = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t P = prior_len[b], C = chunk_len[b];
+    if (P < 0 || C < 0 || C > C_max || C > static_cast<int64_t>(NQ_max) * CA_BLOCK || P + C > L ||
+        P + C > static_cast<int64_t>(NKB_max) * CA_BLOCK)
+      return CA_ERR_SHAPE;
+    if (P % CA_BLOCK != 0 || C % CA_BLOCK != 0) return CA_ERR_UNSUPPORTED;
+    seq.prior[b] = static_cast<int32_t>(P);
+    seq.chunk[b] = static_cast<int32_t>(C);
+    seq.order[b] = b;
+    max_pblk = std::max(max_pblk, static_cast<int>(P / CA_BLOCK));
+    max_nq = std::max(max_nq, static_cast<int>(C / CA_BLOCK));
+  }
+  const int64_t n_pool = static_cast<int64_t>(B) * (H_q + H_kv) * max_nq + B * H_kv;
+  if (n_pool > INT32_MAX) return CA_ERR_SHAPE;
+  return hip_status(ca::launch_select_chunk(Q_chunk, K_cache, dtype == CA_BF16 ? 2 : 4, B, H_q,
+                                            H_kv, C_max, L, D, seq, max_nq, max_pblk, budget,
+                                            local, qbar, NQ_max, kbar, NKB_max, scores, mask, T,
+                                            len, stream));
+}
+
 }  // extern "C"

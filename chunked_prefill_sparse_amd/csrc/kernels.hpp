@@ -108,6 +108,12 @@ hipError_t launch_union_tables(const uint8_t* mask, int B, int H_q, int H_kv, in
                                const int32_t* dev_nkb, int32_t* T, int32_t* len, int cus,
                                hipStream_t stream);
 
+// Compaction of union bitmaps parked at the tail of each T row (n_rep copies
+// of ceil(NKB_max / 32) words, ORed together; n_rep * words <= NKB_max) into
+// the rows themselves and len, one workgroup per row.
+hipError_t launch_union_compact(int n_bg, int NKB_max, int n_rep, int32_t* T, int32_t* len,
+                                hipStream_t stream);
+
 hipError_t launch_check_tables(const int32_t* T, const int32_t* len, int n_bg, int H_kv,
                                int NKB_max, const UnionExtents& ext, int32_t* row_bad,
                                hipStream_t stream);
@@ -176,6 +182,16 @@ hipError_t launch_compact_kv(const void* K, const void* V, const int32_t* T, con
 hipError_t launch_pool_blocks(const void* X, int esz, int B, int H, int64_t R, int D,
                               const BlockRange& rng, int max_span, float* out, int NB_out,
                               hipStream_t stream);
+
+// A chunk's whole selection step in four launches: pool its new key blocks
+// and its Q-blocks (clearing the union bitmap words of T), the scores, the
+// top-k mask with the union bits ORed in, the union compaction (esz = 2:
+// bf16, 4: fp32 for Q and K).
+hipError_t launch_select_chunk(const void* Q, const void* K, int esz, int B, int H_q, int H_kv,
+                               int C_max, int64_t L, int D, const SeqInfo& seq, int max_nq,
+                               int max_pblk, int budget, int local, float* qbar, int NQ_max,
+                               float* kbar, int NKB_max, float* scores, uint8_t* mask,
+                               int32_t* T, int32_t* len, hipStream_t stream);
 
 // Block-mask producer: pooled scores, then per-row top-k selection.
 hipError_t launch_block_mask(const float* qbar, const float* kbar, int B, int H_q, int H_kv,

@@ -247,16 +247,37 @@ __global__ __launch_bounds__(kSliceThreads) void union_slice_kernel(
 
 // Step 2 after union_slice_kernel: load the parked words of row u into LDS,
 // then compact them over the whole row.
+// n_rep copies of the bitmap lie side by side at the tail (the fused selection
+// spreads its atomics over them); they are ORed together.
 template <int kThreads>  // 256 for bitmaps of up to 256 words (8192 blocks), else 1024
 __global__ __launch_bounds__(kThreads) void union_compact_kernel(
-    int NKB_max, int32_t* __restrict__ T, int32_t* __restrict__ len) {
+    int NKB_max, int n_rep, int32_t* __restrict__ T, int32_t* __restrict__ len) {
   extern __shared__ uint32_t bitmap[];  // ceil(NKB_max / 32) words
   __shared__ int wave_total[kThreads / 64];
   const int u = blockIdx.x;
   const int nwords = (NKB_max + 31) >> 5;
   int32_t* trow = T + static_cast<size_t>(u) * NKB_max;
-  for (int w = threadIdx.x; w < nwords; w += kThreads)
-    bitmap[w] = static_cast<uint32_t>(trow[NKB_max - nwords + w]);
+  const int32_t* tail = trow + NKB_max - n_rep * nwords;
+  if (n_rep == 1) {
+    for (int w = threadIdx.x; w < nwords; w += kThreads) bitmap[w] = static_cast<uint32_t>(tail[w]);
+  } else {
+    const int total = n_rep * nwords;
+    for (int w = threadIdx.x; w < nwords; w += kThreads) bitmap[w] = 0u;
+    __syncthreads();
+    for (int base = 0; base < total; base += 4 * kThreads) {
+      uint32_t x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // clamped index: the four loads go out together
+        const int i = base + j * kThreads + static_cast<int>(threadIdx.x);
+        x[j] = static_cast<uint32_t>(tail[i < total ? i : total - 1]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = base + j * kThreads + static_cast<int>(threadIdx.x);
+        if (i < total && x[j] != 0u) atomicOr(&bitmap[i % nwords], x[j]);
+      }
+    }
+  }
   __syncthreads();  // every parked word is in LDS before the row is overwritten
   compact_bitmap<kThreads>(bitmap, nwords, NKB_max, trow, len + u, wave_total);
 }
@@ -353,13 +374,7 @@ hipError_t launch_union_tables(const uint8_t* mask, int B, int H_q, int H_kv, in
                          dev_nkb, T);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      if ((NKB_max + 31) / 32 <= 256)
-        hipLaunchKernelGGL(union_compact_kernel<256>, dim3(n_bg), dim3(256), lds, stream,
-                           NKB_max, T, len);
-      else
-        hipLaunchKernelGGL(union_compact_kernel<kUnionThreads>, dim3(n_bg), dim3(kUnionThreads),
-                           lds, stream, NKB_max, T, len);
-      return hipGetLastError();
+      return launch_union_compact(n_bg, NKB_max, 1, T, len, stream);
     }
   }
   dim3 grid(n_bg), block(kUnionThreads);
@@ -369,6 +384,18 @@ hipError_t launch_union_tables(const uint8_t* mask, int B, int H_q, int H_kv, in
   else
     hipLaunchKernelGGL(union_tables_kernel<1>, grid, block, lds, stream, mask, H_q, H_kv,
                        NQ_max, NKB_max, ext, dev_nq, dev_nkb, T, len);
+  return hipGetLastError();
+}
+
+hipError_t launch_union_compact(int n_bg, int NKB_max, int n_rep, int32_t* T, int32_t* len,
+                                hipStream_t stream) {
+  const size_t lds = static_cast<size_t>((NKB_max + 31) / 32) * sizeof(uint32_t);
+  if ((NKB_max + 31) / 32 <= 256)
+    hipLaunchKernelGGL(union_compact_kernel<256>, dim3(n_bg), dim3(256), lds, stream, NKB_max,
+                       n_rep, T, len);
+  else
+    hipLaunchKernelGGL(union_compact_kernel<kUnionThreads>, dim3(n_bg), dim3(kUnionThreads), lds,
+                       stream, NKB_max, n_rep, T, len);
   return hipGetLastError();
 }
 

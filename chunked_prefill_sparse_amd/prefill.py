@@ -17,7 +17,7 @@ from typing import Optional
 import torch
 
 from . import (append_kv, balanced_workspace_size, block_mask_topk, build_union_tables,
-               chunk_attention, pool_blocks)
+               chunk_attention, pool_blocks, select_chunk)
 from ._lib import CA_BLOCK
 
 
@@ -73,7 +73,15 @@ class ChunkedPrefill:
 
     def select(self, q_chunk: torch.Tensor, prior: int, stream=None) -> None:
         """Pool the chunk's new key blocks and its queries, make the mask and
-        build the union tables (into self.mask / self.T / self.lens)."""
+        build the union tables (into self.mask / self.T / self.lens): the fused
+        ``ca_select_chunk``, four launches."""
+        B, C = self.B, self.C
+        select_chunk(q_chunk, self.k, [prior] * B, [C] * B, self.budget, self.local, self.qbar,
+                     self.kbar, self.scores, self.mask, self.T, self.lens, stream=stream)
+
+    def select_separate(self, q_chunk: torch.Tensor, prior: int, stream=None) -> None:
+        """The same selection as ``select`` through the separate calls (six
+        launches): pooling of keys, pooling of queries, scores and top-k, union."""
         B, C = self.B, self.C
         p_blk, n_blk = prior // CA_BLOCK, (prior + C) // CA_BLOCK
         pool_blocks(self.k, [p_blk] * B, [n_blk] * B, out=self.kbar, stream=stream)

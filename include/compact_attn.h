@@ -517,6 +517,46 @@ CA_EXPORT ca_status ca_block_mask_topk(const float* qbar, const float* kbar, int
                              const int32_t* prior_len, const int32_t* chunk_len, int budget,
                              int local, float* scores, uint8_t* mask, hipStream_t stream);
 
+/*
+ * ca_select_chunk -- the whole selection step of one chunk in four launches
+ * (problem statement and "Methodology", selection stage: the search runs over
+ * the grown cache at every chunk, and its mask becomes the union tables).
+ * Same outputs as the calls it fuses, bit for bit:
+ *
+ *   ca_pool_blocks(K_cache -> kbar, blocks [prior/64, (prior+chunk)/64))
+ *   ca_pool_blocks(Q_chunk -> qbar, blocks [0, chunk/64))
+ *   ca_block_mask_topk(qbar, kbar, prior, chunk, budget, local -> scores, mask)
+ *   ca_build_union_tables(mask, n_q_blocks = chunk/64,
+ *                         n_kv_blocks = (prior+chunk)/64 -> T, len)
+ *
+ * The launches: pooling of the new key blocks and of the Q-blocks together
+ * (which also clears the union bitmap words kept at the tail of each T row),
+ * the scores, the top-k mask with each selected cell ORed into its group's
+ * bitmap, and the compaction of the bitmaps into T and len.  The mask is read
+ * by nothing: the union comes from the selection directly.
+ *
+ * Q_chunk    device [B, H_q, C_max, D] (dtype), 16-byte aligned.
+ * K_cache    device [B, H_kv, L, D] (dtype), 16-byte aligned; rows up to
+ *            prior_len[b] + chunk_len[b] hold the keys (append first).
+ * prior_len, chunk_len  host int32 [B], multiples of 64 (else
+ *            CA_ERR_UNSUPPORTED); chunk_len <= min(C_max, 64*NQ_max),
+ *            prior_len + chunk_len <= min(L, 64*NKB_max).
+ * qbar       device float [B, H_q, NQ_max, D] (out; the chunk's Q-blocks).
+ * kbar       device float [B, H_kv, NKB_max, D] (in/out: blocks below
+ *            prior/64 must hold the pooled keys of earlier chunks; the
+ *            chunk's own blocks are written).  16-byte aligned.
+ * scores, mask  as for ca_block_mask_topk.
+ * T, len     as for ca_build_union_tables (NKB_max <= 524288).
+ * B*H_kv <= 65535, D in {64, 128}, budget, local >= 0.
+ * Errors: CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_DTYPE, CA_ERR_UNSUPPORTED, CA_ERR_HIP.
+ */
+CA_EXPORT ca_status ca_select_chunk(const void* Q_chunk, const void* K_cache, ca_dtype dtype,
+                                    int B, int H_q, int H_kv, int C_max, int64_t L, int D,
+                                    const int32_t* prior_len, const int32_t* chunk_len,
+                                    int budget, int local, float* qbar, int NQ_max, float* kbar,
+                                    int NKB_max, float* scores, uint8_t* mask, int32_t* T,
+                                    int32_t* len, hipStream_t stream);
+
 /* Human-readable name of a status code (static string; never NULL). */
 CA_EXPORT const char* ca_status_string(ca_status s);
 

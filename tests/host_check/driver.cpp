@@ -137,6 +137,16 @@ int main() {
                                 FAKE, nullptr, 0) == CA_OK);
       EXPECT(stub::last.p.stamps == nullptr);
     }
+    // fused selection: per-batch maxima and the shape reach the launcher
+    {
+      const int32_t pr[2] = {3072, 1024}, ch[2] = {256, 192};
+      EXPECT(ca_select_chunk(FAKE, FAKE, CA_BF16, 2, 8, 2, 256, 4096, 128, pr, ch, 8, 2,
+                             (float*)FAKE, 4, (float*)FAKE, 64, (float*)FAKE, (uint8_t*)FAKE,
+                             (int32_t*)FAKE, (int32_t*)FAKE, 0) == CA_OK);
+      EXPECT(strcmp(stub::last.what, "select") == 0 && stub::last.ints[0] == 4 &&
+             stub::last.ints[1] == 48 && stub::last.ints[7] == 8002 && stub::last.ints[6] == 2);
+      EXPECT(stub::last.seq.prior[1] == 1024 && stub::last.seq.chunk[1] == 192);
+    }
     // no-alloc split: the partials go to the static array (its stand-in address),
     // same layout; a split past the array's size is refused before any launch
     {

@@ -124,6 +124,38 @@ hipError_t launch_append_kv(const void*, const void*, int B, int H_kv, int C_max
   return hipSuccess;
 }
 
+hipError_t launch_select_chunk(const void*, const void*, int esz, int B, int H_q, int H_kv,
+                               int C_max, int64_t L, int D, const SeqInfo& seq, int max_nq,
+                               int max_pblk, int budget, int local, float*, int NQ_max, float*,
+                               int NKB_max, float*, uint8_t*, int32_t*, int32_t*, hipStream_t) {
+  stub::last = stub::Record{};
+  stub::last.what = "select";
+  stub::last.B = B;
+  stub::last.D = D;
+  stub::last.ints[0] = max_nq;
+  stub::last.ints[1] = max_pblk;
+  stub::last.ints[2] = budget;
+  stub::last.ints[3] = local;
+  stub::last.ints[4] = NQ_max;
+  stub::last.ints[5] = NKB_max;
+  stub::last.ints[6] = esz;
+  stub::last.ints[7] = H_q * 1000 + H_kv;
+  stub::last.seq = seq;
+  (void)C_max;
+  (void)L;
+  return hipSuccess;
+}
+
+hipError_t launch_union_compact(int n_bg, int NKB_max, int n_rep, int32_t*, int32_t*,
+                                hipStream_t) {
+  stub::last = stub::Record{};
+  stub::last.what = "union_compact";
+  stub::last.ints[0] = n_bg;
+  stub::last.ints[1] = NKB_max;
+  stub::last.ints[2] = n_rep;
+  return hipSuccess;
+}
+
 hipError_t launch_compact_kv(const void*, const void*, const int32_t*, const int32_t*, int NKB_max,
                              int B, int H_kv, int64_t L, int D, int esz, const SeqInfo& seq,
                              void*, void*, int32_t*, hipStream_t) {

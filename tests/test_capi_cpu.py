@@ -282,3 +282,25 @@ def test_stamped_validation():
     assert st(*base[:16], 0, *base[17:], FAKE, 16, ctypes.byref(n), None) == 4  # fp32
     assert st(*base, FAKE + 2, 16, ctypes.byref(n), None) == 4
     assert st(*base[:6], _ints(1000), *base[7:], FAKE, 16, ctypes.byref(n), None) == 4
+
+
+def test_select_chunk_validation():
+    lib = _lib.lib()
+    # Q, K, dtype, B, H_q, H_kv, C_max, L, D, prior, chunk, budget, local, qbar, NQ_max, kbar,
+    # NKB_max, scores, mask, T, len
+    base = [FAKE, FAKE, 1, 1, 8, 2, 256, 4096, 64, _ints(1024), _ints(256), 8, 2, FAKE, 4, FAKE,
+            64, FAKE, FAKE, FAKE, FAKE]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.ca_select_chunk(*a, None)
+
+    assert call(a0=None) == 1 and call(a18=None) == 1 and call(a20=None) == 1
+    assert call(a2=3) == 3
+    assert call(a5=3) == 2 and call(a11=-1) == 2 and call(a16=1 << 20) == 2
+    assert call(a10=_ints(320)) == 2            # chunk > C_max
+    assert call(a14=3) == 2                     # chunk > 64 * NQ_max
+    assert call(a9=_ints(4096 - 128)) == 2      # prior + chunk > L
+    assert call(a8=96) == 4 and call(a9=_ints(1000)) == 4 and call(a13=FAKE + 4) == 4

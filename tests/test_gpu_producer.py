@@ -122,6 +122,29 @@ def test_producer_full_size_128k():
     assert (m[0, :, :, 1:2016 - 8].sum(axis=-1) == 64).all()
 
 
+@pytest.mark.parametrize("NKB", [15360, 16064])
+def test_topk_long_rows(NKB):
+    # the top-k stages a row's keys in LDS up to 15360 blocks and reads them
+    # from the scores in global memory past that: both sides of the limit, with
+    # exact ties (repeated pooled keys) among thousands of candidates
+    rng = np.random.default_rng(NKB)
+    B, H_q, H_kv, D, C = 1, 2, 1, 64, 128
+    P = (NKB - C // 64) * 64
+    pblk = P // 64
+    qbar = rng.standard_normal((B, H_q, C // 64, D)).astype(np.float32)
+    kbar = rng.standard_normal((B, H_kv, NKB, D)).astype(np.float32)
+    kbar[:, :, 1::7] = kbar[:, :, 1:2]
+    d_q, d_k = torch.from_numpy(qbar).cuda(), torch.from_numpy(kbar).cuda()
+    for budget, local in ((64, 8), (3000, 0), (1, 3)):
+        say(f"top-k long rows NKB={NKB} budget={budget} local={local}")
+        mask, scores = ca.block_mask_topk(d_q, d_k, [P], [C], budget, local)
+        torch.cuda.synchronize()
+        sel_in = np.zeros((B, H_q, C // 64, pblk), np.float64)
+        sel_in[...] = scores.cpu().numpy()[:, :, :, :pblk]
+        ref = topk_mask_ref(sel_in, [P], [C], budget, local, NKB)
+        np.testing.assert_array_equal(mask.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("seed", range(16))
 def test_producer_fuzz(seed):
     # seeded random batch, heads, group size, head dim, element type, ragged
