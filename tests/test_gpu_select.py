@@ -123,3 +123,39 @@ def test_select_chunk_long_rows():
     Tr, lr = union_tables_ref(mask.cpu().numpy(), H_kv, [C // 64], [L // 64])
     np.testing.assert_array_equal(T.cpu().numpy(), Tr)
     np.testing.assert_array_equal(lens.cpu().numpy(), lr)
+
+
+@pytest.mark.parametrize("L,prior,chunk", [
+    (64, [0, 0], [64, 0]),          # one block: one bitmap word, one copy of it
+    (128, [64, 0], [64, 128]),      # two blocks: two copies of the one word
+    (320, [128, 256], [192, 64]),   # five blocks: five copies
+    (2112, [1920, 0], [192, 0]),    # 33 blocks: two words, 16 copies; one sequence empty
+])
+def test_select_chunk_small_tables(L, prior, chunk):
+    # T rows shorter than 16 bitmap copies: the copies take the whole row
+    B, H_kv, G, D, C_max = 2, 2, 3, 64, 192
+    H_q = H_kv * G
+    gq = torch.Generator().manual_seed(99 + L)
+    k = torch.randn((B, H_kv, L, D), generator=gq).to(torch.bfloat16).cuda()
+    q = torch.randn((B, H_q, C_max, D), generator=gq).to(torch.bfloat16).cuda()
+    NQ, NKB = C_max // 64, L // 64
+    kbar0 = torch.zeros((B, H_kv, NKB, D), dtype=torch.float32, device="cuda")
+    ca.pool_blocks(k, [0] * B, [p // 64 for p in prior], out=kbar0)
+    for budget, local in ((1, 0), (2, 1)):
+        say(f"select_chunk small tables L={L} prior={prior} chunk={chunk} budget={budget}")
+        ref = _separate(q, k, prior, chunk, budget, local, NQ, NKB, kbar0)
+        kbar = kbar0.clone()
+        qbar = torch.zeros((B, H_q, NQ, D), dtype=torch.float32, device="cuda")
+        scores = torch.zeros((B, H_q, NQ, NKB), dtype=torch.float32, device="cuda")
+        mask = torch.full((B, H_q, NQ, NKB), 7, dtype=torch.uint8, device="cuda")
+        T = torch.full((B, H_kv, NKB), 12345, dtype=torch.int32, device="cuda")
+        lens = torch.full((B, H_kv), -3, dtype=torch.int32, device="cuda")
+        ca.select_chunk(q, k, prior, chunk, budget, local, qbar, kbar, scores, mask, T, lens)
+        torch.cuda.synchronize()
+        for name, got, want in (("kbar", kbar, ref[0]), ("mask", mask, ref[3]),
+                                ("T", T, ref[4]), ("lens", lens, ref[5])):
+            assert torch.equal(got, want), name
+        Tr, lr = union_tables_ref(mask.cpu().numpy(), H_kv, [c // 64 for c in chunk],
+                                  [(p + c) // 64 for p, c in zip(prior, chunk)])
+        np.testing.assert_array_equal(T.cpu().numpy(), Tr)
+        np.testing.assert_array_equal(lens.cpu().numpy(), lr)
