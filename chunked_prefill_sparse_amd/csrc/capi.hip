@@ -143,23 +143,31 @@ CA_EXPORT ca_status ca_tables_to_csr(const int32_t* T, const int32_t* len, int B
 namespace {
 
 // Byte offsets of the balanced path's workspace parts (each 16-byte aligned)
-// and its total size: partial outputs and (max, denominator) pairs for up to
-// kMaxPieces pieces of every row, the plan (count, then one int4 per piece),
-// and the pieces per (b, g, tile).
+// and its total size.  A part is one cut tile's partial results (256 rows of D
+// floats, then 256 (max, denominator) pairs); a call with n tiles on up to
+// kPlanMaxSlots slots writes at most 2 n + kPlanMaxSlots parts; then the
+// plan's part numbering (n + 1 ints).  Shapes with more tiles than
+// kPlanMaxSlots always run the plain kernel and use no workspace.
 struct BalancedLayout {
-  size_t part_o, part_ml, plan, pieces, total;
+  size_t part_o, part_ml, pre, total;
+  int64_t units, parts;
 };
 BalancedLayout balanced_layout(int B, int H_q, int H_kv, int C_max, int D) {
   auto up16 = [](size_t x) { return (x + 15) & ~static_cast<size_t>(15); };
-  const size_t rows = static_cast<size_t>(B) * H_q * C_max;
-  const size_t n_pb = (static_cast<size_t>(C_max) + 31) / 32;
-  const size_t n_units = static_cast<size_t>(B) * H_kv * (((H_q / H_kv) * n_pb + 7) / 8);
+  const int64_t n_pb = (static_cast<int64_t>(C_max) + 31) / 32;
   BalancedLayout l;
-  l.part_o = 0;
-  l.part_ml = up16(l.part_o + ca::kMaxPieces * rows * D * sizeof(float));
-  l.plan = up16(l.part_ml + ca::kMaxPieces * rows * 2 * sizeof(float));
-  l.pieces = up16(l.plan + (4 + 4 * (n_units + 2 * ca::kPlanMaxSlots)) * sizeof(int32_t));
-  l.total = up16(l.pieces + n_units * sizeof(int32_t));
+  l.units = static_cast<int64_t>(B) * H_kv * (((H_q / H_kv) * n_pb + 7) / 8);
+  l.part_o = l.part_ml = l.pre = 0;
+  if (l.units > ca::kPlanMaxSlots) {
+    l.parts = 0;
+    l.total = 16;
+    return l;
+  }
+  l.parts = 2 * l.units + ca::kPlanMaxSlots;
+  const size_t rows = static_cast<size_t>(l.parts) * 256;
+  l.part_ml = up16(rows * D * sizeof(float));
+  l.pre = up16(l.part_ml + rows * 2 * sizeof(float));
+  l.total = up16(l.pre + static_cast<size_t>(l.units + 1) * sizeof(int32_t));
   return l;
 }
 
@@ -223,8 +231,9 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
   p.n_split = n_split;
   p.rows_total = static_cast<int64_t>(B) * H_q * C_max;
   p.cus = device_cus();
-  p.plan_items = nullptr;
-  p.plan_pieces = nullptr;
+  p.bal_units = 0;
+  p.bal_parts = 0;
+  p.bal_pre = nullptr;
   p.dev_prior = dev_lengths ? prior_len : nullptr;
   p.dev_chunk = dev_lengths ? chunk_len : nullptr;
   p.stamps = nullptr;
@@ -239,23 +248,26 @@ ca_status attention(const void* Q, const void* K_cache, const void* V_cache, con
     // one 64-row Q-block of one head with per-Q-block tables
     const int64_t n_t8 = (p.G * n_pb + 7) / 8;
     if (balanced) {
-      p.waves = 8;
-      p.n_t = static_cast<int>(n_t8);
-      p.xcd = 0;
-      p.n_split = ca::kMaxPieces;
+      // planned in the kernel while every tile has a slot (one workgroup per
+      // compute unit) and the plan's sums fit in 32 bits; otherwise the plain
+      // kernel below, which gives the same result
       const BalancedLayout ws = balanced_layout(B, H_q, H_kv, C_max, D);
-      // planned-piece grid (tiles + 2 x slots), merge grid (8 x tiles), and
-      // the plan's 32-bit piece arithmetic
-      if (n_bg * n_t8 * 8 + 2 * ca::kPlanMaxSlots > INT32_MAX || NKB_max > ca::kPlanMaxBlocks)
-        return CA_ERR_SHAPE;
-      char* base = static_cast<char*>(workspace);
-      float* part_o = reinterpret_cast<float*>(base + ws.part_o);
-      float* part_ml = reinterpret_cast<float*>(base + ws.part_ml);
-      p.plan_items = reinterpret_cast<const int32_t*>(base + ws.plan);
-      p.plan_pieces = reinterpret_cast<const int32_t*>(base + ws.pieces);
-      return hip_status(ca::launch_chunk_attn_bf16_balanced(Q, K_cache, V_cache, T, len, O, lse,
-                                                            B, D, p, seq, part_o, part_ml,
-                                                            stream));
+      const int64_t units = n_bg * n_t8;
+      const int slots = std::min(p.cus, ca::kPlanMaxSlots);
+      if (units <= slots && units * NKB_max <= INT32_MAX) {
+        p.waves = 8;
+        p.n_t = static_cast<int>(n_t8);
+        p.xcd = (n_bg % 8 == 0) ? 1 : 0;
+        p.bal_units = static_cast<int>(units);
+        p.bal_parts = static_cast<int>(ws.parts);
+        char* base = static_cast<char*>(workspace);
+        float* part_o = reinterpret_cast<float*>(base + ws.part_o);
+        float* part_ml = reinterpret_cast<float*>(base + ws.part_ml);
+        p.bal_pre = reinterpret_cast<int32_t*>(base + ws.pre);
+        return hip_status(ca::launch_chunk_attn_bf16_balanced(Q, K_cache, V_cache, T, len, O,
+                                                              lse, D, p, seq, part_o, part_ml,
+                                                              slots, stream));
+      }
     }
     p.waves = (n_split == 1 && n_bg * n_t8 >= p.cus) ? 8 : 4;
     p.n_t = row_tables ? static_cast<int>(p.G * ((C_max + 63) / 64))

@@ -108,25 +108,31 @@ __device__ __forceinline__ void body_schedule() {
   body_pairs<D, W>(std::make_integer_sequence<int, D / 8>{});
 }
 
+// Entries of the compacted list in LDS (see attn_job).
+constexpr int kListCap = 4096;
+
+// One job of a workgroup: the rows of tile t of pseudo-request (b, g) over its
+// share [lo, hi) of the tile's w work units.  The tile's plain entries are
+// split in proportion (entries [n_all lo / w, n_all hi / w)), and the blocks
+// that straddle its rows go with the share that ends at w.  A whole tile is
+// lo = 0, hi = w = 1.  With partials the job writes its unnormalised output,
+// running max and denominator to partial row part_base + the row's index in
+// O (kSplit = 1) or + its place in the tile, wave * 32 + row (kSplit = 3);
+// else it writes O and lse.
 // W = waves per workgroup.  kRows = false: union tables, T[b,g] shared by the
 // W waves (8: one workgroup per CU, two waves per SIMD; 4, two workgroups
-// per CU, when 8 would leave CUs idle, and with kSplit).  kRows = true: one table per (b, h, Q-block), the
-// per-Q-block lists of a block-sparse kernel, so a workgroup is the 2 waves
-// (W = 2) of one 64-row Q-block of one head.
-// kSplit = 1: the table of a (b, g) is cut into p.n_split contiguous ranges,
-// one per workgroup (the straddling blocks go to the last range), and each
-// workgroup writes its unnormalised partial output, running max and
-// denominator to part_o / part_ml for split_combine_kernel.  More workgroups
-// for shapes with few (b, g) pairs.  kSplit = 2: workgroup w runs the piece
-// that a balance plan lists at p.plan_items[w] (sequence and group, tile,
-// piece k of n), cut the same way; pieces of an uncut tile (n = 1) write O
-// and lse themselves.
+// per CU, when 8 would leave CUs idle, and with kSplit = 1).  kRows = true: one
+// table per (b, h, Q-block), the per-Q-block lists of a block-sparse kernel,
+// so a workgroup is the 2 waves (W = 2) of one 64-row Q-block of one head, and
+// t = Q-block * G + head in group.
 template <int D, int W, bool kRows, int kSplit>
-__global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
+__device__ __forceinline__ void attn_job(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const int32_t* __restrict__ T, const int32_t* __restrict__ len, __bf16* __restrict__ O,
-    float* __restrict__ lse, AttnParams p, SeqInfo seq, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
+    float* __restrict__ lse, const AttnParams& p, const SeqInfo& seq,
+    float* __restrict__ part_o, float* __restrict__ part_ml, char* lds, int b, int g, int t,
+    int lo, int hi, int w, bool partials, int64_t part_base, uint64_t t_start,
+    uint64_t c_start) {
   constexpr int DS = D / 16;
   constexpr int DT = D / 32;
   constexpr int RB = Tile<D>::kRowBytes;
@@ -137,13 +143,14 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   static_assert(kRows ? W == 2 : (W == 4 || W == 8), "workgroup shape");
   static_assert(!(kRows && kSplit != 0), "split ranges are for union tables");
   // LDS: two K tiles, two V tiles, then the compacted entry list (below) and
-  // per-wave counts for building it.  One array: with the list in a separate
-  // LDS object the compiler no longer proves that the tile reads stay clear of
-  // the in-flight tile copies and waits for those copies before every read.
-  constexpr int kListCap = 4096;
-  __shared__ __attribute__((aligned(1024))) char lds[4 * Tile<D>::kBytes + 2 * kListCap + 4 * W];
+  // per-wave counts and last positions for building it, all in the kernel's
+  // one array: with the
+  // list in a separate LDS object the compiler no longer proves that the tile
+  // reads stay clear of the in-flight tile copies and waits for those copies
+  // before every read.
   uint16_t* const plist = reinterpret_cast<uint16_t*>(lds + 4 * Tile<D>::kBytes);
   int* const wcount = reinterpret_cast<int*>(lds + 4 * Tile<D>::kBytes + 2 * kListCap);
+  int* const wlast = wcount + W;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -152,46 +159,6 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // stamped calls: the counters at the start (uniform; a scalar read each)
-  uint64_t t_start = 0, c_start = 0;
-  if (kSplit == 0 && !kRows && p.stamps != nullptr) {
-    t_start = __builtin_amdgcn_s_memrealtime();
-    c_start = __builtin_amdgcn_s_memtime();
-  }
-  // ---- workgroup -> (sequence, group, tile[, split])
-  const int wg = blockIdx.x;
-  int b, g, t;
-  int split = 0, n_split = 1;  // this workgroup's range k of n of the tile's plain entries
-  if (kSplit == 2) {
-    if (wg >= p.plan_items[0]) return;  // past the plan's pieces (uniform)
-    const int4 it = reinterpret_cast<const int4*>(p.plan_items)[1 + wg];
-    b = it.x / p.H_kv;
-    g = it.x - b * p.H_kv;
-    t = it.y;
-    split = it.z;
-    n_split = it.w;
-  } else {
-    const int n_tt = kSplit ? p.n_t * p.n_split : p.n_t;  // workgroups per (b, g)
-    int u;
-    if (p.xcd) {
-      const int x = wg & 7, k = wg >> 3;
-      const int jj = k / n_tt;
-      u = x + 8 * jj;
-      t = k - jj * n_tt;
-    } else {
-      u = wg / n_tt;
-      t = wg - u * n_tt;
-    }
-    if (kSplit) {
-      n_split = p.n_split;
-      split = t / p.n_t;
-      t -= split * p.n_t;
-    }
-    const int rank = u / p.H_kv;
-    g = u - rank * p.H_kv;
-    b = seq.order[rank];
-  }
-  const bool partials = kSplit != 0 && n_split > 1;  // else O and lse written here
   int P, C;
   seq_lengths(p, seq, b, P, C);
   const int bg = b * p.H_kv + g;
@@ -310,27 +277,26 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   // T ascending they are the last entries, [e, nT)
   auto needs_mask = [&](int kb) { return kb * kBlk + kBlk - 1 > P + row0_wg; };
   auto valid = [&](int kb) { return kb >= 0 && kb < nkb && kb <= kb_limit; };
-  int e = nT;
-  while (e > 0) {
-    const int kb = Trow[e - 1];
-    if (valid(kb) && !needs_mask(kb)) break;
-    --e;
-  }
-  // The plain entries of [0, e) (valid, no mask needed), compacted into LDS
-  // in table order when they fit (block indices below 2^16, at most kListCap
-  // of them), so that a step reads the entry after next from LDS, in order
-  // with its other LDS reads, rather than by a scalar load it must wait for
-  // in its tail (measured 0.8% faster at 128K, 5% on one GPU's
-  // tensor-parallel share).  Longer tables walk T itself.
-  const bool use_list = e <= kListCap && nkb <= 65536;
-  int n_plain = 0;
+  // The plain entries (valid, no mask needed), compacted into LDS in table
+  // order when they fit (block indices below 2^16, at most kListCap entries
+  // in T), so that a step reads the entry after next from LDS, in order with
+  // its other LDS reads, rather than by a scalar load it must wait for in its
+  // tail (measured 0.8% faster at 128K, 5% on one GPU's tensor-parallel
+  // share).  The same pass finds e, one past the last plain entry: the
+  // entries after it, [e, nT), are the ones that need the mask.  Longer
+  // tables walk T itself, and find e by a scan from the end.
+  const bool use_list = nT <= kListCap && nkb <= 65536;
+  int n_plain = 0, e = 0;
   if (use_list) {
-    for (int c0 = 0; c0 < e; c0 += kThreads) {
+    for (int c0 = 0; c0 < nT; c0 += kThreads) {
       const int pos = c0 + tid;
-      const int kb = pos < e ? Trow[pos] : -1;
-      const bool pl = pos < e && valid(kb) && !needs_mask(kb);
+      const int kb = pos < nT ? Trow[pos] : -1;
+      const bool pl = pos < nT && valid(kb) && !needs_mask(kb);
       const uint64_t m = __ballot(pl);
-      if (lane == 0) wcount[wave] = __popcll(m);
+      if (lane == 0) {
+        wcount[wave] = __popcll(m);
+        wlast[wave] = m ? c0 + wave * 64 + 63 - __builtin_clzll(m) : -1;
+      }
       __syncthreads();
       int before = n_plain, total = n_plain;
 #pragma unroll
@@ -338,17 +304,24 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
         const int cw = wcount[w];
         before += w < wave ? cw : 0;
         total += cw;
+        e = max(e, wlast[w] + 1);
       }
       if (pl) plist[before + __popcll(m & ((1ull << lane) - 1ull))] = static_cast<uint16_t>(kb);
       n_plain = total;
       __syncthreads();
     }
+  } else {
+    e = nT;
+    while (e > 0) {
+      const int kb = Trow[e - 1];
+      if (valid(kb) && !needs_mask(kb)) break;
+      --e;
+    }
   }
   const int n_all = use_list ? n_plain : e;
   // this workgroup's range of [0, n_all); all of it without splitting
-  const int e_lo = static_cast<int>((static_cast<int64_t>(n_all) * split) / n_split);
-  const int ee =
-      static_cast<int>((static_cast<int64_t>(n_all) * (split + 1)) / n_split);
+  const int e_lo = static_cast<int>((static_cast<int64_t>(n_all) * lo) / w);
+  const int ee = hi >= w ? n_all : static_cast<int>((static_cast<int64_t>(n_all) * hi) / w);
   auto entry = [&](int jj) -> int {
     return use_list ? __builtin_amdgcn_readfirstlane(static_cast<int>(plist[jj])) : Trow[jj];
   };
@@ -460,7 +433,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
 
   // Blocks that straddle the workgroup's rows (usually one): one at a time,
   // with the causal mask.
-  for (int jt = e; jt < (split == n_split - 1 ? nT : e); ++jt) {
+  for (int jt = e; jt < (hi >= w ? nT : e); ++jt) {
     const int kb = Trow[jt];
     if (!valid(kb)) continue;
     __syncthreads();  // every wave is done with the buffers
@@ -482,7 +455,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
     const uint64_t c_end = __builtin_amdgcn_s_memtime();
     constexpr uint32_t kHwId = 4 | (31 << 11);    // HW_REG_HW_ID, bits 0..31
     constexpr uint32_t kXccId = 20 | (31 << 11);  // HW_REG_XCC_ID
-    uint32_t* st = p.stamps + static_cast<size_t>(wg) * kStampWords;
+    uint32_t* st = p.stamps + static_cast<size_t>(blockIdx.x) * kStampWords;
     st[0] = static_cast<uint32_t>(t_start);
     st[1] = static_cast<uint32_t>(t_end - t_start);
     st[2] = static_cast<uint32_t>(c_end - c_start);
@@ -495,7 +468,8 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   if (!row_in) return;
   if (partials) {  // partial results: acc (unnormalised), running max, denominator
     if (!row_live) return;
-    const size_t prow = static_cast<size_t>(split) * p.rows_total + qo_row;
+    const size_t prow = static_cast<size_t>(part_base) +
+                        (kSplit == 3 ? static_cast<size_t>(wave * kRowsPerWave + l32) : qo_row);
     float* po = part_o + prow * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -530,6 +504,411 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
   }
   if (lse && hh == 0)
     lse[qo_row] = (row_live && l_tot > 0.f) ? ws.m_used * p.scale + __logf(l_tot) : -INFINITY;
+}
+
+// ---- balanced attention (kSplit = 3)
+
+// LDS of a kernel instance: the job's tiles, entry list and per-wave counts,
+// then (kSplit = 3) the plan: work per tile, tail and partial prefix sums,
+// spare prefix sums per slot, and a few words of reductions and flags.
+constexpr int kPlanMisc = 64;
+template <int D, int W>
+constexpr int job_lds_bytes() {
+  return 4 * Tile<D>::kBytes + 2 * kListCap + 8 * W;
+}
+constexpr int kJobCap = 16;  // jobs of one slot (at most 11, see balanced_slots)
+template <int D, int W, int kSplit>
+constexpr int kernel_lds_bytes() {
+  return job_lds_bytes<D, W>() +
+         (kSplit == 3 ? 4 * (6 * (kPlanMaxSlots + 1) + 4 * kJobCap + kPlanMisc) : 0);
+}
+
+// threadIdx.x through an opaque move.  The balanced plan takes its thread
+// index from here: lane predicates it computes (lane == 0, tid < n, ...) are
+// then not merged with the same predicates in the jobs' code, which would
+// keep their lane masks alive through the first job's pipeline, whose
+// schedule needs every register.
+__device__ __forceinline__ int opaque_tid() {
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(static_cast<int>(threadIdx.x)));
+  return t;
+}
+
+// Exclusive prefix sums of K arrays a[k][0, n) (LDS) in place, by all W * 64
+// threads of the workgroup (tid: this thread's index; each takes a run of
+// consecutive entries); the totals go to total[k].  red: K * W ints of LDS.
+template <int W, int K>
+__device__ void block_exscan(int* const (&a)[K], int n, int* red, int (&total)[K], int tid) {
+  constexpr int kThreads = W * 64;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int per = (n + kThreads - 1) / kThreads;
+  const int i0 = min(tid * per, n), i1 = min(i0 + per, n);
+  int sum[K], inc[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    sum[k] = 0;
+    for (int i = i0; i < i1; ++i) sum[k] += a[k][i];
+    inc[k] = sum[k];
+  }
+  for (int o = 1; o < 64; o <<= 1) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int y = __shfl_up(inc[k], o);
+      if (lane >= o) inc[k] += y;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) red[k * W + wave] = inc[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    int run = inc[k] - sum[k], tot = 0;
+#pragma unroll
+    for (int v = 0; v < W; ++v) {
+      const int r = red[k * W + v];
+      run += v < wave ? r : 0;
+      tot += r;
+    }
+    total[k] = tot;
+    for (int i = i0; i < i1; ++i) {
+      const int x = a[k][i];
+      a[k][i] = run;
+      run += x;
+    }
+  }
+  __syncthreads();
+}
+
+// First index in [0, n) whose value exceeds x (a non-decreasing), else n.
+__device__ __forceinline__ int upper_bound_lds(const int* a, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] <= x)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+// Tile i of the balanced plan -> (sequence, group, tile): the tile a plain
+// launch runs on workgroup i (pseudo-requests in p's sequence order; with
+// p.xcd the tiles of one pseudo-request on one XCD, workgroup i running on
+// XCD i % 8).
+__device__ __forceinline__ void plan_tile(const AttnParams& p, const SeqInfo& seq, int i, int& b,
+                                          int& g, int& t) {
+  int u;
+  if (p.xcd) {
+    const int x = i & 7, k = i >> 3;
+    const int jj = k / p.n_t;
+    u = x + 8 * jj;
+    t = k - jj * p.n_t;
+  } else {
+    u = i / p.n_t;
+    t = i - u * p.n_t;
+  }
+  const int rank = u / p.H_kv;
+  g = u - rank * p.H_kv;
+  b = seq.order[rank];
+}
+
+// Work units of tile t of (b, g) for the plan: the table entries up to the
+// last block any of its rows may see, i.e. all of them but the chunk's blocks
+// above that block (a table lacking some of those only makes this high); at
+// least 1, so that every tile, one of padding rows only included, gets a job.
+template <int W>
+__device__ __forceinline__ int tile_work(const AttnParams& p, const SeqInfo& seq,
+                                         const int32_t* __restrict__ len, int b, int g, int t) {
+  int P, C;
+  seq_lengths(p, seq, b, P, C);
+  if ((t * W) / p.G * kRowsPerWave >= C) return 1;
+  const int n_pb = (p.C_max + kRowsPerWave - 1) / kRowsPerWave;
+  const int last_pb = min((t * W + W - 1) / p.G, n_pb - 1);
+  const int kb_limit = (P + min(C, (last_pb + 1) * kRowsPerWave) - 1) / kBlk;
+  const int nkb = (P + C + kBlk - 1) / kBlk;
+  const int n = min(max(len[b * p.H_kv + g], 0), p.NKB_max);
+  return max(n - (nkb - 1 - kb_limit), 1);
+}
+
+// kSplit = 3: workgroup s of the launch is slot s, one per compute unit, with
+// at most as many tiles as slots.  Every workgroup derives the same plan from
+// the table lengths, in LDS.  c = kBalJobCost, what a job costs on its own
+// (set-up, pipeline fill and drain) in work units:
+//   w_i    work units of tile i (tile_work); A = ceil(sum / slots), at least
+//          kBalMinShare.  When the longest walk is within 2c of A nothing is
+//          cut: slot s runs tile s, as a plain launch would.  Otherwise:
+//   heads  slot s first runs tile s (the tile a plain launch runs on workgroup
+//          s, so on the same XCD): all of it when w_s - A < max(A/8, 2c),
+//          else its first A units;
+//   tails  the rest of the cut tiles, laid end to end in tile order, fill the
+//          slots' spare capacity A - head_s - c (c kept for the piece's own
+//          cost; A grows until the tails fit, and after six rounds the c is
+//          dropped, where they always fit), laid end to end in slot order:
+//          slot s then runs the tails that fall in its spare range, one piece
+//          per tile they cover.
+// Tails are at least A/8 long, so a slot runs no more than 11 jobs (its head
+// and the at most 10 tails that meet a spare range of length <= A).  A tile
+// run in one piece writes O and lse; the pieces of a cut tile (its head, then
+// its tail pieces in slot order) write partials, numbered from the prefix sum
+// of the piece counts over the cut tiles (at most n + n + slots parts: heads,
+// plus a piece per tail and per slot boundary), which slot 0 also writes to
+// p.bal_pre for plan_merge_kernel.  The first two jobs of a slot are inlined
+// as straight-line code: a loop around the job would keep the values its
+// set-up needs live through the previous job's pipeline, past the registers
+// the pipeline's schedule needs.  For the same reason the plan takes its
+// thread index from opaque_tid, and the jobs read what they need from LDS.
+template <int D, int W>
+__device__ __forceinline__ void balanced_slots(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const int32_t* __restrict__ T, const int32_t* __restrict__ len, __bf16* __restrict__ O,
+    float* __restrict__ lse, const AttnParams& p, const SeqInfo& seq,
+    float* __restrict__ part_o, float* __restrict__ part_ml, char* lds) {
+  constexpr int kThreads = W * 64;
+  constexpr int kN = kPlanMaxSlots + 1;
+  int* const wk = reinterpret_cast<int*>(lds + job_lds_bytes<D, W>());  // [kN]
+  int* const tpre = wk + kN;         // [kN] tail prefix sums (tiles; zero past n)
+  int* const spre = tpre + kN;       // [kN] spare prefix sums (slots)
+  int* const srank = spre + kN;      // [kN] ranks of the slots with spare capacity
+  int* const nzpre = srank + kN;     // [kN] ranks of the tiles with a tail
+  int* const bpre = nzpre + kN;      // [kN] part prefix sums
+  int* const jobs = bpre + kN;       // [kJobCap][4] this slot's jobs: tile, lo, hi, piece
+  int* const misc = jobs + 4 * kJobCap;
+  int* const red = misc;             // [4 W] scan totals
+  int* const n_jobs = misc + 32;
+  int* const parts_fit = misc + 33;  // the parts fit the workspace (always; kept as a guard)
+  static_assert(W <= 8, "plan words");
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int n = p.bal_units;
+  const int S = static_cast<int>(gridDim.x);
+
+  int sum = 0, mx = 0;
+  for (int i = tid; i < n; i += kThreads) {
+    int b, g, t;
+    plan_tile(p, seq, i, b, g, t);
+    const int wv = tile_work<W>(p, seq, len, b, g, t);
+    wk[i] = wv;
+    sum += wv;
+    mx = max(mx, wv);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    sum += __shfl_xor(sum, o);
+    mx = max(mx, __shfl_xor(mx, o));
+  }
+  if (lane == 0) {
+    red[wave] = sum;
+    red[8 + wave] = mx;
+  }
+  __syncthreads();
+  int total = 0, wmax = 0;
+#pragma unroll
+  for (int v = 0; v < W; ++v) {
+    total += red[v];
+    wmax = max(wmax, red[8 + v]);
+  }
+  int A = max((total + S - 1) / S, kBalMinShare);
+  const int s = blockIdx.x;
+  if (wmax <= A + 2 * kBalJobCost) {
+    // nothing cut: slot s runs tile s whole, as a plain launch would
+    if (s == 0)
+      for (int i = tid; i <= n; i += kThreads) p.bal_pre[i] = 0;
+    if (s < n) {
+      int b, g, t;
+      plan_tile(p, seq, s, b, g, t);
+      attn_job<D, W, false, 3>(Q, K, V, T, len, O, lse, p, seq, part_o, part_ml, lds, b, g, t, 0,
+                               1, 1, false, 0, 0, 0);
+    }
+    return;
+  }
+  int reserve = kBalJobCost;
+  auto head_of = [&](int wv) { return wv - A < max(A / 8, 2 * kBalJobCost) ? wv : A; };
+  for (int round = 0;; ++round) {
+    if (round == 6) {
+      reserve = 0;
+      break;
+    }
+    int dem = 0, cap = 0, nsp = 0;
+    for (int x = tid; x < S; x += kThreads) {
+      const int head = x < n ? head_of(wk[x]) : 0;
+      dem += x < n ? wk[x] - head : 0;
+      const int spare = max(A - head - reserve, 0);
+      cap += spare;
+      nsp += spare > 0 ? 1 : 0;
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      dem += __shfl_xor(dem, o);
+      cap += __shfl_xor(cap, o);
+      nsp += __shfl_xor(nsp, o);
+    }
+    __syncthreads();  // every thread is done reading red
+    if (lane == 0) {
+      red[wave] = dem;
+      red[8 + wave] = cap;
+      red[16 + wave] = nsp;
+    }
+    __syncthreads();
+    dem = cap = nsp = 0;
+#pragma unroll
+    for (int v = 0; v < W; ++v) {
+      dem += red[v];
+      cap += red[8 + v];
+      nsp += red[16 + v];
+    }
+    if (cap >= dem) break;
+    A += (dem - cap + max(nsp, 1) - 1) / max(nsp, 1);
+  }
+  for (int x = tid; x < S; x += kThreads) {  // n <= S
+    const int head = x < n ? head_of(wk[x]) : 0;
+    const int tail = x < n ? wk[x] - head : 0;
+    const int spare = max(A - head - reserve, 0);
+    tpre[x] = tail;
+    spre[x] = spare;
+    srank[x] = spare > 0 ? 1 : 0;
+    nzpre[x] = tail > 0 ? 1 : 0;
+  }
+  __syncthreads();  // (also: every thread has read red)
+  {
+    int* const arrs[4] = {tpre, spre, srank, nzpre};
+    int tot[4];
+    block_exscan<W, 4>(arrs, S, red, tot, tid);
+    if (tid == 0) {
+      tpre[S] = tot[0];
+      spre[S] = tot[1];
+      srank[S] = tot[2];
+      nzpre[S] = tot[3];
+    }
+  }
+  __syncthreads();
+  const int tails = tpre[S];
+  // the slot whose spare range holds tail unit x (always one with spare
+  // capacity), and the rank of a slot among those: a tail over the slots of
+  // ranks r0 .. r1 is cut into r1 - r0 + 1 pieces
+  auto slot_of = [&](int x) { return upper_bound_lds(spre, S + 1, x) - 1; };
+  for (int i = tid; i < n; i += kThreads) {
+    const int tail = tpre[i + 1] - tpre[i];
+    const int pieces =
+        tail > 0 ? 1 + srank[slot_of(tpre[i + 1] - 1)] - srank[slot_of(tpre[i])] + 1 : 1;
+    bpre[i] = pieces > 1 ? pieces : 0;
+  }
+  __syncthreads();
+  int parts;
+  {
+    int* const arrs[1] = {bpre};
+    int tot[1];
+    block_exscan<W, 1>(arrs, n, red, tot, tid);
+    parts = tot[0];
+  }
+  if (s == 0)  // the part numbering, for the merge
+    for (int i = tid; i <= n; i += kThreads) p.bal_pre[i] = i < n ? bpre[i] : parts;
+  // this slot's jobs: its head, then one piece for each tile whose tail meets
+  // the slot's spare range [x0, x1), in tile order (the tiles with a tail
+  // between the first and the last met)
+  const int x0 = spre[s], x1 = min(spre[s + 1], tails);
+  const int has_head = s < n ? 1 : 0;
+  int i_first = 0, n_tail_jobs = 0;
+  if (x0 < x1) {
+    i_first = upper_bound_lds(tpre, n + 1, x0) - 1;
+    const int i_last = upper_bound_lds(tpre, n + 1, x1 - 1) - 1;
+    n_tail_jobs = nzpre[i_last + 1] - nzpre[i_first];
+  }
+  if (tid == 0) {
+    bpre[n] = parts;
+    *parts_fit = parts <= p.bal_parts ? 1 : 0;
+    *n_jobs = min(has_head + n_tail_jobs, kJobCap);
+    if (has_head) {
+      jobs[0] = s;
+      jobs[1] = 0;
+      jobs[2] = head_of(wk[s]);
+      jobs[3] = 0;
+    }
+  }
+  for (int i = i_first + tid; x0 < x1 && i < n; i += kThreads) {
+    const int t0 = tpre[i], t1 = tpre[i + 1];
+    if (t0 >= x1) break;
+    if (t1 <= t0 || t1 <= x0) continue;
+    const int j = has_head + nzpre[i] - nzpre[i_first];
+    if (j >= kJobCap) break;
+    const int head = wk[i] - (t1 - t0);
+    jobs[4 * j] = i;
+    jobs[4 * j + 1] = head + max(x0, t0) - t0;
+    jobs[4 * j + 2] = head + min(x1, t1) - t0;
+    jobs[4 * j + 3] = 1 + srank[s] - srank[slot_of(t0)];
+  }
+  __syncthreads();
+
+  // job j of this slot: units [lo, hi) of tile i, piece k of the tile
+  auto job = [&](int j) __attribute__((always_inline)) {
+    const int i = __builtin_amdgcn_readfirstlane(jobs[4 * j]);
+    const int lo = __builtin_amdgcn_readfirstlane(jobs[4 * j + 1]);
+    const int hi = __builtin_amdgcn_readfirstlane(jobs[4 * j + 2]);
+    const int k = __builtin_amdgcn_readfirstlane(jobs[4 * j + 3]);
+    const int wv = __builtin_amdgcn_readfirstlane(wk[i]);
+    const int b0 = __builtin_amdgcn_readfirstlane(bpre[i]);
+    // (values the set-up needs come from LDS, none from registers kept since
+    // the plan: a register live through the previous job's pipeline spills)
+    const bool cut = __builtin_amdgcn_readfirstlane(bpre[i + 1]) > b0 &&
+                     __builtin_amdgcn_readfirstlane(*parts_fit) != 0;
+    int b, g, t;
+    plan_tile(p, seq, i, b, g, t);
+    __syncthreads();  // the previous job is done with the tiles and the list
+    attn_job<D, W, false, 3>(Q, K, V, T, len, O, lse, p, seq, part_o, part_ml, lds, b, g, t, lo,
+                             hi, wv, cut, static_cast<int64_t>(b0 + k) * (W * kRowsPerWave), 0,
+                             0);
+  };
+  const int nj = __builtin_amdgcn_readfirstlane(*n_jobs);
+  if (nj > 0) job(0);
+  if (nj > 1) job(1);
+  for (int j = 2; j < nj; ++j) job(j);
+}
+
+// The kernel: one job per workgroup (a whole tile, or with kSplit = 1 one of
+// p.n_split ranges of its table), or with kSplit = 3 a slot of the balanced
+// plan.
+template <int D, int W, bool kRows, int kSplit>
+__global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_bf16_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const int32_t* __restrict__ T, const int32_t* __restrict__ len, __bf16* __restrict__ O,
+    float* __restrict__ lse, AttnParams p, SeqInfo seq, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  __shared__ __attribute__((aligned(1024))) char lds[kernel_lds_bytes<D, W, kSplit>()];
+  // stamped calls: the counters at the start (uniform; a scalar read each)
+  uint64_t t_start = 0, c_start = 0;
+  if (kSplit == 0 && !kRows && p.stamps != nullptr) {
+    t_start = __builtin_amdgcn_s_memrealtime();
+    c_start = __builtin_amdgcn_s_memtime();
+  }
+  if constexpr (kSplit == 3) {
+    balanced_slots<D, W>(Q, K, V, T, len, O, lse, p, seq, part_o, part_ml, lds);
+  } else {
+    // ---- workgroup -> (sequence, group, tile[, split])
+    const int wg = blockIdx.x;
+    int b, g, t;
+    int split = 0, n_split = 1;  // this workgroup's range k of n of the tile's plain entries
+    const int n_tt = kSplit ? p.n_t * p.n_split : p.n_t;  // workgroups per (b, g)
+    int u;
+    if (p.xcd) {
+      const int x = wg & 7, k = wg >> 3;
+      const int jj = k / n_tt;
+      u = x + 8 * jj;
+      t = k - jj * n_tt;
+    } else {
+      u = wg / n_tt;
+      t = wg - u * n_tt;
+    }
+    if (kSplit) {
+      n_split = p.n_split;
+      split = t / p.n_t;
+      t -= split * p.n_t;
+    }
+    const int rank = u / p.H_kv;
+    g = u - rank * p.H_kv;
+    b = seq.order[rank];
+    attn_job<D, W, kRows, kSplit>(Q, K, V, T, len, O, lse, p, seq, part_o, part_ml, lds, b, g, t,
+                                  split, split + 1, n_split, kSplit != 0 && n_split > 1,
+                                  static_cast<int64_t>(split) * p.rows_total, t_start, c_start);
+  }
 }
 
 }  // namespace
@@ -619,198 +998,6 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const float* __restr
   if (lse && lane == 0) lse[r] = l > 0.f ? M * p.scale + __logf(l) : -INFINITY;
 }
 
-// Balance plan for planned pieces of W-wave workgroups, in one workgroup.
-//   work(u, t): the table entries that tile t of pseudo-request u = b*H_kv + g
-//     walks, from len alone: the entries up to the last block any of its rows
-//     may see are all but the chunk's blocks above that block (a table that
-//     lacks some of those only makes the estimate high), 0 for a tile of
-//     padding rows only.
-//   When the longest walk is within 1/8 of the total work per compute unit,
-//     nothing is cut (those shapes already balance).  Otherwise walks longer
-//     than tau = max(3/4 of the work per compute unit, 16) are cut into
-//     min(kMaxPieces, ceil(work / tau)) pieces of even length (measured: tau
-//     at the full work per compute unit cut about as many tiles and balanced
-//     worse).
-//   Pieces are listed longest first (by size class), so the dispatcher, which
-//     hands workgroups to compute units in order as they free up, runs a
-//     greedy longest-first schedule.
-// The piece count is below n_units + 4/3 slots (tau >= 3/4 work / slots).
-// The order within a size class depends on atomics and changes no result: a
-// piece's work and its partial slot follow from (u, t, k) alone.  Each
-// tile's work is kept between the passes in LDS (up to kPlanCached tiles), or
-// else in pieces[] (each thread rereads what it wrote), which ends with the
-// piece counts.
-constexpr int kPlanThreads = 256;
-constexpr int kPlanCached = 8192;
-constexpr int kPlanClasses = 64;
-
-template <int W>
-__global__ __launch_bounds__(kPlanThreads) void balance_plan_kernel(
-    const int32_t* __restrict__ len, AttnParams p, SeqInfo seq,
-    int n_units, int slots, int32_t* __restrict__ plan, int32_t* __restrict__ pieces) {
-  __shared__ unsigned long long s_total;
-  __shared__ int s_max;
-  __shared__ int s_count[kPlanClasses];
-  __shared__ int s_cursor[kPlanClasses];
-  __shared__ int s_work[kPlanCached];
-  int* const wbuf = n_units <= kPlanCached ? s_work : pieces;
-  const int tid = threadIdx.x;
-  if (tid == 0) {
-    s_total = 0ull;
-    s_max = 0;
-  }
-  if (tid < kPlanClasses) s_count[tid] = 0;
-  __syncthreads();
-  const int n_pb = (p.C_max + kRowsPerWave - 1) / kRowsPerWave;
-  auto work = [&](int unit) -> int {
-    const int u = unit / p.n_t;
-    const int t = unit - u * p.n_t;
-    const int b = u / p.H_kv;
-    const int P = seq.prior[b], C = seq.chunk[b];
-    if ((t * W) / p.G * kRowsPerWave >= C) return 0;
-    const int last_pb = min((t * W + W - 1) / p.G, n_pb - 1);
-    const int kb_limit = (P + min(C, (last_pb + 1) * kRowsPerWave) - 1) / kBlk;
-    const int nkb = (P + C + kBlk - 1) / kBlk;
-    // the chunk's own blocks are in the table (its causal block triangle is
-    // selected), so the entries past the tile's last visible block are the
-    // nkb - 1 - kb_limit chunk blocks above it
-    const int n = min(max(len[u], 0), p.NKB_max);
-    return max(n - (nkb - 1 - kb_limit), 0);
-  };
-  unsigned long long part = 0ull;
-  int wmax = 0;
-  for (int unit = tid; unit < n_units; unit += kPlanThreads) {
-    const int w = work(unit);
-    wbuf[unit] = w;
-    part += static_cast<unsigned long long>(w);
-    wmax = max(wmax, w);
-  }
-  for (int o = 32; o > 0; o >>= 1) {  // wave sums first: one LDS atomic per wave
-    part += __shfl_xor(part, o);
-    wmax = max(wmax, __shfl_xor(wmax, o));
-  }
-  if ((tid & 63) == 0) {
-    atomicAdd(&s_total, part);
-    atomicMax(&s_max, wmax);
-  }
-  __syncthreads();
-  const long long total = static_cast<long long>(s_total);
-  wmax = s_max;
-  const long long per_slot = (total + slots - 1) / slots;
-  // walks are at most NKB_max <= kPlanMaxBlocks entries, so the per-piece
-  // arithmetic below stays in 32 bits
-  const int tau = 8ll * wmax <= 9ll * per_slot
-                      ? INT_MAX
-                      : static_cast<int>(max((3ll * total + 4ll * slots - 1) / (4ll * slots), 16ll));
-  const int class_step = wmax / kPlanClasses + 1;
-  auto n_of = [&](int w) { return w > tau ? min(kMaxPieces, (w - 1) / tau + 1) : 1; };
-  auto size_class = [&](int w, int n, int k) {
-    const int sz = (w * (k + 1)) / n - (w * k) / n;
-    return min(kPlanClasses - 1, sz / class_step);
-  };
-  for (int unit = tid; unit < n_units; unit += kPlanThreads) {
-    const int w = wbuf[unit];
-    const int n = n_of(w);
-    for (int k = 0; k < n; ++k) atomicAdd(&s_count[size_class(w, n, k)], 1);
-  }
-  __syncthreads();
-  if (tid < 64) {  // longest class first: lane l takes class 63 - l; a scan over lanes
-    static_assert(kPlanClasses == 64, "one class per lane");
-    const int cnt = s_count[kPlanClasses - 1 - tid];
-    int inc = cnt;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(inc, o);
-      if (tid >= o) inc += y;
-    }
-    s_cursor[kPlanClasses - 1 - tid] = inc - cnt;
-    if (tid == 63) plan[0] = inc;
-  }
-  __syncthreads();
-  int4* items = reinterpret_cast<int4*>(plan) + 1;
-  for (int unit = tid; unit < n_units; unit += kPlanThreads) {
-    const int w = wbuf[unit];
-    const int n = n_of(w);
-    const int u = unit / p.n_t;
-    for (int k = 0; k < n; ++k) {
-      const int pos = atomicAdd(&s_cursor[size_class(w, n, k)], 1);
-      items[pos] = make_int4(u, unit - u * p.n_t, k, n);
-    }
-    pieces[unit] = n;
-  }
-}
-
-// Merge of the pieces of cut tiles: workgroup (tile (b, g, t), wave tile w)
-// holds the 32 rows that wave w of the tile's attention workgroup owns, one
-// row per wave at a time; a tile left whole returns at once (its workgroup
-// wrote O and lse).  With m_s, l_s, a_s the running max (raw score units),
-// denominator and unnormalised output of piece s, M = max_s m_s and
-// w_s = exp2((m_s - M) * scale * log2 e):
-//   O = sum_s w_s a_s / sum_s w_s l_s,   lse = M * scale + log(sum_s w_s l_s).
-// Every piece's loads of a row are issued before any is used.
-constexpr int kCombineThreads = 256;
-
-template <int D, int W>
-__global__ __launch_bounds__(kCombineThreads) void plan_combine_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_ml, AttnParams p,
-    SeqInfo seq, __bf16* __restrict__ O, float* __restrict__ lse) {
-  constexpr int E = D / 64;  // elements per lane
-  const int unit = blockIdx.x / W;
-  const int n = p.plan_pieces[unit];
-  if (n <= 1) return;
-  const int u = unit / p.n_t;
-  const int t = unit - u * p.n_t;
-  const int b = u / p.H_kv;
-  const int g = u - b * p.H_kv;
-  const int wt = t * W + static_cast<int>(blockIdx.x - unit * W);
-  const int pb = wt / p.G;
-  const int h = g * p.G + (wt - pb * p.G);
-  const int C = seq.chunk[b];
-  const int lane = threadIdx.x & 63;
-  for (int rr = threadIdx.x >> 6; rr < kRowsPerWave; rr += kCombineThreads / 64) {
-    const int i = pb * kRowsPerWave + rr;
-    if (i >= p.C_max) break;
-    const int64_t r = (static_cast<int64_t>(b) * p.H_q + h) * p.C_max + i;
-    float ms[kMaxPieces], ls[kMaxPieces], a[kMaxPieces][E];
-#pragma unroll
-    for (int sp = 0; sp < kMaxPieces; ++sp) {
-      ms[sp] = -INFINITY;
-      ls[sp] = 0.f;
-#pragma unroll
-      for (int k = 0; k < E; ++k) a[sp][k] = 0.f;
-      if (sp < n && i < C) {
-        const size_t pr = static_cast<size_t>(sp) * p.rows_total + r;
-        const float2 ml = *reinterpret_cast<const float2*>(part_ml + 2 * pr);
-        ms[sp] = ml.x;
-        ls[sp] = ml.y;
-        const float* po = part_o + pr * D + E * lane;
-#pragma unroll
-        for (int k = 0; k < E; ++k) a[sp][k] = po[k];
-      }
-    }
-    float M = -INFINITY;
-#pragma unroll
-    for (int sp = 0; sp < kMaxPieces; ++sp) M = fmaxf(M, ms[sp]);
-    float acc[E], l = 0.f;
-#pragma unroll
-    for (int k = 0; k < E; ++k) acc[k] = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int sp = 0; sp < kMaxPieces; ++sp) {
-        if (ms[sp] == -INFINITY) continue;
-        const float wgt = __builtin_amdgcn_exp2f((ms[sp] - M) * p.scale_log2);
-        l += wgt * ls[sp];
-#pragma unroll
-        for (int k = 0; k < E; ++k) acc[k] += wgt * a[sp][k];
-      }
-    }
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    __bf16* orow = O + r * D + E * lane;
-#pragma unroll
-    for (int k = 0; k < E; ++k) orow[k] = static_cast<__bf16>(acc[k] * inv);
-    if (lse && lane == 0) lse[r] = l > 0.f ? M * p.scale + __logf(l) : -INFINITY;
-  }
-}
-
 }  // namespace
 
 hipError_t launch_chunk_attn_bf16_split(const void* Q, const void* K, const void* V,
@@ -834,38 +1021,109 @@ hipError_t launch_chunk_attn_bf16_split(const void* Q, const void* K, const void
   return launch_split_combine(part_o, part_ml, D, false, o, lse, p, seq, stream);
 }
 
+namespace {
+
+// Merge of the parts of the cut tiles of a balanced call: workgroup
+// (tile i, wave tile w) takes the 32 rows that wave w of tile i owns, 8
+// threads per row, each with D/8 consecutive columns; a tile left whole
+// (p.bal_pre[i + 1] == p.bal_pre[i]) returns at once.  With m_s, l_s, a_s the
+// running max (raw score units), denominator and unnormalised output of part
+// s, M = max_s m_s and w_s = exp2((m_s - M) * scale * log2 e):
+//   O = sum_s w_s a_s / sum_s w_s l_s,   lse = M * scale + log(sum_s w_s l_s).
+// Rows past the chunk, and rows no part saw a key for, give O = 0 and
+// lse = -inf.
+constexpr int kMergeThreads = 256;
+
+template <int D, int W>
+__global__ __launch_bounds__(kMergeThreads) void plan_merge_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, AttnParams p,
+    SeqInfo seq, __bf16* __restrict__ O, float* __restrict__ lse) {
+  constexpr int E = D / 8;                   // columns per thread
+  constexpr size_t kPart = W * kRowsPerWave;  // rows per part
+  const int i = blockIdx.x / W;
+  const int w = blockIdx.x - i * W;
+  const int base = p.bal_pre[i];
+  const int n = p.bal_pre[i + 1] - base;
+  if (n <= 0 || p.bal_pre[p.bal_units] > p.bal_parts) return;
+  int b, g, t;
+  plan_tile(p, seq, i, b, g, t);
+  const int r = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * E;
+  const int wt = t * W + w;
+  const int pb = wt / p.G;
+  const int n_pb = (p.C_max + kRowsPerWave - 1) / kRowsPerWave;
+  if (pb >= n_pb) return;
+  const int h = g * p.G + (wt - pb * p.G);
+  const int row = pb * kRowsPerWave + r;
+  if (row >= p.C_max) return;
+  int P, C;
+  seq_lengths(p, seq, b, P, C);
+  const size_t qo_row = (static_cast<size_t>(b) * p.H_q + h) * p.C_max + row;
+  const size_t prow0 = static_cast<size_t>(base) * kPart + w * kRowsPerWave + r;
+  float M = -INFINITY;
+  if (row < C) {
+#pragma unroll 8
+    for (int s = 0; s < n; ++s) M = fmaxf(M, part_ml[2 * (prow0 + s * kPart)]);
+  }
+  float acc[E];
+#pragma unroll
+  for (int k = 0; k < E; ++k) acc[k] = 0.f;
+  float l = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll 4
+    for (int s = 0; s < n; ++s) {
+      const size_t pr = prow0 + s * kPart;
+      const float2 ml = *reinterpret_cast<const float2*>(part_ml + 2 * pr);
+      const float4* src = reinterpret_cast<const float4*>(part_o + pr * D + c0);
+      float4 v[E / 4];
+#pragma unroll
+      for (int k = 0; k < E / 4; ++k) v[k] = src[k];
+      const float wgt = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ml.x - M) * p.scale_log2);
+      l += wgt * ml.y;
+#pragma unroll
+      for (int k = 0; k < E / 4; ++k) {
+        acc[4 * k] += wgt * v[k].x;
+        acc[4 * k + 1] += wgt * v[k].y;
+        acc[4 * k + 2] += wgt * v[k].z;
+        acc[4 * k + 3] += wgt * v[k].w;
+      }
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  uint32_t* dst = reinterpret_cast<uint32_t*>(O + qo_row * D + c0);
+#pragma unroll
+  for (int k = 0; k < E / 2; ++k) {
+    const bf16x2 v2 = {static_cast<__bf16>(acc[2 * k] * inv), static_cast<__bf16>(acc[2 * k + 1] * inv)};
+    dst[k] = __builtin_bit_cast(uint32_t, v2);
+  }
+  if (lse && (threadIdx.x & 7) == 0) lse[qo_row] = l > 0.f ? M * p.scale + __logf(l) : -INFINITY;
+}
+
+}  // namespace
+
 hipError_t launch_chunk_attn_bf16_balanced(const void* Q, const void* K, const void* V,
                                            const int32_t* T, const int32_t* len, void* O,
-                                           float* lse, int B, int D, const AttnParams& p,
+                                           float* lse, int D, const AttnParams& p,
                                            const SeqInfo& seq, float* part_o, float* part_ml,
-                                           hipStream_t stream) {
-  const int n_units = B * p.H_kv * p.n_t;
-  const int slots = min(p.cus, kPlanMaxSlots);
-  int32_t* plan = const_cast<int32_t*>(p.plan_items);
-  int32_t* pieces = const_cast<int32_t*>(p.plan_pieces);
-  hipLaunchKernelGGL(balance_plan_kernel<8>, dim3(1), dim3(kPlanThreads), 0, stream, len, p,
-                     seq, n_units, slots, plan, pieces);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 grid(n_units + 2 * slots);  // at least the plan's pieces
+                                           int slots, hipStream_t stream) {
+  const dim3 grid(slots);  // one workgroup per compute unit
   const __bf16* q = static_cast<const __bf16*>(Q);
   const __bf16* k = static_cast<const __bf16*>(K);
   const __bf16* v = static_cast<const __bf16*>(V);
   __bf16* o = static_cast<__bf16*>(O);
   if (D == 128)
-    hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 8, false, 2>), grid, dim3(512), 0, stream, q,
+    hipLaunchKernelGGL((chunk_attn_bf16_kernel<128, 8, false, 3>), grid, dim3(512), 0, stream, q,
                        k, v, T, len, o, lse, p, seq, part_o, part_ml);
   else
-    hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 8, false, 2>), grid, dim3(512), 0, stream, q,
+    hipLaunchKernelGGL((chunk_attn_bf16_kernel<64, 8, false, 3>), grid, dim3(512), 0, stream, q,
                        k, v, T, len, o, lse, p, seq, part_o, part_ml);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 cgrid(n_units * 8);  // one workgroup per wave tile of every tile
+  const dim3 mgrid(static_cast<unsigned>(p.bal_units) * 8);  // one workgroup per wave tile
   if (D == 128)
-    hipLaunchKernelGGL((plan_combine_kernel<128, 8>), cgrid, dim3(kCombineThreads), 0, stream,
+    hipLaunchKernelGGL((plan_merge_kernel<128, 8>), mgrid, dim3(kMergeThreads), 0, stream,
                        part_o, part_ml, p, seq, o, lse);
   else
-    hipLaunchKernelGGL((plan_combine_kernel<64, 8>), cgrid, dim3(kCombineThreads), 0, stream,
+    hipLaunchKernelGGL((plan_merge_kernel<64, 8>), mgrid, dim3(kMergeThreads), 0, stream,
                        part_o, part_ml, p, seq, o, lse);
   return hipGetLastError();
 }

@@ -30,11 +30,13 @@ struct BlockRange {
   int32_t end[CA_MAX_BATCH];
 };
 
-// Balance plan limits: pieces per (b, g, tile), and compute units the plan
-// spreads pieces over (the device's count, up to this many).
-constexpr int kMaxPieces = 8;
+// Balanced attention limits: slots (one workgroup per compute unit, the
+// device's count up to this many) and the least work per slot before tiles
+// are cut.  Calls with more tiles than slots, or with tiles * NKB_max past
+// 2^31 - 1 (the plan's 32-bit sums), run the plain kernel instead.
 constexpr int kPlanMaxSlots = 1024;
-constexpr int kPlanMaxBlocks = 1 << 24;  // NKB_max the plan's 32-bit piece arithmetic allows
+constexpr int kBalMinShare = 32;
+constexpr int kBalJobCost = 12;  // work units a job costs on its own, in the plan
 
 struct AttnParams {
   int H_q, H_kv, G;     // heads; G = H_q / H_kv query heads per KV head
@@ -51,11 +53,13 @@ struct AttnParams {
   int n_split;          // split-KV: table ranges per (b, g) (1: no split)
   int64_t rows_total;   // B * H_q * C_max (split-KV partial layout)
   int cus;              // compute units of the device (launch shape choices only)
-  // balance plan (bf16 planned pieces): plan_items[0] = number of pieces, then
-  // one int4 (b * H_kv + g, tile, piece k, pieces n) per piece from int 4 on;
-  // plan_pieces[(b * H_kv + g) * n_t + tile] = n
-  const int32_t* plan_items;
-  const int32_t* plan_pieces;
+  // balanced attention: tiles of the plan (B * H_kv * n_t), partial tiles the
+  // workspace holds, and the plan's part numbering (bal_units + 1 ints: parts
+  // of the cut tiles before tile i, then the total), written by the attention
+  // kernel and read by the merge
+  int bal_units;
+  int bal_parts;
+  int32_t* bal_pre;
   // device-length calls: prior and chunk lengths read from device int32 [B]
   // arrays (nullptr: the host values in SeqInfo)
   const int32_t* dev_prior;
@@ -137,16 +141,17 @@ hipError_t launch_chunk_attn_bf16_split(const void* Q, const void* K, const void
                                         const SeqInfo& seq, float* part_o, float* part_ml,
                                         hipStream_t stream);
 
-// bf16 path with a balance plan: a planning kernel cuts the (b, g, tile)
-// workgroups whose table walks are longest into pieces so that the pieces
-// spread evenly over p.cus compute units (longest first), writes the plan to
-// plan (p.plan_items / p.plan_pieces point into it), then the pieces run
-// (8-wave workgroups) and a merge combines the cut tiles' partials.
+// bf16 path, balanced: one 8-wave workgroup per slot (slots <= kPlanMaxSlots,
+// the device's compute units); each derives the plan from the table lengths
+// and runs its pieces; the pieces of cut tiles write partials (part_o: float
+// [p.bal_parts, 256, D]; part_ml: float [p.bal_parts, 256, 2]) that a merge
+// kernel then combines (p.bal_pre: the part numbering, p.bal_units + 1 ints).
+// p.n_t = tiles of 8 waves per (b, g); p.bal_units <= slots.
 hipError_t launch_chunk_attn_bf16_balanced(const void* Q, const void* K, const void* V,
                                            const int32_t* T, const int32_t* len, void* O,
-                                           float* lse, int B, int D, const AttnParams& p,
+                                           float* lse, int D, const AttnParams& p,
                                            const SeqInfo& seq, float* part_o, float* part_ml,
-                                           hipStream_t stream);
+                                           int slots, hipStream_t stream);
 
 // fp32 path on the vector ALUs; D in {64, 128}.
 hipError_t launch_chunk_attn_f32(const float* Q, const float* K, const float* V,

@@ -296,23 +296,31 @@ CA_EXPORT ca_status ca_chunk_attention_split_noalloc(const void* Q, const void* 
  * holds what each group's union selected, so lengths differ by group), and
  * the causal part, which grows along the chunk.  The pages do not describe
  * how work is scheduled; this is the merge of partial softmax results given
- * for ca_chunk_attention_split, applied only where it pays:
- *   - a planning kernel measures each tile's walk (the entries its 32-row
- *     query blocks can see) and, unless the walks already balance, cuts the
- *     longest into up to 8 pieces of even length, then lists all pieces
- *     longest first;
- *   - the pieces run; a tile left whole writes O and lse itself, and the
- *     pieces of a cut tile are merged as in ca_chunk_attention_split.
+ * for ca_chunk_attention_split, applied only where it pays.  One launch of one
+ * workgroup per compute unit ("slot"); each derives the same plan from len:
+ *   - a tile (32-row query blocks of 8 waves) has w work units, its table
+ *     entries up to the last block its rows may see; A = the even share of
+ *     the total per slot, at least 32; a job costs about 12 units on its own;
+ *   - when the longest walk is within 24 units of A nothing is cut (slot s
+ *     runs tile s); otherwise slot s runs tile s, whole when w - A <
+ *     max(A/8, 24), else its first A units, then its share of the cut tiles'
+ *     remaining units, laid end to end (filling each slot to A less one job
+ *     cost);
+ *   - a tile run whole writes O and lse; the pieces of a cut tile write
+ *     partial results to the workspace, and a second kernel merges them (as
+ *     in ca_chunk_attention_split).
  * Same result as ca_chunk_attention (the same admissible keys and softmax),
  * bit for bit where nothing is cut, else up to the rounding of the merge.
+ * Shapes with more tiles (B * H_kv * ceil(H_q/H_kv * ceil(C_max/32) / 8)) than
+ * the device's compute units (or than 1024), or with tiles * NKB_max above
+ * 2^31 - 1, run ca_chunk_attention.
  *
  * workspace  device memory owned by the caller, 16-byte aligned, at least
  *            ca_chunk_attention_balanced_workspace_size(B, H_q, H_kv, C_max, D)
- *            bytes (else CA_ERR_SHAPE; NULL gives CA_ERR_NULL).  The plan
- *            lives there: calls that share one workspace must be ordered on
- *            one stream.
+ *            bytes (else CA_ERR_SHAPE; NULL gives CA_ERR_NULL).  Its contents
+ *            need no initialisation (every call writes what it reads).  Calls
+ *            that share one workspace must be ordered on one stream.
  * dtype      CA_BF16; CA_F32 runs ca_chunk_attention (workspace unused).
- * NKB_max    at most 2^24 for CA_BF16 (else CA_ERR_SHAPE).
  * Other arguments, layouts and errors as for ca_chunk_attention.
  */
 CA_EXPORT ca_status ca_chunk_attention_balanced(const void* Q, const void* K_cache,
@@ -323,10 +331,12 @@ CA_EXPORT ca_status ca_chunk_attention_balanced(const void* Q, const void* K_cac
                                       ca_dtype dtype, void* workspace, size_t workspace_bytes,
                                       void* O, float* lse, hipStream_t stream);
 
-/* Bytes of workspace ca_chunk_attention_balanced needs: partial outputs for
- * up to 8 pieces of every output row (8 * B * H_q * C_max * (D + 2) * 4) plus
- * the plan (a few KiB); 0 for invalid sizes (H_q % H_kv != 0, D not 64 or
- * 128, nonpositive sizes). */
+/* Bytes of workspace ca_chunk_attention_balanced needs, with tiles as above
+ * and parts = 2 * tiles + 1024 (the most partial tiles a call on up to 1024
+ * compute units writes): parts * 256 * (D + 2) * 4 bytes of partial results
+ * and (tiles + 1) * 4 bytes of part numbering (each part 16-byte aligned); 16
+ * for shapes with more than 1024 tiles (they run ca_chunk_attention); 0 for
+ * invalid sizes (H_q % H_kv != 0, D not 64 or 128, nonpositive sizes). */
 CA_EXPORT size_t ca_chunk_attention_balanced_workspace_size(int B, int H_q, int H_kv,
                                                             int C_max, int D);
 

@@ -171,13 +171,15 @@ int main() {
                                               nullptr, 0) == CA_ERR_TOO_LARGE);
       EXPECT(strcmp(stub::last.what, "") == 0);
     }
-    // balanced: workspace layout (partials for 8 pieces, then the plan and the
-    // pieces per tile), size check, 8-wave tiles, fp32 runs unplanned
+    // balanced: workspace layout (partial tiles for 2 tiles + 1024 parts, then
+    // the part numbering), size check, 8-wave tiles, one workgroup per slot,
+    // fp32 runs unplanned
     const size_t bneed = ca_chunk_attention_balanced_workspace_size(3, 32, 8, 256, 128);
     const long long units = 3LL * 8 * ((4 * 8 + 7) / 8);
-    const long long po = 8LL * 3 * 32 * 256 * 128 * 4, pml = 8LL * 3 * 32 * 256 * 2 * 4;
-    const long long plan_bytes = (4 + 4 * (units + 2 * 1024)) * 4;
-    EXPECT(bneed == (size_t)(po + pml + ((plan_bytes + 15) / 16) * 16 + ((units * 4 + 15) / 16) * 16));
+    const long long parts = 2 * units + 1024;
+    const long long po = parts * 256 * 128 * 4, pml = parts * 256 * 2 * 4;
+    const long long pre_off = ((po + pml + 15) / 16) * 16;
+    EXPECT(bneed == (size_t)(((pre_off + (units + 1) * 4) + 15) / 16 * 16));
     EXPECT(ca_chunk_attention_balanced_workspace_size(3, 32, 7, 256, 128) == 0);
     EXPECT(ca_chunk_attention_balanced_workspace_size(3, 32, 8, 256, 96) == 0);
     EXPECT(ca_chunk_attention_balanced(FAKE, FAKE, FAKE, (const int32_t*)FAKE,
@@ -185,12 +187,24 @@ int main() {
                                        8448, 128, 64, 0.125f, CA_BF16, FAKE, bneed, FAKE, nullptr,
                                        0) == CA_OK);
     EXPECT(strcmp(stub::last.what, "attn_bf16_balanced") == 0 && stub::last.p.waves == 8 &&
-           stub::last.p.n_t == (4 * 8 + 7) / 8 && stub::last.p.xcd == 0);
+           stub::last.p.n_t == (4 * 8 + 7) / 8 && stub::last.p.xcd == 1);
+    EXPECT(stub::last.p.bal_units == units && stub::last.p.bal_parts == parts);
+    EXPECT(stub::last.ints[0] >= 1 && stub::last.ints[0] <= 1024);
     EXPECT((char*)stub::last.ptrs[1] - (char*)stub::last.ptrs[0] == (ptrdiff_t)po);
-    EXPECT((const char*)stub::last.p.plan_items - (char*)stub::last.ptrs[0] ==
-           (ptrdiff_t)(po + pml));
-    EXPECT((const char*)stub::last.p.plan_pieces - (const char*)stub::last.p.plan_items ==
-           (ptrdiff_t)(((plan_bytes + 15) / 16) * 16));
+    EXPECT((const char*)stub::last.p.bal_pre - (char*)stub::last.ptrs[0] == (ptrdiff_t)pre_off);
+    {  // more tiles than slots: the plain kernel, no workspace needed past 16 bytes
+      int32_t p17[17], c17[17];
+      for (int i = 0; i < 17; ++i) {
+        p17[i] = 64 * i;
+        c17[i] = 2048;
+      }
+      EXPECT(ca_chunk_attention_balanced_workspace_size(17, 64, 8, 2048, 64) == 16);
+      EXPECT(ca_chunk_attention_balanced(FAKE, FAKE, FAKE, (const int32_t*)FAKE,
+                                         (const int32_t*)FAKE, 64, p17, c17, 17, 64, 8, 2048,
+                                         4096, 64, 64, 0.125f, CA_BF16, FAKE, 16, FAKE, nullptr,
+                                         0) == CA_OK);
+      EXPECT(strcmp(stub::last.what, "attn_bf16") == 0);
+    }
     EXPECT(ca_chunk_attention_balanced(FAKE, FAKE, FAKE, (const int32_t*)FAKE,
                                        (const int32_t*)FAKE, 200, prior, chunk, 3, 32, 8, 256,
                                        8448, 128, 64, 0.125f, CA_BF16, FAKE, bneed - 1, FAKE,

@@ -84,12 +84,14 @@ hipError_t launch_chunk_attn_bf16_split(const void*, const void*, const void*, c
 }
 
 hipError_t launch_chunk_attn_bf16_balanced(const void*, const void*, const void*,
-                                           const int32_t*, const int32_t*, void*, float*, int B,
-                                           int D, const AttnParams& p, const SeqInfo& seq,
-                                           float* part_o, float* part_ml, hipStream_t) {
-  record_attn("attn_bf16_balanced", B, D, p, seq);
+                                           const int32_t*, const int32_t*, void*, float*, int D,
+                                           const AttnParams& p, const SeqInfo& seq,
+                                           float* part_o, float* part_ml, int slots,
+                                           hipStream_t) {
+  record_attn("attn_bf16_balanced", 0, D, p, seq);
   stub::last.ptrs[0] = part_o;
   stub::last.ptrs[1] = part_ml;
+  stub::last.ints[0] = slots;
   return hipSuccess;
 }
 

@@ -170,13 +170,16 @@ def test_split_validation_and_workspace_size():
 
 def test_balanced_validation_and_workspace_size():
     lib = _lib.lib()
-    # 8 pieces of partials per output row, then the plan (4 + 4 * (tiles + 2048) ints) and
-    # the pieces per tile (tiles = B * H_kv * ceil(G * ceil(C_max / 32) / 8)), 16-byte aligned
+    # parts = 2 * tiles + 1024 partial tiles of 256 rows (D floats, then 2 floats per row), then
+    # the part numbering, tiles + 1 ints (tiles = B * H_kv * ceil(G * ceil(C_max / 32) / 8)),
+    # each part 16-byte aligned
     tiles = 1 * 8 * ((4 * 64 + 7) // 8)
+    parts = 2 * tiles + 1024
     up16 = lambda x: (x + 15) // 16 * 16
-    want = (8 * 32 * 2048 * 128 * 4 + 8 * 32 * 2048 * 2 * 4 + up16((4 + 4 * (tiles + 2048)) * 4)
-            + up16(tiles * 4))
+    want = up16(up16(up16(parts * 256 * 128 * 4) + parts * 256 * 2 * 4) + (tiles + 1) * 4)
     assert lib.ca_chunk_attention_balanced_workspace_size(1, 32, 8, 2048, 128) == want
+    # more than 1024 tiles: the plain kernel runs, no workspace is used
+    assert lib.ca_chunk_attention_balanced_workspace_size(5, 32, 8, 2048, 64) == 16
     assert lib.ca_chunk_attention_balanced_workspace_size(1, 32, 7, 2048, 128) == 0
     assert lib.ca_chunk_attention_balanced_workspace_size(1, 32, 8, 2048, 80) == 0
     assert lib.ca_chunk_attention_balanced_workspace_size(0, 32, 8, 2048, 128) == 0

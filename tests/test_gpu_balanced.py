@@ -1,20 +1,22 @@
 """GPU parity of balanced chunk attention (ca_chunk_attention_balanced).
 
-A planning kernel cuts the longest per-tile table walks into pieces and lists
-every piece longest first; the pieces run, and cut tiles are merged.  Checked
-here:
+One workgroup per compute unit ("slot"); each derives the same plan from the
+table lengths: slot s first runs tile s (whole, or its first A work units, A
+the even share), then the tails of the cut tiles, laid end to end over the
+slots' spare capacity.  A cut tile's pieces write partials, which a second
+kernel merges.  Checked here:
 * outputs and LSE against the float64 oracle (full at small sizes, sampled
   rows at 128K), on uneven per-group tables and on one GPU's tensor-parallel
-  share (one KV head, so every tile is cut);
+  share (one KV head: every tile is cut into many pieces);
+* the pieces of every tile, read back from the part numbering the kernel
+  leaves in the workspace, against a model of the plan written here from its
+  description;
 * bit-identical output to ca_chunk_attention where the walks already balance
   (nothing cut: the same kernel arithmetic);
-* the plan read back from the workspace: every tile's pieces listed exactly
-  once, piece counts consistent, size classes non-increasing, the count within
-  the launch grid;
 * NaN outside the selected blocks changes nothing; one workspace serves calls
-  of different shapes in a row; fp32 runs the unplanned kernel;
-* more tiles than the planner keeps in LDS (its walks then pass through the
-  workspace).
+  of different shapes in a row and a workspace of garbage bytes works; a
+  captured graph replayed between eager calls matches the eager result; fp32 and shapes with more tiles than compute
+  units run the plain kernel.
 """
 import zlib
 
@@ -29,8 +31,9 @@ from tests.gpu_util import (F32_MAX_ABS, check_lse, Dev, compare_bf16, oracle_fu
 
 pytestmark = pytest.mark.gpu
 
-MAX_PIECES = 8
-PLAN_MAX_SLOTS = 1024
+PLAN_MAX_SLOTS = 1024   # slots the workspace is sized for
+BAL_MIN_SHARE = 32      # least work units per slot
+JOB_COST = 12           # work units the plan counts per job
 
 
 def _bern(p):
@@ -55,61 +58,108 @@ def _n_t(w):
     return (w.G * ((w.C_max + 31) // 32) + 7) // 8
 
 
-def _read_plan(ws, w):
-    """(count, items [count, 4] of (b*H_kv+g, tile, piece, pieces), pieces per tile)."""
-    rows = w.B * w.H_q * w.C_max
+def _workspace(w, zero=True):
+    n = ca.balanced_workspace_size(w.B, w.H_q, w.H_kv, w.C_max, w.D)
+    return (torch.zeros if zero else torch.empty)(n, dtype=torch.uint8, device="cuda")
+
+
+def _part_numbering(ws, w):
+    """The plan's part numbering (tiles + 1 ints, plan order) from the workspace."""
     units = w.B * w.H_kv * _n_t(w)
-    plan_off = MAX_PIECES * rows * w.D * 4 + MAX_PIECES * rows * 2 * 4
-    plan_bytes = (4 + 4 * (units + 2 * PLAN_MAX_SLOTS)) * 4
-    pieces_off = plan_off + (plan_bytes + 15) // 16 * 16
-    ints = ws.cpu().view(torch.int32).numpy()
-    count = int(ints[plan_off // 4])
-    items = ints[plan_off // 4 + 4: plan_off // 4 + 4 + 4 * count].reshape(-1, 4)
-    return count, items, ints[pieces_off // 4: pieces_off // 4 + units]
+    parts = 2 * units + PLAN_MAX_SLOTS
+    up16 = lambda x: (x + 15) // 16 * 16
+    off = up16(up16(parts * 256 * w.D * 4) + parts * 256 * 2 * 4)
+    return ws[off: off + 4 * (units + 1)].cpu().numpy().view(np.int32).astype(np.int64)
 
 
-def _walks(w, T, lens):
-    """The planner's measure of each 8-wave tile's work: the table's entries
-    less the chunk blocks above the last block the tile's rows may see (exact
-    when the chunk's causal block triangle is selected, as here)."""
-    Th, lh = T.cpu().numpy(), lens.cpu().numpy()
-    n_t, n_pb = _n_t(w), (w.C_max + 31) // 32
-    out = np.zeros((w.B, w.H_kv, n_t), np.int64)
-    for b in range(w.B):
-        P, C = w.prior[b], w.chunk[b]
-        nkb = (P + C + 63) // 64
-        for t in range(n_t):
-            if (t * 8) // w.G * 32 >= C:
-                continue
-            last_pb = min((t * 8 + 7) // w.G, n_pb - 1)
-            kb_limit = (P + min(C, (last_pb + 1) * 32) - 1) // 64
-            for g in range(w.H_kv):
-                row = Th[b, g, :lh[b, g]]
-                walk = int(np.searchsorted(row, kb_limit, side="right"))
-                out[b, g, t] = max(int(lh[b, g]) - (nkb - 1 - kb_limit), 0)
-                assert out[b, g, t] == walk  # every chunk block is in the table
-    return out.reshape(-1)
-
-
-def _check_plan(ws, w, T, lens):
-    count, items, pieces = _read_plan(ws, w)
+def _plan_tiles(w):
+    """Plan order of the tiles: tile i -> (b, g, t), as a plain launch maps
+    workgroup i (sequences longest first by (P + C) * C, stable; with
+    B * H_kv a multiple of 8, tile i's pseudo-request on XCD i % 8)."""
     n_t = _n_t(w)
-    units = w.B * w.H_kv * n_t
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    assert 1 <= count <= units + 2 * min(cus, PLAN_MAX_SLOTS)
-    assert np.all((pieces >= 1) & (pieces <= MAX_PIECES))
-    assert int(pieces.sum()) == count
-    want = sorted((u, t, k) for u in range(w.B * w.H_kv) for t in range(n_t)
-                  for k in range(int(pieces[u * n_t + t])))
-    assert sorted(map(tuple, items[:, :3].tolist())) == want
-    assert np.all(items[:, 3] == pieces[items[:, 0] * n_t + items[:, 1]])
-    walk = _walks(w, T, lens)
-    wmax = int(walk.max())
-    n = items[:, 3]
-    wu = walk[items[:, 0] * n_t + items[:, 1]]
-    size = wu * (items[:, 2] + 1) // n - wu * items[:, 2] // n
-    cls = np.minimum(63, size // (wmax // 64 + 1))  # the planner's 64 size classes
-    assert np.all(np.diff(cls) <= 0), "pieces not listed longest first"
+    order = sorted(range(w.B), key=lambda b: -(w.prior[b] + w.chunk[b]) * w.chunk[b])
+    xcd = (w.B * w.H_kv) % 8 == 0
+    out = []
+    for i in range(w.B * w.H_kv * n_t):
+        if xcd:
+            x, k = i & 7, i >> 3
+            jj = k // n_t
+            u, t = x + 8 * jj, k - jj * n_t
+        else:
+            u, t = i // n_t, i % n_t
+        out.append((order[u // w.H_kv], u % w.H_kv, t))
+    return out
+
+
+def _model_cuts(w, T, lens, slots):
+    """The plan's pieces per tile (plan order), from its description: work
+    w_i = table entries up to the last block tile i's rows may see (at least
+    1); A = max(ceil(sum / slots), 32), or the longest walk when that is
+    within 2 job costs (12 units each) of it, and then nothing is cut; tile i
+    runs whole when w_i - A < max(A / 8, 24), else its first A units on slot i
+    and the rest as a tail; a slot's spare capacity is A - head - 12 (A growing
+    by ceil(shortfall / slots with spare) until the tails fit, for at most 6
+    rounds, then without the 12); the tails fill the spare capacity in order."""
+    Th, lh = T.cpu().numpy(), lens.cpu().numpy()
+    n_pb = (w.C_max + 31) // 32
+    work = []
+    for b, g, t in _plan_tiles(w):
+        P, C = w.prior[b], w.chunk[b]
+        if (t * 8) // w.G * 32 >= C:
+            work.append(1)
+            continue
+        last_pb = min((t * 8 + 7) // w.G, n_pb - 1)
+        kb_limit = (P + min(C, (last_pb + 1) * 32) - 1) // 64
+        nkb = (P + C + 63) // 64
+        n = min(max(int(lh[b, g]), 0), Th.shape[2])
+        work.append(max(n - (nkb - 1 - kb_limit), 1))
+    work = np.asarray(work, np.int64)
+    n = len(work)
+    assert n <= slots
+    A = max(-(-int(work.sum()) // slots), BAL_MIN_SHARE)
+    if int(work.max()) <= A + 2 * JOB_COST:
+        return np.zeros(n, bool), np.ones(n, np.int64)
+    heads = lambda: np.array([int(x) if x - A < max(A // 8, 2 * JOB_COST) else A for x in work])
+    reserve = JOB_COST
+    for rnd in range(7):
+        if rnd == 6:
+            reserve = 0
+            break
+        head = heads()
+        spare = np.array([max(A - (int(head[s]) if s < n else 0) - reserve, 0) for s in range(slots)])
+        dem, cap, nsp = int((work - head).sum()), int(spare.sum()), int((spare > 0).sum())
+        if cap >= dem:
+            break
+        A += -(-(dem - cap) // max(nsp, 1))
+    head = heads()
+    tail = work - head
+    tpre = np.concatenate([[0], np.cumsum(tail)])
+    spare = np.array([max(A - (int(head[s]) if s < n else 0) - reserve, 0) for s in range(slots)])
+    spre = np.concatenate([[0], np.cumsum(spare)])
+    assert tpre[-1] <= spre[-1]
+    # walk every slot's spare range and count the tiles whose tails it meets
+    pieces = np.ones(n, np.int64)
+    jobs = np.array([1 if s < n else 0 for s in range(slots)])
+    for s in range(slots):
+        lo, hi = int(spre[s]), min(int(spre[s + 1]), int(tpre[-1]))
+        for i in range(n):
+            if lo < hi and tail[i] > 0 and tpre[i] < hi and tpre[i + 1] > lo:
+                pieces[i] += 1
+                jobs[s] += 1
+    assert jobs.max() <= 11
+    return pieces > 1, pieces
+
+
+def _check_cuts(ws, w, T, lens):
+    """Pieces per tile read from the part numbering (a cut tile's parts; 0 for
+    a tile run whole) equal the model's."""
+    slots = min(torch.cuda.get_device_properties(0).multi_processor_count, PLAN_MAX_SLOTS)
+    pre = _part_numbering(ws, w)
+    got = np.diff(pre)
+    want_cut, pieces = _model_cuts(w, T, lens, slots)
+    want = np.where(want_cut, pieces, 0)
+    assert pre[0] == 0 and np.array_equal(got, want), (np.nonzero(got != want)[0][:10], got[:16],
+                                                       want[:16])
     return pieces
 
 
@@ -129,11 +179,10 @@ def test_balanced_small_full_parity(B, H_q, H_kv, D, prior, chunk, C_max, dens):
     say(f"balanced small B={B} H={H_q}/{H_kv} D={D} prior={prior} chunk={chunk} dens={dens}")
     d = Dev(w)
     T, lens = d.tables()
-    ws = torch.empty(ca.balanced_workspace_size(B, H_q, H_kv, C_max, D), dtype=torch.uint8,
-                     device="cuda")
+    ws = _workspace(w)
     O, lse = _balanced(d, T, lens, ws)
     torch.cuda.synchronize()
-    pieces = _check_plan(ws, w, T, lens)
+    pieces = _check_cuts(ws, w, T, lens)
     say(f"  tiles {pieces.size}, pieces {int(pieces.sum())}, cut tiles {int((pieces > 1).sum())}")
     assert (pieces > 1).any()  # small grids: tiles are cut to fill the compute units
     Or, lr = oracle_full(w)
@@ -157,12 +206,11 @@ def test_balanced_equals_plain_when_even():
     say("balanced == plain on even tables")
     d = Dev(w)
     T, lens = d.tables()
-    ws = torch.empty(ca.balanced_workspace_size(1, 32, 8, 2048, 128), dtype=torch.uint8,
-                     device="cuda")
+    ws = _workspace(w)
     Ob, lb = _balanced(d, T, lens, ws)
     Op, lp = d.attention(T, lens, return_lse=True)
     torch.cuda.synchronize()
-    pieces = _check_plan(ws, w, T, lens)
+    pieces = _check_cuts(ws, w, T, lens)
     assert np.all(pieces == 1)
     assert torch.equal(Ob, Op)
     assert torch.equal(lb, lp)
@@ -176,11 +224,11 @@ def test_balanced_tp_shard_128k_sampled(variant):
     w = _tp_shard(variant)
     d = Dev(w)
     T, lens = d.tables()
-    ws = torch.empty(ca.balanced_workspace_size(1, 4, 1, 2048, 128), dtype=torch.uint8,
-                     device="cuda")
+    ws = _workspace(w)
     O, lse = _balanced(d, T, lens, ws)
     torch.cuda.synchronize()
-    pieces = _check_plan(ws, w, T, lens)
+    pieces = _check_cuts(ws, w, T, lens)
+    say(f"  pieces per tile {sorted(set(pieces.tolist()))}")
     assert pieces.min() > 1
     rows = sample_rows(w, seed=zlib.crc32(variant.encode()) % 1000, heads_per_group=4, extra=16)
     Or, lr = oracle_rows(w, rows)
@@ -240,9 +288,82 @@ def test_balanced_fp32_runs_plain_kernel():
     assert float(np.abs(to_np(Ob) - Or).max()) <= F32_MAX_ABS
 
 
-def test_balanced_many_tiles_plan_in_global_scratch():
-    # more tiles (B * H_kv * tiles per group = 17 * 8 * 64) than the planner
-    # keeps in LDS: the walks go through the pieces array between its passes
+def test_balanced_more_tiles_than_slots_runs_plain_kernel():
+    # 8 sequences x 8 groups x 16 tiles = 1024 tiles, more than the compute
+    # units: the call runs the plain kernel (bit for bit) and leaves the
+    # workspace alone
+    B, H_q, H_kv, D, C_max = 8, 32, 8, 128, 1024
+    rng = np.random.default_rng(95)
+    prior = [64 * int(x) for x in rng.integers(0, 64, B)]
+    chunk = [64 * int(x) for x in rng.integers(1, 17, B)]
+    chunk[0] = C_max
+    w = gen.make_custom(B, H_q, H_kv, D, prior, chunk, "bf16", 96,
+                        _by_group([1.0, 0.1, 0.5, 0.0, 0.3, 1.0, 0.05, 0.7], H_q // H_kv),
+                        C_max=C_max, name="balanced_more_tiles")
+    n = B * H_kv * _n_t(w)
+    if n <= min(torch.cuda.get_device_properties(0).multi_processor_count, PLAN_MAX_SLOTS):
+        pytest.skip("needs more tiles than compute units")
+    say(f"balanced with {n} tiles")
+    d = Dev(w)
+    T, lens = d.tables()
+    ws = _workspace(w)
+    O, lse = _balanced(d, T, lens, ws)
+    Op, lp = d.attention(T, lens, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(O, Op) and torch.equal(lse, lp)
+    assert not ws.any()
+    rows = sample_rows(w, seed=97, heads_per_group=1, extra=4)
+    Or, lr = oracle_rows(w, rows)
+    r = torch.from_numpy(rows).cuda()
+    compare_bf16(to_np(O[r[:, 0], r[:, 1], r[:, 2]]), Or, f"{len(rows)} sampled rows")
+    check_lse(to_np(lse[r[:, 0], r[:, 1], r[:, 2]]), lr)
+
+
+def test_balanced_garbage_workspace_and_graph_replay():
+    # a workspace of garbage bytes, then one captured call replayed three times
+    # with eager calls on the same workspace between the replays: every result
+    # equals the first eager one bit for bit
+    w = gen.make_custom(1, 16, 4, 128, [8192], [1024], "bf16", 98,
+                        _by_group([1.0, 0.05, 0.4, 0.1], 4), name="balanced_graph")
+    say("balanced: garbage workspace, graph replays between eager calls")
+    d = Dev(w)
+    T, lens = d.tables()
+    n = ca.balanced_workspace_size(w.B, w.H_q, w.H_kv, w.C_max, w.D)
+    ws = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+    O_ref, l_ref = _balanced(d, T, lens, ws)
+    O_ref, l_ref = O_ref.clone(), l_ref.clone()
+    torch.cuda.synchronize()
+    Or, lr = oracle_full(w)
+    compare_bf16(to_np(O_ref), Or, "O")
+    live = np.isfinite(lr)
+    check_lse(to_np(l_ref)[live], lr[live])
+    O_g = torch.empty_like(d.q)
+    l_g = torch.empty((w.B, w.H_q, w.C_max), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up call outside the capture
+        ca.chunk_attention(d.q, d.k, d.v, T, lens, w.prior, w.chunk, w.scale, out=O_g,
+                           lse=l_g, balanced=True, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ca.chunk_attention(d.q, d.k, d.v, T, lens, w.prior, w.chunk, w.scale, out=O_g,
+                           lse=l_g, balanced=True, workspace=ws)
+    for rep in range(3):
+        O_g.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(O_g, O_ref) and torch.equal(l_g, l_ref), f"replay {rep}"
+        O_e, l_e = _balanced(d, T, lens, ws)  # eager call in between
+        torch.cuda.synchronize()
+        assert torch.equal(O_e, O_ref) and torch.equal(l_e, l_ref), f"eager {rep}"
+
+
+def test_balanced_past_workspace_limit_runs_plain_kernel():
+    # more tiles (B * H_kv * tiles per group = 17 * 8 * 64) than the workspace
+    # is ever sized for (1024): 16 bytes of workspace, the plain kernel runs
+    # (same result, bit for bit)
     B, H_q, H_kv, D, C_max = 17, 64, 8, 64, 2048
     rng = np.random.default_rng(91)
     prior = [64 * int(x) for x in rng.integers(0, 12, B)]
@@ -251,15 +372,16 @@ def test_balanced_many_tiles_plan_in_global_scratch():
     w = gen.make_custom(B, H_q, H_kv, D, prior, chunk, "bf16", 92,
                         _by_group([1.0, 0.1, 0.5, 0.0, 0.3, 1.0, 0.05, 0.7], H_q // H_kv),
                         C_max=C_max, name="balanced_many_tiles")
-    assert B * H_kv * _n_t(w) > 8192
+    assert B * H_kv * _n_t(w) > PLAN_MAX_SLOTS
+    assert ca.balanced_workspace_size(B, H_q, H_kv, C_max, D) == 16
     say(f"balanced with {B * H_kv * _n_t(w)} tiles")
     d = Dev(w)
     T, lens = d.tables()
-    ws = torch.empty(ca.balanced_workspace_size(B, H_q, H_kv, C_max, D), dtype=torch.uint8,
-                     device="cuda")
+    ws = _workspace(w)
     O, lse = _balanced(d, T, lens, ws)
+    Op, lp = d.attention(T, lens, return_lse=True)
     torch.cuda.synchronize()
-    _check_plan(ws, w, T, lens)
+    assert torch.equal(O, Op) and torch.equal(lse, lp)
     rows = sample_rows(w, seed=93, heads_per_group=1, extra=2)
     Or, lr = oracle_rows(w, rows)
     r = torch.from_numpy(rows).cuda()
