@@ -1028,7 +1028,8 @@ namespace {
 // threads per row, each with D/8 consecutive columns; a tile left whole
 // (p.bal_pre[i + 1] == p.bal_pre[i]) returns at once.  With m_s, l_s, a_s the
 // running max (raw score units), denominator and unnormalised output of part
-// s, M = max_s m_s and w_s = exp2((m_s - M) * scale * log2 e):
+// s, M = max_s m_s and w_s = exp2((m_s - M) * scale * log2 e) (taken in one
+// pass, the sums rescaled as the running M grows):
 //   O = sum_s w_s a_s / sum_s w_s l_s,   lse = M * scale + log(sum_s w_s l_s).
 // Rows past the chunk, and rows no part saw a key for, give O = 0 and
 // lse = -inf.
@@ -1059,34 +1060,44 @@ __global__ __launch_bounds__(kMergeThreads) void plan_merge_kernel(
   seq_lengths(p, seq, b, P, C);
   const size_t qo_row = (static_cast<size_t>(b) * p.H_q + h) * p.C_max + row;
   const size_t prow0 = static_cast<size_t>(base) * kPart + w * kRowsPerWave + r;
-  float M = -INFINITY;
-  if (row < C) {
-#pragma unroll 8
-    for (int s = 0; s < n; ++s) M = fmaxf(M, part_ml[2 * (prow0 + s * kPart)]);
-  }
-  float acc[E];
+  // one pass over the parts, four at a time (their loads in flight together):
+  // the running max M and the sums rescale when a group raises M
+  float M = -INFINITY, l = 0.f, acc[E];
 #pragma unroll
   for (int k = 0; k < E; ++k) acc[k] = 0.f;
-  float l = 0.f;
-  if (M != -INFINITY) {
-#pragma unroll 4
-    for (int s = 0; s < n; ++s) {
-      const size_t pr = prow0 + s * kPart;
-      const float2 ml = *reinterpret_cast<const float2*>(part_ml + 2 * pr);
-      const float4* src = reinterpret_cast<const float4*>(part_o + pr * D + c0);
-      float4 v[E / 4];
+  for (int s0 = 0; row < C && s0 < n; s0 += 4) {
+    float2 ml[4];
+    float4 v[4][E / 4];
 #pragma unroll
-      for (int k = 0; k < E / 4; ++k) v[k] = src[k];
-      const float wgt = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ml.x - M) * p.scale_log2);
-      l += wgt * ml.y;
+    for (int u = 0; u < 4; ++u) {
+      const size_t pr = prow0 + static_cast<size_t>(s0 + u) * kPart;
+      const bool in = s0 + u < n;
+      ml[u] = in ? *reinterpret_cast<const float2*>(part_ml + 2 * pr) : make_float2(-INFINITY, 0.f);
+      const float4* src = reinterpret_cast<const float4*>(part_o + pr * D + c0);
+#pragma unroll
+      for (int k = 0; k < E / 4; ++k) v[u][k] = in ? src[k] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float mn = M;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mn = fmaxf(mn, ml[u].x);
+    if (mn == -INFINITY) continue;
+    const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((M - mn) * p.scale_log2);
+    l *= sc;
+#pragma unroll
+    for (int k = 0; k < E; ++k) acc[k] *= sc;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wgt = ml[u].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ml[u].x - mn) * p.scale_log2);
+      l += wgt * ml[u].y;
 #pragma unroll
       for (int k = 0; k < E / 4; ++k) {
-        acc[4 * k] += wgt * v[k].x;
-        acc[4 * k + 1] += wgt * v[k].y;
-        acc[4 * k + 2] += wgt * v[k].z;
-        acc[4 * k + 3] += wgt * v[k].w;
+        acc[4 * k] += wgt * v[u][k].x;
+        acc[4 * k + 1] += wgt * v[u][k].y;
+        acc[4 * k + 2] += wgt * v[u][k].z;
+        acc[4 * k + 3] += wgt * v[u][k].w;
       }
     }
+    M = mn;
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   uint32_t* dst = reinterpret_cast<uint32_t*>(O + qo_row * D + c0);
