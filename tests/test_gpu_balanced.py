@@ -92,7 +92,8 @@ def _plan_tiles(w):
 
 
 def _model_cuts(w, T, lens, slots):
-    """The plan's pieces per tile (plan order), from its description: work
+    """The plan's cut tiles, pieces per tile (plan order) and jobs per slot,
+    from its description: work
     w_i = table entries up to the last block tile i's rows may see (at least
     1); A = max(ceil(sum / slots), 32), or the longest walk when that is
     within 2 job costs (12 units each) of it, and then nothing is cut; tile i
@@ -118,7 +119,8 @@ def _model_cuts(w, T, lens, slots):
     assert n <= slots
     A = max(-(-int(work.sum()) // slots), BAL_MIN_SHARE)
     if int(work.max()) <= A + 2 * JOB_COST:
-        return np.zeros(n, bool), np.ones(n, np.int64)
+        return np.zeros(n, bool), np.ones(n, np.int64), np.array([1 if s < n else 0
+                                                                  for s in range(slots)])
     heads = lambda: np.array([int(x) if x - A < max(A // 8, 2 * JOB_COST) else A for x in work])
     reserve = JOB_COST
     for rnd in range(7):
@@ -147,7 +149,7 @@ def _model_cuts(w, T, lens, slots):
                 pieces[i] += 1
                 jobs[s] += 1
     assert jobs.max() <= 11
-    return pieces > 1, pieces
+    return pieces > 1, pieces, jobs
 
 
 def _check_cuts(ws, w, T, lens):
@@ -156,24 +158,25 @@ def _check_cuts(ws, w, T, lens):
     slots = min(torch.cuda.get_device_properties(0).multi_processor_count, PLAN_MAX_SLOTS)
     pre = _part_numbering(ws, w)
     got = np.diff(pre)
-    want_cut, pieces = _model_cuts(w, T, lens, slots)
+    want_cut, pieces, jobs = _model_cuts(w, T, lens, slots)
     want = np.where(want_cut, pieces, 0)
     assert pre[0] == 0 and np.array_equal(got, want), (np.nonzero(got != want)[0][:10], got[:16],
                                                        want[:16])
-    return pieces
+    return pieces, jobs
 
 
 SHAPES = [
-    # B, H_q, H_kv, D, prior, chunk, C_max, per-group densities
-    (1, 8, 2, 128, [4096], [512], 512, [1.0, 0.05]),
-    (2, 16, 4, 128, [4096, 1024], [512, 256], 512, [1.0, 0.05, 0.3, 0.0]),
-    (3, 8, 1, 64, [1920, 0, 4096], [384, 256, 192], 448, [0.2]),
-    (2, 4, 4, 64, [6144, 640], [128, 64], 192, [0.5, 0.0, 1.0, 0.02]),
+    # B, H_q, H_kv, D, prior, chunk, C_max, per-group densities, whether some slot runs a
+    # third job (the jobs past the second run in a loop, compiled apart from the first two)
+    (1, 8, 2, 128, [4096], [512], 512, [1.0, 0.05], False),
+    (2, 16, 4, 128, [4096, 1024], [512, 256], 512, [1.0, 0.05, 0.3, 0.0], True),
+    (3, 8, 1, 64, [1920, 0, 4096], [384, 256, 192], 448, [0.2], True),
+    (2, 4, 4, 64, [6144, 640], [128, 64], 192, [0.5, 0.0, 1.0, 0.02], True),
 ]
 
 
-@pytest.mark.parametrize("B,H_q,H_kv,D,prior,chunk,C_max,dens", SHAPES)
-def test_balanced_small_full_parity(B, H_q, H_kv, D, prior, chunk, C_max, dens):
+@pytest.mark.parametrize("B,H_q,H_kv,D,prior,chunk,C_max,dens,third_job", SHAPES)
+def test_balanced_small_full_parity(B, H_q, H_kv, D, prior, chunk, C_max, dens, third_job):
     w = gen.make_custom(B, H_q, H_kv, D, prior, chunk, "bf16", 300 + sum(prior) % 97,
                         _by_group(dens, H_q // H_kv), C_max=C_max, name="balanced_small")
     say(f"balanced small B={B} H={H_q}/{H_kv} D={D} prior={prior} chunk={chunk} dens={dens}")
@@ -182,9 +185,11 @@ def test_balanced_small_full_parity(B, H_q, H_kv, D, prior, chunk, C_max, dens):
     ws = _workspace(w)
     O, lse = _balanced(d, T, lens, ws)
     torch.cuda.synchronize()
-    pieces = _check_cuts(ws, w, T, lens)
-    say(f"  tiles {pieces.size}, pieces {int(pieces.sum())}, cut tiles {int((pieces > 1).sum())}")
+    pieces, jobs = _check_cuts(ws, w, T, lens)
+    say(f"  tiles {pieces.size}, pieces {int(pieces.sum())}, cut tiles {int((pieces > 1).sum())}, "
+        f"jobs per slot up to {int(jobs.max())}")
     assert (pieces > 1).any()  # small grids: tiles are cut to fill the compute units
+    assert (jobs.max() >= 3) == third_job
     Or, lr = oracle_full(w)
     compare_bf16(to_np(O), Or, "O")
     live = np.isfinite(lr)
@@ -210,7 +215,7 @@ def test_balanced_equals_plain_when_even():
     Ob, lb = _balanced(d, T, lens, ws)
     Op, lp = d.attention(T, lens, return_lse=True)
     torch.cuda.synchronize()
-    pieces = _check_cuts(ws, w, T, lens)
+    pieces, _ = _check_cuts(ws, w, T, lens)
     assert np.all(pieces == 1)
     assert torch.equal(Ob, Op)
     assert torch.equal(lb, lp)
@@ -227,7 +232,7 @@ def test_balanced_tp_shard_128k_sampled(variant):
     ws = _workspace(w)
     O, lse = _balanced(d, T, lens, ws)
     torch.cuda.synchronize()
-    pieces = _check_cuts(ws, w, T, lens)
+    pieces, _ = _check_cuts(ws, w, T, lens)
     say(f"  pieces per tile {sorted(set(pieces.tolist()))}")
     assert pieces.min() > 1
     rows = sample_rows(w, seed=zlib.crc32(variant.encode()) % 1000, heads_per_group=4, extra=16)
@@ -236,6 +241,27 @@ def test_balanced_tp_shard_128k_sampled(variant):
     compare_bf16(to_np(O[r[:, 0], r[:, 1], r[:, 2]]), Or, f"{len(rows)} sampled rows")
     check_lse(to_np(lse[r[:, 0], r[:, 1], r[:, 2]]), lr)
     assert bool(torch.isfinite(O).all())
+
+
+def test_balanced_groupshared_128k_sampled():
+    # the 128K chunk with one mask per KV group: group tables of 119-172 blocks, so the
+    # longest groups' tiles are cut and slots run up to four jobs (the loop past the first
+    # two included); the part numbering matches the model, sampled rows match the oracle
+    w = gen.make_workload("llama8b_128k", variant="groupshared")
+    say("balanced groupshared 128K")
+    d = Dev(w)
+    T, lens = d.tables()
+    ws = _workspace(w)
+    O, lse = _balanced(d, T, lens, ws)
+    torch.cuda.synchronize()
+    pieces, jobs = _check_cuts(ws, w, T, lens)
+    say(f"  cut tiles {int((pieces > 1).sum())}, jobs per slot up to {int(jobs.max())}")
+    assert (pieces > 1).any() and jobs.max() >= 3
+    rows = sample_rows(w, seed=101, heads_per_group=4, extra=8)
+    Or, lr = oracle_rows(w, rows)
+    r = torch.from_numpy(rows).cuda()
+    compare_bf16(to_np(O[r[:, 0], r[:, 1], r[:, 2]]), Or, f"{len(rows)} sampled rows")
+    check_lse(to_np(lse[r[:, 0], r[:, 1], r[:, 2]]), lr)
 
 
 def test_balanced_poison_and_workspace_reuse():
