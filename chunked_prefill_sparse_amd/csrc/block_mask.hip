@@ -1,7 +1,7 @@
 // A lightweight block-mask producer on gfx950 (the step upstream of the
 // union).  CompactAttention, "Methodology" (selection stage) and the problem
 // statement of the technical summaries: the union takes a per-head 2D block
-// mask from any lightweight pattern search, and that search runs again over
+// mask from whatever cheap searcher the caller uses, and that search runs again over
 // the growing KV cache at every chunk, so its cost matters.  The pages leave
 // the searcher open; this one is training-free:
 //

@@ -7,7 +7,10 @@ lightweight search makes the per-head block mask over the cache so far, the
 union turns it into per-group tables, and zero-copy attention runs the
 chunk's queries over the selected blocks.  Every step is a call into the HIP
 library; this class only keeps the per-prompt buffers (allocated once, reused
-by every chunk) and issues the calls in order on one stream.
+by every chunk) and issues the calls, in order on one stream or, with
+``run(..., overlap=True)``, on two streams so that the next chunk's append and
+selection fill the compute units that the current chunk's attention leaves
+idle near its end.
 """
 from __future__ import annotations
 
@@ -55,6 +58,11 @@ class ChunkedPrefill:
         self.mask = torch.empty((B, H_q, self.NQ, self.NKB), dtype=torch.uint8, device=dev)
         self.T = torch.empty((B, H_kv, self.NKB), dtype=torch.int32, device=dev)
         self.lens = torch.empty((B, H_kv), dtype=torch.int32, device=dev)
+        # table sets for the overlapped run: chunk i uses tables[i % 3], so a
+        # selection running ahead never writes the tables an attention still reads
+        self.tables = ((self.T, self.lens),) + tuple(
+            (torch.empty_like(self.T), torch.empty_like(self.lens)) for _ in range(2))
+        self._side = None
         self.T_dense = torch.arange(self.NKB, dtype=torch.int32, device=dev).repeat(B * H_kv, 1) \
             .view(B, H_kv, self.NKB)
         self.out = torch.empty((B, H_q, C, D), dtype=k_cache.dtype, device=dev)
@@ -71,13 +79,14 @@ class ChunkedPrefill:
         append_kv(k_chunk, v_chunk, self.k, self.v, [prior] * self.B, [self.C] * self.B,
                   stream=stream)
 
-    def select(self, q_chunk: torch.Tensor, prior: int, stream=None) -> None:
+    def select(self, q_chunk: torch.Tensor, prior: int, stream=None, tables=None) -> None:
         """Pool the chunk's new key blocks and its queries, make the mask and
-        build the union tables (into self.mask / self.T / self.lens): the fused
-        ``ca_select_chunk``, four launches."""
+        build the union tables (into self.mask and ``tables``, default
+        (self.T, self.lens)): the fused ``ca_select_chunk``, four launches."""
         B, C = self.B, self.C
+        T, lens = tables if tables is not None else (self.T, self.lens)
         select_chunk(q_chunk, self.k, [prior] * B, [C] * B, self.budget, self.local, self.qbar,
-                     self.kbar, self.scores, self.mask, self.T, self.lens, stream=stream)
+                     self.kbar, self.scores, self.mask, T, lens, stream=stream)
 
     def select_separate(self, q_chunk: torch.Tensor, prior: int, stream=None) -> None:
         """The same selection as ``select`` through the separate calls (six
@@ -91,9 +100,11 @@ class ChunkedPrefill:
         build_union_tables(self.mask, self.H_kv, [self.NQ] * B, [n_blk] * B, T=self.T,
                            lens=self.lens, stream=stream)
 
-    def attend(self, q_chunk: torch.Tensor, prior: int, out=None, stream=None) -> torch.Tensor:
+    def attend(self, q_chunk: torch.Tensor, prior: int, out=None, stream=None,
+               tables=None) -> torch.Tensor:
         out = self.out if out is None else out
-        return chunk_attention(q_chunk, self.k, self.v, self.T, self.lens, [prior] * self.B,
+        T, lens = tables if tables is not None else (self.T, self.lens)
+        return chunk_attention(q_chunk, self.k, self.v, T, lens, [prior] * self.B,
                                [self.C] * self.B, self.scale, out=out, stream=stream,
                                balanced=self.balanced, workspace=self.ws)
 
@@ -105,8 +116,72 @@ class ChunkedPrefill:
         self.select(q_chunk, prior, stream)
         return self.attend(q_chunk, prior, out, stream)
 
+    def run(self, q_chunks, priors, outs=None, kv_chunks=None, overlap: bool = True) -> None:
+        """A sequence of chunks (``outs[i]``, ``kv_chunks[i]`` as in ``capture``).
+
+        overlap=False issues ``step`` for each chunk on the current stream.
+        overlap=True issues the attention on the current stream and each
+        chunk's append and selection on a second stream (default priority),
+        ahead of the attention: chunk i+1's append, pooling, mask and tables
+        run while earlier chunks attend, and take the compute units the
+        attention's workgroups leave as they finish.  Events order the two
+        streams:
+        - chunk i's attention waits for chunk i's selection;
+        - chunk i's selection writes tables[i % 3], so it waits for chunk
+          i-3's attention, the last reader of that set (the selections may
+          run up to two chunks ahead);
+        - the appends write cache rows [prior, prior + C), which no earlier
+          chunk's attention reads (its keys end at its own prior + C);
+        - the pooled keys, queries, scores and mask are used by the selections
+          alone, which stay in order on the second stream.
+        The current stream waits for the second one at the end.  Every kernel
+        gets the same inputs as in the sequential order, so the outputs are
+        the same, bit for bit."""
+        n = len(q_chunks)
+        if outs is not None and len(outs) != n:
+            raise ValueError("outs must give one output per chunk")
+        if len(priors) != n:
+            raise ValueError("priors must give one offset per chunk")
+        if kv_chunks is not None and len(kv_chunks) != n:
+            raise ValueError("kv_chunks must give one (k, v) pair per chunk")
+        if not overlap:
+            for i in range(n):
+                kc, vc = kv_chunks[i] if kv_chunks is not None else (None, None)
+                self.step(q_chunks[i], priors[i], out=outs[i] if outs is not None else None,
+                          k_chunk=kc, v_chunk=vc)
+            return
+        main = torch.cuda.current_stream(self.k.device)
+        if self._side is None:
+            self._side = torch.cuda.Stream(device=self.k.device)
+        side = self._side
+        selected = [torch.cuda.Event() for _ in range(n)]
+        attended = [torch.cuda.Event() for _ in range(n)]
+        side.wait_stream(main)  # inputs written on the current stream come first
+
+        depth = len(self.tables)
+
+        def issue_select(i):
+            if kv_chunks is not None:
+                self.append(kv_chunks[i][0], kv_chunks[i][1], priors[i], stream=side)
+            if i >= depth:
+                side.wait_event(attended[i - depth])
+            self.select(q_chunks[i], priors[i], stream=side, tables=self.tables[i % depth])
+            selected[i].record(side)
+
+        if n > 0:
+            issue_select(0)
+        for i in range(n):
+            main.wait_event(selected[i])
+            self.attend(q_chunks[i], priors[i], out=outs[i] if outs is not None else None,
+                        stream=main, tables=self.tables[i % depth])
+            attended[i].record(main)
+            if i + 1 < n:
+                issue_select(i + 1)
+        main.wait_stream(side)
+
     def capture(self, q_chunks, priors, outs=None, dense: bool = False,
-                select_only: bool = False, kv_chunks=None) -> torch.cuda.CUDAGraph:
+                select_only: bool = False, kv_chunks=None,
+                overlap: bool = False) -> torch.cuda.CUDAGraph:
         """Record ``step`` (or ``step_dense``, or only ``select``) for a
         sequence of chunks into one HIP graph; ``replay()`` then reissues every
         kernel with the same arguments and buffers, without the per-call host
@@ -115,29 +190,39 @@ class ChunkedPrefill:
         (k_chunk, v_chunk) makes chunk i append its keys and values first.
         The library records no memset, copy, allocation or synchronisation, so
         the whole call sequence can be captured; inputs must stay at the same
-        addresses between replays."""
+        addresses between replays.  overlap=True records ``run(...,
+        overlap=True)``: the two streams become two branches of the graph,
+        joined by the same event edges."""
         if outs is not None and len(outs) != len(q_chunks):
             raise ValueError("outs must give one output per chunk")
         if len(priors) != len(q_chunks):
             raise ValueError("priors must give one offset per chunk")
         if kv_chunks is not None and len(kv_chunks) != len(q_chunks):
             raise ValueError("kv_chunks must give one (k, v) pair per chunk")
+        if overlap and (dense or select_only):
+            raise ValueError("overlap records the sparse steps only")
         lens = [self.dense_lens(p) for p in priors] if dense else None
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for i, (q, p) in enumerate(zip(q_chunks, priors)):
-                o = outs[i] if outs is not None else None
-                kc, vc = kv_chunks[i] if kv_chunks is not None else (None, None)
-                if select_only:
-                    if kc is not None:
-                        self.append(kc, vc, p)
-                    self.select(q, p)
-                elif dense:
-                    self.step_dense(q, p, lens[i], out=o, k_chunk=kc, v_chunk=vc)
-                else:
-                    self.step(q, p, out=o, k_chunk=kc, v_chunk=vc)
+            if overlap:
+                self.run(q_chunks, priors, outs=outs, kv_chunks=kv_chunks, overlap=True)
+            else:
+                self._record_steps(q_chunks, priors, outs, kv_chunks, lens, select_only)
         g.ca_dense_lens = lens  # device buffers the graph reads: keep them alive
         return g
+
+    def _record_steps(self, q_chunks, priors, outs, kv_chunks, lens, select_only):
+        for i, (q, p) in enumerate(zip(q_chunks, priors)):
+            o = outs[i] if outs is not None else None
+            kc, vc = kv_chunks[i] if kv_chunks is not None else (None, None)
+            if select_only:
+                if kc is not None:
+                    self.append(kc, vc, p)
+                self.select(q, p)
+            elif lens is not None:
+                self.step_dense(q, p, lens[i], out=o, k_chunk=kc, v_chunk=vc)
+            else:
+                self.step(q, p, out=o, k_chunk=kc, v_chunk=vc)
 
     def dense_lens(self, prior: int) -> torch.Tensor:
         n = (prior + self.C) // CA_BLOCK

@@ -2,7 +2,7 @@
 
 CompactAttention, "Methodology" (selection stage) and the problem statement
 of the technical summaries: the union consumes a per-head 2D block mask made
-by any lightweight pattern search, and that search is repeated over the
+by whatever cheap searcher the caller uses, and that search is repeated over the
 growing KV cache at every chunk.  The pages leave the searcher open (they name
 trained and training-free ones from other work).  The stand-in here is a
 training-free one whose result has a plain definition:

@@ -104,6 +104,53 @@ def test_prefill_graph_replay_matches_eager(balanced):
         assert torch.equal(drv.T, eager_T) and torch.equal(drv.lens, eager_lens)
 
 
+@pytest.mark.parametrize("balanced", [False, True])
+def test_prefill_overlap_matches_sequential(balanced):
+    # run(overlap=True): each chunk's append and selection on a second stream, one
+    # chunk ahead of the attention, into caches that hold NaN past the appended rows.
+    # Every chunk's output equals the sequential steps' over the resident prompt, bit
+    # for bit, eagerly and from a graph of the two streams replayed three times with
+    # eager work in between; the caches end up equal to the prompt.
+    s = gen.make_prefill_stream("prefill_small")
+    k_full, v_full = s.k.cuda(), s.v.cuda()
+    ref = ChunkedPrefill(k_full, v_full, s.H_q, s.C, budget=4, local=2)
+    qs = [s.q_chunk(c).cuda() for c in range(s.n_chunks)]
+    priors = [c * s.C for c in range(s.n_chunks)]
+    want = [ref.step(q, p).clone() for q, p in zip(qs, priors)]
+    kv = [(k_full[:, :, p:p + s.C].contiguous(), v_full[:, :, p:p + s.C].contiguous())
+          for p in priors]
+    kc = torch.full_like(k_full, float("nan"))
+    vc = torch.full_like(v_full, float("nan"))
+    drv = ChunkedPrefill(kc, vc, s.H_q, s.C, budget=4, local=2, balanced=balanced)
+    outs = [torch.full_like(qs[0], float("nan")) for _ in qs]
+    torch.cuda.synchronize()
+    say(f"overlapped prefill_small, eager, balanced={balanced}")
+    drv.run(qs, priors, outs=outs, kv_chunks=kv, overlap=True)
+    torch.cuda.synchronize()
+    for c in range(s.n_chunks):
+        assert torch.equal(outs[c], want[c]), c
+    last = drv.tables[(s.n_chunks - 1) % len(drv.tables)]
+    assert torch.equal(last[0], ref.T) and torch.equal(last[1], ref.lens)
+    assert torch.equal(kc, k_full) and torch.equal(vc, v_full)
+    kc.fill_(float("nan"))
+    vc.fill_(float("nan"))
+    g = drv.capture(qs, priors, outs=outs, kv_chunks=kv, overlap=True)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say(f"overlapped graph replay {rep}")
+        for o in outs:
+            o.fill_(float("nan"))
+        kc.fill_(float("nan"))
+        vc.fill_(float("nan"))
+        drv.run(qs[:1], priors[:1], kv_chunks=kv[:1], overlap=False)  # eager work between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for c in range(s.n_chunks):
+            assert torch.equal(outs[c], want[c]), (rep, c)
+        assert torch.equal(kc, k_full) and torch.equal(vc, v_full)
+
+
 def test_prefill_small_append_from_poisoned_cache():
     # Each chunk's keys and values are appended at its step into caches that hold
     # NaN everywhere else: every chunk's mask, tables and outputs (sparse and dense)
