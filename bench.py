@@ -503,7 +503,7 @@ def tp_shard_leg(stream, reps):
 # --------------------------------------------------------------------------- whole prefill
 
 
-def prefill_leg(stream, budget=32, local=8):
+def prefill_leg(stream, budget=32, local=8, overlap=True):
     """A 128K prompt in 64 chunks of 2048 (planted-structure synthetic stream):
     per chunk, append its keys and values to the cache, pool the new key
     blocks and the queries, make the top-k block mask, build the union tables
@@ -511,7 +511,10 @@ def prefill_leg(stream, budget=32, local=8):
     reference); the dense baseline appends and runs the same attention over
     every block.  The caches start empty.  Cumulative times from HIP events on
     the launch stream, for the Python loop of calls and for the same calls
-    recorded into HIP graphs and replayed."""
+    recorded into HIP graphs and replayed; with overlap, also for the run that
+    issues each chunk's append and selection on a second stream ahead of the
+    attention (left out of kernel traces, whose per-kernel durations assume
+    kernels that do not run side by side)."""
     import torch
     import gen
     from chunked_prefill_sparse_amd.prefill import ChunkedPrefill
@@ -574,7 +577,7 @@ def prefill_leg(stream, budget=32, local=8):
         for c in range(s.n_chunks):
             drv_bal.step(qs[c], priors[c], k_chunk=kv[c][0], v_chunk=kv[c][1])
 
-    def run_overlap():  # each chunk's append and selection on a second stream, one ahead
+    def run_overlap():  # each chunk's append and selection on a second stream, ahead
         drv.run(qs, priors, kv_chunks=kv, overlap=True)
 
     def run_overlap_balanced():
@@ -591,10 +594,11 @@ def prefill_leg(stream, budget=32, local=8):
     attn_ms = sparse_ms - select_ms - append_ms
     run_balanced()
     bal_ms = statistics.median(timed(run_balanced) for _ in range(reps))
-    run_overlap()
-    run_overlap_balanced()
-    ov_ms = statistics.median(timed(run_overlap) for _ in range(reps))
-    ovb_ms = statistics.median(timed(run_overlap_balanced) for _ in range(reps))
+    if overlap:
+        run_overlap()
+        run_overlap_balanced()
+        ov_ms = statistics.median(timed(run_overlap) for _ in range(reps))
+        ovb_ms = statistics.median(timed(run_overlap_balanced) for _ in range(reps))
     # the same call sequences recorded once into HIP graphs and replayed: the
     # GPU time without the per-call host work of the loop above
     g_sparse = drv.capture(qs, priors, kv_chunks=kv)
@@ -604,20 +608,22 @@ def prefill_leg(stream, budget=32, local=8):
         run_select_separate()
     g_dense = drv.capture(qs, priors, dense=True, kv_chunks=kv)
     g_bal = drv_bal.capture(qs, priors, kv_chunks=kv)
-    g_ov = drv.capture(qs, priors, kv_chunks=kv, overlap=True)
-    g_ovb = drv_bal.capture(qs, priors, kv_chunks=kv, overlap=True)
+    g_ov = drv.capture(qs, priors, kv_chunks=kv, overlap=True) if overlap else None
+    g_ovb = drv_bal.capture(qs, priors, kv_chunks=kv, overlap=True) if overlap else None
     g_sparse.replay()
     g_dense.replay()
     g_bal.replay()
-    g_ov.replay()
-    g_ovb.replay()
+    if overlap:
+        g_ov.replay()
+        g_ovb.replay()
     gs_ms = statistics.median(timed(g_sparse.replay) for _ in range(reps))
     gb_ms = statistics.median(timed(g_bal.replay) for _ in range(reps))
     gsel_ms = statistics.median(timed(g_select.replay) for _ in range(reps))
     gsel_sep_ms = statistics.median(timed(g_select_sep.replay) for _ in range(reps))
     gd_ms = statistics.median(timed(g_dense.replay) for _ in range(reps))
-    gov_ms = statistics.median(timed(g_ov.replay) for _ in range(reps))
-    govb_ms = statistics.median(timed(g_ovb.replay) for _ in range(reps))
+    if overlap:
+        gov_ms = statistics.median(timed(g_ov.replay) for _ in range(reps))
+        govb_ms = statistics.median(timed(g_ovb.replay) for _ in range(reps))
     moved = 2 * 2 * s.n_chunks * s.H_kv * s.C * s.D * 2  # K and V, read once and written once
     r = dict(
         chunks=s.n_chunks, chunk=s.C, prompt=s.L, budget_blocks=budget, local_blocks=local,
@@ -641,13 +647,13 @@ def prefill_leg(stream, budget=32, local=8):
                    dense_total_ms=round(gd_ms, 3), x_vs_dense=round(gd_ms / gs_ms, 3),
                    balanced_total_ms=round(gb_ms, 3),
                    balanced_x_vs_dense=round(gd_ms / gb_ms, 3)),
-        # append + selection of chunk i+1 on a second stream while chunk i attends
+        # append + selection on a second stream, ahead of the attention
         overlap=dict(total_ms=round(ov_ms, 3), x_vs_dense=round(dense_ms / ov_ms, 3),
                      balanced_total_ms=round(ovb_ms, 3),
                      balanced_x_vs_dense=round(dense_ms / ovb_ms, 3),
                      graph_total_ms=round(gov_ms, 3), graph_x_vs_dense=round(gd_ms / gov_ms, 3),
                      graph_balanced_total_ms=round(govb_ms, 3),
-                     graph_balanced_x_vs_dense=round(gd_ms / govb_ms, 3)),
+                     graph_balanced_x_vs_dense=round(gd_ms / govb_ms, 3)) if overlap else None,
         data=("synthetic planted-structure stream: K, V, Q ~ N(0,1), 3% salient KV blocks per "
               "KV head shifted along a per-head direction that the group's queries share; the "
               "caches start empty and each chunk appends its own K/V"),
@@ -659,10 +665,11 @@ def prefill_leg(stream, budget=32, local=8):
     log(f"prefill_128k as HIP graphs: total {gs_ms:.2f} ms (select {gsel_ms:.2f}, through the "
         f"separate calls {gsel_sep_ms:.2f}) vs dense {gd_ms:.2f} ms -> x{gd_ms / gs_ms:.2f}; "
         f"with balanced attention {gb_ms:.2f} ms -> x{gd_ms / gb_ms:.2f}")
-    log(f"prefill_128k overlapped (append + selection one chunk ahead on a second stream): "
-        f"{ov_ms:.2f} ms -> x{dense_ms / ov_ms:.2f}, balanced {ovb_ms:.2f} ms; as graphs "
-        f"{gov_ms:.2f} ms -> x{gd_ms / gov_ms:.2f}, balanced {govb_ms:.2f} ms -> "
-        f"x{gd_ms / govb_ms:.2f}")
+    if overlap:
+        log(f"prefill_128k overlapped (append + selection ahead, on a second stream): "
+            f"{ov_ms:.2f} ms -> x{dense_ms / ov_ms:.2f}, balanced {ovb_ms:.2f} ms; as graphs "
+            f"{gov_ms:.2f} ms -> x{gd_ms / gov_ms:.2f}, balanced {govb_ms:.2f} ms -> "
+            f"x{gd_ms / govb_ms:.2f}")
     del qs, k, v, kv, drv, drv_bal, g_sparse, g_select, g_select_sep, g_dense, g_bal, g_ov, g_ovb
     torch.cuda.empty_cache()
     return r
@@ -758,7 +765,7 @@ def main():
         return
 
     if args.profile == "prefill":
-        prefill_leg(stream)
+        prefill_leg(stream, overlap=False)
         return
 
     log(f"generating {WORKLOAD} (pairwise mask) ...")
