@@ -725,6 +725,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-prefill", action="store_true", help="skip the 64-chunk prefill leg")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the 64-chunk prefill leg and print its JSON object")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the leg that measures every config (1-5)")
     ap.add_argument("--config-oracle-seconds", type=float, default=120.0,
@@ -766,6 +768,9 @@ def main():
 
     if args.profile == "prefill":
         prefill_leg(stream, overlap=False)
+        return
+    if args.prefill_only:
+        print(json.dumps(prefill_leg(stream)))
         return
 
     log(f"generating {WORKLOAD} (pairwise mask) ...")
