@@ -173,5 +173,56 @@ def compare_bf16(got, ref, what=""):
     return mx, mean
 
 
+# Unit roundoff of bf16: 8 significant bits, round to nearest even, so a rounded
+# value moves by at most 2^-8 of itself.
+U_BF16 = 2.0 ** -8
+
+
+def oracle_full_absv(w):
+    """The oracle's attention of |V| (same rows, tables and weights): for each
+    output element, sum_t softmax(x)_t |V[t, d]|."""
+    T, ln = oracle_tables(w)
+    q, k, v = f32_arrays(w)
+    return chunk_attention_ref(q, k, np.abs(v), T, ln, w.prior, w.chunk, w.scale)[0]
+
+
+def check_bf16_rounding(got, ref, ref_absv, lse_ref, what=""):
+    """Per-element bound of the bf16 path's roundings (every output element).
+
+    The kernel forms p_t = exp(x_t - m) in fp32, rounds it to bf16 for the P.V
+    product (p~_t = p_t (1 + r_t), |r_t| <= u = 2^-8), divides by the fp32 sum of
+    the unrounded p_t and rounds O to bf16.  Against the exact result
+    O* = sum_t p*_t v_t / sum_t p*_t that gives
+
+      |O - O*| <= u |sum_t p_t r_t v_t| / l                 (P rounding)
+                + u |O|                                      (output rounding)
+                + 2 delta sum_t p_t |v_t| / l                (logit errors)
+                <= u (A|V| + |O*|)(1 + 2^-7) + 2 delta A|V| + 1e-6,
+
+    with A|V| = sum_t softmax(x)_t |v_t| (the oracle run on |V|, ``ref_absv``)
+    and delta the logit error per key, taken at the row's lse bound
+    (3e-5 + 2^-20 |lse|: both come from the fp32 score accumulation, which
+    grows with the largest logits).  The fp32 accumulations of P.V and of the
+    denominator add a few 2^-24 relative, inside the slack.  A worst case of
+    the P rounding needs every r_t at u with the sign of v_t; it is what lets
+    one dominant key with |v| near 5 reach about 2e-2.  Returns the largest
+    ratio of error to bound."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    absv = np.asarray(ref_absv, np.float64)
+    lse_ref = np.asarray(lse_ref, np.float64)
+    delta = np.where(np.isfinite(lse_ref), LSE_ABS + LSE_REL * np.abs(lse_ref), 0.0)[..., None]
+    bound = U_BF16 * (absv + np.abs(ref)) * (1 + 2.0 ** -7) + 2 * delta * absv + 1e-6
+    err = np.abs(got - ref)
+    ratio = err / bound
+    worst = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    r = float(ratio[worst])
+    say(f"  {what}: rounding-model bound, worst element at {tuple(int(x) for x in worst)}: "
+        f"error {float(err[worst]):.3e}, bound {float(bound[worst]):.3e} ({r:.3f} of it); "
+        f"median ratio {float(np.median(ratio)):.3f}")
+    assert r <= 1.0, f"{what}: error {float(err[worst])} beyond the rounding bound {float(bound[worst])}"
+    return r
+
+
 def to_np(t: torch.Tensor) -> np.ndarray:
     return gen.tensor_to_f32(t.detach().cpu())

@@ -21,7 +21,8 @@ import torch
 
 import gen
 import chunked_prefill_sparse_amd as ca
-from tests.gpu_util import (BF16_MAX_ABS, F32_MAX_ABS, Dev, check_lse, compare_bf16,
+from tests.gpu_util import (BF16_MAX_ABS, F32_MAX_ABS, Dev, check_bf16_rounding, check_lse,
+                            compare_bf16, oracle_full_absv,
                             f32_arrays, oracle_full, oracle_full_parallel, oracle_rows,
                             sample_rows, say, to_np)
 
@@ -90,6 +91,7 @@ def test_bf16_small_full_parity(B, H_q, H_kv, D, prior, chunk, C_max):
     _, _, _, (O, lse) = _run(w)
     Or, lr = oracle_full(w)
     compare_bf16(to_np(O), Or, "O")
+    check_bf16_rounding(to_np(O), Or, oracle_full_absv(w), lr, "O")
     live = np.isfinite(lr)
     assert np.array_equal(np.isfinite(to_np(lse)), live)
     check_lse(to_np(lse)[live], lr[live])
@@ -218,6 +220,10 @@ def test_full_size_whole_output_parity(name, kw):
     Or, lr = oracle_full_parallel(w, arrays=w.meta["arrays"])
     compare_bf16(to_np(O), Or, f"all {w.B * w.H_q * w.C_max} rows")
     check_lse(to_np(lse), lr)
+    if name == "llama8b_32k":  # every element against the rounding model (oracle on |V|)
+        q, k, v = w.meta["arrays"]
+        absv, _ = oracle_full_parallel(w, arrays=(q, k, np.abs(v)))
+        check_bf16_rounding(to_np(O), Or, absv, lr, "all rows")
     _whole_output_properties(w, d, O)
 
 
@@ -335,6 +341,7 @@ def test_bf16_running_max_moves(D, growth):
     _, _, _, (O, lse) = _run(w)
     Or, lr = oracle_full(w)
     compare_bf16(to_np(O), Or, "O")
+    check_bf16_rounding(to_np(O), Or, oracle_full_absv(w), lr, "O")
     live = np.isfinite(lr)
     check_lse(to_np(lse)[live], lr[live])
 
@@ -357,6 +364,7 @@ def test_bf16_logit_spikes(D):
     _, _, _, (O, lse) = _run(w)
     Or, lr = oracle_full(w)
     compare_bf16(to_np(O), Or, "O")
+    check_bf16_rounding(to_np(O), Or, oracle_full_absv(w), lr, "O")
     live = np.isfinite(lr)
     check_lse(to_np(lse)[live], lr[live])
 

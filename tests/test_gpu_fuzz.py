@@ -11,7 +11,8 @@ import torch
 import gen
 import chunked_prefill_sparse_amd as ca
 from oracle import sparse_attention_ref
-from tests.gpu_util import (F32_MAX_ABS, check_lse, Dev, compare_bf16, oracle_full, oracle_tables,
+from tests.gpu_util import (F32_MAX_ABS, check_bf16_rounding, check_lse, Dev, compare_bf16,
+                            oracle_full, oracle_full_absv, oracle_tables,
                             say, to_np)
 
 pytestmark = pytest.mark.gpu
@@ -39,9 +40,11 @@ def _case(seed):
     return w, n_split
 
 
-def _compare(w, O, lse, Or, lr, what):
+def _compare(w, O, lse, Or, lr, what, absv=None):
     if w.dtype == "bf16":
         compare_bf16(to_np(O), Or, what)
+        if absv is not None:
+            check_bf16_rounding(to_np(O), Or, absv, lr, what)
     else:
         err = float(np.abs(to_np(O) - Or).max())
         assert err <= F32_MAX_ABS, (what, err)
@@ -69,9 +72,10 @@ def test_fuzz_shapes_all_entry_points(seed):
     Ob, lseb = ca.chunk_attention(d.q, d.k, d.v, T, lens, w.prior, w.chunk, w.scale,
                                   return_lse=True, balanced=True)
     torch.cuda.synchronize()
-    _compare(w, O, lse, Or, lr, "union")
-    _compare(w, Os, lses, Or, lr, f"union, {n_split} splits")
-    _compare(w, Ob, lseb, Or, lr, "union, balanced")
+    absv = oracle_full_absv(w) if w.dtype == "bf16" else None
+    _compare(w, O, lse, Or, lr, "union", absv)
+    _compare(w, Os, lses, Or, lr, f"union, {n_split} splits", absv)
+    _compare(w, Ob, lseb, Or, lr, "union, balanced", absv)
     # block-sparse execution of the same mask (per-(head, Q-block) lists)
     Trw, lrw = ca.build_row_tables(d.mask, w.n_kv_blocks)
     Orw, lserw = ca.chunk_attention_rows(d.q, d.k, d.v, Trw, lrw, w.prior, w.chunk, w.scale,
