@@ -565,6 +565,10 @@ def prefill_leg(stream, budget=32, local=8, overlap=True):
         for c in range(s.n_chunks):
             drv.select(qs[c], priors[c])
 
+    def run_append_select():  # the fused call the sparse step issues
+        for c in range(s.n_chunks):
+            drv.append_select(kv[c][0], kv[c][1], qs[c], priors[c])
+
     def run_select_separate():  # the same selection through the six separate launches
         for c in range(s.n_chunks):
             drv.select_separate(qs[c], priors[c])
@@ -590,8 +594,9 @@ def prefill_leg(stream, budget=32, local=8, overlap=True):
     append_ms = statistics.median(timed(run_append) for _ in range(reps))
     select_ms = statistics.median(timed(run_select) for _ in range(reps))
     select_sep_ms = statistics.median(timed(run_select_separate) for _ in range(reps))
+    appsel_ms = statistics.median(timed(run_append_select) for _ in range(reps))
     dense_ms = statistics.median(timed(run_dense) for _ in range(reps))
-    attn_ms = sparse_ms - select_ms - append_ms
+    attn_ms = sparse_ms - appsel_ms
     run_balanced()
     bal_ms = statistics.median(timed(run_balanced) for _ in range(reps))
     if overlap:
@@ -603,6 +608,7 @@ def prefill_leg(stream, budget=32, local=8, overlap=True):
     # GPU time without the per-call host work of the loop above
     g_sparse = drv.capture(qs, priors, kv_chunks=kv)
     g_select = drv.capture(qs, priors, select_only=True)
+    g_appsel = drv.capture(qs, priors, select_only=True, kv_chunks=kv)
     g_select_sep = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_select_sep):
         run_select_separate()
@@ -620,6 +626,7 @@ def prefill_leg(stream, budget=32, local=8, overlap=True):
     gb_ms = statistics.median(timed(g_bal.replay) for _ in range(reps))
     gsel_ms = statistics.median(timed(g_select.replay) for _ in range(reps))
     gsel_sep_ms = statistics.median(timed(g_select_sep.replay) for _ in range(reps))
+    gappsel_ms = statistics.median(timed(g_appsel.replay) for _ in range(reps))
     gd_ms = statistics.median(timed(g_dense.replay) for _ in range(reps))
     if overlap:
         gov_ms = statistics.median(timed(g_ov.replay) for _ in range(reps))
@@ -627,7 +634,8 @@ def prefill_leg(stream, budget=32, local=8, overlap=True):
     moved = 2 * 2 * s.n_chunks * s.H_kv * s.C * s.D * 2  # K and V, read once and written once
     r = dict(
         chunks=s.n_chunks, chunk=s.C, prompt=s.L, budget_blocks=budget, local_blocks=local,
-        total_ms=round(sparse_ms, 3), append_ms=round(append_ms, 3),
+        total_ms=round(sparse_ms, 3), append_select_ms=round(appsel_ms, 3),
+        append_ms=round(append_ms, 3),
         append_GBps=round(moved / (append_ms * 1e-3) / 1e9, 1), select_ms=round(select_ms, 3),
         select_separate_ms=round(select_sep_ms, 3),
         attention_ms=round(attn_ms, 3), dense_total_ms=round(dense_ms, 3),
@@ -638,11 +646,12 @@ def prefill_leg(stream, budget=32, local=8, overlap=True):
         union_block_frac_first_mid_last=[round(frac[0], 3), round(frac[len(frac) // 2], 3),
                                          round(frac[-1], 3)],
         balanced=dict(total_ms=round(bal_ms, 3),
-                      attention_ms=round(bal_ms - select_ms - append_ms, 3),
+                      attention_ms=round(bal_ms - appsel_ms, 3),
                       x_vs_dense=round(dense_ms / bal_ms, 3),
                       attention_eff_tflops=round(
-                          flops / ((bal_ms - select_ms - append_ms) * 1e-3) / 1e12, 1)),
-        graph=dict(total_ms=round(gs_ms, 3), select_ms=round(gsel_ms, 3),
+                          flops / ((bal_ms - appsel_ms) * 1e-3) / 1e12, 1)),
+        graph=dict(total_ms=round(gs_ms, 3), append_select_ms=round(gappsel_ms, 3),
+                   select_ms=round(gsel_ms, 3),
                    select_separate_ms=round(gsel_sep_ms, 3),
                    dense_total_ms=round(gd_ms, 3), x_vs_dense=round(gd_ms / gs_ms, 3),
                    balanced_total_ms=round(gb_ms, 3),
@@ -658,11 +667,13 @@ def prefill_leg(stream, budget=32, local=8, overlap=True):
               "KV head shifted along a per-head direction that the group's queries share; the "
               "caches start empty and each chunk appends its own K/V"),
     )
-    log(f"prefill_128k: total {sparse_ms:.2f} ms (append {append_ms:.2f}, select {select_ms:.2f}, "
-        f"attention {attn_ms:.2f}) vs dense {dense_ms:.2f} ms -> x{dense_ms / sparse_ms:.2f}; "
+    log(f"prefill_128k: total {sparse_ms:.2f} ms (append + select {appsel_ms:.2f}; alone: append "
+        f"{append_ms:.2f}, select {select_ms:.2f}; attention {attn_ms:.2f}) vs dense "
+        f"{dense_ms:.2f} ms -> x{dense_ms / sparse_ms:.2f}; "
         f"union fraction first/mid/last {r['union_block_frac_first_mid_last']}")
     log(f"prefill_128k with balanced attention: total {bal_ms:.2f} ms -> x{dense_ms / bal_ms:.2f}")
-    log(f"prefill_128k as HIP graphs: total {gs_ms:.2f} ms (select {gsel_ms:.2f}, through the "
+    log(f"prefill_128k as HIP graphs: total {gs_ms:.2f} ms (append + select {gappsel_ms:.2f}, "
+        f"select {gsel_ms:.2f}, through the "
         f"separate calls {gsel_sep_ms:.2f}) vs dense {gd_ms:.2f} ms -> x{gd_ms / gs_ms:.2f}; "
         f"with balanced attention {gb_ms:.2f} ms -> x{gd_ms / gb_ms:.2f}")
     if overlap:
@@ -670,7 +681,8 @@ def prefill_leg(stream, budget=32, local=8, overlap=True):
             f"{ov_ms:.2f} ms -> x{dense_ms / ov_ms:.2f}, balanced {ovb_ms:.2f} ms; as graphs "
             f"{gov_ms:.2f} ms -> x{gd_ms / gov_ms:.2f}, balanced {govb_ms:.2f} ms -> "
             f"x{gd_ms / govb_ms:.2f}")
-    del qs, k, v, kv, drv, drv_bal, g_sparse, g_select, g_select_sep, g_dense, g_bal, g_ov, g_ovb
+    del qs, k, v, kv, drv, drv_bal, g_sparse, g_select, g_appsel, g_select_sep, g_dense, g_bal
+    del g_ov, g_ovb
     torch.cuda.empty_cache()
     return r
 

@@ -27,6 +27,7 @@ __all__ = ["build_union_tables", "chunk_attention", "tables_to_csr", "check_tabl
            "stamps_summary",
            "compact_kv", "append_kv",
            "build_row_tables", "chunk_attention_rows", "pool_blocks", "block_mask_topk", "select_chunk",
+           "append_select_chunk",
            "workspace_size", "balanced_workspace_size", "chunk_attention_split_noalloc",
            "CompactAttnError", "library_path"]
 
@@ -593,3 +594,45 @@ def select_chunk(q_chunk: torch.Tensor, k_cache: torch.Tensor, prior_len: Sequen
         int(budget), int(local), qbar.data_ptr(), NQ, kbar.data_ptr(), NKB, scores.data_ptr(),
         mask.data_ptr(), T.data_ptr(), lens.data_ptr(), _stream_ptr(stream))
     _lib.check(st, "ca_select_chunk")
+
+
+def append_select_chunk(k_new: torch.Tensor, v_new: torch.Tensor, q_chunk: torch.Tensor,
+                        k_cache: torch.Tensor, v_cache: torch.Tensor, prior_len: Sequence[int],
+                        chunk_len: Sequence[int], budget: int, local: int, qbar: torch.Tensor,
+                        kbar: torch.Tensor, scores: torch.Tensor, mask: torch.Tensor,
+                        T: torch.Tensor, lens: torch.Tensor,
+                        stream: Optional[torch.cuda.Stream] = None) -> None:
+    """``append_kv`` then ``select_chunk`` in the selection's four launches
+    (``ca_append_select_chunk``): the first launch also writes the chunk's keys
+    and values (k_new, v_new [B, H_kv, C_max, D]) into the caches and pools the
+    new key blocks from them.  Same outputs as the two calls, bit for bit."""
+    _need_cuda("k_new", k_new)
+    if k_new.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("k_new must be bfloat16 or float32")
+    for name, t in (("v_new", v_new), ("q_chunk", q_chunk), ("k_cache", k_cache),
+                    ("v_cache", v_cache)):
+        _need_cuda(name, t, k_new.dtype)
+    for name, t, dt in (("qbar", qbar, torch.float32), ("kbar", kbar, torch.float32),
+                        ("scores", scores, torch.float32), ("mask", mask, torch.uint8),
+                        ("T", T, torch.int32), ("lens", lens, torch.int32)):
+        _need_cuda(name, t, dt)
+    if q_chunk.dim() != 4 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q_chunk must be [B, H_q, C_max, D] and the caches [B, H_kv, L, D]")
+    B, H_q, C_max, D = q_chunk.shape
+    H_kv, L = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_new.shape) != (B, H_kv, C_max, D) or v_new.shape != k_new.shape or \
+            k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("k_new / v_new must be [B, H_kv, C_max, D] of the caches and q_chunk")
+    NQ, NKB = qbar.shape[2], kbar.shape[2]
+    if tuple(qbar.shape) != (B, H_q, NQ, D) or tuple(kbar.shape) != (B, H_kv, NKB, D) or \
+            tuple(scores.shape) != (B, H_q, NQ, NKB) or tuple(mask.shape) != (B, H_q, NQ, NKB) or \
+            tuple(T.shape) != (B, H_kv, NKB) or tuple(lens.shape) != (B, H_kv):
+        raise ValueError("qbar / kbar / scores / mask / T / lens shapes do not match")
+    dt = _lib.CA_BF16 if q_chunk.dtype == torch.bfloat16 else _lib.CA_F32
+    st = _lib.lib().ca_append_select_chunk(
+        k_new.data_ptr(), v_new.data_ptr(), q_chunk.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), dt, B, H_q, H_kv, C_max, L, D,
+        _host_ints("prior_len", prior_len, B), _host_ints("chunk_len", chunk_len, B),
+        int(budget), int(local), qbar.data_ptr(), NQ, kbar.data_ptr(), NKB, scores.data_ptr(),
+        mask.data_ptr(), T.data_ptr(), lens.data_ptr(), _stream_ptr(stream))
+    _lib.check(st, "ca_append_select_chunk")

@@ -39,6 +39,7 @@ EXPORTED = (
     "ca_pool_blocks",
     "ca_block_mask_topk",
     "ca_select_chunk",
+    "ca_append_select_chunk",
     "ca_status_string",
     "ca_last_hip_error",
 )
@@ -113,6 +114,10 @@ def _declare(lib):
                                     _i32p, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp,
                                     _vp]
     lib.ca_select_chunk.restype = _i32
+    lib.ca_append_select_chunk.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                           _i64, _i32, _i32p, _i32p, _i32, _i32, _vp, _i32, _vp,
+                                           _i32, _vp, _vp, _vp, _vp, _vp]
+    lib.ca_append_select_chunk.restype = _i32
     lib.ca_status_string.argtypes = [_i32]
     lib.ca_status_string.restype = ctypes.c_char_p
     lib.ca_last_hip_error.argtypes = []

@@ -31,42 +31,78 @@ constexpr int kTopkLdsMax = 15360;   // rows up to this many blocks stage keys i
 
 // ---------------------------------------------------------------- pooling
 
-// Mean of the 64 rows of one block (src points at its first row, row stride
-// D) into out[0 .. D): each thread sums a 16-byte column slice over every
-// RPI-th row; the RPI partial sums of a column are then added in row-group
-// order.  All of a thread's row loads are in flight before the sums.
+// How the pooling's threads hold one 64-row block (row stride D): thread tid
+// owns the 16-byte column slice (tid % TPR) * V of rows tid / TPR + k * RPI,
+// k < NR, which covers the block once.
 template <typename TIn, int D>
-__device__ __forceinline__ void pool_one_block(const TIn* __restrict__ src,
-                                               float* __restrict__ out, float* part) {
-  constexpr int V = 16 / static_cast<int>(sizeof(TIn));  // elements per 16-byte load
-  constexpr int TPR = D / V;                              // threads per row
-  constexpr int RPI = kMaskThreads / TPR;                 // rows per iteration
+struct PoolShape {
+  static constexpr int V = 16 / static_cast<int>(sizeof(TIn));  // elements per 16-byte load
+  static constexpr int TPR = D / V;                              // threads per row
+  static constexpr int RPI = kMaskThreads / TPR;                 // rows per iteration
+  static constexpr int NR = 64 / RPI;                            // vectors per thread
   static_assert(64 % RPI == 0, "rows of a block split evenly over the row groups");
+};
+
+// This thread's NR vectors of the block at src, all loads in flight together.
+template <typename TIn, int D>
+__device__ __forceinline__ void load_block_vecs(const TIn* __restrict__ src, uint4* raw) {
+  using S = PoolShape<TIn, D>;
   const int tid = threadIdx.x;
-  const int col = (tid % TPR) * V;
-  const int rsub = tid / TPR;
-  constexpr int NR = 64 / RPI;
-  uint4 raw[NR];
+  const int col = (tid % S::TPR) * S::V;
+  const int rsub = tid / S::TPR;
 #pragma unroll
-  for (int k = 0; k < NR; ++k)
-    raw[k] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(rsub + k * RPI) * D + col);
-  float acc[V];
+  for (int k = 0; k < S::NR; ++k)
+    raw[k] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(rsub + k * S::RPI) * D + col);
+}
+
+// The same vectors written to the block at dst (the append's copy).
+template <typename TIn, int D>
+__device__ __forceinline__ void store_block_vecs(TIn* __restrict__ dst, const uint4* raw) {
+  using S = PoolShape<TIn, D>;
+  const int tid = threadIdx.x;
+  const int col = (tid % S::TPR) * S::V;
+  const int rsub = tid / S::TPR;
 #pragma unroll
-  for (int i = 0; i < V; ++i) acc[i] = 0.f;
+  for (int k = 0; k < S::NR; ++k)
+    *reinterpret_cast<uint4*>(dst + static_cast<size_t>(rsub + k * S::RPI) * D + col) = raw[k];
+}
+
+// Mean of the 64 rows of one block into out[0 .. D), from the vectors the
+// threads hold: each thread sums its column slice over its rows, then the RPI
+// partial sums of a column are added in row-group order.
+template <typename TIn, int D>
+__device__ __forceinline__ void pool_block_vecs(const uint4* raw, float* __restrict__ out,
+                                                float* part) {
+  using S = PoolShape<TIn, D>;
+  const int tid = threadIdx.x;
+  const int col = (tid % S::TPR) * S::V;
+  const int rsub = tid / S::TPR;
+  float acc[S::V];
 #pragma unroll
-  for (int k = 0; k < NR; ++k) {
+  for (int i = 0; i < S::V; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int k = 0; k < S::NR; ++k) {
     const TIn* e = reinterpret_cast<const TIn*>(&raw[k]);
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] += static_cast<float>(e[i]);
+    for (int i = 0; i < S::V; ++i) acc[i] += static_cast<float>(e[i]);
   }
 #pragma unroll
-  for (int i = 0; i < V; ++i) part[rsub * D + col + i] = acc[i];
+  for (int i = 0; i < S::V; ++i) part[rsub * D + col + i] = acc[i];
   __syncthreads();
   if (tid < D) {
     float s = 0.f;
-    for (int k = 0; k < RPI; ++k) s += part[k * D + tid];
+    for (int k = 0; k < S::RPI; ++k) s += part[k * D + tid];
     out[tid] = s * (1.f / 64.f);
   }
+}
+
+// Mean of the 64 rows of one block (src points at its first row, row stride D).
+template <typename TIn, int D>
+__device__ __forceinline__ void pool_one_block(const TIn* __restrict__ src,
+                                               float* __restrict__ out, float* part) {
+  uint4 raw[PoolShape<TIn, D>::NR];
+  load_block_vecs<TIn, D>(src, raw);
+  pool_block_vecs<TIn, D>(raw, out, part);
 }
 
 template <typename TIn, int D>
@@ -93,23 +129,43 @@ __global__ __launch_bounds__(kMaskThreads) void pool_blocks_kernel(const TIn* __
 // Q-block (b, h, y) into qbar; the last B * H_kv workgroups clear the union
 // bitmaps at the tail of each T[b,g] row (n_rep copies of ceil(NKB_max / 32)
 // words), which the selection then ORs into.
-template <typename TIn, int D>
+// kAppend (the chunk's append fused in): the key blocks come from k_new (the
+// chunk's rows, [B, H_kv, C_max, D]) and are also written to the cache at rows
+// P + 64y, and nK more workgroups (after the key blocks) copy the value
+// blocks of v_new the same way.  The pooled values are the same as pooling
+// the cache after the append, bit for bit: the same rows, summed in the same
+// order.
+template <typename TIn, int D, bool kAppend>
 __global__ __launch_bounds__(kMaskThreads) void select_pool_kernel(
     const TIn* __restrict__ K, const TIn* __restrict__ Q, int H_q, int H_kv, int64_t L,
     int C_max, int NQ_max, int NKB_max, int span, int n_k, int n_q, int n_rep, SeqInfo seq,
-    float* __restrict__ kbar, float* __restrict__ qbar, int32_t* __restrict__ T) {
+    float* __restrict__ kbar, float* __restrict__ qbar, int32_t* __restrict__ T,
+    const TIn* __restrict__ k_new, const TIn* __restrict__ v_new, TIn* __restrict__ k_cache,
+    TIn* __restrict__ v_cache) {
   __shared__ float part[kPoolPart<TIn, D>];
   int w = blockIdx.x;  // n_k = B * H_kv * span key blocks, n_q = B * H_q * span Q-blocks
-  if (w < n_k) {
+  if (w < (kAppend ? 2 * n_k : n_k)) {
+    const bool is_v = w >= n_k;
+    if (is_v) w -= n_k;
     const int bg = w / span, y = w - bg * span;
     const int b = bg / H_kv;
     const int kb = seq.prior[b] / 64 + y;
     if (y >= seq.chunk[b] / 64) return;
-    pool_one_block<TIn, D>(K + (static_cast<size_t>(bg) * L + static_cast<size_t>(kb) * 64) * D,
-                           kbar + (static_cast<size_t>(bg) * NKB_max + kb) * D, part);
+    const size_t cache_off = (static_cast<size_t>(bg) * L + static_cast<size_t>(kb) * 64) * D;
+    if constexpr (kAppend) {
+      const size_t new_off = (static_cast<size_t>(bg) * C_max + static_cast<size_t>(y) * 64) * D;
+      uint4 raw[PoolShape<TIn, D>::NR];
+      load_block_vecs<TIn, D>((is_v ? v_new : k_new) + new_off, raw);
+      store_block_vecs<TIn, D>((is_v ? v_cache : k_cache) + cache_off, raw);
+      if (!is_v)
+        pool_block_vecs<TIn, D>(raw, kbar + (static_cast<size_t>(bg) * NKB_max + kb) * D, part);
+    } else {
+      pool_one_block<TIn, D>(K + cache_off, kbar + (static_cast<size_t>(bg) * NKB_max + kb) * D,
+                             part);
+    }
     return;
   }
-  w -= n_k;
+  w -= kAppend ? 2 * n_k : n_k;
   if (w < n_q) {
     const int bh = w / span, y = w - bh * span;
     const int b = bh / H_q;
@@ -477,19 +533,35 @@ hipError_t launch_scores(const float* qbar, const float* kbar, int B, int H_q, i
 template <typename TIn>
 void launch_select_pool(const void* Q, const void* K, int B, int H_q, int H_kv, int C_max,
                         int64_t L, int D, const SeqInfo& seq, int span, float* qbar, int NQ_max,
-                        float* kbar, int NKB_max, int32_t* T, int n_rep, hipStream_t stream) {
+                        float* kbar, int NKB_max, int32_t* T, int n_rep, const AppendSrc* app,
+                        hipStream_t stream) {
   const int n_k = B * H_kv * span, n_q = B * H_q * span;
-  const dim3 grid(n_k + n_q + B * H_kv);
+  const dim3 grid((app ? 2 * n_k : n_k) + n_q + B * H_kv);
   const TIn* k = static_cast<const TIn*>(K);
   const TIn* q = static_cast<const TIn*>(Q);
+  if (app) {
+    const TIn* kn = static_cast<const TIn*>(app->k_new);
+    const TIn* vn = static_cast<const TIn*>(app->v_new);
+    TIn* kc = static_cast<TIn*>(app->k_cache);
+    TIn* vc = static_cast<TIn*>(app->v_cache);
+    if (D == 128)
+      hipLaunchKernelGGL((select_pool_kernel<TIn, 128, true>), grid, dim3(kMaskThreads), 0,
+                         stream, nullptr, q, H_q, H_kv, L, C_max, NQ_max, NKB_max, span, n_k, n_q,
+                         n_rep, seq, kbar, qbar, T, kn, vn, kc, vc);
+    else
+      hipLaunchKernelGGL((select_pool_kernel<TIn, 64, true>), grid, dim3(kMaskThreads), 0,
+                         stream, nullptr, q, H_q, H_kv, L, C_max, NQ_max, NKB_max, span, n_k, n_q,
+                         n_rep, seq, kbar, qbar, T, kn, vn, kc, vc);
+    return;
+  }
   if (D == 128)
-    hipLaunchKernelGGL((select_pool_kernel<TIn, 128>), grid, dim3(kMaskThreads), 0, stream, k, q,
-                       H_q, H_kv, L, C_max, NQ_max, NKB_max, span, n_k, n_q, n_rep, seq, kbar,
-                       qbar, T);
+    hipLaunchKernelGGL((select_pool_kernel<TIn, 128, false>), grid, dim3(kMaskThreads), 0, stream,
+                       k, q, H_q, H_kv, L, C_max, NQ_max, NKB_max, span, n_k, n_q, n_rep, seq,
+                       kbar, qbar, T, nullptr, nullptr, nullptr, nullptr);
   else
-    hipLaunchKernelGGL((select_pool_kernel<TIn, 64>), grid, dim3(kMaskThreads), 0, stream, k, q,
-                       H_q, H_kv, L, C_max, NQ_max, NKB_max, span, n_k, n_q, n_rep, seq, kbar,
-                       qbar, T);
+    hipLaunchKernelGGL((select_pool_kernel<TIn, 64, false>), grid, dim3(kMaskThreads), 0, stream,
+                       k, q, H_q, H_kv, L, C_max, NQ_max, NKB_max, span, n_k, n_q, n_rep, seq,
+                       kbar, qbar, T, nullptr, nullptr, nullptr, nullptr);
 }
 
 }  // namespace
@@ -510,17 +582,18 @@ hipError_t launch_select_chunk(const void* Q, const void* K, int esz, int B, int
                                int C_max, int64_t L, int D, const SeqInfo& seq, int max_nq,
                                int max_pblk, int budget, int local, float* qbar, int NQ_max,
                                float* kbar, int NKB_max, float* scores, uint8_t* mask,
-                               int32_t* T, int32_t* len, hipStream_t stream) {
+                               int32_t* T, int32_t* len, const AppendSrc* app,
+                               hipStream_t stream) {
   // copies of the union bitmap the top-k rows spread their atomics over (as many
   // as the T row's tail holds, up to 16)
   const int nwords = (NKB_max + 31) / 32;
   const int n_rep = std::max(1, std::min(kSelectReplicas, NKB_max / nwords));
   if (esz == 2)
     launch_select_pool<__bf16>(Q, K, B, H_q, H_kv, C_max, L, D, seq, max_nq, qbar, NQ_max, kbar,
-                               NKB_max, T, n_rep, stream);
+                               NKB_max, T, n_rep, app, stream);
   else
     launch_select_pool<float>(Q, K, B, H_q, H_kv, C_max, L, D, seq, max_nq, qbar, NQ_max, kbar,
-                              NKB_max, T, n_rep, stream);
+                              NKB_max, T, n_rep, app, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_scores(qbar, kbar, B, H_q, H_kv, NQ_max, NKB_max, D, seq, max_pblk, scores, stream);

@@ -565,12 +565,18 @@ CA_EXPORT ca_status ca_block_mask_topk(const float* qbar, const float* kbar, int
                                           max_pblk, budget, local, scores, mask, stream));
 }
 
-CA_EXPORT ca_status ca_select_chunk(const void* Q_chunk, const void* K_cache, ca_dtype dtype,
-                                    int B, int H_q, int H_kv, int C_max, int64_t L, int D,
-                                    const int32_t* prior_len, const int32_t* chunk_len,
-                                    int budget, int local, float* qbar, int NQ_max, float* kbar,
-                                    int NKB_max, float* scores, uint8_t* mask, int32_t* T,
-                                    int32_t* len, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// ca_select_chunk and ca_append_select_chunk: checks, then the launches (app:
+// the chunk's new rows to append, or null).
+ca_status select_chunk_common(const void* Q_chunk, const void* K_cache, ca_dtype dtype, int B,
+                              int H_q, int H_kv, int C_max, int64_t L, int D,
+                              const int32_t* prior_len, const int32_t* chunk_len, int budget,
+                              int local, float* qbar, int NQ_max, float* kbar, int NKB_max,
+                              float* scores, uint8_t* mask, int32_t* T, int32_t* len,
+                              const ca::AppendSrc* app, hipStream_t stream) {
   if (!Q_chunk || !K_cache || !prior_len || !chunk_len || !qbar || !kbar || !scores || !mask ||
       !T || !len)
     return CA_ERR_NULL;
@@ -599,12 +605,44 @@ CA_EXPORT ca_status ca_select_chunk(const void* Q_chunk, const void* K_cache, ca
     max_pblk = std::max(max_pblk, static_cast<int>(P / CA_BLOCK));
     max_nq = std::max(max_nq, static_cast<int>(C / CA_BLOCK));
   }
-  const int64_t n_pool = static_cast<int64_t>(B) * (H_q + H_kv) * max_nq + B * H_kv;
+  const int64_t n_pool =
+      static_cast<int64_t>(B) * (H_q + (app ? 2 : 1) * H_kv) * max_nq + B * H_kv;
   if (n_pool > INT32_MAX) return CA_ERR_SHAPE;
   return hip_status(ca::launch_select_chunk(Q_chunk, K_cache, dtype == CA_BF16 ? 2 : 4, B, H_q,
                                             H_kv, C_max, L, D, seq, max_nq, max_pblk, budget,
                                             local, qbar, NQ_max, kbar, NKB_max, scores, mask, T,
-                                            len, stream));
+                                            len, app, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+CA_EXPORT ca_status ca_select_chunk(const void* Q_chunk, const void* K_cache, ca_dtype dtype,
+                                    int B, int H_q, int H_kv, int C_max, int64_t L, int D,
+                                    const int32_t* prior_len, const int32_t* chunk_len,
+                                    int budget, int local, float* qbar, int NQ_max, float* kbar,
+                                    int NKB_max, float* scores, uint8_t* mask, int32_t* T,
+                                    int32_t* len, hipStream_t stream) {
+  return select_chunk_common(Q_chunk, K_cache, dtype, B, H_q, H_kv, C_max, L, D, prior_len,
+                             chunk_len, budget, local, qbar, NQ_max, kbar, NKB_max, scores, mask,
+                             T, len, nullptr, stream);
+}
+
+CA_EXPORT ca_status ca_append_select_chunk(const void* K_new, const void* V_new,
+                                           const void* Q_chunk, void* K_cache, void* V_cache,
+                                           ca_dtype dtype, int B, int H_q, int H_kv, int C_max,
+                                           int64_t L, int D, const int32_t* prior_len,
+                                           const int32_t* chunk_len, int budget, int local,
+                                           float* qbar, int NQ_max, float* kbar, int NKB_max,
+                                           float* scores, uint8_t* mask, int32_t* T,
+                                           int32_t* len, hipStream_t stream) {
+  if (!K_new || !V_new || !V_cache) return CA_ERR_NULL;
+  if (!aligned16(K_new) || !aligned16(V_new) || !aligned16(V_cache)) return CA_ERR_UNSUPPORTED;
+  const ca::AppendSrc app{K_new, V_new, K_cache, V_cache};
+  return select_chunk_common(Q_chunk, K_cache, dtype, B, H_q, H_kv, C_max, L, D, prior_len,
+                             chunk_len, budget, local, qbar, NQ_max, kbar, NKB_max, scores, mask,
+                             T, len, &app, stream);
 }
 
 }  // extern "C"

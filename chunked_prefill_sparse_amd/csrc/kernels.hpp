@@ -192,11 +192,20 @@ hipError_t launch_pool_blocks(const void* X, int esz, int B, int H, int64_t R, i
 // and its Q-blocks (clearing the union bitmap words of T), the scores, the
 // top-k mask with the union bits ORed in, the union compaction (esz = 2:
 // bf16, 4: fp32 for Q and K).
+// With `app`, the first launch also appends the chunk's keys and values to
+// the caches (K is then not read: the key blocks are pooled from app->k_new).
+struct AppendSrc {
+  const void* k_new;  // [B, H_kv, C_max, D], the chunk's rows
+  const void* v_new;
+  void* k_cache;      // [B, H_kv, L, D], written at rows [prior, prior + chunk)
+  void* v_cache;
+};
 hipError_t launch_select_chunk(const void* Q, const void* K, int esz, int B, int H_q, int H_kv,
                                int C_max, int64_t L, int D, const SeqInfo& seq, int max_nq,
                                int max_pblk, int budget, int local, float* qbar, int NQ_max,
                                float* kbar, int NKB_max, float* scores, uint8_t* mask,
-                               int32_t* T, int32_t* len, hipStream_t stream);
+                               int32_t* T, int32_t* len, const AppendSrc* app,
+                               hipStream_t stream);
 
 // Block-mask producer: pooled scores, then per-row top-k selection.
 hipError_t launch_block_mask(const float* qbar, const float* kbar, int B, int H_q, int H_kv,

@@ -19,8 +19,8 @@ from typing import Optional
 
 import torch
 
-from . import (append_kv, balanced_workspace_size, block_mask_topk, build_union_tables,
-               chunk_attention, pool_blocks, select_chunk)
+from . import (append_kv, append_select_chunk, balanced_workspace_size, block_mask_topk,
+               build_union_tables, chunk_attention, pool_blocks, select_chunk)
 from ._lib import CA_BLOCK
 
 
@@ -37,11 +37,14 @@ class ChunkedPrefill:
     attention through ``chunk_attention(..., balanced=True)``: the union's
     per-group tables differ in length from group to group, and the plan spreads
     that work evenly over the compute units (the workspace is allocated here,
-    once)."""
+    once).  ``fused_append`` (default) issues a chunk's append and selection as
+    one call, ``ca_append_select_chunk``, whose first launch copies the new
+    rows and pools them; without it they are ``ca_append_kv`` then
+    ``ca_select_chunk``, with the same results bit for bit."""
 
     def __init__(self, k_cache: torch.Tensor, v_cache: torch.Tensor, H_q: int, C: int,
                  budget: int, local: int, scale: Optional[float] = None,
-                 balanced: bool = False):
+                 balanced: bool = False, fused_append: bool = True):
         B, H_kv, L, D = k_cache.shape
         if C % CA_BLOCK or L % CA_BLOCK:
             raise ValueError("chunk length and cache capacity must be multiples of 64")
@@ -67,6 +70,7 @@ class ChunkedPrefill:
             .view(B, H_kv, self.NKB)
         self.out = torch.empty((B, H_q, C, D), dtype=k_cache.dtype, device=dev)
         self.balanced = bool(balanced)
+        self.fused_append = bool(fused_append)
         self.ws = None
         if self.balanced:
             self.ws = torch.empty(balanced_workspace_size(B, H_q, H_kv, C, D), dtype=torch.uint8,
@@ -87,6 +91,20 @@ class ChunkedPrefill:
         T, lens = tables if tables is not None else (self.T, self.lens)
         select_chunk(q_chunk, self.k, [prior] * B, [C] * B, self.budget, self.local, self.qbar,
                      self.kbar, self.scores, self.mask, T, lens, stream=stream)
+
+    def append_select(self, k_chunk: torch.Tensor, v_chunk: torch.Tensor,
+                      q_chunk: torch.Tensor, prior: int, stream=None, tables=None) -> None:
+        """``append`` then ``select``: one ``ca_append_select_chunk`` call (four
+        launches) when ``fused_append``, else the two calls (five launches)."""
+        if not self.fused_append:
+            self.append(k_chunk, v_chunk, prior, stream)
+            self.select(q_chunk, prior, stream, tables)
+            return
+        B, C = self.B, self.C
+        T, lens = tables if tables is not None else (self.T, self.lens)
+        append_select_chunk(k_chunk, v_chunk, q_chunk, self.k, self.v, [prior] * B, [C] * B,
+                            self.budget, self.local, self.qbar, self.kbar, self.scores,
+                            self.mask, T, lens, stream=stream)
 
     def select_separate(self, q_chunk: torch.Tensor, prior: int, stream=None) -> None:
         """The same selection as ``select`` through the separate calls (six
@@ -112,8 +130,9 @@ class ChunkedPrefill:
              k_chunk: Optional[torch.Tensor] = None,
              v_chunk: Optional[torch.Tensor] = None) -> torch.Tensor:
         if k_chunk is not None:
-            self.append(k_chunk, v_chunk, prior, stream)
-        self.select(q_chunk, prior, stream)
+            self.append_select(k_chunk, v_chunk, q_chunk, prior, stream)
+        else:
+            self.select(q_chunk, prior, stream)
         return self.attend(q_chunk, prior, out, stream)
 
     def run(self, q_chunks, priors, outs=None, kv_chunks=None, overlap: bool = True) -> None:
@@ -161,11 +180,18 @@ class ChunkedPrefill:
         depth = len(self.tables)
 
         def issue_select(i):
-            if kv_chunks is not None:
+            # the append needs no wait (its rows are past every key an earlier
+            # chunk's attention reads), but with fused_append it shares the
+            # selection's first launch, which writes tables[i % depth]
+            if kv_chunks is not None and not self.fused_append:
                 self.append(kv_chunks[i][0], kv_chunks[i][1], priors[i], stream=side)
             if i >= depth:
                 side.wait_event(attended[i - depth])
-            self.select(q_chunks[i], priors[i], stream=side, tables=self.tables[i % depth])
+            if kv_chunks is not None and self.fused_append:
+                self.append_select(kv_chunks[i][0], kv_chunks[i][1], q_chunks[i], priors[i],
+                                   stream=side, tables=self.tables[i % depth])
+            else:
+                self.select(q_chunks[i], priors[i], stream=side, tables=self.tables[i % depth])
             selected[i].record(side)
 
         if n > 0:
@@ -217,8 +243,9 @@ class ChunkedPrefill:
             kc, vc = kv_chunks[i] if kv_chunks is not None else (None, None)
             if select_only:
                 if kc is not None:
-                    self.append(kc, vc, p)
-                self.select(q, p)
+                    self.append_select(kc, vc, q, p)
+                else:
+                    self.select(q, p)
             elif lens is not None:
                 self.step_dense(q, p, lens[i], out=o, k_chunk=kc, v_chunk=vc)
             else:

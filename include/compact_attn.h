@@ -567,6 +567,38 @@ CA_EXPORT ca_status ca_select_chunk(const void* Q_chunk, const void* K_cache, ca
                                     int NKB_max, float* scores, uint8_t* mask, int32_t* T,
                                     int32_t* len, hipStream_t stream);
 
+/*
+ * ca_append_select_chunk -- a chunk's append (ca_append_kv) and its selection
+ * (ca_select_chunk) in the four launches of the selection: the first launch
+ * also copies the chunk's keys and values into the caches, and pools the new
+ * key blocks from the rows it copies instead of reading them back from the
+ * cache (problem statement of the technical summaries: each chunk's K/V join
+ * the cache before it attends, and the search runs again over the grown
+ * cache).  Outputs are those of
+ *
+ *   ca_append_kv(K_new, V_new, ..., prior_len, chunk_len, K_cache, V_cache)
+ *   ca_select_chunk(Q_chunk, K_cache, ..., prior_len, chunk_len, ...)
+ *
+ * bit for bit (caches, kbar, qbar, scores, mask, T, len).
+ *
+ * K_new, V_new  device [B, H_kv, C_max, D] (dtype), 16-byte aligned: the
+ *               chunk's keys and values, rows [0, chunk_len[b]) used.
+ * K_cache, V_cache  device [B, H_kv, L, D] (dtype), 16-byte aligned (in/out):
+ *               rows [prior_len[b], prior_len[b] + chunk_len[b]) are written,
+ *               rows below prior_len[b] must hold the earlier chunks.
+ * Every other argument as for ca_select_chunk (prior_len and chunk_len
+ * multiples of 64).  The new rows must not overlap the caches.
+ * Errors: CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_DTYPE, CA_ERR_UNSUPPORTED, CA_ERR_HIP.
+ */
+CA_EXPORT ca_status ca_append_select_chunk(const void* K_new, const void* V_new,
+                                           const void* Q_chunk, void* K_cache, void* V_cache,
+                                           ca_dtype dtype, int B, int H_q, int H_kv, int C_max,
+                                           int64_t L, int D, const int32_t* prior_len,
+                                           const int32_t* chunk_len, int budget, int local,
+                                           float* qbar, int NQ_max, float* kbar, int NKB_max,
+                                           float* scores, uint8_t* mask, int32_t* T,
+                                           int32_t* len, hipStream_t stream);
+
 /* Human-readable name of a status code (static string; never NULL). */
 CA_EXPORT const char* ca_status_string(ca_status s);
 

@@ -146,6 +146,27 @@ int main() {
       EXPECT(strcmp(stub::last.what, "select") == 0 && stub::last.ints[0] == 4 &&
              stub::last.ints[1] == 48 && stub::last.ints[7] == 8002 && stub::last.ints[6] == 2);
       EXPECT(stub::last.seq.prior[1] == 1024 && stub::last.seq.chunk[1] == 192);
+      // the same with the append fused in: the new rows and the V cache reach
+      // the launcher, and a missing V cache or a misaligned source is refused
+      void* const kn = reinterpret_cast<void*>(static_cast<uintptr_t>(0x7000));
+      void* const vc = reinterpret_cast<void*>(static_cast<uintptr_t>(0x9000));
+      EXPECT(ca_append_select_chunk(kn, FAKE, FAKE, FAKE, vc, CA_BF16, 2, 8, 2, 256, 4096, 128,
+                                    pr, ch, 8, 2, (float*)FAKE, 4, (float*)FAKE, 64,
+                                    (float*)FAKE, (uint8_t*)FAKE, (int32_t*)FAKE,
+                                    (int32_t*)FAKE, 0) == CA_OK);
+      EXPECT(strcmp(stub::last.what, "append_select") == 0 && stub::last.ptrs[0] == kn &&
+             stub::last.ptrs[1] == vc && stub::last.ints[0] == 4 && stub::last.ints[1] == 48);
+      stub::last = stub::Record{};
+      EXPECT(ca_append_select_chunk(kn, FAKE, FAKE, FAKE, nullptr, CA_BF16, 2, 8, 2, 256, 4096,
+                                    128, pr, ch, 8, 2, (float*)FAKE, 4, (float*)FAKE, 64,
+                                    (float*)FAKE, (uint8_t*)FAKE, (int32_t*)FAKE,
+                                    (int32_t*)FAKE, 0) == CA_ERR_NULL);
+      EXPECT(ca_append_select_chunk(reinterpret_cast<void*>(static_cast<uintptr_t>(0x7008)),
+                                    FAKE, FAKE, FAKE, vc, CA_BF16, 2, 8, 2, 256, 4096, 128, pr,
+                                    ch, 8, 2, (float*)FAKE, 4, (float*)FAKE, 64, (float*)FAKE,
+                                    (uint8_t*)FAKE, (int32_t*)FAKE, (int32_t*)FAKE,
+                                    0) == CA_ERR_UNSUPPORTED);
+      EXPECT(strcmp(stub::last.what, "") == 0);
     }
     // no-alloc split: the partials go to the static array (its stand-in address),
     // same layout; a split past the array's size is refused before any launch

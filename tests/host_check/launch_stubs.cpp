@@ -129,9 +129,14 @@ hipError_t launch_append_kv(const void*, const void*, int B, int H_kv, int C_max
 hipError_t launch_select_chunk(const void*, const void*, int esz, int B, int H_q, int H_kv,
                                int C_max, int64_t L, int D, const SeqInfo& seq, int max_nq,
                                int max_pblk, int budget, int local, float*, int NQ_max, float*,
-                               int NKB_max, float*, uint8_t*, int32_t*, int32_t*, hipStream_t) {
+                               int NKB_max, float*, uint8_t*, int32_t*, int32_t*,
+                               const AppendSrc* app, hipStream_t) {
   stub::last = stub::Record{};
-  stub::last.what = "select";
+  stub::last.what = app ? "append_select" : "select";
+  if (app) {
+    stub::last.ptrs[0] = const_cast<void*>(app->k_new);
+    stub::last.ptrs[1] = app->v_cache;
+  }
   stub::last.B = B;
   stub::last.D = D;
   stub::last.ints[0] = max_nq;

@@ -104,8 +104,8 @@ def test_prefill_graph_replay_matches_eager(balanced):
         assert torch.equal(drv.T, eager_T) and torch.equal(drv.lens, eager_lens)
 
 
-@pytest.mark.parametrize("balanced", [False, True])
-def test_prefill_overlap_matches_sequential(balanced):
+@pytest.mark.parametrize("balanced,fused", [(False, True), (True, True), (False, False)])
+def test_prefill_overlap_matches_sequential(balanced, fused):
     # run(overlap=True): each chunk's append and selection on a second stream, one
     # chunk ahead of the attention, into caches that hold NaN past the appended rows.
     # Every chunk's output equals the sequential steps' over the resident prompt, bit
@@ -121,10 +121,11 @@ def test_prefill_overlap_matches_sequential(balanced):
           for p in priors]
     kc = torch.full_like(k_full, float("nan"))
     vc = torch.full_like(v_full, float("nan"))
-    drv = ChunkedPrefill(kc, vc, s.H_q, s.C, budget=4, local=2, balanced=balanced)
+    drv = ChunkedPrefill(kc, vc, s.H_q, s.C, budget=4, local=2, balanced=balanced,
+                         fused_append=fused)
     outs = [torch.full_like(qs[0], float("nan")) for _ in qs]
     torch.cuda.synchronize()
-    say(f"overlapped prefill_small, eager, balanced={balanced}")
+    say(f"overlapped prefill_small, eager, balanced={balanced}, fused append={fused}")
     drv.run(qs, priors, outs=outs, kv_chunks=kv, overlap=True)
     torch.cuda.synchronize()
     for c in range(s.n_chunks):

@@ -159,3 +159,82 @@ def test_select_chunk_small_tables(L, prior, chunk):
                                   [(p + c) // 64 for p, c in zip(prior, chunk)])
         np.testing.assert_array_equal(T.cpu().numpy(), Tr)
         np.testing.assert_array_equal(lens.cpu().numpy(), lr)
+
+
+@pytest.mark.parametrize("dtype,D,G", [(torch.bfloat16, 128, 4), (torch.bfloat16, 64, 2),
+                                       (torch.float32, 128, 2), (torch.float32, 64, 4)])
+def test_append_select_matches_append_then_select(dtype, D, G):
+    # ca_append_select_chunk against ca_append_kv then ca_select_chunk: caches
+    # (rows past the chunk untouched), kbar, qbar, scores, mask, T and lens bit
+    # for bit; ragged priors and chunks, caches poisoned with NaN beyond the
+    # earlier chunks' rows
+    B, H_kv, C_max, L = 2, 2, 256, 4096
+    H_q = H_kv * G
+    prior, chunk = [3072, 1024], [256, 192]
+    gq = torch.Generator().manual_seed(131)
+    k0 = torch.randn((B, H_kv, L, D), generator=gq).to(dtype)
+    v0 = torch.randn((B, H_kv, L, D), generator=gq).to(dtype)
+    for b in range(B):
+        k0[b, :, prior[b]:] = float("nan")
+        v0[b, :, prior[b]:] = float("nan")
+    k_new = torch.randn((B, H_kv, C_max, D), generator=gq).to(dtype).cuda()
+    v_new = torch.randn((B, H_kv, C_max, D), generator=gq).to(dtype).cuda()
+    q = torch.randn((B, H_q, C_max, D), generator=gq).to(dtype).cuda()
+    NQ, NKB = C_max // 64, L // 64
+    kbar0 = torch.zeros((B, H_kv, NKB, D), dtype=torch.float32, device="cuda")
+    ca.pool_blocks(k0.cuda(), [0] * B, [p // 64 for p in prior], out=kbar0)
+
+    def buffers():
+        return (k0.cuda(), v0.cuda(), kbar0.clone(),
+                torch.zeros((B, H_q, NQ, D), dtype=torch.float32, device="cuda"),
+                torch.zeros((B, H_q, NQ, NKB), dtype=torch.float32, device="cuda"),
+                torch.full((B, H_q, NQ, NKB), 7, dtype=torch.uint8, device="cuda"),
+                torch.full((B, H_kv, NKB), 12345, dtype=torch.int32, device="cuda"),
+                torch.full((B, H_kv), -3, dtype=torch.int32, device="cuda"))
+
+    for budget, local in ((8, 2), (0, 4)):
+        say(f"append_select_chunk {dtype} D={D} G={G} budget={budget} local={local}")
+        kc, vc, kbar, qbar, scores, mask, T, lens = ref = buffers()
+        ca.append_kv(k_new, v_new, kc, vc, prior, chunk)
+        ca.select_chunk(q, kc, prior, chunk, budget, local, qbar, kbar, scores, mask, T, lens)
+        got = buffers()
+        kc2, vc2, kbar2, qbar2, scores2, mask2, T2, lens2 = got
+        ca.append_select_chunk(k_new, v_new, q, kc2, vc2, prior, chunk, budget, local, qbar2,
+                               kbar2, scores2, mask2, T2, lens2)
+        torch.cuda.synchronize()
+        names = ("k_cache", "v_cache", "kbar", "qbar", "scores", "mask", "T", "lens")
+        for name, g, r in zip(names, got, ref):
+            if name == "scores":  # written only where qb < chunk/64 and kb < prior/64
+                for b in range(B):
+                    nq, pb = chunk[b] // 64, prior[b] // 64
+                    assert torch.equal(g[b, :, :nq, :pb], r[b, :, :nq, :pb]), name
+            elif name in ("k_cache", "v_cache"):  # NaN rows past the chunk stay NaN
+                assert torch.equal(torch.nan_to_num(g, nan=1e30), torch.nan_to_num(r, nan=1e30))
+                for b in range(B):
+                    e = prior[b] + chunk[b]
+                    assert bool(torch.isnan(g[b, :, e:].float()).all()), name
+                    src = (k_new if name == "k_cache" else v_new)[b, :, :chunk[b]]
+                    assert torch.equal(g[b, :, prior[b]:e], src), name
+            else:
+                assert torch.equal(g, r), name
+
+
+def test_append_select_rejects_bad_arguments():
+    B, H_kv, H_q, C_max, L, D = 1, 2, 4, 128, 1024, 64
+    t = lambda *s, dt=torch.bfloat16: torch.zeros(s, dtype=dt, device="cuda")
+    k_new, v_new, q = t(B, H_kv, C_max, D), t(B, H_kv, C_max, D), t(B, H_q, C_max, D)
+    kc, vc = t(B, H_kv, L, D), t(B, H_kv, L, D)
+    qbar, kbar = t(B, H_q, 2, D, dt=torch.float32), t(B, H_kv, 16, D, dt=torch.float32)
+    scores, mask = t(B, H_q, 2, 16, dt=torch.float32), t(B, H_q, 2, 16, dt=torch.uint8)
+    T, lens = t(B, H_kv, 16, dt=torch.int32), t(B, H_kv, dt=torch.int32)
+    args = (qbar, kbar, scores, mask, T, lens)
+    with pytest.raises(ValueError):  # new rows of another dtype
+        ca.append_select_chunk(k_new.float(), v_new, q, kc, vc, [0], [128], 4, 1, *args)
+    with pytest.raises(ValueError):  # new rows of the wrong shape
+        ca.append_select_chunk(k_new[:, :, :64], v_new, q, kc, vc, [0], [128], 4, 1, *args)
+    with pytest.raises(ca.CompactAttnError) as e:  # chunk not a multiple of 64
+        ca.append_select_chunk(k_new, v_new, q, kc, vc, [0], [96], 4, 1, *args)
+    assert e.value.status == 4
+    with pytest.raises(ca.CompactAttnError) as e:  # past the cache
+        ca.append_select_chunk(k_new, v_new, q, kc, vc, [960], [128], 4, 1, *args)
+    assert e.value.status == 2
