@@ -295,22 +295,27 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 // threshold and, of the keys equal to it, the lowest kb first.
 //
 // kUnion: the fused selection also ORs each selected cell into its group's
-// union bitmap at the tail of the T[b,g] row (cleared by select_pool_kernel):
-// per wave, one ballot over 64 consecutive blocks and up to two device-scope
-// atomicOr.  The 128 rows of a group would all hit the same words, and
-// atomics on one address serialize, so row r ORs into copy r % n_rep of the
-// bitmap (n_rep copies side by side; the compaction ORs them together).  What
-// is ORed is exactly the union over the chunk's Q-blocks and the group's heads
-// (rows past the chunk select nothing).
+// union bitmap at the tail of the T[b,g] row (cleared by select_pool_kernel).
+// The row's bits are gathered in an LDS bitmap and ORed into the group's
+// bitmap once, one device-scope atomicOr per nonzero word (rows that do not
+// stage their keys in LDS, and rows with ties at the budget: per wave, one
+// ballot over 64 consecutive blocks and up to two atomics).  The 128 rows of a
+// group would all hit the same words, and atomics on one address serialize,
+// so row r ORs into copy r % n_rep of the bitmap (n_rep copies side by side;
+// the compaction ORs them together).  What is ORed is exactly the union over
+// the chunk's Q-blocks and the group's heads (rows past the chunk select
+// nothing).
 // kLds: the row's candidate keys are read from the scores once (kTopkStage
 // loads in flight per thread) into dynamic LDS (NKB_max words), and every pass
 // reads them there; without it each pass re-reads the scores row.
+// Where no tie straddles the budget, a thread decides four consecutive blocks
+// at a time and writes their mask bytes as one 32-bit store.
 template <bool kUnion, bool kLds>
 __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
     const float* __restrict__ scores, int H_q, int NQ_max, int NKB_max, SeqInfo seq,
     int budget, int local, uint8_t* __restrict__ mask, int H_kv, int32_t* __restrict__ T,
     int n_rep) {
-  extern __shared__ uint32_t keys[];
+  extern __shared__ uint32_t keys[];  // kLds: NKB_max keys; then (kUnion) the row's bitmap
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh_prefix, sh_need, sh_bin;
   __shared__ int wave_eq[kMaskThreads / 64];
@@ -343,9 +348,24 @@ __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
       if (hi != 0u && w0 + 1 < nwords) atomicOr(&ubits[w0 + 1], hi);
     }
   };
+  // mask bytes of four consecutive blocks as one 32-bit store when the row allows
+  const bool store4 = (NKB_max & 3) == 0 && (reinterpret_cast<uintptr_t>(mrow) & 3) == 0;
   if (qb >= nq) {
-    for (int kb = tid; kb < NKB_max; kb += kMaskThreads) mrow[kb] = 0;
+    if (store4) {
+      for (int kb = 4 * tid; kb < NKB_max; kb += 4 * kMaskThreads)
+        *reinterpret_cast<uint32_t*>(mrow + kb) = 0u;
+    } else {
+      for (int kb = tid; kb < NKB_max; kb += kMaskThreads) mrow[kb] = 0;
+    }
     return;
+  }
+  // the row's union bits, gathered in LDS (after the keys) and ORed into the
+  // group's bitmap once; rows too long to stage their keys OR per wave instead
+  constexpr bool kLdsBits = kUnion && kLds;
+  uint32_t* lbits = keys + NKB_max;
+  if (kLdsBits) {
+    for (int i = tid; i < nwords; i += kMaskThreads) lbits[i] = 0u;
+    __syncthreads();
   }
   const int lo_local = pblk - local > 1 ? pblk - local : 1;  // candidates: [1, lo_local)
   const int n_cand = lo_local - 1 > 0 ? lo_local - 1 : 0;
@@ -427,7 +447,38 @@ __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
   // prefix = the fixed bits of the budget-th largest candidate's key; take the
   // candidates above it, and `need` of those equal to it (lowest kb first)
 
-  if (whole_bin) {  // no equal key is left out: no ordering across the row
+  if (whole_bin && !(kUnion && !kLds)) {  // no equal key is left out: no ordering across the row
+    // each thread decides four consecutive blocks per step
+    for (int kb0 = 4 * tid; kb0 < NKB_max; kb0 += 4 * kMaskThreads) {
+      uint32_t bytes = 0u, bits = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kb = kb0 + j;
+        bool sel = (pblk > 0 && kb == 0) || (kb >= lo_local && kb < pblk) ||
+                   (kb >= pblk && kb <= pblk + qb);
+        if (kk > 0u && kb >= 1 && kb < lo_local)
+          sel = sel || (key_at(kb) & lvl_mask) >= prefix;
+        sel = sel && kb < NKB_max;
+        bytes |= static_cast<uint32_t>(sel) << (8 * j);
+        bits |= static_cast<uint32_t>(sel) << j;
+      }
+      if (store4) {
+        *reinterpret_cast<uint32_t*>(mrow + kb0) = bytes;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (kb0 + j < NKB_max) mrow[kb0 + j] = static_cast<uint8_t>(bytes >> (8 * j));
+      }
+      if (kLdsBits && bits != 0u) atomicOr(&lbits[kb0 >> 5], bits << (kb0 & 31));
+    }
+    if (kLdsBits) {
+      __syncthreads();
+      for (int i = tid; i < nwords; i += kMaskThreads)
+        if (lbits[i] != 0u) atomicOr(&ubits[i], lbits[i]);
+    }
+    return;
+  }
+  if (whole_bin) {  // rows too long for LDS: one block per thread, ORs per wave
     for (int base = 0; base < NKB_max; base += kMaskThreads) {
       const int kb = base + tid;
       bool sel = false;
@@ -438,7 +489,7 @@ __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
           sel = sel || (key_at(kb) & lvl_mask) >= prefix;
         mrow[kb] = sel ? 1 : 0;
       }
-      if (kUnion) or_bits(base, sel);
+      or_bits(base, sel);
     }
     return;
   }
@@ -476,10 +527,11 @@ void launch_topk(const float* scores, int B, int H_q, int NQ_max, int NKB_max, c
                  int budget, int local, uint8_t* mask, int H_kv, int32_t* T, int n_rep,
                  hipStream_t stream) {
   const dim3 grid(B * H_q * NQ_max);
-  if (NKB_max <= kTopkLdsMax)
+  const size_t bitmap = kUnion ? static_cast<size_t>((NKB_max + 31) / 32) * sizeof(uint32_t) : 0;
+  if (NKB_max <= kTopkLdsMax)  // keys, then the row's union bits
     hipLaunchKernelGGL((topk_mask_kernel<kUnion, true>), grid, dim3(kMaskThreads),
-                       static_cast<size_t>(NKB_max) * sizeof(uint32_t), stream, scores, H_q,
-                       NQ_max, NKB_max, seq, budget, local, mask, H_kv, T, n_rep);
+                       static_cast<size_t>(NKB_max) * sizeof(uint32_t) + bitmap, stream, scores,
+                       H_q, NQ_max, NKB_max, seq, budget, local, mask, H_kv, T, n_rep);
   else
     hipLaunchKernelGGL((topk_mask_kernel<kUnion, false>), grid, dim3(kMaskThreads), 0, stream,
                        scores, H_q, NQ_max, NKB_max, seq, budget, local, mask, H_kv, T, n_rep);
