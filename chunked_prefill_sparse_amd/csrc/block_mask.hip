@@ -9,7 +9,8 @@
 //   kbar[b,g,kb]  = mean of the 64 rows of KV block kb         (pool_blocks,
 //                   kept across chunks: only the new blocks are pooled)
 //   s[b,h,qb,kb]  = qbar . kbar                                (block_scores,
-//                   fp32 on the matrix cores)
+//                   bf16 hi/lo parts of the fp32 values on the
+//                   matrix cores, within 2^-14 of sum_d |q_d k_d|)
 //   mask row      = sink + last `local` prior blocks + causal block triangle
 //                   + the `budget` best remaining prior blocks  (topk_mask)
 //
@@ -184,27 +185,49 @@ __global__ __launch_bounds__(kMaskThreads) void select_pool_kernel(
 
 // Workgroup (b*H_kv + g, y, z) computes the 64 x 64 tile of scores of the
 // group's pooled Q-block rows 64z .. 64z+63 (row r = head r / nq, Q-block
-// r % nq) against KV blocks 64y .. 64y+63, on the fp32 matrix cores
-// (v_mfma_f32_32x32x2_f32, twice the fp32 rate of the vector ALUs with packed
-// fp32 off).  Both 64 x D operand tiles are staged in LDS whole (rows padded
-// by 16 bytes, so the 32 rows a read touches fall in distinct banks); wave w
-// computes the 32 x 32 block (KV blocks 32 (w / 2) .., Q rows 32 (w % 2) ..)
-// as S^T = Kbar Qbar^T over D/2 steps of 2 dimensions.  Lane l takes the
-// dimensions (l / 32) * D/2 + s of step s, so its operands for four steps are
-// one 16-byte read.  Its 16 results are KV blocks 8(r/4) + 4(l/32) + r%4 of
-// Q row l % 32: four 16-byte stores (when rows of the score matrix are
+// r % nq) against KV blocks 64y .. 64y+63 on the bf16 matrix cores, with each
+// fp32 operand split in two bf16 parts: x = hi + lo, hi = bf16(x),
+// lo = bf16(x - hi), so that |x - hi - lo| <= 2^-16 |x|.  A product is taken
+// as hi*hi + hi*lo + lo*hi (three v_mfma_f32_32x32x16_bf16 per 16 dimensions;
+// products of bf16 values are exact in fp32), which leaves out lo*lo and the
+// two split residuals, each at most 2^-16 of |q_d k_d|: a score is within
+// 3 * 2^-16 sum_d |q_d k_d| (plus fp32 accumulation) of the fp32 dot product.
+// The split is made once, as the 64 x D fp32 tiles are staged into LDS as
+// four bf16 tiles (rows padded by 16 bytes); wave w computes the 32 x 32
+// block (KV blocks 32 (w / 2) .., Q rows 32 (w % 2) ..) as S^T = Kbar Qbar^T,
+// lane l taking dimensions 8 (l / 32) .. + 7 of each 16-wide step of row
+// l % 32 of both operands.  Its 16 results are KV blocks 8(r/4) + 4(l/32) +
+// r%4 of Q row l % 32: four 16-byte stores (when rows of the score matrix are
 // 16-byte aligned; else single floats).
 constexpr int kScoreTile = 64;
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// hi and lo bf16 parts of four fp32 values
+__device__ __forceinline__ void split_bf16x4(const float4 x, uint2& hi, uint2& lo) {
+  const float v[4] = {x.x, x.y, x.z, x.w};
+  __bf16 h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = static_cast<__bf16>(v[i]);
+    l[i] = static_cast<__bf16>(v[i] - static_cast<float>(h[i]));
+  }
+  hi = make_uint2(__builtin_bit_cast(uint16_t, h[0]) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h[1])) << 16),
+                  __builtin_bit_cast(uint16_t, h[2]) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h[3])) << 16));
+  lo = make_uint2(__builtin_bit_cast(uint16_t, l[0]) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l[1])) << 16),
+                  __builtin_bit_cast(uint16_t, l[2]) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l[3])) << 16));
+}
 
 template <int D>
 __global__ __launch_bounds__(kMaskThreads) void block_scores_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int H_q, int H_kv,
     int NQ_max, int NKB_max, SeqInfo seq, float* __restrict__ scores) {
-  constexpr int RS = D + 4;  // padded row stride (floats)
-  __shared__ __attribute__((aligned(16))) float Qs[kScoreTile * RS];
-  __shared__ __attribute__((aligned(16))) float Ks[kScoreTile * RS];
+  constexpr int RB = 2 * D + 16;  // padded row stride of a bf16 tile (bytes)
+  __shared__ __attribute__((aligned(16))) char Qh[kScoreTile * RB];
+  __shared__ __attribute__((aligned(16))) char Ql[kScoreTile * RB];
+  __shared__ __attribute__((aligned(16))) char Kh[kScoreTile * RB];
+  __shared__ __attribute__((aligned(16))) char Kl[kScoreTile * RB];
   const int bg = blockIdx.x;
   const int b = bg / H_kv;
   const int g = bg - b * H_kv;
@@ -222,7 +245,7 @@ __global__ __launch_bounds__(kMaskThreads) void block_scores_kernel(
     return head_row0 + static_cast<size_t>(hl) * NQ_max + (r - hl * nq);
   };
   // stage both tiles: D / 4 float4 per row, rows past the range as zeros; all
-  // loads in flight before the LDS writes
+  // loads in flight before the split and the LDS writes
   constexpr int F4 = kScoreTile * D / 4 / kMaskThreads;  // float4 per thread per tile
   float4 qv[F4], kv[F4];
 #pragma unroll
@@ -240,24 +263,31 @@ __global__ __launch_bounds__(kMaskThreads) void block_scores_kernel(
   for (int i = 0; i < F4; ++i) {
     const int e = tid + i * kMaskThreads;
     const int row = e / (D / 4), c4 = e - row * (D / 4);
-    *reinterpret_cast<float4*>(&Qs[row * RS + 4 * c4]) = qv[i];
-    *reinterpret_cast<float4*>(&Ks[row * RS + 4 * c4]) = kv[i];
+    const int off = row * RB + 8 * c4;
+    uint2 hi, lo;
+    split_bf16x4(qv[i], hi, lo);
+    *reinterpret_cast<uint2*>(&Qh[off]) = hi;
+    *reinterpret_cast<uint2*>(&Ql[off]) = lo;
+    split_bf16x4(kv[i], hi, lo);
+    *reinterpret_cast<uint2*>(&Kh[off]) = hi;
+    *reinterpret_cast<uint2*>(&Kl[off]) = lo;
   }
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
   const int kb_blk = 32 * (wave >> 1), q_blk = 32 * (wave & 1);
-  const float* ka = &Ks[(kb_blk + l32) * RS + hh * (D / 2)];
-  const float* qa = &Qs[(q_blk + l32) * RS + hh * (D / 2)];
+  const int ka = (kb_blk + l32) * RB + 16 * hh;
+  const int qa = (q_blk + l32) * RB + 16 * hh;
   f32x16_t acc = {};
 #pragma unroll
-  for (int s = 0; s < D / 2; s += 4) {
-    const float4 a4 = *reinterpret_cast<const float4*>(ka + s);
-    const float4 b4 = *reinterpret_cast<const float4*>(qa + s);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.x, b4.x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.y, b4.y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.z, b4.z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.w, b4.w, acc, 0, 0, 0);
+  for (int s = 0; s < D / 16; ++s) {  // dimensions 16 s + 8 hh .. + 7 of this lane
+    const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&Kh[ka + 32 * s]);
+    const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&Kl[ka + 32 * s]);
+    const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(&Qh[qa + 32 * s]);
+    const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(&Ql[qa + 32 * s]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
   }
   const int r = r0 + q_blk + l32;
   if (r >= n_rows) return;

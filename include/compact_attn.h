@@ -501,7 +501,10 @@ CA_EXPORT ca_status ca_pool_blocks(const void* X, ca_dtype dtype, int B, int H, 
  * P = prior_len[b]/64, nq = chunk_len[b]/64, g = h / (H_q/H_kv):
  *
  *   scores[b,h,qb,kb] = sum_d qbar[b,h,qb,d] * kbar[b,g,kb,d]  (qb < nq, kb < P;
- *                       fp32, on the fp32 matrix cores)
+ *                       each fp32 value split into bf16 hi + lo parts, the
+ *                       products hi*hi + hi*lo + lo*hi summed in fp32 on the
+ *                       bf16 matrix cores: within 3 * 2^-16 sum_d |q_d k_d|
+ *                       of the fp32 dot product, plus fp32 accumulation)
  *   mask[b,h,qb,kb]   = 1 for kb = 0 (when P > 0), for P - local <= kb < P,
  *                       for P <= kb <= P + qb (causal block triangle), and for
  *                       the `budget` candidates 1 <= kb < max(P - local, 1)

@@ -224,5 +224,30 @@ def check_bf16_rounding(got, ref, ref_absv, lse_ref, what=""):
     return r
 
 
+# Block scores of the mask producer: each fp32 operand is split into bf16 hi + lo
+# parts and a product taken as hi*hi + hi*lo + lo*hi on the bf16 matrix cores;
+# what is left out (lo*lo and the two split residuals) is at most 3 * 2^-16 of
+# |q_d k_d|, and the fp32 accumulation adds about 2^-19 of sum_d |q_d k_d|.
+# The absolute term covers the pooling's fp32 error carried into the D products.
+SCORE_ATOL = 2e-5
+SCORE_REL = 2.0 ** -14
+
+
+def score_bound(qbar_ref, kbar_ref):
+    """Per-score bound of |GPU score - float64 score|, from the pooled operands:
+    SCORE_ATOL + 2^-14 sum_d |qbar_d kbar_d|."""
+    from oracle import block_scores_ref
+    return SCORE_ATOL + SCORE_REL * block_scores_ref(np.abs(qbar_ref), np.abs(kbar_ref))
+
+
+def check_scores(got, ref, bound, what="scores"):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    ratio = float((np.abs(got - ref) / bound).max()) if got.size else 0.0
+    say(f"  {what}: max |error| / bound {ratio:.3f}")
+    assert ratio <= 1.0, f"{what}: score error beyond its bound ({ratio:.3f})"
+    return ratio
+
+
 def to_np(t: torch.Tensor) -> np.ndarray:
     return gen.tensor_to_f32(t.detach().cpu())

@@ -1,5 +1,7 @@
-"""The per-element rounding bound used by the bf16 parity tests, checked on the
-CPU against an emulation of the bf16 path's arithmetic (no GPU).
+"""The per-element rounding bounds used by the GPU parity tests, checked on the
+CPU against emulations of the GPU arithmetic (no GPU).
+
+Attention outputs (``check_bf16_rounding``):
 
 The emulation takes the kernel's roundings one by one: logits and
 exponentials in fp32, each probability rounded to bf16 (round to nearest
@@ -12,7 +14,7 @@ dropped, or a denominator 1% off) must not.
 import numpy as np
 import pytest
 
-from tests.gpu_util import check_bf16_rounding
+from tests.gpu_util import check_bf16_rounding, check_scores, score_bound
 
 
 def _bf16_rne(x):
@@ -69,3 +71,47 @@ def test_planted_mistake_breaks_the_bound(mistake):
     O, absv, lse = _exact(q, k, v, scale)
     with pytest.raises(AssertionError):
         check_bf16_rounding(_emulated(q, k, v, scale, **mistake), O, absv, lse, "planted")
+
+
+# Block scores (``score_bound``): each fp32 pooled value is split into bf16 hi
+# and lo parts, and a product is taken as hi*hi + hi*lo + lo*hi, accumulated
+# in fp32.
+
+
+def _split(x):
+    hi = _bf16_rne(x)
+    lo = _bf16_rne((x - hi).astype(np.float32))
+    return hi, lo
+
+
+def _split_scores(qbar, kbar, terms=("hl", "lh", "hh")):
+    qh, ql = _split(qbar)
+    kh, kl = _split(kbar)
+    parts = {"hh": (qh, kh), "hl": (qh, kl), "lh": (ql, kh)}
+    s = np.zeros(qbar.shape[:-1] + (kbar.shape[-2],), np.float32)
+    for t in terms:  # products of bf16 values are exact in fp32
+        a, b = parts[t]
+        s = (s + np.einsum("bhqd,bhkd->bhqk", a.astype(np.float64), b.astype(np.float64))
+             .astype(np.float32)).astype(np.float32)
+    return s
+
+
+def _pooled(seed, scale):
+    rng = np.random.default_rng(seed)
+    q = (rng.standard_normal((1, 2, 32, 128)) * scale).astype(np.float32)
+    k = (rng.standard_normal((1, 2, 96, 128)) * scale).astype(np.float32)
+    return q, k
+
+
+@pytest.mark.parametrize("scale", [0.125, 1.0, 8.0])
+def test_split_scores_are_inside_the_bound(scale):
+    q, k = _pooled(11, scale)
+    ref = np.einsum("bhqd,bhkd->bhqk", q.astype(np.float64), k.astype(np.float64))
+    check_scores(_split_scores(q, k), ref, score_bound(q, k), f"split scores, scale {scale}")
+
+
+def test_split_scores_without_a_cross_term_break_the_bound():
+    q, k = _pooled(13, 8.0)
+    ref = np.einsum("bhqd,bhkd->bhqk", q.astype(np.float64), k.astype(np.float64))
+    with pytest.raises(AssertionError):
+        check_scores(_split_scores(q, k, terms=("hh", "hl")), ref, score_bound(q, k), "planted")
