@@ -561,6 +561,18 @@ def block_mask_topk(qbar: torch.Tensor, kbar: torch.Tensor, prior_len: Sequence[
     return mask, scores
 
 
+def _select_lengths(fn: str, prior_len, chunk_len, B: int):
+    """The selection calls take host sequences (``fn``) or device int32 [B]
+    tensors (``fn``_devlen, read by the kernels when they run)."""
+    dev = isinstance(prior_len, torch.Tensor) or isinstance(chunk_len, torch.Tensor)
+    if not dev:
+        return fn, _host_ints("prior_len", prior_len, B), _host_ints("chunk_len", chunk_len, B)
+    if not (isinstance(prior_len, torch.Tensor) and isinstance(chunk_len, torch.Tensor)):
+        raise ValueError("prior_len and chunk_len must both be host sequences or both device tensors")
+    return (fn + "_devlen", _dev_ints("prior_len", prior_len, B),
+            _dev_ints("chunk_len", chunk_len, B))
+
+
 def select_chunk(q_chunk: torch.Tensor, k_cache: torch.Tensor, prior_len: Sequence[int],
                  chunk_len: Sequence[int], budget: int, local: int, qbar: torch.Tensor,
                  kbar: torch.Tensor, scores: torch.Tensor, mask: torch.Tensor, T: torch.Tensor,
@@ -569,7 +581,9 @@ def select_chunk(q_chunk: torch.Tensor, k_cache: torch.Tensor, prior_len: Sequen
     key blocks into kbar and its Q-blocks into qbar, score, take the top-k
     mask and build the union tables T / lens, in four launches; every output
     buffer is the caller's (qbar [B, H_q, NQ, D], kbar [B, H_kv, NKB, D] kept
-    across chunks, scores / mask [B, H_q, NQ, NKB], T [B, H_kv, NKB], lens [B, H_kv])."""
+    across chunks, scores / mask [B, H_q, NQ, NKB], T [B, H_kv, NKB], lens [B, H_kv]).
+    prior_len / chunk_len as device int32 [B] tensors use ``ca_select_chunk_devlen``
+    (the kernels read them when they run)."""
     _need_cuda("q_chunk", q_chunk)
     if q_chunk.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("q_chunk must be bfloat16 or float32")
@@ -588,12 +602,12 @@ def select_chunk(q_chunk: torch.Tensor, k_cache: torch.Tensor, prior_len: Sequen
             tuple(T.shape) != (B, H_kv, NKB) or tuple(lens.shape) != (B, H_kv):
         raise ValueError("qbar / kbar / scores / mask / T / lens shapes do not match")
     dt = _lib.CA_BF16 if q_chunk.dtype == torch.bfloat16 else _lib.CA_F32
-    st = _lib.lib().ca_select_chunk(
-        q_chunk.data_ptr(), k_cache.data_ptr(), dt, B, H_q, H_kv, C_max, L, D,
-        _host_ints("prior_len", prior_len, B), _host_ints("chunk_len", chunk_len, B),
+    fn, pr, ch = _select_lengths("ca_select_chunk", prior_len, chunk_len, B)
+    st = getattr(_lib.lib(), fn)(
+        q_chunk.data_ptr(), k_cache.data_ptr(), dt, B, H_q, H_kv, C_max, L, D, pr, ch,
         int(budget), int(local), qbar.data_ptr(), NQ, kbar.data_ptr(), NKB, scores.data_ptr(),
         mask.data_ptr(), T.data_ptr(), lens.data_ptr(), _stream_ptr(stream))
-    _lib.check(st, "ca_select_chunk")
+    _lib.check(st, fn)
 
 
 def append_select_chunk(k_new: torch.Tensor, v_new: torch.Tensor, q_chunk: torch.Tensor,
@@ -605,7 +619,9 @@ def append_select_chunk(k_new: torch.Tensor, v_new: torch.Tensor, q_chunk: torch
     """``append_kv`` then ``select_chunk`` in the selection's four launches
     (``ca_append_select_chunk``): the first launch also writes the chunk's keys
     and values (k_new, v_new [B, H_kv, C_max, D]) into the caches and pools the
-    new key blocks from them.  Same outputs as the two calls, bit for bit."""
+    new key blocks from them.  Same outputs as the two calls, bit for bit.
+    prior_len / chunk_len as device int32 [B] tensors use
+    ``ca_append_select_chunk_devlen``."""
     _need_cuda("k_new", k_new)
     if k_new.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("k_new must be bfloat16 or float32")
@@ -629,10 +645,10 @@ def append_select_chunk(k_new: torch.Tensor, v_new: torch.Tensor, q_chunk: torch
             tuple(T.shape) != (B, H_kv, NKB) or tuple(lens.shape) != (B, H_kv):
         raise ValueError("qbar / kbar / scores / mask / T / lens shapes do not match")
     dt = _lib.CA_BF16 if q_chunk.dtype == torch.bfloat16 else _lib.CA_F32
-    st = _lib.lib().ca_append_select_chunk(
+    fn, pr, ch = _select_lengths("ca_append_select_chunk", prior_len, chunk_len, B)
+    st = getattr(_lib.lib(), fn)(
         k_new.data_ptr(), v_new.data_ptr(), q_chunk.data_ptr(), k_cache.data_ptr(),
-        v_cache.data_ptr(), dt, B, H_q, H_kv, C_max, L, D,
-        _host_ints("prior_len", prior_len, B), _host_ints("chunk_len", chunk_len, B),
+        v_cache.data_ptr(), dt, B, H_q, H_kv, C_max, L, D, pr, ch,
         int(budget), int(local), qbar.data_ptr(), NQ, kbar.data_ptr(), NKB, scores.data_ptr(),
         mask.data_ptr(), T.data_ptr(), lens.data_ptr(), _stream_ptr(stream))
-    _lib.check(st, "ca_append_select_chunk")
+    _lib.check(st, fn)

@@ -40,6 +40,8 @@ EXPORTED = (
     "ca_block_mask_topk",
     "ca_select_chunk",
     "ca_append_select_chunk",
+    "ca_select_chunk_devlen",
+    "ca_append_select_chunk_devlen",
     "ca_status_string",
     "ca_last_hip_error",
 )
@@ -118,6 +120,14 @@ def _declare(lib):
                                            _i64, _i32, _i32p, _i32p, _i32, _i32, _vp, _i32, _vp,
                                            _i32, _vp, _vp, _vp, _vp, _vp]
     lib.ca_append_select_chunk.restype = _i32
+    lib.ca_select_chunk_devlen.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i32,
+                                           _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp,
+                                           _vp, _vp, _vp]
+    lib.ca_select_chunk_devlen.restype = _i32
+    lib.ca_append_select_chunk_devlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                                  _i32, _i32, _i64, _i32, _vp, _vp, _i32, _i32,
+                                                  _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
+    lib.ca_append_select_chunk_devlen.restype = _i32
     lib.ca_status_string.argtypes = [_i32]
     lib.ca_status_string.restype = ctypes.c_char_p
     lib.ca_last_hip_error.argtypes = []

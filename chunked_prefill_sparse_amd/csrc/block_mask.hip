@@ -30,6 +30,26 @@ constexpr int kSelectReplicas = 16;  // union bitmap copies of the fused selecti
 constexpr int kTopkStage = 8;        // score loads in flight per thread when staging keys
 constexpr int kTopkLdsMax = 15360;   // rows up to this many blocks stage keys in LDS (60 KiB)
 
+// Prior and chunk length of sequence b for the selection kernels: the host
+// values in SeqInfo, or (device-length calls, dl.prior != nullptr) the values
+// in device memory, checked here: lengths that are negative, not multiples of
+// 64, a chunk past dl.chunk_cap, or a total past dl.total_cap make an empty
+// chunk (no block pooled, no row selected, an empty table).
+__device__ __forceinline__ void sel_lengths(const SelLens& dl, const SeqInfo& seq, int b,
+                                            int& P, int& C) {
+  if (dl.prior == nullptr) {
+    P = seq.prior[b];
+    C = seq.chunk[b];
+    return;
+  }
+  const int P_ = dl.prior[b];
+  const int C_ = dl.chunk[b];
+  const bool ok = P_ >= 0 && C_ >= 0 && ((P_ | C_) & 63) == 0 && C_ <= dl.chunk_cap &&
+                  static_cast<int64_t>(P_) + C_ <= dl.total_cap;
+  P = ok ? P_ : 0;
+  C = ok ? C_ : 0;
+}
+
 // ---------------------------------------------------------------- pooling
 
 // How the pooling's threads hold one 64-row block (row stride D): thread tid
@@ -142,7 +162,7 @@ __global__ __launch_bounds__(kMaskThreads) void select_pool_kernel(
     int C_max, int NQ_max, int NKB_max, int span, int n_k, int n_q, int n_rep, SeqInfo seq,
     float* __restrict__ kbar, float* __restrict__ qbar, int32_t* __restrict__ T,
     const TIn* __restrict__ k_new, const TIn* __restrict__ v_new, TIn* __restrict__ k_cache,
-    TIn* __restrict__ v_cache) {
+    TIn* __restrict__ v_cache, SelLens dl) {
   __shared__ float part[kPoolPart<TIn, D>];
   int w = blockIdx.x;  // n_k = B * H_kv * span key blocks, n_q = B * H_q * span Q-blocks
   if (w < (kAppend ? 2 * n_k : n_k)) {
@@ -150,8 +170,10 @@ __global__ __launch_bounds__(kMaskThreads) void select_pool_kernel(
     if (is_v) w -= n_k;
     const int bg = w / span, y = w - bg * span;
     const int b = bg / H_kv;
-    const int kb = seq.prior[b] / 64 + y;
-    if (y >= seq.chunk[b] / 64) return;
+    int P, C;
+    sel_lengths(dl, seq, b, P, C);
+    const int kb = P / 64 + y;
+    if (y >= C / 64) return;
     const size_t cache_off = (static_cast<size_t>(bg) * L + static_cast<size_t>(kb) * 64) * D;
     if constexpr (kAppend) {
       const size_t new_off = (static_cast<size_t>(bg) * C_max + static_cast<size_t>(y) * 64) * D;
@@ -170,7 +192,9 @@ __global__ __launch_bounds__(kMaskThreads) void select_pool_kernel(
   if (w < n_q) {
     const int bh = w / span, y = w - bh * span;
     const int b = bh / H_q;
-    if (y >= seq.chunk[b] / 64) return;
+    int P, C;
+    sel_lengths(dl, seq, b, P, C);
+    if (y >= C / 64) return;
     pool_one_block<TIn, D>(Q + (static_cast<size_t>(bh) * C_max + static_cast<size_t>(y) * 64) * D,
                            qbar + (static_cast<size_t>(bh) * NQ_max + y) * D, part);
     return;
@@ -222,7 +246,7 @@ __device__ __forceinline__ void split_bf16x4(const float4 x, uint2& hi, uint2& l
 template <int D>
 __global__ __launch_bounds__(kMaskThreads) void block_scores_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int H_q, int H_kv,
-    int NQ_max, int NKB_max, SeqInfo seq, float* __restrict__ scores) {
+    int NQ_max, int NKB_max, SeqInfo seq, float* __restrict__ scores, SelLens dl) {
   constexpr int RB = 2 * D + 16;  // padded row stride of a bf16 tile (bytes)
   __shared__ __attribute__((aligned(16))) char Qh[kScoreTile * RB];
   __shared__ __attribute__((aligned(16))) char Ql[kScoreTile * RB];
@@ -232,8 +256,10 @@ __global__ __launch_bounds__(kMaskThreads) void block_scores_kernel(
   const int b = bg / H_kv;
   const int g = bg - b * H_kv;
   const int G = H_q / H_kv;
-  const int pblk = seq.prior[b] / 64;
-  const int nq = seq.chunk[b] / 64;
+  int P, C;
+  sel_lengths(dl, seq, b, P, C);
+  const int pblk = P / 64;
+  const int nq = C / 64;
   const int kb0 = static_cast<int>(blockIdx.y) * kScoreTile;
   const int r0 = static_cast<int>(blockIdx.z) * kScoreTile;
   const int n_rows = G * nq;
@@ -344,7 +370,7 @@ template <bool kUnion, bool kLds>
 __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
     const float* __restrict__ scores, int H_q, int NQ_max, int NKB_max, SeqInfo seq,
     int budget, int local, uint8_t* __restrict__ mask, int H_kv, int32_t* __restrict__ T,
-    int n_rep) {
+    int n_rep, SelLens dl) {
   extern __shared__ uint32_t keys[];  // kLds: NKB_max keys; then (kUnion) the row's bitmap
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh_prefix, sh_need, sh_bin;
@@ -356,8 +382,10 @@ __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   uint8_t* mrow = mask + row * NKB_max;
-  const int pblk = seq.prior[b] / 64;
-  const int nq = seq.chunk[b] / 64;
+  int P, C;
+  sel_lengths(dl, seq, b, P, C);
+  const int pblk = P / 64;
+  const int nq = C / 64;
   // union bitmap of this row's group (kUnion): words at the tail of T[b,g]
   const int nwords = (NKB_max + 31) >> 5;
   uint32_t* ubits = nullptr;
@@ -555,16 +583,17 @@ __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
 template <bool kUnion>
 void launch_topk(const float* scores, int B, int H_q, int NQ_max, int NKB_max, const SeqInfo& seq,
                  int budget, int local, uint8_t* mask, int H_kv, int32_t* T, int n_rep,
-                 hipStream_t stream) {
+                 const SelLens& dl, hipStream_t stream) {
   const dim3 grid(B * H_q * NQ_max);
   const size_t bitmap = kUnion ? static_cast<size_t>((NKB_max + 31) / 32) * sizeof(uint32_t) : 0;
   if (NKB_max <= kTopkLdsMax)  // keys, then the row's union bits
     hipLaunchKernelGGL((topk_mask_kernel<kUnion, true>), grid, dim3(kMaskThreads),
                        static_cast<size_t>(NKB_max) * sizeof(uint32_t) + bitmap, stream, scores,
-                       H_q, NQ_max, NKB_max, seq, budget, local, mask, H_kv, T, n_rep);
+                       H_q, NQ_max, NKB_max, seq, budget, local, mask, H_kv, T, n_rep, dl);
   else
     hipLaunchKernelGGL((topk_mask_kernel<kUnion, false>), grid, dim3(kMaskThreads), 0, stream,
-                       scores, H_q, NQ_max, NKB_max, seq, budget, local, mask, H_kv, T, n_rep);
+                       scores, H_q, NQ_max, NKB_max, seq, budget, local, mask, H_kv, T, n_rep,
+                       dl);
 }
 
 }  // namespace
@@ -598,17 +627,17 @@ namespace {
 
 hipError_t launch_scores(const float* qbar, const float* kbar, int B, int H_q, int H_kv,
                          int NQ_max, int NKB_max, int D, const SeqInfo& seq, int max_pblk,
-                         float* scores, hipStream_t stream) {
+                         float* scores, const SelLens& dl, hipStream_t stream) {
   if (max_pblk <= 0) return hipSuccess;
   const int ny = (max_pblk + kScoreTile - 1) / kScoreTile;
   const int nz = ((H_q / H_kv) * NQ_max + kScoreTile - 1) / kScoreTile;
   const dim3 grid(B * H_kv, ny, nz);
   if (D == 128)
     hipLaunchKernelGGL(block_scores_kernel<128>, grid, dim3(kMaskThreads), 0, stream, qbar, kbar,
-                       H_q, H_kv, NQ_max, NKB_max, seq, scores);
+                       H_q, H_kv, NQ_max, NKB_max, seq, scores, dl);
   else
     hipLaunchKernelGGL(block_scores_kernel<64>, grid, dim3(kMaskThreads), 0, stream, qbar, kbar,
-                       H_q, H_kv, NQ_max, NKB_max, seq, scores);
+                       H_q, H_kv, NQ_max, NKB_max, seq, scores, dl);
   return hipGetLastError();
 }
 
@@ -616,7 +645,7 @@ template <typename TIn>
 void launch_select_pool(const void* Q, const void* K, int B, int H_q, int H_kv, int C_max,
                         int64_t L, int D, const SeqInfo& seq, int span, float* qbar, int NQ_max,
                         float* kbar, int NKB_max, int32_t* T, int n_rep, const AppendSrc* app,
-                        hipStream_t stream) {
+                        const SelLens& dl, hipStream_t stream) {
   const int n_k = B * H_kv * span, n_q = B * H_q * span;
   const dim3 grid((app ? 2 * n_k : n_k) + n_q + B * H_kv);
   const TIn* k = static_cast<const TIn*>(K);
@@ -629,21 +658,21 @@ void launch_select_pool(const void* Q, const void* K, int B, int H_q, int H_kv, 
     if (D == 128)
       hipLaunchKernelGGL((select_pool_kernel<TIn, 128, true>), grid, dim3(kMaskThreads), 0,
                          stream, nullptr, q, H_q, H_kv, L, C_max, NQ_max, NKB_max, span, n_k, n_q,
-                         n_rep, seq, kbar, qbar, T, kn, vn, kc, vc);
+                         n_rep, seq, kbar, qbar, T, kn, vn, kc, vc, dl);
     else
       hipLaunchKernelGGL((select_pool_kernel<TIn, 64, true>), grid, dim3(kMaskThreads), 0,
                          stream, nullptr, q, H_q, H_kv, L, C_max, NQ_max, NKB_max, span, n_k, n_q,
-                         n_rep, seq, kbar, qbar, T, kn, vn, kc, vc);
+                         n_rep, seq, kbar, qbar, T, kn, vn, kc, vc, dl);
     return;
   }
   if (D == 128)
     hipLaunchKernelGGL((select_pool_kernel<TIn, 128, false>), grid, dim3(kMaskThreads), 0, stream,
                        k, q, H_q, H_kv, L, C_max, NQ_max, NKB_max, span, n_k, n_q, n_rep, seq,
-                       kbar, qbar, T, nullptr, nullptr, nullptr, nullptr);
+                       kbar, qbar, T, nullptr, nullptr, nullptr, nullptr, dl);
   else
     hipLaunchKernelGGL((select_pool_kernel<TIn, 64, false>), grid, dim3(kMaskThreads), 0, stream,
                        k, q, H_q, H_kv, L, C_max, NQ_max, NKB_max, span, n_k, n_q, n_rep, seq,
-                       kbar, qbar, T, nullptr, nullptr, nullptr, nullptr);
+                       kbar, qbar, T, nullptr, nullptr, nullptr, nullptr, dl);
 }
 
 }  // namespace
@@ -652,11 +681,12 @@ hipError_t launch_block_mask(const float* qbar, const float* kbar, int B, int H_
                              int NQ_max, int NKB_max, int D, const SeqInfo& seq, int max_pblk,
                              int budget, int local, float* scores, uint8_t* mask,
                              hipStream_t stream) {
+  const SelLens host{};  // host lengths
   const hipError_t e = launch_scores(qbar, kbar, B, H_q, H_kv, NQ_max, NKB_max, D, seq, max_pblk,
-                                     scores, stream);
+                                     scores, host, stream);
   if (e != hipSuccess) return e;
   launch_topk<false>(scores, B, H_q, NQ_max, NKB_max, seq, budget, local, mask, H_kv, nullptr, 1,
-                     stream);
+                     host, stream);
   return hipGetLastError();
 }
 
@@ -664,7 +694,7 @@ hipError_t launch_select_chunk(const void* Q, const void* K, int esz, int B, int
                                int C_max, int64_t L, int D, const SeqInfo& seq, int max_nq,
                                int max_pblk, int budget, int local, float* qbar, int NQ_max,
                                float* kbar, int NKB_max, float* scores, uint8_t* mask,
-                               int32_t* T, int32_t* len, const AppendSrc* app,
+                               int32_t* T, int32_t* len, const AppendSrc* app, const SelLens& dl,
                                hipStream_t stream) {
   // copies of the union bitmap the top-k rows spread their atomics over (as many
   // as the T row's tail holds, up to 16)
@@ -672,16 +702,17 @@ hipError_t launch_select_chunk(const void* Q, const void* K, int esz, int B, int
   const int n_rep = std::max(1, std::min(kSelectReplicas, NKB_max / nwords));
   if (esz == 2)
     launch_select_pool<__bf16>(Q, K, B, H_q, H_kv, C_max, L, D, seq, max_nq, qbar, NQ_max, kbar,
-                               NKB_max, T, n_rep, app, stream);
+                               NKB_max, T, n_rep, app, dl, stream);
   else
     launch_select_pool<float>(Q, K, B, H_q, H_kv, C_max, L, D, seq, max_nq, qbar, NQ_max, kbar,
-                              NKB_max, T, n_rep, app, stream);
+                              NKB_max, T, n_rep, app, dl, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_scores(qbar, kbar, B, H_q, H_kv, NQ_max, NKB_max, D, seq, max_pblk, scores, stream);
+  e = launch_scores(qbar, kbar, B, H_q, H_kv, NQ_max, NKB_max, D, seq, max_pblk, scores, dl,
+                    stream);
   if (e != hipSuccess) return e;
   launch_topk<true>(scores, B, H_q, NQ_max, NKB_max, seq, budget, local, mask, H_kv, T, n_rep,
-                    stream);
+                    dl, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_union_compact(B * H_kv, NKB_max, n_rep, T, len, stream);

@@ -569,14 +569,16 @@ CA_EXPORT ca_status ca_block_mask_topk(const float* qbar, const float* kbar, int
 
 namespace {
 
-// ca_select_chunk and ca_append_select_chunk: checks, then the launches (app:
-// the chunk's new rows to append, or null).
+// ca_select_chunk, ca_append_select_chunk and their device-length forms:
+// checks, then the launches (app: the chunk's new rows to append, or null;
+// dev_lengths: prior_len and chunk_len are device int32 [B], checked by the
+// kernels).
 ca_status select_chunk_common(const void* Q_chunk, const void* K_cache, ca_dtype dtype, int B,
                               int H_q, int H_kv, int C_max, int64_t L, int D,
                               const int32_t* prior_len, const int32_t* chunk_len, int budget,
                               int local, float* qbar, int NQ_max, float* kbar, int NKB_max,
                               float* scores, uint8_t* mask, int32_t* T, int32_t* len,
-                              const ca::AppendSrc* app, hipStream_t stream) {
+                              const ca::AppendSrc* app, bool dev_lengths, hipStream_t stream) {
   if (!Q_chunk || !K_cache || !prior_len || !chunk_len || !qbar || !kbar || !scores || !mask ||
       !T || !len)
     return CA_ERR_NULL;
@@ -593,17 +595,32 @@ ca_status select_chunk_common(const void* Q_chunk, const void* K_cache, ca_dtype
   ca::SeqInfo seq;
   memset(&seq, 0, sizeof(seq));
   int max_pblk = 0, max_nq = 0;
-  for (int b = 0; b < B; ++b) {
-    const int64_t P = prior_len[b], C = chunk_len[b];
-    if (P < 0 || C < 0 || C > C_max || C > static_cast<int64_t>(NQ_max) * CA_BLOCK || P + C > L ||
-        P + C > static_cast<int64_t>(NKB_max) * CA_BLOCK)
-      return CA_ERR_SHAPE;
-    if (P % CA_BLOCK != 0 || C % CA_BLOCK != 0) return CA_ERR_UNSUPPORTED;
-    seq.prior[b] = static_cast<int32_t>(P);
-    seq.chunk[b] = static_cast<int32_t>(C);
-    seq.order[b] = b;
-    max_pblk = std::max(max_pblk, static_cast<int>(P / CA_BLOCK));
-    max_nq = std::max(max_nq, static_cast<int>(C / CA_BLOCK));
+  ca::SelLens dl;
+  if (dev_lengths) {
+    if ((reinterpret_cast<uintptr_t>(prior_len) & 3) != 0 ||
+        (reinterpret_cast<uintptr_t>(chunk_len) & 3) != 0)
+      return CA_ERR_UNSUPPORTED;
+    dl.prior = prior_len;
+    dl.chunk = chunk_len;
+    dl.chunk_cap = static_cast<int>(std::min<int64_t>(C_max, static_cast<int64_t>(NQ_max) * CA_BLOCK));
+    dl.total_cap = std::min<int64_t>(L, static_cast<int64_t>(NKB_max) * CA_BLOCK);
+    for (int b = 0; b < B; ++b) seq.order[b] = b;
+    // the largest extents the caps allow: the grids do not depend on the lengths
+    max_nq = dl.chunk_cap / CA_BLOCK;
+    max_pblk = static_cast<int>(dl.total_cap / CA_BLOCK);
+  } else {
+    for (int b = 0; b < B; ++b) {
+      const int64_t P = prior_len[b], C = chunk_len[b];
+      if (P < 0 || C < 0 || C > C_max || C > static_cast<int64_t>(NQ_max) * CA_BLOCK ||
+          P + C > L || P + C > static_cast<int64_t>(NKB_max) * CA_BLOCK)
+        return CA_ERR_SHAPE;
+      if (P % CA_BLOCK != 0 || C % CA_BLOCK != 0) return CA_ERR_UNSUPPORTED;
+      seq.prior[b] = static_cast<int32_t>(P);
+      seq.chunk[b] = static_cast<int32_t>(C);
+      seq.order[b] = b;
+      max_pblk = std::max(max_pblk, static_cast<int>(P / CA_BLOCK));
+      max_nq = std::max(max_nq, static_cast<int>(C / CA_BLOCK));
+    }
   }
   const int64_t n_pool =
       static_cast<int64_t>(B) * (H_q + (app ? 2 : 1) * H_kv) * max_nq + B * H_kv;
@@ -611,7 +628,7 @@ ca_status select_chunk_common(const void* Q_chunk, const void* K_cache, ca_dtype
   return hip_status(ca::launch_select_chunk(Q_chunk, K_cache, dtype == CA_BF16 ? 2 : 4, B, H_q,
                                             H_kv, C_max, L, D, seq, max_nq, max_pblk, budget,
                                             local, qbar, NQ_max, kbar, NKB_max, scores, mask, T,
-                                            len, app, stream));
+                                            len, app, dl, stream));
 }
 
 }  // namespace
@@ -626,7 +643,19 @@ CA_EXPORT ca_status ca_select_chunk(const void* Q_chunk, const void* K_cache, ca
                                     int32_t* len, hipStream_t stream) {
   return select_chunk_common(Q_chunk, K_cache, dtype, B, H_q, H_kv, C_max, L, D, prior_len,
                              chunk_len, budget, local, qbar, NQ_max, kbar, NKB_max, scores, mask,
-                             T, len, nullptr, stream);
+                             T, len, nullptr, false, stream);
+}
+
+CA_EXPORT ca_status ca_select_chunk_devlen(const void* Q_chunk, const void* K_cache,
+                                           ca_dtype dtype, int B, int H_q, int H_kv, int C_max,
+                                           int64_t L, int D, const int32_t* prior_len,
+                                           const int32_t* chunk_len, int budget, int local,
+                                           float* qbar, int NQ_max, float* kbar, int NKB_max,
+                                           float* scores, uint8_t* mask, int32_t* T,
+                                           int32_t* len, hipStream_t stream) {
+  return select_chunk_common(Q_chunk, K_cache, dtype, B, H_q, H_kv, C_max, L, D, prior_len,
+                             chunk_len, budget, local, qbar, NQ_max, kbar, NKB_max, scores, mask,
+                             T, len, nullptr, true, stream);
 }
 
 CA_EXPORT ca_status ca_append_select_chunk(const void* K_new, const void* V_new,
@@ -642,7 +671,21 @@ CA_EXPORT ca_status ca_append_select_chunk(const void* K_new, const void* V_new,
   const ca::AppendSrc app{K_new, V_new, K_cache, V_cache};
   return select_chunk_common(Q_chunk, K_cache, dtype, B, H_q, H_kv, C_max, L, D, prior_len,
                              chunk_len, budget, local, qbar, NQ_max, kbar, NKB_max, scores, mask,
-                             T, len, &app, stream);
+                             T, len, &app, false, stream);
+}
+
+CA_EXPORT ca_status ca_append_select_chunk_devlen(
+    const void* K_new, const void* V_new, const void* Q_chunk, void* K_cache, void* V_cache,
+    ca_dtype dtype, int B, int H_q, int H_kv, int C_max, int64_t L, int D,
+    const int32_t* prior_len, const int32_t* chunk_len, int budget, int local, float* qbar,
+    int NQ_max, float* kbar, int NKB_max, float* scores, uint8_t* mask, int32_t* T, int32_t* len,
+    hipStream_t stream) {
+  if (!K_new || !V_new || !V_cache) return CA_ERR_NULL;
+  if (!aligned16(K_new) || !aligned16(V_new) || !aligned16(V_cache)) return CA_ERR_UNSUPPORTED;
+  const ca::AppendSrc app{K_new, V_new, K_cache, V_cache};
+  return select_chunk_common(Q_chunk, K_cache, dtype, B, H_q, H_kv, C_max, L, D, prior_len,
+                             chunk_len, budget, local, qbar, NQ_max, kbar, NKB_max, scores, mask,
+                             T, len, &app, true, stream);
 }
 
 }  // extern "C"

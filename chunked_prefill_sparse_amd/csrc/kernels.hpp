@@ -200,11 +200,23 @@ struct AppendSrc {
   void* k_cache;      // [B, H_kv, L, D], written at rows [prior, prior + chunk)
   void* v_cache;
 };
+// Device-length selection calls: prior and chunk lengths in device int32 [B]
+// arrays, checked by the kernels against chunk_cap and total_cap (prior and
+// total_cap = min(L, 64 * NKB_max), chunk_cap = min(C_max, 64 * NQ_max)); a
+// default-constructed SelLens (prior == nullptr) means the host values in
+// SeqInfo.  With device lengths, max_nq and max_pblk are the bounds those caps
+// allow, so the grids do not depend on the lengths.
+struct SelLens {
+  const int32_t* prior = nullptr;
+  const int32_t* chunk = nullptr;
+  int chunk_cap = 0;
+  int64_t total_cap = 0;
+};
 hipError_t launch_select_chunk(const void* Q, const void* K, int esz, int B, int H_q, int H_kv,
                                int C_max, int64_t L, int D, const SeqInfo& seq, int max_nq,
                                int max_pblk, int budget, int local, float* qbar, int NQ_max,
                                float* kbar, int NKB_max, float* scores, uint8_t* mask,
-                               int32_t* T, int32_t* len, const AppendSrc* app,
+                               int32_t* T, int32_t* len, const AppendSrc* app, const SelLens& dl,
                                hipStream_t stream);
 
 // Block-mask producer: pooled scores, then per-row top-k selection.

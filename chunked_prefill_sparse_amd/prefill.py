@@ -20,7 +20,8 @@ from typing import Optional
 import torch
 
 from . import (append_kv, append_select_chunk, balanced_workspace_size, block_mask_topk,
-               build_union_tables, chunk_attention, pool_blocks, select_chunk)
+               build_union_tables, chunk_attention, chunk_attention_devlen, pool_blocks,
+               select_chunk)
 from ._lib import CA_BLOCK
 
 
@@ -71,6 +72,10 @@ class ChunkedPrefill:
         self.out = torch.empty((B, H_q, C, D), dtype=k_cache.dtype, device=dev)
         self.balanced = bool(balanced)
         self.fused_append = bool(fused_append)
+        # the chunk offset and length in device memory, for the steps whose
+        # graph serves every chunk (capture_chunk)
+        self.prior_dev = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.chunk_dev = torch.full((B,), C, dtype=torch.int32, device=dev)
         self.ws = None
         if self.balanced:
             self.ws = torch.empty(balanced_workspace_size(B, H_q, H_kv, C, D), dtype=torch.uint8,
@@ -250,6 +255,35 @@ class ChunkedPrefill:
                 self.step_dense(q, p, lens[i], out=o, k_chunk=kc, v_chunk=vc)
             else:
                 self.step(q, p, out=o, k_chunk=kc, v_chunk=vc)
+
+    def set_prior(self, prior: int) -> None:
+        """Chunk offset read by ``step_devlen`` and by graphs from ``capture_chunk``."""
+        self.prior_dev.fill_(int(prior))
+
+    def step_devlen(self, q_chunk: torch.Tensor, k_chunk: torch.Tensor, v_chunk: torch.Tensor,
+                    out=None, stream=None) -> torch.Tensor:
+        """``step`` with the chunk's keys and values, taking the chunk offset
+        from device memory (``set_prior``): ``ca_append_select_chunk_devlen``
+        then ``ca_chunk_attention_devlen``.  No argument depends on the offset,
+        so the same calls, captured once, serve every chunk.  Same results as
+        ``step`` bit for bit (plain attention, not balanced)."""
+        out = self.out if out is None else out
+        append_select_chunk(k_chunk, v_chunk, q_chunk, self.k, self.v, self.prior_dev,
+                            self.chunk_dev, self.budget, self.local, self.qbar, self.kbar,
+                            self.scores, self.mask, self.T, self.lens, stream=stream)
+        return chunk_attention_devlen(q_chunk, self.k, self.v, self.T, self.lens, self.prior_dev,
+                                      self.chunk_dev, self.scale, out=out, stream=stream)
+
+    def capture_chunk(self, q_buf: torch.Tensor, k_buf: torch.Tensor, v_buf: torch.Tensor,
+                      out=None) -> torch.cuda.CUDAGraph:
+        """One HIP graph of ``step_devlen`` on fixed input buffers (q_buf
+        [B, H_q, C, D], k_buf / v_buf [B, H_kv, C, D]) that serves every chunk of
+        every prompt this object holds: write the chunk's queries, keys and
+        values into the buffers and its offset with ``set_prior``, then replay."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step_devlen(q_buf, k_buf, v_buf, out=out)
+        return g
 
     def dense_lens(self, prior: int) -> torch.Tensor:
         n = (prior + self.C) // CA_BLOCK

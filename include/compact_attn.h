@@ -602,6 +602,40 @@ CA_EXPORT ca_status ca_append_select_chunk(const void* K_new, const void* V_new,
                                            float* scores, uint8_t* mask, int32_t* T,
                                            int32_t* len, hipStream_t stream);
 
+/*
+ * ca_select_chunk_devlen, ca_append_select_chunk_devlen -- ca_select_chunk and
+ * ca_append_select_chunk with prior_len and chunk_len in device memory
+ * (problem statement of the technical summaries: the selection runs again for
+ * every chunk as the cache grows; with the lengths in device memory, one
+ * captured HIP graph of a chunk's selection, or of its whole step with
+ * ca_chunk_attention_devlen, serves every chunk offset: between replays only
+ * the device lengths and the inputs' contents change).
+ *
+ * prior_len,  device int32 [B], 4-byte aligned (else CA_ERR_UNSUPPORTED),
+ * chunk_len   read by the kernels when they run and checked there: lengths
+ *             that are negative, not multiples of 64, a chunk past
+ *             min(C_max, 64*NQ_max) or a total past min(L, 64*NKB_max) make
+ *             that sequence an empty chunk (nothing appended, pooled or
+ *             selected; its mask rows 0 and its tables empty).
+ * The grids are sized for the largest lengths those bounds allow.  With valid
+ * lengths the outputs equal those of the host-length calls bit for bit.
+ * Every other argument and the errors as for ca_select_chunk and
+ * ca_append_select_chunk.
+ */
+CA_EXPORT ca_status ca_select_chunk_devlen(const void* Q_chunk, const void* K_cache,
+                                           ca_dtype dtype, int B, int H_q, int H_kv, int C_max,
+                                           int64_t L, int D, const int32_t* prior_len,
+                                           const int32_t* chunk_len, int budget, int local,
+                                           float* qbar, int NQ_max, float* kbar, int NKB_max,
+                                           float* scores, uint8_t* mask, int32_t* T,
+                                           int32_t* len, hipStream_t stream);
+CA_EXPORT ca_status ca_append_select_chunk_devlen(
+    const void* K_new, const void* V_new, const void* Q_chunk, void* K_cache, void* V_cache,
+    ca_dtype dtype, int B, int H_q, int H_kv, int C_max, int64_t L, int D,
+    const int32_t* prior_len, const int32_t* chunk_len, int budget, int local, float* qbar,
+    int NQ_max, float* kbar, int NKB_max, float* scores, uint8_t* mask, int32_t* T, int32_t* len,
+    hipStream_t stream);
+
 /* Human-readable name of a status code (static string; never NULL). */
 CA_EXPORT const char* ca_status_string(ca_status s);
 

@@ -167,6 +167,28 @@ int main() {
                                     (uint8_t*)FAKE, (int32_t*)FAKE, (int32_t*)FAKE,
                                     0) == CA_ERR_UNSUPPORTED);
       EXPECT(strcmp(stub::last.what, "") == 0);
+      // device lengths: nothing read on the host, grids from the caps
+      // (chunk_cap = min(C_max, 64 NQ_max) = 256, total_cap = min(L, 64 NKB_max) = 4096)
+      const int32_t* const dp = reinterpret_cast<const int32_t*>(static_cast<uintptr_t>(0x5000));
+      EXPECT(ca_append_select_chunk_devlen(kn, FAKE, FAKE, FAKE, vc, CA_BF16, 2, 8, 2, 256, 4096,
+                                           128, dp, dp + 2, 8, 2, (float*)FAKE, 4, (float*)FAKE,
+                                           64, (float*)FAKE, (uint8_t*)FAKE, (int32_t*)FAKE,
+                                           (int32_t*)FAKE, 0) == CA_OK);
+      EXPECT(strcmp(stub::last.what, "append_select_devlen") == 0 && stub::last.ints[0] == 4 &&
+             stub::last.ints[1] == 64 && stub::last.ints[8] == 256 &&
+             stub::last.ints[9] == 4096 && stub::last.seq.prior[1] == 0);
+      EXPECT(ca_select_chunk_devlen(FAKE, FAKE, CA_BF16, 2, 8, 2, 200, 3000, 128, dp, dp + 2, 8,
+                                    2, (float*)FAKE, 4, (float*)FAKE, 64, (float*)FAKE,
+                                    (uint8_t*)FAKE, (int32_t*)FAKE, (int32_t*)FAKE, 0) == CA_OK);
+      EXPECT(strcmp(stub::last.what, "select_devlen") == 0 && stub::last.ints[0] == 3 &&
+             stub::last.ints[8] == 200 && stub::last.ints[9] == 3000);
+      stub::last = stub::Record{};
+      EXPECT(ca_select_chunk_devlen(FAKE, FAKE, CA_BF16, 2, 8, 2, 256, 4096, 128,
+                                    reinterpret_cast<const int32_t*>(static_cast<uintptr_t>(0x5002)),
+                                    dp, 8, 2, (float*)FAKE, 4, (float*)FAKE, 64, (float*)FAKE,
+                                    (uint8_t*)FAKE, (int32_t*)FAKE, (int32_t*)FAKE,
+                                    0) == CA_ERR_UNSUPPORTED);
+      EXPECT(strcmp(stub::last.what, "") == 0);
     }
     // no-alloc split: the partials go to the static array (its stand-in address),
     // same layout; a split past the array's size is refused before any launch

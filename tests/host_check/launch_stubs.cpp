@@ -130,9 +130,12 @@ hipError_t launch_select_chunk(const void*, const void*, int esz, int B, int H_q
                                int C_max, int64_t L, int D, const SeqInfo& seq, int max_nq,
                                int max_pblk, int budget, int local, float*, int NQ_max, float*,
                                int NKB_max, float*, uint8_t*, int32_t*, int32_t*,
-                               const AppendSrc* app, hipStream_t) {
+                               const AppendSrc* app, const SelLens& dl, hipStream_t) {
   stub::last = stub::Record{};
-  stub::last.what = app ? "append_select" : "select";
+  stub::last.what = dl.prior ? (app ? "append_select_devlen" : "select_devlen")
+                             : (app ? "append_select" : "select");
+  stub::last.ints[8] = dl.chunk_cap;
+  stub::last.ints[9] = static_cast<int>(dl.total_cap);
   if (app) {
     stub::last.ptrs[0] = const_cast<void*>(app->k_new);
     stub::last.ptrs[1] = app->v_cache;

@@ -1,5 +1,6 @@
 """GPU parity of the device-length calls (ca_build_union_tables_devlen,
-ca_chunk_attention_devlen), through the C ABI.
+ca_chunk_attention_devlen, ca_select_chunk_devlen, ca_append_select_chunk_devlen),
+through the C ABI.
 
 * With valid lengths they equal the host-length calls bit for bit (same
   kernels) and the oracle within the parity bounds.
@@ -9,6 +10,8 @@ ca_chunk_attention_devlen), through the C ABI.
   a prompt with only device memory changed between replays (lengths, the
   chunk's queries and mask), matches eager host-length calls bit for bit on
   every replay, with eager library work and synchronisations in between.
+* The same for a whole prefill step (append + selection + attention): one
+  graph replayed for every chunk of a prompt equals ChunkedPrefill.step.
 """
 import numpy as np
 import pytest
@@ -16,6 +19,7 @@ import torch
 
 import gen
 import chunked_prefill_sparse_amd as ca
+from chunked_prefill_sparse_amd.prefill import ChunkedPrefill
 from oracle import chunk_attention_ref, union_tables_ref
 from tests.gpu_util import (F32_MAX_ABS, Dev, check_lse, compare_bf16, oracle_full, say,
                             to_np)
@@ -183,4 +187,124 @@ def test_one_graph_replayed_over_chunk_offsets():
             Or, lser = chunk_attention_ref(q32, k32, v32, Tr, lr, priors, chunks, s.scale)
             compare_bf16(to_np(got[2]), Or, f"chunk {c} O")
             check_lse(to_np(got[3]), lser, f"chunk {c} lse")
+    del g
+
+
+def _select_buffers(B, H_q, H_kv, NQ, NKB, D, kbar0):
+    return (kbar0.clone(),
+            torch.zeros((B, H_q, NQ, D), dtype=torch.float32, device="cuda"),
+            torch.zeros((B, H_q, NQ, NKB), dtype=torch.float32, device="cuda"),
+            torch.full((B, H_q, NQ, NKB), 7, dtype=torch.uint8, device="cuda"),
+            torch.full((B, H_kv, NKB), 12345, dtype=torch.int32, device="cuda"),
+            torch.full((B, H_kv), -3, dtype=torch.int32, device="cuda"))
+
+
+@pytest.mark.parametrize("append", [False, True])
+def test_select_devlen_matches_host_lengths(append):
+    # ca_select_chunk_devlen / ca_append_select_chunk_devlen against the host-length
+    # calls on a ragged batch, bit for bit; then sequence 1 given lengths that break
+    # the limits (a chunk not a multiple of 64, a total past the cache) selects
+    # nothing and appends nothing, and sequence 0 is unchanged
+    B, H_kv, G, D, C_max, L = 3, 2, 4, 128, 256, 4096
+    H_q = H_kv * G
+    prior, chunk = [3072, 1024, 0], [256, 192, 128]
+    gq = torch.Generator().manual_seed(211)
+    k0 = torch.randn((B, H_kv, L, D), generator=gq).to(torch.bfloat16).cuda()
+    v0 = torch.randn((B, H_kv, L, D), generator=gq).to(torch.bfloat16).cuda()
+    k_new = torch.randn((B, H_kv, C_max, D), generator=gq).to(torch.bfloat16).cuda()
+    v_new = torch.randn((B, H_kv, C_max, D), generator=gq).to(torch.bfloat16).cuda()
+    q = torch.randn((B, H_q, C_max, D), generator=gq).to(torch.bfloat16).cuda()
+    NQ, NKB = C_max // 64, L // 64
+    kbar0 = torch.zeros((B, H_kv, NKB, D), dtype=torch.float32, device="cuda")
+    ca.pool_blocks(k0, [0] * B, [p // 64 for p in prior], out=kbar0)
+
+    def run(pr, ch):
+        kc, vc = k0.clone(), v0.clone()
+        bufs = _select_buffers(B, H_q, H_kv, NQ, NKB, D, kbar0)
+        kbar, qbar, scores, mask, T, lens = bufs
+        if append:
+            ca.append_select_chunk(k_new, v_new, q, kc, vc, pr, ch, 8, 2, qbar, kbar, scores,
+                                   mask, T, lens)
+        else:
+            ca.select_chunk(q, kc, pr, ch, 8, 2, qbar, kbar, scores, mask, T, lens)
+        torch.cuda.synchronize()
+        return (kc, vc) + bufs
+
+    names = ("k_cache", "v_cache", "kbar", "qbar", "scores", "mask", "T", "lens")
+    say(f"select devlen vs host lengths, append={append}")
+    host = run(prior, chunk)
+    dev = run(_dev(prior), _dev(chunk))
+    for name, a, b in zip(names, dev, host):
+        assert torch.equal(a, b), name
+    # sequence 1 with broken lengths: empty; sequence 0 unchanged
+    for bad in ((1024, 96), (4032, 128)):
+        say(f"  sequence 1 given prior {bad[0]} chunk {bad[1]}")
+        pr, ch = list(prior), list(chunk)
+        pr[1], ch[1] = bad
+        got = run(_dev(pr), _dev(ch))
+        kc, vc, kbar, qbar, scores, mask, T, lens = got
+        assert int(lens[1].max()) == 0 and bool((T[1] == -1).all())
+        assert bool((mask[1] == 0).all())
+        assert torch.equal(kc[1], k0[1]) and torch.equal(vc[1], v0[1])
+        assert torch.equal(kbar[1], kbar0[1])
+        for name, a, b in zip(names, got, host):
+            if name == "scores":
+                nq, pb = chunk[0] // 64, prior[0] // 64
+                assert torch.equal(a[0, :, :nq, :pb], b[0, :, :nq, :pb]), name
+            else:
+                assert torch.equal(a[0], b[0]), name
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_prefill_one_graph_serves_every_chunk(dtype):
+    # ChunkedPrefill.capture_chunk: one graph of the whole step (append + selection +
+    # attention, device chunk offset), captured once and replayed for every chunk of
+    # prefill_small with the chunk's inputs copied into its buffers, into caches that
+    # hold NaN past the appended rows; every chunk's output, mask and tables equal
+    # ChunkedPrefill.step's (host offsets, resident prompt) bit for bit
+    s = gen.make_prefill_stream("prefill_small")
+    k_full, v_full = s.k.to(dtype).cuda(), s.v.to(dtype).cuda()
+    ref = ChunkedPrefill(k_full, v_full, s.H_q, s.C, budget=4, local=2)
+    qs = [s.q_chunk(c).to(dtype).cuda() for c in range(s.n_chunks)]
+    priors = [c * s.C for c in range(s.n_chunks)]
+    want = []
+    for q, p in zip(qs, priors):
+        o = ref.step(q, p).clone()
+        want.append((o, ref.mask.clone(), ref.T.clone(), ref.lens.clone()))
+    kc = torch.full_like(k_full, float("nan"))
+    vc = torch.full_like(v_full, float("nan"))
+    drv = ChunkedPrefill(kc, vc, s.H_q, s.C, budget=4, local=2)
+    q_buf = torch.empty_like(qs[0])
+    k_buf = torch.empty((1, s.H_kv, s.C, s.D), dtype=dtype, device="cuda")
+    v_buf = torch.empty_like(k_buf)
+    out = torch.empty_like(qs[0])
+
+    def load(c):
+        q_buf.copy_(qs[c])
+        k_buf.copy_(k_full[:, :, priors[c]:priors[c] + s.C])
+        v_buf.copy_(v_full[:, :, priors[c]:priors[c] + s.C])
+        drv.set_prior(priors[c])
+
+    # eager device-offset steps first (they also warm up before the capture)
+    for c in range(s.n_chunks):
+        load(c)
+        drv.step_devlen(q_buf, k_buf, v_buf, out=out)
+        torch.cuda.synchronize()
+        assert torch.equal(out, want[c][0]), f"eager chunk {c}"
+    kc.fill_(float("nan"))
+    vc.fill_(float("nan"))
+    g = drv.capture_chunk(q_buf, k_buf, v_buf, out=out)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        kc.fill_(float("nan"))
+        vc.fill_(float("nan"))
+        for c in range(s.n_chunks):
+            load(c)
+            say(f"one-chunk graph, {dtype}, pass {rep}, replay for chunk {c}")
+            g.replay()
+            torch.cuda.synchronize()
+            for name, a, b in zip(("O", "mask", "T", "lens"), (out, drv.mask, drv.T, drv.lens),
+                                  want[c]):
+                assert torch.equal(a, b), f"pass {rep} chunk {c}: {name}"
+        assert torch.equal(kc, k_full) and torch.equal(vc, v_full)
     del g
