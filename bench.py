@@ -581,6 +581,22 @@ def prefill_leg(stream, budget=32, local=8, overlap=True):
         for c in range(s.n_chunks):
             drv_bal.step(qs[c], priors[c], k_chunk=kv[c][0], v_chunk=kv[c][1])
 
+    # one graph of a whole chunk step, captured once and replayed for every chunk:
+    # each chunk's inputs are copied into the graph's buffers first
+    drv_dl = ChunkedPrefill(k, v, s.H_q, s.C, budget=budget, local=local)
+    q_buf, k_buf, v_buf = torch.empty_like(qs[0]), torch.empty_like(kv[0][0]), \
+        torch.empty_like(kv[0][1])
+
+    def load_chunk(c):
+        q_buf.copy_(qs[c])
+        k_buf.copy_(kv[c][0])
+        v_buf.copy_(kv[c][1])
+        drv_dl.set_prior(priors[c])
+
+    def run_loads():
+        for c in range(s.n_chunks):
+            load_chunk(c)
+
     def run_overlap():  # each chunk's append and selection on a second stream, ahead
         drv.run(qs, priors, kv_chunks=kv, overlap=True)
 
@@ -616,9 +632,19 @@ def prefill_leg(stream, budget=32, local=8, overlap=True):
     g_bal = drv_bal.capture(qs, priors, kv_chunks=kv)
     g_ov = drv.capture(qs, priors, kv_chunks=kv, overlap=True) if overlap else None
     g_ovb = drv_bal.capture(qs, priors, kv_chunks=kv, overlap=True) if overlap else None
+    load_chunk(0)
+    drv_dl.step_devlen(q_buf, k_buf, v_buf)
+    g_chunk = drv_dl.capture_chunk(q_buf, k_buf, v_buf)
+
+    def run_chunk_graph():
+        for c in range(s.n_chunks):
+            load_chunk(c)
+            g_chunk.replay()
+
     g_sparse.replay()
     g_dense.replay()
     g_bal.replay()
+    run_chunk_graph()
     if overlap:
         g_ov.replay()
         g_ovb.replay()
@@ -628,6 +654,8 @@ def prefill_leg(stream, budget=32, local=8, overlap=True):
     gsel_sep_ms = statistics.median(timed(g_select_sep.replay) for _ in range(reps))
     gappsel_ms = statistics.median(timed(g_appsel.replay) for _ in range(reps))
     gd_ms = statistics.median(timed(g_dense.replay) for _ in range(reps))
+    gchunk_ms = statistics.median(timed(run_chunk_graph) for _ in range(reps))
+    loads_ms = statistics.median(timed(run_loads) for _ in range(reps))
     if overlap:
         gov_ms = statistics.median(timed(g_ov.replay) for _ in range(reps))
         govb_ms = statistics.median(timed(g_ovb.replay) for _ in range(reps))
@@ -655,7 +683,11 @@ def prefill_leg(stream, budget=32, local=8, overlap=True):
                    select_separate_ms=round(gsel_sep_ms, 3),
                    dense_total_ms=round(gd_ms, 3), x_vs_dense=round(gd_ms / gs_ms, 3),
                    balanced_total_ms=round(gb_ms, 3),
-                   balanced_x_vs_dense=round(gd_ms / gb_ms, 3)),
+                   balanced_x_vs_dense=round(gd_ms / gb_ms, 3),
+                   # one graph of a chunk step (device chunk offset) replayed per chunk,
+                   # with the copies of each chunk's Q, K, V into its input buffers
+                   one_chunk_graph_total_ms=round(gchunk_ms, 3),
+                   one_chunk_graph_input_copies_ms=round(loads_ms, 3)),
         # append + selection on a second stream, ahead of the attention
         overlap=dict(total_ms=round(ov_ms, 3), x_vs_dense=round(dense_ms / ov_ms, 3),
                      balanced_total_ms=round(ovb_ms, 3),
@@ -681,8 +713,10 @@ def prefill_leg(stream, budget=32, local=8, overlap=True):
             f"{ov_ms:.2f} ms -> x{dense_ms / ov_ms:.2f}, balanced {ovb_ms:.2f} ms; as graphs "
             f"{gov_ms:.2f} ms -> x{gd_ms / gov_ms:.2f}, balanced {govb_ms:.2f} ms -> "
             f"x{gd_ms / govb_ms:.2f}")
+    log(f"prefill_128k, one graph of a chunk step replayed per chunk: {gchunk_ms:.2f} ms, of "
+        f"which copying each chunk's inputs into its buffers {loads_ms:.2f} ms")
     del qs, k, v, kv, drv, drv_bal, g_sparse, g_select, g_appsel, g_select_sep, g_dense, g_bal
-    del g_ov, g_ovb
+    del g_ov, g_ovb, g_chunk, drv_dl, q_buf, k_buf, v_buf
     torch.cuda.empty_cache()
     return r
 
