@@ -721,6 +721,48 @@ def prefill_leg(stream, budget=32, local=8, overlap=True):
     return r
 
 
+def select_profile_leg(calls, chunk=32, budget=32, local=8):
+    """For counter runs of the fused append + selection: the 128K prefill stream
+    appended and selected up to chunk `chunk` (prior 2048 * chunk), then
+    `calls` more ca_append_select_chunk calls for that chunk, each printed with
+    the algorithmic bytes of its four kernels (the counters of the last calls are
+    the ones to read)."""
+    import torch
+    import gen
+    from chunked_prefill_sparse_amd.prefill import ChunkedPrefill
+    s = gen.make_prefill_stream("prefill_128k")
+    k_src, v_src = s.k.cuda(), s.v.cuda()
+    k = torch.zeros((1, s.H_kv, s.L, s.D), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(k)
+    drv = ChunkedPrefill(k, v, s.H_q, s.C, budget=budget, local=local)
+
+    def kv(c):
+        return (k_src[:, :, c * s.C:(c + 1) * s.C].contiguous(),
+                v_src[:, :, c * s.C:(c + 1) * s.C].contiguous())
+
+    for c in range(chunk):
+        kc, vc = kv(c)
+        drv.append_select(kc, vc, s.q_chunk(c).cuda(), c * s.C)
+    kc, vc = kv(chunk)
+    q = s.q_chunk(chunk).cuda()
+    torch.cuda.synchronize()
+    P, C, D, Hq, Hkv = chunk * s.C, s.C, s.D, s.H_q, s.H_kv
+    pblk, nq, nkb = P // 64, C // 64, s.L // 64
+    nwords = (nkb + 31) // 32
+    alg = {  # bytes each kernel must move at least (B = 1)
+        "select_pool (with the append)": 2 * (2 * Hkv * C * D * 2) + Hq * C * D * 2
+        + (Hkv + Hq) * nq * D * 4 + Hkv * 16 * nwords * 4,
+        "block_scores": Hq * nq * D * 4 + Hkv * pblk * D * 4 + Hq * nq * pblk * 4,
+        "topk_mask": Hq * nq * pblk * 4 + Hq * nq * nkb,
+        "union_compact": Hkv * 16 * nwords * 4 + Hkv * nkb * 4 + Hkv * 4,
+    }
+    log(f"select profile: chunk {chunk}, prior {P}, algorithmic bytes per kernel {alg}")
+    for i in range(calls):
+        drv.append_select(kc, vc, q, P)
+        torch.cuda.synchronize()
+        log(f"append_select call {i}")
+
+
 # --------------------------------------------------------------------------- main
 
 
@@ -766,7 +808,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--reps", type=int, default=100, help="per-kernel timed calls")
-    ap.add_argument("--profile", choices=["attn", "union", "copy", "compact", "prefill"],
+    ap.add_argument("--profile", choices=["attn", "union", "copy", "compact", "prefill", "select"],
                     default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
@@ -814,6 +856,9 @@ def main():
 
     if args.profile == "prefill":
         prefill_leg(stream, overlap=False)
+        return
+    if args.profile == "select":
+        select_profile_leg(args.steps)
         return
     if args.prefill_only:
         print(json.dumps(prefill_leg(stream)))
