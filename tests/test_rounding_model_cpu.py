@@ -1,15 +1,17 @@
 """The per-element rounding bounds used by the GPU parity tests, checked on the
 CPU against emulations of the GPU arithmetic (no GPU).
 
-Attention outputs (``check_bf16_rounding``):
-
-The emulation takes the kernel's roundings one by one: logits and
-exponentials in fp32, each probability rounded to bf16 (round to nearest
-even) for the P.V product, the numerator and the denominator (of the
-unrounded probabilities) summed in fp32, and the quotient rounded to bf16.
-Its outputs must sit inside ``check_bf16_rounding``'s bound on every
+Attention outputs (``check_bf16_rounding``): the emulation takes the kernel's
+roundings one by one: logits and exponentials in fp32, each probability
+rounded to bf16 (round to nearest even) for the P.V product, the numerator and
+the denominator (of the unrounded probabilities) summed in fp32, and the
+quotient rounded to bf16.  Its outputs must sit inside the bound on every
 element, for smooth and for peaky rows; a planted mistake (one P.V term
 dropped, or a denominator 1% off) must not.
+
+Block scores of the mask producer (``score_bound``): products of the bf16
+hi / lo parts of fp32 values must sit inside the bound; with a cross term
+dropped they must not.
 """
 import numpy as np
 import pytest
