@@ -199,21 +199,23 @@ def _select_buffers(B, H_q, H_kv, NQ, NKB, D, kbar0):
             torch.full((B, H_kv), -3, dtype=torch.int32, device="cuda"))
 
 
-@pytest.mark.parametrize("append", [False, True])
-def test_select_devlen_matches_host_lengths(append):
+@pytest.mark.parametrize("append,D,dtype", [(False, 128, torch.bfloat16),
+                                            (True, 128, torch.bfloat16),
+                                            (True, 64, torch.float32)])
+def test_select_devlen_matches_host_lengths(append, D, dtype):
     # ca_select_chunk_devlen / ca_append_select_chunk_devlen against the host-length
     # calls on a ragged batch, bit for bit; then sequence 1 given lengths that break
     # the limits (a chunk not a multiple of 64, a total past the cache) selects
     # nothing and appends nothing, and sequence 0 is unchanged
-    B, H_kv, G, D, C_max, L = 3, 2, 4, 128, 256, 4096
+    B, H_kv, G, C_max, L = 3, 2, 4, 256, 4096
     H_q = H_kv * G
     prior, chunk = [3072, 1024, 0], [256, 192, 128]
     gq = torch.Generator().manual_seed(211)
-    k0 = torch.randn((B, H_kv, L, D), generator=gq).to(torch.bfloat16).cuda()
-    v0 = torch.randn((B, H_kv, L, D), generator=gq).to(torch.bfloat16).cuda()
-    k_new = torch.randn((B, H_kv, C_max, D), generator=gq).to(torch.bfloat16).cuda()
-    v_new = torch.randn((B, H_kv, C_max, D), generator=gq).to(torch.bfloat16).cuda()
-    q = torch.randn((B, H_q, C_max, D), generator=gq).to(torch.bfloat16).cuda()
+    k0 = torch.randn((B, H_kv, L, D), generator=gq).to(dtype).cuda()
+    v0 = torch.randn((B, H_kv, L, D), generator=gq).to(dtype).cuda()
+    k_new = torch.randn((B, H_kv, C_max, D), generator=gq).to(dtype).cuda()
+    v_new = torch.randn((B, H_kv, C_max, D), generator=gq).to(dtype).cuda()
+    q = torch.randn((B, H_q, C_max, D), generator=gq).to(dtype).cuda()
     NQ, NKB = C_max // 64, L // 64
     kbar0 = torch.zeros((B, H_kv, NKB, D), dtype=torch.float32, device="cuda")
     ca.pool_blocks(k0, [0] * B, [p // 64 for p in prior], out=kbar0)
@@ -231,7 +233,7 @@ def test_select_devlen_matches_host_lengths(append):
         return (kc, vc) + bufs
 
     names = ("k_cache", "v_cache", "kbar", "qbar", "scores", "mask", "T", "lens")
-    say(f"select devlen vs host lengths, append={append}")
+    say(f"select devlen vs host lengths, append={append}, D={D}, {dtype}")
     host = run(prior, chunk)
     dev = run(_dev(prior), _dev(chunk))
     for name, a, b in zip(names, dev, host):
